@@ -1,0 +1,275 @@
+/*
+ * ORACLE -- test infrastructure only.
+ *
+ * A plain, slow, obviously correct CPU implementation of the indexer -> Top-K ->
+ * sparse MLA attention path, in double precision. Only the test suite, the smoke
+ * check and the benchmark's CPU-baseline leg load it; the product path never does.
+ * It shares no code, header or table with the HIP library.
+ *
+ * It follows the unfused decode step that the page "Day 0 Inference Adaptation
+ * and Performance Optimization for Hybrid Sparse Attention LLMs" lays out in its
+ * section "Operator Fusion and Multi-Stream Scheduling": score every historical
+ * position against the index cache, combine the heads with their weights, take
+ * the Top-K positions, gather those rows of the main KV cache through the paging,
+ * and run softmax attention over them. Fusion (same page; also "Rapid Adaptation
+ * and Inference Optimization", section IV) moves intermediates out of memory but
+ * does not change what is computed, so this unfused form is the definition.
+ *
+ * Readings fixed here (the pages leave them open):
+ *  - score[j,s] = sigma_s * sum_h w[j,h] * max(0, q[j,h,:] . k_s), with sigma_s the
+ *    per-token fp32 scale of an fp8 index cache and 1 for a bf16 one; q.k uses the
+ *    exact values of the stored bf16 / e4m3fn elements ("low-precision cache
+ *    de-quantized to higher precision", "Rapid Adaptation ...", section V).
+ *  - query j at position t_j sees positions 0..t_j that are also < n_b.
+ *  - Top-K orders by (score descending, position ascending), keeps the first
+ *    min(K, row length), and lists them by ascending position, -1 padded.
+ *  - the latent row is 576 wide; keys use all 576 columns, values the first 512.
+ *  - an empty selection gives a zero output and lse = -inf.
+ *
+ * Every function returns 0 on success and a negative value on a bad argument.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define SIA_ORACLE_PAGE 64
+
+/* bfloat16: the upper 16 bits of an IEEE binary32. */
+double oracle_bf16_value(uint16_t bits) {
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* OCP 8-bit float E4M3 ("FN": no infinities, only S.1111.111 is NaN).
+ * Normal: (-1)^s * 2^(e-7) * (1 + m/8); subnormal (e = 0): (-1)^s * 2^-6 * m/8. */
+double oracle_e4m3fn_value(uint8_t code) {
+    int s = code >> 7, e = (code >> 3) & 0xF, m = code & 0x7;
+    double v;
+    if (e == 0xF && m == 0x7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, -6);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+int oracle_decode_bf16(const uint16_t *bits, double *out, int64_t n) {
+    if (!bits || !out || n < 0) return -1;
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_bf16_value(bits[i]);
+    return 0;
+}
+
+int oracle_decode_e4m3fn(const uint8_t *codes, double *out, int64_t n) {
+    if (!codes || !out || n < 0) return -1;
+    for (int64_t i = 0; i < n; i++) out[i] = oracle_e4m3fn_value(codes[i]);
+    return 0;
+}
+
+/* Physical row of logical position s of sequence b, or -1 if unmapped. */
+static int64_t phys_row(const int32_t *page_table, int32_t max_pages, int32_t b, int64_t s) {
+    int64_t p = s / SIA_ORACLE_PAGE;
+    if (p >= max_pages) return -1;
+    int32_t page = page_table[(int64_t)b * max_pages + p];
+    if (page < 0) return -1;
+    return (int64_t)page * SIA_ORACLE_PAGE + (s % SIA_ORACLE_PAGE);
+}
+
+/* Visible row length of query j: positions 0..t_j that are < n_b. */
+static int64_t row_length(int32_t t, int32_t n_b) {
+    int64_t r = (int64_t)t + 1;
+    if (r > n_b) r = n_b;
+    return r < 0 ? 0 : r;
+}
+
+/*
+ * Steps 1-2 of the unfused decode step: relevance per head, then the
+ * head-weighted sum.
+ *   k_dtype: 0 = bf16 rows (uint16 bits), 1 = e4m3fn rows (uint8 codes) with
+ *            k_scale[num_pages*64] per-token scales.
+ *   scores[j*ld + s] for s < row_len[j]; -inf for s in [row_len[j], ld).
+ */
+int oracle_indexer_scores(int32_t num_q, const int32_t *q_seq, const int32_t *q_pos,
+                          int32_t batch, const int32_t *seq_lens, const int32_t *page_table,
+                          int32_t max_pages, int64_t num_pages, const void *k_pool,
+                          int32_t k_dtype, const float *k_scale, int32_t dim,
+                          const uint16_t *q_idx, const float *w, int32_t heads,
+                          double *scores, int64_t ld, int32_t *row_len) {
+    if (num_q < 0 || !q_seq || !q_pos || !seq_lens || !page_table || !k_pool || !q_idx ||
+        !w || !scores || !row_len || dim <= 0 || heads <= 0 || batch <= 0)
+        return -1;
+    if (k_dtype != 0 && k_dtype != 1) return -1;
+    if (k_dtype == 1 && !k_scale) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t j = 0; j < num_q; j++) {
+        int32_t b = q_seq[j];
+        double *row = scores + (int64_t)j * ld;
+        for (int64_t s = 0; s < ld; s++) row[s] = -INFINITY;
+        row_len[j] = 0;
+        if (b < 0 || b >= batch) { bad = 1; continue; }
+        int64_t n = row_length(q_pos[j], seq_lens[b]);
+        if (n > ld) { bad = 1; continue; }
+        row_len[j] = (int32_t)n;
+        double *qd = (double *)malloc(sizeof(double) * (size_t)heads * dim);
+        double *kd = (double *)malloc(sizeof(double) * (size_t)dim);
+        for (int64_t i = 0; i < (int64_t)heads * dim; i++)
+            qd[i] = oracle_bf16_value(q_idx[(int64_t)j * heads * dim + i]);
+        for (int64_t s = 0; s < n; s++) {
+            int64_t r = phys_row(page_table, max_pages, b, s);
+            if (r < 0 || r >= num_pages * SIA_ORACLE_PAGE) { bad = 1; continue; }
+            double sigma = 1.0;
+            if (k_dtype == 0) {
+                const uint16_t *kr = (const uint16_t *)k_pool + r * dim;
+                for (int32_t d = 0; d < dim; d++) kd[d] = oracle_bf16_value(kr[d]);
+            } else {
+                const uint8_t *kr = (const uint8_t *)k_pool + r * dim;
+                for (int32_t d = 0; d < dim; d++) kd[d] = oracle_e4m3fn_value(kr[d]);
+                sigma = (double)k_scale[r];
+            }
+            double acc = 0.0;
+            for (int32_t h = 0; h < heads; h++) {
+                const double *qh = qd + (int64_t)h * dim;
+                double a = 0.0; /* relevance of head h: q_h . k_s */
+                for (int32_t d = 0; d < dim; d++) a += qh[d] * kd[d];
+                acc += (double)w[(int64_t)j * heads + h] * (a > 0.0 ? a : 0.0);
+            }
+            row[s] = sigma * acc;
+        }
+        free(qd);
+        free(kd);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Total order of the selection: higher score first, then lower position.
+ * NaN ranks below every number; -0.0 equals +0.0. */
+typedef struct { double v; int32_t s; } cand_t;
+
+static int rank_cmp(const void *pa, const void *pb) {
+    const cand_t *a = (const cand_t *)pa, *b = (const cand_t *)pb;
+    int an = isnan(a->v), bn = isnan(b->v);
+    if (an != bn) return an ? 1 : -1;
+    if (!an && a->v != b->v) return a->v > b->v ? -1 : 1;
+    return (a->s > b->s) - (a->s < b->s);
+}
+
+static int pos_cmp(const void *pa, const void *pb) {
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/*
+ * Step 3: Top-K of each row. Row j has candidates 0..row_len[j]-1 with values
+ * scores[j*ld + s]. Writes out_idx[j*K + i] (ascending position, -1 padded) and,
+ * if out_score is not NULL, the matching scores (-inf for padding).
+ */
+int oracle_topk(int32_t num_q, const double *scores, int64_t ld, const int32_t *row_len,
+                int32_t K, int32_t *out_idx, double *out_score) {
+    if (num_q < 0 || !scores || !row_len || !out_idx || K <= 0) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t j = 0; j < num_q; j++) {
+        int64_t n = row_len[j];
+        int32_t *oi = out_idx + (int64_t)j * K;
+        for (int32_t i = 0; i < K; i++) oi[i] = -1;
+        if (out_score)
+            for (int32_t i = 0; i < K; i++) out_score[(int64_t)j * K + i] = -INFINITY;
+        if (n < 0 || n > ld) { bad = 1; continue; }
+        if (n == 0) continue;
+        cand_t *c = (cand_t *)malloc(sizeof(cand_t) * (size_t)n);
+        for (int64_t s = 0; s < n; s++) {
+            c[s].v = scores[(int64_t)j * ld + s];
+            c[s].s = (int32_t)s;
+        }
+        qsort(c, (size_t)n, sizeof(cand_t), rank_cmp);
+        int64_t m = n < K ? n : K;
+        for (int64_t i = 0; i < m; i++) oi[i] = c[i].s;
+        qsort(oi, (size_t)m, sizeof(int32_t), pos_cmp);
+        if (out_score)
+            for (int64_t i = 0; i < m; i++)
+                out_score[(int64_t)j * K + i] = scores[(int64_t)j * ld + oi[i]];
+        free(c);
+    }
+    return bad ? -2 : 0;
+}
+
+/*
+ * Steps 4-5: gather the selected latent rows through the page table and run
+ * softmax attention over them, per head a:
+ *   z_i = sm_scale * (q[j,a,:] . c_i)        over all dim_kv columns
+ *   p_i = exp(z_i - max z) / sum exp(z - max z)
+ *   out[j,a,:] = sum_i p_i c_i[0:d_v],  lse[j,a] = max z + ln sum exp(z - max z)
+ * Entries of idx that are < 0 are padding and ignored; idx holds logical
+ * positions of sequence q_seq[j].
+ */
+int oracle_sparse_mla(int32_t num_q, const int32_t *q_seq, int32_t batch,
+                      const int32_t *page_table, int32_t max_pages, int64_t num_pages,
+                      const uint16_t *kv_pool, int32_t dim_kv, int32_t d_v,
+                      const uint16_t *q, int32_t heads, const int32_t *idx, int32_t K,
+                      double sm_scale, double *out, double *lse) {
+    if (num_q < 0 || !q_seq || !page_table || !kv_pool || !q || !idx || !out || !lse ||
+        dim_kv <= 0 || d_v <= 0 || d_v > dim_kv || heads <= 0 || K <= 0 || batch <= 0)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t j = 0; j < num_q; j++) {
+        int32_t b = q_seq[j];
+        double *oj = out + (int64_t)j * heads * d_v;
+        for (int64_t i = 0; i < (int64_t)heads * d_v; i++) oj[i] = 0.0;
+        for (int32_t a = 0; a < heads; a++) lse[(int64_t)j * heads + a] = -INFINITY;
+        if (b < 0 || b >= batch) { bad = 1; continue; }
+        /* gather */
+        int32_t m = 0;
+        double *c = (double *)malloc(sizeof(double) * (size_t)K * dim_kv);
+        for (int32_t i = 0; i < K; i++) {
+            int32_t s = idx[(int64_t)j * K + i];
+            if (s < 0) continue;
+            int64_t r = phys_row(page_table, max_pages, b, s);
+            if (r < 0 || r >= num_pages * SIA_ORACLE_PAGE) { bad = 1; continue; }
+            for (int32_t d = 0; d < dim_kv; d++)
+                c[(int64_t)m * dim_kv + d] = oracle_bf16_value(kv_pool[r * dim_kv + d]);
+            m++;
+        }
+        if (m == 0) { free(c); continue; }
+        double *qa = (double *)malloc(sizeof(double) * (size_t)dim_kv);
+        double *z = (double *)malloc(sizeof(double) * (size_t)m);
+        for (int32_t a = 0; a < heads; a++) {
+            for (int32_t d = 0; d < dim_kv; d++)
+                qa[d] = oracle_bf16_value(q[((int64_t)j * heads + a) * dim_kv + d]);
+            double zmax = -INFINITY;
+            for (int32_t i = 0; i < m; i++) {
+                double dot = 0.0;
+                for (int32_t d = 0; d < dim_kv; d++) dot += qa[d] * c[(int64_t)i * dim_kv + d];
+                z[i] = sm_scale * dot;
+                if (z[i] > zmax) zmax = z[i];
+            }
+            double l = 0.0;
+            for (int32_t i = 0; i < m; i++) {
+                z[i] = exp(z[i] - zmax);
+                l += z[i];
+            }
+            double *o = oj + (int64_t)a * d_v;
+            for (int32_t i = 0; i < m; i++) {
+                double p = z[i] / l;
+                for (int32_t d = 0; d < d_v; d++) o[d] += p * c[(int64_t)i * dim_kv + d];
+            }
+            lse[(int64_t)j * heads + a] = zmax + log(l);
+        }
+        free(qa);
+        free(z);
+        free(c);
+    }
+    return bad ? -2 : 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
