@@ -1,0 +1,165 @@
+"""Throughput of the sparse path (indexer + Top-K + sparse MLA attention) on one
+MI355X.
+
+Default workload: speculative decode, 64 sequences x 131072 positions, two draft
+tokens per sequence (128 query tokens), fp8 index-K (64 heads x 128) with
+per-token scales, Top-2048, bf16 latent KV (576/512) with 128 attention heads,
+page size 64, shuffled page tables. One step = one fused indexer + Top-K pass
+and one sparse attention pass over every query token, with all inputs resident
+in HBM. Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", default="spec_decode_128k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def algorithmic_bytes(wl, idx):
+    """Bytes the method must move per step: every visible index-K row (+ scale)
+    of each sequence once, each selected latent row once per sequence (rows
+    shared by a sequence's draft tokens count once), queries, weights, outputs
+    and the page-table entries used."""
+    import torch
+    s = wl.spec
+    lens = wl.seq_lens.long()
+    es = 1 if s.idx_fp8 else 2
+    row_idx = s.dim_idx * es + (4 if s.idx_fp8 else 0)
+    idx_bytes = int(lens.sum()) * row_idx
+    # latent rows: union of the selected positions of each sequence's queries
+    B = int(lens.numel())
+    q_seq = wl.q_seq.long()
+    key = (q_seq[:, None] * (1 << 32) + idx.long())[idx >= 0]
+    uniq = int(torch.unique(key).numel())
+    kv_bytes = uniq * 576 * 2
+    Q = wl.num_q
+    q_bytes = Q * (s.heads_idx * s.dim_idx * 2 + s.heads_idx * 4 + s.heads_attn * 576 * 2)
+    out_bytes = Q * (s.heads_attn * 512 * 2 + s.topk * 4)
+    pt_bytes = int(((lens + 63) // 64).sum()) * 4
+    return dict(index_k=idx_bytes, latent=kv_bytes, queries=q_bytes, outputs=out_bytes,
+                page_table=pt_bytes, total=idx_bytes + kv_bytes + q_bytes + out_bytes + pt_bytes,
+                indexer=idx_bytes + Q * (s.heads_idx * s.dim_idx * 2 + s.heads_idx * 4) + pt_bytes
+                + Q * s.topk * 4)
+
+
+def cpu_baseline(wl_gpu, s):
+    """The oracle on a bounded sample of the same workload (one sequence)."""
+    import oracle
+    import workloads as W
+    seq = 0
+    sub = W.subset(wl_gpu, [seq], device="cpu")
+    oracle.build(force=False)
+    t0 = time.perf_counter()
+    oracle.run(sub, attention=True)
+    dt = time.perf_counter() - t0
+    nq = sub.num_q
+    return {"value": nq / dt, "unit": "query tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{nq} query tokens (sequence {seq}, {int(sub.seq_lens[0])} positions) of "
+                      f"{s.name}: indexer, Top-K and attention, {dt:.2f} s"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+
+    import indexer_top_sparse_02_amd as sia
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = W.spec(a.config)
+    if s.prefill:
+        raise SystemExit("bench times the decode workloads; prefill is timed by tests")
+    wl = W.make(s, device=dev)
+    group = s.q_per_seq
+    maxv = int(torch.minimum(wl.q_pos.long() + 1, wl.seq_lens.long()[wl.q_seq.long()]).max())
+    ws_i = sia.new_workspace(sia.indexer_workspace_size(wl.page_table, wl.seq_lens, wl.idx_k,
+                                                        wl.idx_scale, wl.q_seq, wl.q_pos,
+                                                        s.heads_idx, s.topk, group=group,
+                                                        max_visible=maxv), dev)
+    ws_a = sia.new_workspace(sia.mla_workspace_size(wl.num_q, s.heads_attn, s.topk), dev)
+    idx = torch.empty((wl.num_q, s.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.num_q, s.heads_attn, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.num_q, s.heads_attn), dtype=torch.float32, device=dev)
+
+    def indexer():
+        sia.sparse_indexer_topk(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq,
+                                wl.q_pos, wl.q_idx, wl.w, s.topk, group=group, max_visible=maxv,
+                                out_idx=idx, workspace=ws_i)
+
+    def attention():
+        sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx,
+                                 s.sm_scale, out=out, lse=lse, workspace=ws_a)
+
+    for _ in range(a.warmup):
+        indexer()
+        attention()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for e0, e1, e2 in ev:
+        e0.record()
+        indexer()
+        e1.record()
+        attention()
+        e2.record()
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / a.steps
+    idx_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / a.steps
+    att_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / a.steps
+    by = algorithmic_bytes(wl, idx)
+    step_gbs = by["total"] / (ms * 1e-3) / 1e9
+    idx_gbs = by["indexer"] / (idx_ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode query tokens/s at 128K context (indexer + Top-K + sparse MLA attention)",
+        "value": wl.num_q / (ms * 1e-3),
+        "unit": "query tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8-e4m3fn index cache, bf16 MFMA (fp32 accumulate), bf16 latent KV",
+        "data": "synthetic (seeded N(0,1) caches and queries, shuffled page tables)",
+        "config": {"workload": s.name, "batch": s.batch, "context": s.ctx_hi,
+                   "query_tokens": wl.num_q, "indexer_heads": s.heads_idx, "index_dim": s.dim_idx,
+                   "topk": s.topk, "attention_heads": s.heads_attn, "page_size": 64},
+        "hbm_gbs_step": step_gbs,
+        "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
+        "algorithmic_bytes": by,
+        "roofline": {"bound": "hbm", "kernel": "sparse_indexer_topk (indexer split + top-k merge)",
+                     "achieved": idx_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": idx_gbs / PEAK_HBM_GBS, "traffic": None},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, s)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

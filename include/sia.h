@@ -1,0 +1,219 @@
+/*
+ * sia.h -- C ABI of the sparse-indexer / Top-K / sparse-MLA-attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The library implements the two-stage "filter-then-compute" sparse attention
+ * path of hybrid-attention LLMs:
+ *
+ *   stage 1  sparse_indexer_topk   -- a lightweight indexer scores every visible
+ *            historical position against the query by reading the paged index-K
+ *            cache directly, combines its heads with per-token head weights and
+ *            keeps the Top-K positions, all in one fused pass that writes only
+ *            the selected indices ("Rapid Adaptation and Inference Optimization:
+ *            Key Engineering Practices for Day0 LLM Support", section 4.1
+ *            "Indexer Fusion"; "Day0 Inference Adaptation and Performance
+ *            Optimization for New-Architecture LLMs", section 3.1 "Fused
+ *            Indexer").
+ *   stage 2  sparse_mla_attention -- gathers only the selected rows of the paged
+ *            latent (MLA) KV cache and runs softmax attention over them
+ *            ("Rapid Adaptation ...", section 4.2 "Sparse Attention
+ *            Computation"; "Day0 ... for a New Hybrid-Attention LLM
+ *            Architecture", section 2.2 "Sparse Index Attention Module").
+ *
+ * Indexer score (the pages say only "scores ... aggregates multi-head scores
+ * with weights"; this library fixes the formula):
+ *   score[j,s] = sigma_s * sum_h w[j,h] * max(0, q[j,h,:] . k_s)
+ * where k_s is the exact value of the stored index-K row and sigma_s its fp32
+ * per-token scale (fp8 cache) or 1 (bf16 cache). Query j at absolute position
+ * t_j in sequence b sees positions s with s <= t_j and s < n_b. Top-K keeps the
+ * first min(K, visible) positions in the order (score descending, position
+ * ascending) and lists them by ascending position, padding with -1.
+ *
+ * Conventions for every entry point:
+ *  - Pointers in the descriptors and arguments are DEVICE pointers unless the
+ *    field says "host". The caller owns every buffer; the library never
+ *    allocates, frees or synchronizes; work is enqueued on `stream`
+ *    (a hipStream_t, NULL = the default stream).
+ *  - Arguments are validated on the host before anything is enqueued. A bad
+ *    argument returns a negative sia_status, sets sia_last_error() and launches
+ *    nothing. A failed launch returns SIA_ERR_HIP.
+ *  - Device data that the host cannot see (page ids, sequence ids of queries,
+ *    positions) is bounds-checked by the kernels: an out-of-range page or
+ *    sequence id is never dereferenced; the affected query yields -1 indices
+ *    (stage 1) or a zero output (stage 2) and a bit is set in the status word
+ *    at the start of the workspace, readable with sia_read_device_status().
+ *  - Paged caches: row r of physical page p sits at
+ *    rows + ((size_t)p * page_size + r) * dim * element_size; the page size is
+ *    64. Logical position s of sequence b lives on physical page
+ *    page_table[b * max_pages + s / 64], row s % 64. Both caches share one
+ *    page table.
+ *  - Inputs are never written.
+ */
+#ifndef SIA_H
+#define SIA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SIA_OK = 0,
+    SIA_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shapes */
+    SIA_ERR_UNSUPPORTED = -2, /* valid but not built: head count, dim, dtype, page size */
+    SIA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the size query says */
+    SIA_ERR_HIP = -4          /* a HIP runtime call failed */
+} sia_status;
+
+typedef enum {
+    SIA_BF16 = 0,         /* bfloat16 */
+    SIA_FP8_E4M3FN = 1    /* OCP float8 E4M3 (max 448, no infinities) */
+} sia_dtype;
+
+/* Page table shared by the index-K cache and the latent KV cache. */
+typedef struct {
+    const int32_t *page_table; /* device [batch, max_pages]; physical page ids, -1 = unused */
+    const int32_t *seq_lens;   /* device [batch]; n_b, positions 0..n_b-1 are valid */
+    int32_t batch;
+    int32_t max_pages;         /* row stride of page_table; n_b <= 64 * max_pages */
+    int32_t page_size;         /* must be 64 */
+} sia_page_table;
+
+/* One paged cache: [num_pages, page_size, dim] rows (+ fp8 per-token scales). */
+typedef struct {
+    const void *rows;          /* device [num_pages, 64, dim] elements of `dtype` */
+    const float *scale;        /* device [num_pages, 64]; required for SIA_FP8_E4M3FN, else NULL */
+    int64_t num_pages;
+    int32_t dim;
+    int32_t dtype;             /* sia_dtype */
+} sia_paged_cache;
+
+/* The query tokens of one call. */
+typedef struct {
+    int32_t num_q;
+    const int32_t *q_seq;      /* device [num_q]; sequence id b_j in [0, batch) */
+    const int32_t *q_pos;      /* device [num_q]; absolute position t_j >= 0 */
+    int32_t group;             /* host; queries [g*group, (g+1)*group) belong to one sequence.
+                                  1 is always valid. 2 for two draft tokens per sequence;
+                                  a prefill chunk of one sequence may pass its length. Larger
+                                  groups let one pass over the cache serve several queries. */
+    int32_t max_visible;       /* host; >= max_j min(t_j + 1, n_{b_j}); sizes the launch. A query
+                                  whose visible row is longer is not scored past this bound and
+                                  sets SIA_DEVSTATUS_ROW_TOO_LONG. */
+} sia_queries;
+
+/* Bits of the device status word (first 4 bytes of every workspace). */
+#define SIA_DEVSTATUS_BAD_SEQ 1u        /* q_seq out of [0, batch) */
+#define SIA_DEVSTATUS_BAD_PAGE 2u       /* page id out of [0, num_pages) for a visible position */
+#define SIA_DEVSTATUS_ROW_TOO_LONG 4u   /* visible row longer than max_visible */
+#define SIA_DEVSTATUS_BAD_INDEX 8u      /* stage 2: idx entry >= n_b */
+
+/* Scheduling of long causal rows (prefill) over the compute units. */
+typedef enum {
+    SIA_SCHED_AUTO = -1,     /* library choice (SIA_SCHED_HEAVY_FIRST) */
+    SIA_SCHED_NAIVE = 0,     /* one workgroup per query tile, in tile order */
+    SIA_SCHED_HEAVY_FIRST = 1, /* persistent workgroups take tiles longest-row first */
+    SIA_SCHED_ZIGZAG = 2     /* workgroup i takes tiles i and T-1-i (head paired with tail) */
+} sia_sched;
+
+/* ------------------------------------------------------------------ stage 1 */
+
+/* Bytes of workspace sparse_indexer_topk / sparse_indexer_scores need for these
+ * shapes (always >= 256). Returns 0 if the arguments are invalid. */
+size_t sia_indexer_workspace_size(const sia_page_table *pt, const sia_paged_cache *index_k,
+                                  const sia_queries *qs, int32_t heads, int32_t topk);
+
+/*
+ * Fused indexer + Top-K.
+ *   q_idx     device bf16 [num_q, heads, dim]   indexer query heads (dim = index_k->dim)
+ *   w         device fp32 [num_q, heads]        per-token head weights
+ *   topk      K >= 1
+ *   out_idx   device int32 [num_q, topk]        selected logical positions, ascending, -1 padded
+ *   out_score device fp32 [num_q, topk] or NULL scores of out_idx entries (-inf for padding)
+ *   sched     sia_sched for long causal rows; results do not depend on it
+ * Supported: heads in {4, 8, 16, 32, 64}, dim in {64, 128}, index_k dtype bf16 or
+ * fp8 e4m3fn, page size 64.
+ */
+int sparse_indexer_topk(const sia_page_table *pt, const sia_paged_cache *index_k,
+                        const sia_queries *qs, const void *q_idx, const float *w,
+                        int32_t heads, int32_t topk, int32_t *out_idx, float *out_score,
+                        int32_t sched, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Test hook: the indexer's scores without selection, computed by the same device
+ * code the fused pass uses, so that selection can be checked on identical
+ * scores. scores: device fp32 [num_q, ld]; entry s of row j holds the score of
+ * position s for s < min(t_j + 1, n_b), -inf for the rest of [0, ld).
+ * Requires ld >= max_visible.
+ */
+int sparse_indexer_scores(const sia_page_table *pt, const sia_paged_cache *index_k,
+                          const sia_queries *qs, const void *q_idx, const float *w,
+                          int32_t heads, float *scores, int64_t ld, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Bytes of workspace sparse_topk_from_scores needs. */
+size_t sia_topk_workspace_size(int32_t num_q, int32_t max_row_len, int32_t topk);
+
+/*
+ * Test hook: Top-K of given score rows with the device selection the fused pass
+ * uses. Row j has candidates 0..row_len[j]-1 (device int32 [num_q], each
+ * <= max_row_len <= ld). Same output convention as sparse_indexer_topk.
+ */
+int sparse_topk_from_scores(const float *scores, int64_t ld, const int32_t *row_len,
+                            int32_t num_q, int32_t max_row_len, int32_t topk,
+                            int32_t *out_idx, float *out_score, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ stage 2 */
+
+/* Bytes of workspace sparse_mla_attention needs (always >= 256). */
+size_t sia_mla_workspace_size(const sia_queries *qs, int32_t heads, int32_t d_v, int32_t topk);
+
+/*
+ * Sparse MLA attention over the selected rows of the latent KV cache.
+ *   kv        latent cache, dtype bf16, dim 576 (512 latent + 64 rope)
+ *   q         device bf16 [num_q, heads, 576]
+ *   d_v       value width: the first d_v columns of each row (512)
+ *   idx       device int32 [num_q, topk]; logical positions of sequence q_seq[j],
+ *             entries < 0 are skipped (any order; duplicates count twice)
+ *   sm_scale  softmax scale applied to q . c
+ *   out       device bf16 [num_q, heads, d_v]: sum_i softmax_i(sm_scale q.c_i) c_i[0:d_v]
+ *   lse       device fp32 [num_q, heads] or NULL: natural-log sum-exp of the logits
+ * Only num_q and q_seq of `qs` are read (q_pos may be NULL).
+ * An empty selection gives out = 0 and lse = -inf.
+ * Supported: heads a multiple of 16 up to 128, kv dim 576, d_v 512.
+ */
+int sparse_mla_attention(const sia_page_table *pt, const sia_paged_cache *kv,
+                         const sia_queries *qs, const void *q, int32_t heads, int32_t d_v,
+                         const int32_t *idx, int32_t topk, float sm_scale, void *out,
+                         float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------------------------ misc */
+
+/*
+ * Zigzag pairing of S equal shards over S/2 workers: worker i takes shards i and
+ * S-1-i, so that with a cost growing linearly along a causal sequence every
+ * worker carries the same load ("Day0 ... for a New Hybrid-Attention LLM
+ * Architecture", section 4.3, Zigzag Load Balancing). Host function; the
+ * prefill scheduler's SIA_SCHED_ZIGZAG mode uses the same mapping on the
+ * device. out: host int32 [S]; out[2i], out[2i+1] = the shards of worker i (an
+ * odd S leaves the middle shard alone on the last worker: out[S-1] = S/2).
+ */
+int sia_zigzag_assign(int32_t num_shards, int32_t *out);
+
+/* Zero the device status word of a workspace (enqueued on stream). */
+int sia_clear_device_status(void *workspace, void *stream);
+/* Synchronize `stream` and read the device status word (SIA_DEVSTATUS_* bits). */
+int sia_read_device_status(const void *workspace, void *stream, uint32_t *status);
+
+/* Message for the last non-OK status returned on this thread. */
+const char *sia_last_error(void);
+/* Library version, major*10000 + minor*100 + patch. */
+int sia_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SIA_H */

@@ -1,0 +1,516 @@
+// Host entry points of the C ABI declared in include/sia.h: argument
+// validation (before anything touches the GPU), launch planning, workspace
+// layout and dispatch to the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "sia.h"
+#include "sia_kernels.h"
+#include "sia_sched.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SIA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kHeader = 256;   // status word at 0, work counter at 4
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int round_up_pow2(int64_t x) {
+    int64_t p = 1;
+    while (p < x) p <<= 1;
+    return (int)p;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    return v && *v ? atoi(v) : dflt;
+}
+
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        hipDeviceProp_t p;
+        cus[dev] = hipGetDeviceProperties(&p, dev) == hipSuccess ? p.multiProcessorCount : 256;
+    }
+    return cus[dev];
+}
+
+// ------------------------------------------------------------ validation
+
+int check_page_table(const sia_page_table* pt) {
+    if (!pt) return fail(SIA_ERR_INVALID_ARG, "page table descriptor is NULL");
+    if (!pt->page_table || !pt->seq_lens) return fail(SIA_ERR_INVALID_ARG, "page_table/seq_lens is NULL");
+    if (pt->batch < 1 || pt->max_pages < 1)
+        return fail(SIA_ERR_INVALID_ARG, "batch (%d) and max_pages (%d) must be >= 1", pt->batch, pt->max_pages);
+    if (pt->page_size != 64) return fail(SIA_ERR_UNSUPPORTED, "page_size %d: only 64 is supported", pt->page_size);
+    if ((int64_t)pt->max_pages * 64 > INT32_MAX)
+        return fail(SIA_ERR_UNSUPPORTED, "max_pages %d too large", pt->max_pages);
+    return SIA_OK;
+}
+
+int check_queries(const sia_queries* qs, const sia_page_table* pt) {
+    if (!qs) return fail(SIA_ERR_INVALID_ARG, "query descriptor is NULL");
+    if (qs->num_q < 0) return fail(SIA_ERR_INVALID_ARG, "num_q %d < 0", qs->num_q);
+    if (qs->num_q > 0 && (!qs->q_seq || !qs->q_pos)) return fail(SIA_ERR_INVALID_ARG, "q_seq/q_pos is NULL");
+    if (qs->group < 1) return fail(SIA_ERR_INVALID_ARG, "group %d < 1", qs->group);
+    if (qs->max_visible < 0) return fail(SIA_ERR_INVALID_ARG, "max_visible %d < 0", qs->max_visible);
+    if (pt && (int64_t)qs->max_visible > (int64_t)pt->max_pages * 64)
+        return fail(SIA_ERR_INVALID_ARG, "max_visible %d exceeds max_pages*64 = %lld", qs->max_visible,
+                    (long long)pt->max_pages * 64);
+    return SIA_OK;
+}
+
+int check_index_cache(const sia_paged_cache* c) {
+    if (!c) return fail(SIA_ERR_INVALID_ARG, "index cache descriptor is NULL");
+    if (!c->rows) return fail(SIA_ERR_INVALID_ARG, "index cache rows is NULL");
+    if (c->num_pages < 1) return fail(SIA_ERR_INVALID_ARG, "num_pages %lld < 1", (long long)c->num_pages);
+    if (c->dtype != SIA_BF16 && c->dtype != SIA_FP8_E4M3FN)
+        return fail(SIA_ERR_UNSUPPORTED, "index cache dtype %d", c->dtype);
+    if (c->dim != 64 && c->dim != 128) return fail(SIA_ERR_UNSUPPORTED, "index dim %d: supported 64, 128", c->dim);
+    if (c->dtype == SIA_FP8_E4M3FN && !c->scale) return fail(SIA_ERR_INVALID_ARG, "fp8 index cache needs scale");
+    if (c->dtype == SIA_BF16 && c->scale) return fail(SIA_ERR_INVALID_ARG, "bf16 index cache takes no scale");
+    return SIA_OK;
+}
+
+// ------------------------------------------------------------ indexer plan
+
+struct MergeLevel {
+    int n_in, kc_in, fan_in, n_out;
+    size_t in_key, in_pos, in_cnt;     // workspace offsets of the level's inputs
+    size_t out_key, out_pos, out_cnt;  // intermediate outputs (unused on the last level)
+};
+
+struct IndexerPlan {
+    bool stream = false;
+    int group = 1;               // queries per split workgroup (1 or 2)
+    int chunk = 0, n_chunks = 0, kc = 0;
+    int cap = 0;                 // stream buffer capacity
+    int n_levels = 0;
+    MergeLevel lv[8];
+    size_t total = kHeader;
+};
+
+void plan_merge(IndexerPlan& p, int64_t num_q, int topk, size_t cand_key, size_t cand_pos,
+                size_t cand_cnt) {
+    int n_in = p.n_chunks, kc_in = p.kc;
+    size_t ik = cand_key, ip = cand_pos, ic = cand_cnt;
+    p.n_levels = 0;
+    while (n_in > 1 && p.n_levels < 8) {
+        MergeLevel L;
+        L.n_in = n_in;
+        L.kc_in = kc_in;
+        L.fan_in = std::max(1, std::min(n_in, sia::kMergeCap / kc_in));
+        L.n_out = (int)ceil_div(n_in, L.fan_in);
+        L.in_key = ik; L.in_pos = ip; L.in_cnt = ic;
+        L.out_key = L.out_pos = L.out_cnt = 0;
+        if (L.n_out > 1) {
+            const size_t nset = (size_t)num_q * L.n_out;
+            L.out_key = p.total; p.total += align_up(nset * topk * 4);
+            L.out_pos = p.total; p.total += align_up(nset * topk * 4);
+            L.out_cnt = p.total; p.total += align_up(nset * 4);
+        }
+        p.lv[p.n_levels++] = L;
+        ik = L.out_key; ip = L.out_pos; ic = L.out_cnt;
+        n_in = L.n_out;
+        kc_in = topk;
+    }
+}
+
+void plan_split(IndexerPlan& p, int64_t num_q, int max_visible, int topk, int group_cap) {
+    p.group = group_cap;
+    const int64_t n_groups = ceil_div(num_q, p.group);
+    const int chunk_max = p.group == 2 ? 8192 : 16384;   // 64 KB of keys per workgroup
+    int chunk;
+    const int forced = env_int("SIA_SPLIT_CHUNK", 0);
+    if (forced > 0) {
+        chunk = std::max(32, std::min(chunk_max, forced / 32 * 32));
+    } else if (max_visible <= 4096) {
+        chunk = std::max(32, (max_visible + 31) / 32 * 32);
+    } else {
+        const int64_t target = ceil_div((int64_t)max_visible * n_groups, 1024);
+        chunk = std::max(2048, std::min(chunk_max, round_up_pow2(target)));
+    }
+    p.n_chunks = (int)std::max<int64_t>(1, ceil_div(std::max(max_visible, 1), chunk));
+    if (p.n_chunks == 1) chunk = std::max(32, std::min(chunk_max, (max_visible + 31) / 32 * 32));
+    p.chunk = chunk;
+    p.kc = std::min(topk, chunk);
+    if (p.n_chunks > 1) {
+        const size_t nset = (size_t)num_q * p.n_chunks;
+        const size_t ck = p.total; p.total += align_up(nset * p.kc * 4);
+        const size_t cp = p.total; p.total += align_up(nset * p.kc * 4);
+        const size_t cc = p.total; p.total += align_up(nset * 4);
+        plan_merge(p, num_q, topk, ck, cp, cc);
+    }
+}
+
+IndexerPlan plan_indexer(const sia_queries* qs, int topk) {
+    IndexerPlan p;
+    const int mode = env_int("SIA_INDEXER_PATH", 0);   // 0 auto, 1 split, 2 stream
+    const bool stream_ok = topk <= 2048 && qs->group % 4 == 0;
+    bool stream = stream_ok && qs->num_q >= 256 && qs->max_visible > 2 * topk;
+    if (mode == 1) stream = false;
+    if (mode == 2) stream = stream_ok;
+    if (stream) {
+        p.stream = true;
+        p.cap = std::min(4096, std::max(1024, 2 * topk));
+        return p;
+    }
+    plan_split(p, qs->num_q, qs->max_visible, topk, qs->group % 2 == 0 ? 2 : 1);
+    return p;
+}
+
+sia::IdxArgs idx_args(const sia_page_table* pt, const sia_paged_cache* c, const sia_queries* qs,
+                      const void* q_idx, const float* w, int heads, void* ws) {
+    sia::IdxArgs a;
+    a.page_table = pt->page_table;
+    a.seq_lens = pt->seq_lens;
+    a.batch = pt->batch;
+    a.max_pages = pt->max_pages;
+    a.rows = static_cast<const uint8_t*>(c->rows);
+    a.scale = c->scale;
+    a.num_pages = c->num_pages;
+    a.q_seq = qs->q_seq;
+    a.q_pos = qs->q_pos;
+    a.num_q = qs->num_q;
+    a.max_visible = qs->max_visible;
+    a.q_idx = static_cast<const uint16_t*>(q_idx);
+    a.w = w;
+    a.heads = heads;
+    a.status = static_cast<uint32_t*>(ws);
+    return a;
+}
+
+hipError_t run_merges(const IndexerPlan& p, uint8_t* ws, int num_q, int topk, int32_t* out_idx,
+                      float* out_score, hipStream_t st) {
+    for (int i = 0; i < p.n_levels; i++) {
+        const MergeLevel& L = p.lv[i];
+        sia::MergeArgs m;
+        m.num_q = num_q;
+        m.n_in = L.n_in;
+        m.kc_in = L.kc_in;
+        m.fan_in = L.fan_in;
+        m.n_out = L.n_out;
+        m.topk = topk;
+        m.in_key = reinterpret_cast<const uint32_t*>(ws + L.in_key);
+        m.in_pos = reinterpret_cast<const int32_t*>(ws + L.in_pos);
+        m.in_cnt = reinterpret_cast<const int32_t*>(ws + L.in_cnt);
+        const bool last = L.n_out == 1;
+        m.out_key = last ? nullptr : reinterpret_cast<uint32_t*>(ws + L.out_key);
+        m.out_pos = last ? nullptr : reinterpret_cast<int32_t*>(ws + L.out_pos);
+        m.out_cnt = last ? nullptr : reinterpret_cast<int32_t*>(ws + L.out_cnt);
+        m.out_idx = last ? out_idx : nullptr;
+        m.out_score = last ? out_score : nullptr;
+        hipError_t e = sia::launch_topk_merge(m, st);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+int check_workspace(void* ws, size_t have, size_t need) {
+    if (!ws) return fail(SIA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (have < need) return fail(SIA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", have, need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(SIA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    return SIA_OK;
+}
+
+int check_indexer_common(const sia_page_table* pt, const sia_paged_cache* c, const sia_queries* qs,
+                         const void* q_idx, const float* w, int heads) {
+    int rc;
+    if ((rc = check_page_table(pt)) != SIA_OK) return rc;
+    if ((rc = check_index_cache(c)) != SIA_OK) return rc;
+    if ((rc = check_queries(qs, pt)) != SIA_OK) return rc;
+    if (heads < 1 || heads > 64) return fail(SIA_ERR_UNSUPPORTED, "indexer heads %d: supported 1..64", heads);
+    if (qs->num_q > 0 && (!q_idx || !w)) return fail(SIA_ERR_INVALID_ARG, "q_idx/w is NULL");
+    return SIA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sia_indexer_workspace_size(const sia_page_table* pt, const sia_paged_cache* index_k,
+                                  const sia_queries* qs, int32_t heads, int32_t topk) {
+    if (check_page_table(pt) != SIA_OK || check_index_cache(index_k) != SIA_OK ||
+        check_queries(qs, pt) != SIA_OK || heads < 1 || heads > 64 || topk < 1 || topk > 16384)
+        return 0;
+    return plan_indexer(qs, topk).total;
+}
+
+int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                        const void* q_idx, const float* w, int32_t heads, int32_t topk,
+                        int32_t* out_idx, float* out_score, int32_t sched, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    int rc = check_indexer_common(pt, index_k, qs, q_idx, w, heads);
+    if (rc != SIA_OK) return rc;
+    if (topk < 1 || topk > 16384) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..16384", topk);
+    if (qs->num_q > 0 && !out_idx) return fail(SIA_ERR_INVALID_ARG, "out_idx is NULL");
+    if (sched < -1 || sched > 2) return fail(SIA_ERR_INVALID_ARG, "sched %d", sched);
+    const IndexerPlan p = plan_indexer(qs, topk);
+    if ((rc = check_workspace(workspace, workspace_bytes, p.total)) != SIA_OK) return rc;
+    if (qs->num_q == 0) return SIA_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const sia::IdxArgs a = idx_args(pt, index_k, qs, q_idx, w, heads, workspace);
+    const int mb = heads > 32 ? 2 : 1;
+    const bool fp8 = index_k->dtype == SIA_FP8_E4M3FN;
+    hipError_t e;
+    if (p.stream) {
+        sia::StreamArgs s;
+        s.topk = topk;
+        s.cap = p.cap;
+        s.n_tiles = (int)ceil_div(qs->num_q, sia::kStreamThreads / 64);
+        s.sched = sched < 0 ? env_int("SIA_SCHED", 1) : sched;
+        if (s.sched < 0 || s.sched > 2) s.sched = 1;
+        s.counter = reinterpret_cast<uint32_t*>(ws + 4);
+        s.out_idx = out_idx;
+        s.out_score = out_score;
+        int grid = s.n_tiles;
+        if (s.sched == 2) grid = sia::zigzag_workers(s.n_tiles);
+        if (s.sched == 1) {
+            e = sia::launch_fill_u32(s.counter, 0u, 1, st);
+            if (e != hipSuccess) return hip_fail(e, "counter reset");
+            const int occ = sia::indexer_stream_blocks_per_cu(mb, index_k->dim, fp8, p.cap);
+            grid = std::min<int64_t>(s.n_tiles, (int64_t)occ * device_cus());
+        }
+        e = sia::launch_indexer_stream(a, s, mb, index_k->dim, fp8, grid, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer stream launch");
+        return SIA_OK;
+    }
+    sia::SplitArgs s{};
+    s.chunk = p.chunk;
+    s.n_chunks = p.n_chunks;
+    s.topk = topk;
+    s.kc = p.kc;
+    s.out_idx = out_idx;
+    s.out_score = out_score;
+    if (p.n_chunks > 1) {
+        s.cand_key = reinterpret_cast<uint32_t*>(ws + p.lv[0].in_key);
+        s.cand_pos = reinterpret_cast<int32_t*>(ws + p.lv[0].in_pos);
+        s.cand_cnt = reinterpret_cast<int32_t*>(ws + p.lv[0].in_cnt);
+    }
+    e = sia::launch_indexer_split(a, s, mb, index_k->dim, fp8, p.group, false, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer split launch");
+    e = run_merges(p, ws, qs->num_q, topk, out_idx, out_score, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k merge launch");
+    return SIA_OK;
+}
+
+int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                          const void* q_idx, const float* w, int32_t heads, float* scores, int64_t ld,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_indexer_common(pt, index_k, qs, q_idx, w, heads);
+    if (rc != SIA_OK) return rc;
+    if (qs->num_q > 0 && !scores) return fail(SIA_ERR_INVALID_ARG, "scores is NULL");
+    if (ld < std::max(1, qs->max_visible)) return fail(SIA_ERR_INVALID_ARG, "ld %lld < max_visible %d", (long long)ld, qs->max_visible);
+    if ((rc = check_workspace(workspace, workspace_bytes, kHeader)) != SIA_OK) return rc;
+    if (qs->num_q == 0) return SIA_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = sia::launch_fill_u32(reinterpret_cast<uint32_t*>(scores), 0xff800000u,
+                                        (int64_t)qs->num_q * ld, st);
+    if (e != hipSuccess) return hip_fail(e, "scores fill");
+    const sia::IdxArgs a = idx_args(pt, index_k, qs, q_idx, w, heads, workspace);
+    sia::SplitArgs s{};
+    s.chunk = 8192;
+    s.n_chunks = (int)std::max<int64_t>(1, ceil_div(std::max(qs->max_visible, 1), s.chunk));
+    s.topk = 1;
+    s.kc = 1;
+    s.scores = scores;
+    s.ld = ld;
+    e = sia::launch_indexer_split(a, s, heads > 32 ? 2 : 1, index_k->dim,
+                                  index_k->dtype == SIA_FP8_E4M3FN, 1, true, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer scores launch");
+    return SIA_OK;
+}
+
+size_t sia_topk_workspace_size(int32_t num_q, int32_t max_row_len, int32_t topk) {
+    if (num_q < 0 || max_row_len < 0 || topk < 1 || topk > 16384) return 0;
+    IndexerPlan p;
+    plan_split(p, num_q, max_row_len, topk, 1);
+    return p.total;
+}
+
+int sparse_topk_from_scores(const float* scores, int64_t ld, const int32_t* row_len, int32_t num_q,
+                            int32_t max_row_len, int32_t topk, int32_t* out_idx, float* out_score,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    if (num_q < 0) return fail(SIA_ERR_INVALID_ARG, "num_q %d < 0", num_q);
+    if (num_q > 0 && (!scores || !row_len || !out_idx)) return fail(SIA_ERR_INVALID_ARG, "NULL pointer");
+    if (topk < 1 || topk > 16384) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..16384", topk);
+    if (max_row_len < 0 || ld < max_row_len) return fail(SIA_ERR_INVALID_ARG, "need 0 <= max_row_len <= ld");
+    IndexerPlan p;
+    plan_split(p, num_q, max_row_len, topk, 1);
+    int rc = check_workspace(workspace, workspace_bytes, p.total);
+    if (rc != SIA_OK) return rc;
+    if (num_q == 0) return SIA_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    sia::FromScoresArgs f{scores, ld, row_len, num_q, reinterpret_cast<uint32_t*>(ws)};
+    sia::SplitArgs s{};
+    s.chunk = p.chunk;
+    s.n_chunks = p.n_chunks;
+    s.topk = topk;
+    s.kc = p.kc;
+    s.out_idx = out_idx;
+    s.out_score = out_score;
+    if (p.n_chunks > 1) {
+        s.cand_key = reinterpret_cast<uint32_t*>(ws + p.lv[0].in_key);
+        s.cand_pos = reinterpret_cast<int32_t*>(ws + p.lv[0].in_pos);
+        s.cand_cnt = reinterpret_cast<int32_t*>(ws + p.lv[0].in_cnt);
+    }
+    hipError_t e = sia::launch_topk_from_scores(f, s, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k from scores launch");
+    e = run_merges(p, ws, num_q, topk, out_idx, out_score, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k merge launch");
+    return SIA_OK;
+}
+
+// ------------------------------------------------------------ attention
+
+static int attn_plan(const sia_queries* qs, int heads, int topk, int& hb, int& n_split, int& rows_per_split,
+                     size_t& total) {
+    hb = heads % 64 == 0 ? 64 : heads % 32 == 0 ? 32 : 16;
+    const int64_t base = (int64_t)qs->num_q * (heads / hb);
+    int ns = env_int("SIA_ATTN_SPLIT", 0);
+    if (ns <= 0) ns = (int)std::max<int64_t>(1, ceil_div(1024, std::max<int64_t>(1, base)));
+    const int max_split = std::max(1, (int)ceil_div(topk, 128));
+    ns = std::min(ns, max_split);
+    rows_per_split = (int)ceil_div(ceil_div(topk, ns), 32) * 32;
+    n_split = (int)ceil_div(topk, rows_per_split);
+    total = kHeader;
+    if (n_split > 1) {
+        total += align_up((size_t)qs->num_q * n_split * heads * 512 * 4);
+        total += align_up((size_t)qs->num_q * n_split * heads * 4);
+    }
+    return SIA_OK;
+}
+
+static int check_attn(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queries* qs, int heads,
+                      int d_v, int topk) {
+    int rc;
+    if ((rc = check_page_table(pt)) != SIA_OK) return rc;
+    if (!kv || !kv->rows) return fail(SIA_ERR_INVALID_ARG, "kv cache descriptor/rows is NULL");
+    if (kv->num_pages < 1) return fail(SIA_ERR_INVALID_ARG, "kv num_pages < 1");
+    if (kv->dtype != SIA_BF16) return fail(SIA_ERR_UNSUPPORTED, "kv dtype %d: only bf16", kv->dtype);
+    if (kv->dim != 576) return fail(SIA_ERR_UNSUPPORTED, "kv dim %d: only 576", kv->dim);
+    if (d_v != 512) return fail(SIA_ERR_UNSUPPORTED, "d_v %d: only 512", d_v);
+    if (!qs) return fail(SIA_ERR_INVALID_ARG, "query descriptor is NULL");
+    if (qs->num_q < 0) return fail(SIA_ERR_INVALID_ARG, "num_q %d < 0", qs->num_q);
+    if (qs->num_q > 0 && !qs->q_seq) return fail(SIA_ERR_INVALID_ARG, "q_seq is NULL");
+    if (heads < 16 || heads % 16 || heads > 1024) return fail(SIA_ERR_UNSUPPORTED, "heads %d: multiple of 16 up to 1024", heads);
+    if (topk < 1) return fail(SIA_ERR_INVALID_ARG, "topk %d < 1", topk);
+    return SIA_OK;
+}
+
+size_t sia_mla_workspace_size(const sia_queries* qs, int32_t heads, int32_t d_v, int32_t topk) {
+    if (!qs || qs->num_q < 0 || heads < 16 || heads % 16 || heads > 1024 || d_v != 512 || topk < 1) return 0;
+    int hb, ns, rps;
+    size_t total;
+    attn_plan(qs, heads, topk, hb, ns, rps, total);
+    return total;
+}
+
+int sparse_mla_attention(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queries* qs,
+                         const void* q, int32_t heads, int32_t d_v, const int32_t* idx, int32_t topk,
+                         float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    int rc = check_attn(pt, kv, qs, heads, d_v, topk);
+    if (rc != SIA_OK) return rc;
+    if (qs->num_q > 0 && (!q || !idx || !out)) return fail(SIA_ERR_INVALID_ARG, "q/idx/out is NULL");
+    if (!std::isfinite(sm_scale)) return fail(SIA_ERR_INVALID_ARG, "sm_scale is not finite");
+    int hb, ns, rps;
+    size_t total;
+    attn_plan(qs, heads, topk, hb, ns, rps, total);
+    if ((rc = check_workspace(workspace, workspace_bytes, total)) != SIA_OK) return rc;
+    if (qs->num_q == 0) return SIA_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    sia::AttnArgs a;
+    a.page_table = pt->page_table;
+    a.seq_lens = pt->seq_lens;
+    a.batch = pt->batch;
+    a.max_pages = pt->max_pages;
+    a.kv = static_cast<const uint16_t*>(kv->rows);
+    a.num_pages = kv->num_pages;
+    a.q_seq = qs->q_seq;
+    a.num_q = qs->num_q;
+    a.q = static_cast<const uint16_t*>(q);
+    a.heads = heads;
+    a.d_v = d_v;
+    a.idx = idx;
+    a.topk = topk;
+    a.sm_scale = sm_scale;
+    a.n_split = ns;
+    a.rows_per_split = rps;
+    a.heads_per_block = hb;
+    a.out = static_cast<uint16_t*>(out);
+    a.lse = lse;
+    a.part_o = ns > 1 ? reinterpret_cast<float*>(ws + kHeader) : nullptr;
+    a.part_lse = ns > 1 ? reinterpret_cast<float*>(ws + kHeader + align_up((size_t)qs->num_q * ns * heads * 512 * 4))
+                        : nullptr;
+    a.status = reinterpret_cast<uint32_t*>(ws);
+    hipError_t e = sia::launch_sparse_mla(a, st);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    if (ns > 1) {
+        e = sia::launch_mla_combine(a, st);
+        if (e != hipSuccess) return hip_fail(e, "attention combine launch");
+    }
+    return SIA_OK;
+}
+
+// ------------------------------------------------------------ misc
+
+int sia_zigzag_assign(int32_t num_shards, int32_t* out) {
+    if (num_shards < 1 || !out) return fail(SIA_ERR_INVALID_ARG, "num_shards %d / out", num_shards);
+    const int workers = sia::zigzag_workers(num_shards);
+    int k = 0;
+    for (int i = 0; i < workers; i++)
+        for (int s = 0; s < 2; s++) {
+            const int v = sia::zigzag_shard(num_shards, i, s);
+            if (v >= 0) out[k++] = v;
+        }
+    return SIA_OK;
+}
+
+int sia_clear_device_status(void* workspace, void* stream) {
+    if (!workspace) return fail(SIA_ERR_INVALID_ARG, "workspace is NULL");
+    hipError_t e = sia::launch_fill_u32(static_cast<uint32_t*>(workspace), 0u, 2, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SIA_OK : hip_fail(e, "status clear");
+}
+
+int sia_read_device_status(const void* workspace, void* stream, uint32_t* status) {
+    if (!workspace || !status) return fail(SIA_ERR_INVALID_ARG, "workspace/status is NULL");
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    e = hipMemcpy(status, workspace, 4, hipMemcpyDeviceToHost);
+    return e == hipSuccess ? SIA_OK : hip_fail(e, "status read");
+}
+
+const char* sia_last_error(void) { return g_err.c_str(); }
+
+int sia_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA
+// wrappers, fp8 -> bf16 conversion, the order-preserving score key and
+// wave/block scans.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sia {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 64;
+constexpr int kWave = 64;
+
+// Device status bits (mirror of the SIA_DEVSTATUS_* values of the C header).
+constexpr uint32_t kBadSeq = 1u, kBadPage = 2u, kRowTooLong = 4u, kBadIndex = 8u;
+
+// D[32x32] += A[32x16] * B[16x32], bf16 in, fp32 accumulate.
+// Lane l holds A row l%32, k = 8*(l/32)+i; B column l%32, k = 8*(l/32)+i;
+// accumulator register r holds D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Upper 16 bits of two fp32 packed into one dword (x0 in the low half). Exact
+// for values that are representable in bf16.
+__device__ __forceinline__ uint32_t pack_hi16(float x0, float x1) {
+    return (__float_as_uint(x0) >> 16) | (__float_as_uint(x1) & 0xffff0000u);
+}
+
+// Eight OCP e4m3fn codes (bytes of lo, then hi) -> eight bf16. Exact: every
+// e4m3fn value, subnormals included, is a bf16 value.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+    f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+    f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    u32x4 r;
+    r[0] = pack_hi16(a[0], a[1]);
+    r[1] = pack_hi16(b[0], b[1]);
+    r[2] = pack_hi16(c[0], c[1]);
+    r[3] = pack_hi16(d[0], d[1]);
+    return as_bf16x8(r);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Order-preserving key of a score: larger score <=> larger key. -0 and +0 map
+// to one key; NaN maps to 1, below every number; 0 marks "no candidate".
+__device__ __forceinline__ uint32_t score_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+    if (k <= 1u) return __uint_as_float(0x7fc00000u);  // never emitted for real keys
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Orders this wave's LDS accesses (wave-synchronous code paths).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    const int l = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int o = __shfl_up(v, d, kWave);
+        if (l >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, kWave));
+    return v;
+}
+
+// Exclusive prefix sums of two counters over NT threads (NT = 64: one wave, no
+// barrier; NT > 64: the whole block, with barriers). `scratch` holds >= 2*NT/64
+// ints of LDS private to the caller.
+template <int NT>
+__device__ __forceinline__ void scan2(int a, int b, int& a_pre, int& b_pre, int& a_tot,
+                                      int& b_tot, int* scratch) {
+    // pack both counters into one 32-bit word: each is < 65536 here
+    int v = a | (b << 16);
+    int inc = wave_incl_scan(v);
+    if constexpr (NT == kWave) {
+        int tot = __shfl(inc, kWave - 1, kWave);
+        int exc = inc - v;
+        a_pre = exc & 0xffff; b_pre = exc >> 16;
+        a_tot = tot & 0xffff; b_tot = tot >> 16;
+    } else {
+        constexpr int NW = NT / kWave;
+        const int w = threadIdx.x / kWave;
+        if (lane_id() == kWave - 1) scratch[w] = inc;
+        __syncthreads();
+        int before = 0, tot = 0;
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            int s = scratch[i];
+            before += (i < w) ? s : 0;
+            tot += s;
+        }
+        __syncthreads();
+        int exc = before + inc - v;
+        a_pre = exc & 0xffff; b_pre = exc >> 16;
+        a_tot = tot & 0xffff; b_tot = tot >> 16;
+    }
+}
+
+}  // namespace sia

@@ -256,3 +256,33 @@ def chunk_queries(wl: Workload, c: int) -> Workload:
     ch = wl.spec.chunk
     sub = wl.queries(c * ch, (c + 1) * ch)
     return with_seq_lens(sub, [(c + 1) * ch])
+
+
+def subset(wl: Workload, seqs, device="cpu") -> Workload:
+    """The queries of sequences ``seqs`` with compact caches holding only those
+    sequences' pages (same page order within each sequence, renumbered, shuffled
+    placement kept). Used to hand a slice of a large workload to the CPU."""
+    seqs = [int(s) for s in seqs]
+    table = wl.page_table.cpu()
+    lens = wl.seq_lens.cpu()
+    q_seq = wl.q_seq.cpu()
+    keep_q = torch.zeros(q_seq.numel(), dtype=torch.bool)
+    for s in seqs:
+        keep_q |= q_seq == s
+    qi = torch.nonzero(keep_q).flatten()
+    npg = [int((int(lens[s]) + PAGE - 1) // PAGE) for s in seqs]
+    phys = torch.cat([table[s, :n] for s, n in zip(seqs, npg)]).long()
+    new_table = torch.full((len(seqs), max(npg)), -1, dtype=torch.int32)
+    off = 0
+    for i, n in enumerate(npg):
+        new_table[i, :n] = torch.arange(off, off + n, dtype=torch.int32)
+        off += n
+    src = phys.to(wl.idx_k.device)
+    remap = {s: i for i, s in enumerate(seqs)}
+    new_qseq = torch.tensor([remap[int(s)] for s in q_seq[qi]], dtype=torch.int32)
+    return Workload(
+        wl.spec, lens[seqs].clone().to(device), new_table.to(device),
+        wl.idx_k[src].to(device), None if wl.idx_scale is None else wl.idx_scale[src].to(device),
+        wl.kv[src].to(device), wl.q_idx[qi.to(wl.q_idx.device)].to(device),
+        wl.w[qi.to(wl.w.device)].to(device), wl.q_attn[qi.to(wl.q_attn.device)].to(device),
+        new_qseq.to(device), wl.q_pos.cpu()[qi].to(device), len(phys))
