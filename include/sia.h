@@ -129,7 +129,7 @@ size_t sia_indexer_workspace_size(const sia_page_table *pt, const sia_paged_cach
  * Fused indexer + Top-K.
  *   q_idx     device bf16 [num_q, heads, dim]   indexer query heads (dim = index_k->dim)
  *   w         device fp32 [num_q, heads]        per-token head weights
- *   topk      K >= 1
+ *   topk      1 <= K <= 8192
  *   out_idx   device int32 [num_q, topk]        selected logical positions, ascending, -1 padded
  *   out_score device fp32 [num_q, topk] or NULL scores of out_idx entries (-inf for padding)
  *   sched     sia_sched for long causal rows; results do not depend on it

@@ -30,6 +30,8 @@
 
 namespace sia {
 
+static_assert(kCoarseBins == kCoarseBinsHost, "host and device histogram sizes differ");
+
 // ------------------------------------------------------------ score tile
 
 template <int MB, int D>
@@ -68,6 +70,7 @@ struct KTile {
     static constexpr int NV = BYTES / 16;
     u32x4 v[NV];
     float sc;
+    bool ok;      // this lane's position is visible and its page id valid
 };
 
 // Visible row length of query j (clamped; flags bad input).
@@ -94,40 +97,61 @@ __device__ __forceinline__ int visible_len(const IdxArgs& A, int j, int& b) {
     return (int)r;
 }
 
-// Loads the tile starting at pos0 (a multiple of 32). Lanes whose position is
-// not visible, or whose page id is out of range, load zeros.
+// Physical page of logical page `lp` of sequence b, or -1 (and a status bit)
+// if the table holds an id outside [0, num_pages).
+__device__ __forceinline__ int page_of(const IdxArgs& A, int b, int lp) {
+    const int page = A.page_table[(int64_t)b * A.max_pages + lp];
+    if (page >= 0 && page < A.num_pages) return page;
+    atomicOr(A.status, kBadPage);
+    return -1;
+}
+
+// Loads the tile starting at pos0 (a multiple of 32) that lives on physical
+// page `page` (wave-uniform). Branch-free: a lane whose position is not visible,
+// or whose page is invalid, reads row 0 of the pool instead (always in bounds)
+// and is marked not ok, so that its score is discarded. Keeping loads out of
+// branches lets the compiler wait for exactly the tile being consumed.
 template <int D, bool FP8>
-__device__ __forceinline__ void load_ktile(const IdxArgs& A, int b, int pos0, int row_len,
+__device__ __forceinline__ void load_ktile(const IdxArgs& A, int page, int pos0, int row_len,
                                            KTile<D, FP8>& t) {
     const int l = lane_id(), half = l >> 5;
     const int p = pos0 + (l & 31);
-    int page = A.page_table[(int64_t)b * A.max_pages + (pos0 >> 6)];
-    page = __builtin_amdgcn_readfirstlane(page);
-    const bool page_ok = page >= 0 && page < A.num_pages;
-    if (!page_ok && pos0 < row_len && l == 0) atomicOr(A.status, kBadPage);
-    const bool ok = page_ok && p < row_len;
-    const int64_t row = (int64_t)page * kPage + (p & 63);
+    t.ok = page >= 0 && p < row_len;
+    const int64_t row = t.ok ? (int64_t)page * kPage + (p & 63) : 0;
+    const uint8_t* src = A.rows + row * (D * (FP8 ? 1 : 2)) + half * KTile<D, FP8>::BYTES;
 #pragma unroll
-    for (int i = 0; i < KTile<D, FP8>::NV; i++) t.v[i] = u32x4{0u, 0u, 0u, 0u};
-    t.sc = 1.f;
-    if (ok) {
-        const uint8_t* src = A.rows + row * (D * (FP8 ? 1 : 2)) + half * KTile<D, FP8>::BYTES;
-#pragma unroll
-        for (int i = 0; i < KTile<D, FP8>::NV; i++)
-            t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + i);
-        if constexpr (FP8) t.sc = A.scale[row];
-    }
+    for (int i = 0; i < KTile<D, FP8>::NV; i++) t.v[i] = reinterpret_cast<const u32x4*>(src)[i];
+    if constexpr (FP8) t.sc = A.scale[row];
+    else t.sc = 1.f;
 }
 
-// Scores of the tile's 32 positions; lanes l and l+32 both return the score of
-// position pos0 + l%32. Fixed operation order, so every kernel that uses it
-// produces the same bits.
-template <int MB, int D, bool FP8>
-__device__ __forceinline__ float tile_scores(const IdxQuery<MB, D>& q, const KTile<D, FP8>& t) {
+// max(0, x) in one integer instruction: a negative float is a negative int,
+// -0.0 maps to +0.0.
+__device__ __forceinline__ float relu(float x) {
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// x[lane] + x[lane ^ 32], as (lower-half value) + (upper-half value) in every lane.
+__device__ __forceinline__ float add_halves(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Scores of the tile's 32 positions for G queries that share it; lanes l and
+// l+32 both get the score of position pos0 + l%32 (undefined where the tile
+// lane is not ok). The tile is widened once and feeds every query's MFMAs. Per
+// query the operation order is fixed and independent of G, so every kernel
+// that uses this produces the same bits for the same query and position.
+template <int MB, int D, bool FP8, int G>
+__device__ __forceinline__ void tile_scores(const IdxQuery<MB, D> (&q)[G], const KTile<D, FP8>& t,
+                                            float (&s)[G]) {
     constexpr int KS = D / 16;
-    f32x16 acc[MB];
+    f32x16 acc[G][MB];
 #pragma unroll
-    for (int mb = 0; mb < MB; mb++) acc[mb] = f32x16{};
+    for (int g = 0; g < G; g++)
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) acc[g][mb] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
         bf16x8 bk;
@@ -138,23 +162,35 @@ __device__ __forceinline__ float tile_scores(const IdxQuery<MB, D>& q, const KTi
             bk = as_bf16x8(t.v[ks]);
         }
 #pragma unroll
-        for (int mb = 0; mb < MB; mb++) acc[mb] = mfma32(q.a[mb][ks], bk, acc[mb]);
+        for (int g = 0; g < G; g++)
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++) acc[g][mb] = mfma32(q[g].a[mb][ks], bk, acc[g][mb]);
     }
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < MB; mb++) {
+    for (int g = 0; g < G; g++) {
+        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-            p0 = fmaf(q.w[mb][r + 0], fmaxf(acc[mb][r + 0], 0.f), p0);
-            p1 = fmaf(q.w[mb][r + 1], fmaxf(acc[mb][r + 1], 0.f), p1);
-            p2 = fmaf(q.w[mb][r + 2], fmaxf(acc[mb][r + 2], 0.f), p2);
-            p3 = fmaf(q.w[mb][r + 3], fmaxf(acc[mb][r + 3], 0.f), p3);
+        for (int mb = 0; mb < MB; mb++) {
+#pragma unroll
+            for (int r = 0; r < 16; r += 4) {
+                p0 = fmaf(q[g].w[mb][r + 0], relu(acc[g][mb][r + 0]), p0);
+                p1 = fmaf(q[g].w[mb][r + 1], relu(acc[g][mb][r + 1]), p1);
+                p2 = fmaf(q[g].w[mb][r + 2], relu(acc[g][mb][r + 2]), p2);
+                p3 = fmaf(q[g].w[mb][r + 3], relu(acc[g][mb][r + 3]), p3);
+            }
         }
+        float v = add_halves((p0 + p1) + (p2 + p3));
+        if constexpr (FP8) v = v * t.sc;
+        s[g] = v;
     }
-    const float part = (p0 + p1) + (p2 + p3);
-    float s = part + __shfl_xor(part, 32, kWave);
-    if constexpr (FP8) s = s * t.sc;
-    return s;
+}
+
+template <int MB, int D, bool FP8>
+__device__ __forceinline__ float tile_scores(const IdxQuery<MB, D>& q, const KTile<D, FP8>& t) {
+    const IdxQuery<MB, D> qq[1] = {q};
+    float s[1];
+    tile_scores<MB, D, FP8, 1>(qq, t, s);
+    return s[0];
 }
 
 // ------------------------------------------------------------ emitters
@@ -163,7 +199,8 @@ struct EmitFinal {
     int32_t* idx;
     float* score;
     int base;        // position of key index 0
-    __device__ void prefetch(int, u32x4) {}
+    __device__ void prefetch(int, u32x4, uint32_t) {}
+    __device__ void prefetch2(int, u32x4, uint32_t) {}
     __device__ void operator()(int rank, int i, int, uint32_t k) const {
         idx[rank] = base + i;
         if (score) score[rank] = key_score(k);
@@ -174,21 +211,30 @@ struct EmitCand {
     uint32_t* key;
     int32_t* pos;
     int base;
-    __device__ void prefetch(int, u32x4) {}
+    __device__ void prefetch(int, u32x4, uint32_t) {}
+    __device__ void prefetch2(int, u32x4, uint32_t) {}
     __device__ void operator()(int rank, int i, int, uint32_t k) const {
         key[rank] = k;
         pos[rank] = base + i;
     }
 };
 
-// Positions come from a parallel array (merge inputs).
+// Positions come from a parallel array in global memory (merge inputs).
 struct EmitFinalPos {
     const int32_t* src_pos;
     int32_t* idx;
     float* score;
-    __device__ void prefetch(int, u32x4) {}
-    __device__ void operator()(int rank, int i, int, uint32_t k) const {
-        idx[rank] = src_pos[i];
+    int32_t p4[8];
+    __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
+    }
+    __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
+    }
+    __device__ void operator()(int rank, int, int e, uint32_t k) const {
+        idx[rank] = p4[e];
         if (score) score[rank] = key_score(k);
     }
 };
@@ -197,10 +243,18 @@ struct EmitCandPos {
     const int32_t* src_pos;
     uint32_t* key;
     int32_t* pos;
-    __device__ void prefetch(int, u32x4) {}
-    __device__ void operator()(int rank, int i, int, uint32_t k) const {
+    int32_t p4[8];
+    __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
+    }
+    __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
+    }
+    __device__ void operator()(int rank, int, int e, uint32_t k) const {
         key[rank] = k;
-        pos[rank] = src_pos[i];
+        pos[rank] = p4[e];
     }
 };
 
@@ -209,10 +263,14 @@ struct EmitCandPos {
 struct EmitInPlace {
     uint32_t* key;
     int32_t* pos;
-    int32_t p4[4];
-    __device__ void prefetch(int i, u32x4 k4) {
+    int32_t p4[8];
+    __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) p4[e] = k4[e] != 0u ? pos[i + e] : 0;
+        for (int e = 0; e < 4; e++) p4[e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
+    }
+    __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
     }
     __device__ void operator()(int rank, int, int e, uint32_t k) const {
         key[rank] = k;
@@ -224,10 +282,14 @@ struct EmitFinalBuf {
     const int32_t* pos;
     int32_t* idx;
     float* score;
-    int32_t p4[4];
-    __device__ void prefetch(int i, u32x4 k4) {
+    int32_t p4[8];
+    __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) p4[e] = k4[e] != 0u ? pos[i + e] : 0;
+        for (int e = 0; e < 4; e++) p4[e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
+    }
+    __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
     }
     __device__ void operator()(int rank, int, int e, uint32_t k) const {
         idx[rank] = p4[e];
@@ -253,82 +315,304 @@ __device__ int select_emit(const uint32_t* keys, int n, int m_cap, SelScratch* s
 
 // ------------------------------------------------------------ split kernel
 
-template <int MB, int D, bool FP8, int G, bool SCORES>
-__global__ __launch_bounds__(kSplitThreads) void indexer_split_kernel(IdxArgs A, SplitArgs S) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem);
-    SelScratch* sel = reinterpret_cast<SelScratch*>(smem + (size_t)G * S.chunk * 4);
+#define SIA_LDS __attribute__((address_space(3)))
 
-    constexpr int WPQ = 4 / G;   // waves per query
-    const int g = blockIdx.x / S.n_chunks;
-    const int c = blockIdx.x % S.n_chunks;
-    const int w = threadIdx.x / kWave, l = lane_id();
-    const int qi = w / WPQ, sub = w % WPQ;
-    const int j = g * G + qi;
-    const int chunk0 = c * S.chunk;
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
-    // ---- scores of this chunk
-    if (j < A.num_q) {
-        int b;
-        const int rl = visible_len(A, j, b);
-        const int nvalid = max(0, min(S.chunk, rl - chunk0));
-        uint32_t* keys = keys_all + qi * S.chunk;
-        const int ntiles = (nvalid + 31) / 32;
-        if (sub < ntiles) {
-            IdxQuery<MB, D> q;
-            load_query<MB, D>(A, j, q);
-            KTile<D, FP8> cur, nxt;
-            load_ktile<D, FP8>(A, b, chunk0 + sub * 32, rl, cur);
-            for (int t = sub; t < ntiles; t += WPQ) {
-                if (t + WPQ < ntiles) load_ktile<D, FP8>(A, b, chunk0 + (t + WPQ) * 32, rl, nxt);
-                const float s = tile_scores<MB, D, FP8>(q, cur);
-                const int i = t * 32 + (l & 31);
-                if constexpr (SCORES) {
-                    if (l < 32 && i < nvalid) S.scores[(int64_t)j * S.ld + chunk0 + i] = s;
-                } else {
-                    if (l < 32) keys[i] = i < nvalid ? score_key(s) : 0u;
-                }
-                cur = nxt;
-            }
+// MFMA half of a tile: the raw q.k products of one query against 32
+// positions (heads x positions accumulators). The K tile is widened here.
+template <int MB, int D, bool FP8>
+__device__ __forceinline__ void tile_mfma(const IdxQuery<MB, D>& q, const KTile<D, FP8>& t, f32x16 (&acc)[MB]) {
+    constexpr int KS = D / 16;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) acc[mb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        bf16x8 bk;
+        if constexpr (FP8) {
+            const u32x4 vv = t.v[ks >> 1];
+            bk = e4m3x8_to_bf16x8(vv[(ks & 1) * 2], vv[(ks & 1) * 2 + 1]);
+        } else {
+            bk = as_bf16x8(t.v[ks]);
         }
-        if constexpr (!SCORES) {
-            // zero the keys past the last tile so that groups of four are clean
-            for (int i = ntiles * 32 + threadIdx.x % (WPQ * kWave); i < S.chunk && i < ntiles * 32 + 4;
-                 i += WPQ * kWave)
-                if (sub == 0 || true) keys[i] = 0u;
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) acc[mb] = mfma32(q.a[mb][ks], bk, acc[mb]);
+    }
+}
+
+// Vector half: ReLU, head weights, head sum, token scale. Same operation order
+// as tile_scores.
+template <int MB, int D, bool FP8>
+__device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D>& q, const f32x16 (&acc)[MB], float tsc) {
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+            p0 = fmaf(q.w[mb][r + 0], relu(acc[mb][r + 0]), p0);
+            p1 = fmaf(q.w[mb][r + 1], relu(acc[mb][r + 1]), p1);
+            p2 = fmaf(q.w[mb][r + 2], relu(acc[mb][r + 2]), p2);
+            p3 = fmaf(q.w[mb][r + 3], relu(acc[mb][r + 3]), p3);
         }
     }
+    float v = add_halves((p0 + p1) + (p2 + p3));
+    if constexpr (FP8) v = v * tsc;
+    return v;
+}
+
+// Geometry of the split kernel. Eight waves; wave w scores query w / (8/G)
+// against its tiles sub, sub + 8/G, ... (sub = w % (8/G)) of 32 positions.
+// Each wave streams its tiles through a private ring of NS LDS slots filled by
+// direct global -> LDS copies, 16 bytes per lane and eight lanes per 128-byte
+// row (coalesced), with the 16-byte chunks of a row XOR-swizzled by the row
+// index so that the MFMA operand reads spread over the LDS banks. A wave only
+// waits on its own copies (no barrier in the streaming loop), and issues the
+// MFMAs of tile k before the vector epilogue of tile k-1, so both pipes stay
+// busy. With two queries the waves of a pair copy the same rows; the second
+// copy is served from L2.
+template <int D, bool FP8, int G>
+struct SplitGeom {
+    static constexpr int R = D * (FP8 ? 1 : 2);          // bytes per row
+    static constexpr int CPR = R / 16;                   // 16-byte chunks per row
+    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
+    static constexpr int NWV = 8;                        // waves per workgroup
+    static constexpr int NT = NWV * kWave;
+    static constexpr int WPQ = NWV / G;                  // waves per query
+    static constexpr int TILE = 32 * R;                  // bytes of one tile
+    static constexpr int NS_RAW = 98304 / (NWV * TILE);
+    static constexpr int NS = NS_RAW < 2 ? 2 : (NS_RAW > 4 ? 4 : NS_RAW);   // ring depth
+    static constexpr int DMA = TILE / 1024;              // 1 KB copies per tile
+    static constexpr int PER_TILE = DMA + (FP8 ? 1 : 0); // copies per tile (+ scales)
+    static constexpr size_t STATIC_LDS = (size_t)NS * NWV * (TILE + (FP8 ? 128 : 0));
+};
+
+__host__ __device__ inline size_t split_pages_bytes(int chunk) {
+    return ((size_t)(chunk / kPage) * 4 + 15) / 16 * 16;
+}
+
+template <int MB, int D, bool FP8, int G, bool SCORES>
+__global__ __launch_bounds__(512) void indexer_split_kernel(IdxArgs A, SplitArgs S) {
+    using GM = SplitGeom<D, FP8, G>;
+    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NWV = GM::NWV, NT = GM::NT, WPQ = GM::WPQ;
+    static_assert(NT == 512, "launch bounds assume eight waves");
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[NWV * GM::TILE];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[NWV * GM::TILE];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS > 2 ? NWV * GM::TILE : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS > 3 ? NWV * GM::TILE : 16];
+    __shared__ __attribute__((aligned(16))) float scl0[FP8 ? NWV * 32 : 4];
+    __shared__ __attribute__((aligned(16))) float scl1[FP8 ? NWV * 32 : 4];
+    __shared__ __attribute__((aligned(16))) float scl2[FP8 && NS > 2 ? NWV * 32 : 4];
+    __shared__ __attribute__((aligned(16))) float scl3[FP8 && NS > 3 ? NWV * 32 : 4];
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int* pages = reinterpret_cast<int*>(smem);
+    uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem + split_pages_bytes(S.chunk));
+    uint32_t* hist_all = keys_all + (size_t)G * S.chunk;          // [G][kCoarseBins]
+    SelScratch* sel = reinterpret_cast<SelScratch*>(hist_all + (SCORES ? 0 : G * kCoarseBins));
+
+    const int g = blockIdx.x / S.n_chunks;
+    const int c = blockIdx.x % S.n_chunks;
+    const int w = threadIdx.x / kWave, l = lane_id(), half = l >> 5;
+    const int qi = w / WPQ, sub = w % WPQ;
+    const int chunk0 = c * S.chunk;
+
+    // The group's queries share one sequence; a query naming another sequence is
+    // dropped (status bit) rather than scored against the wrong cache.
+    int rl[G];
+    int b0 = 0, rlmax = 0;
+#pragma unroll
+    for (int i = 0; i < G; i++) {
+        const int j = g * G + i;
+        rl[i] = 0;
+        if (j < A.num_q) {
+            int b;
+            rl[i] = visible_len(A, j, b);
+            if (i == 0) b0 = b;
+            else if (b != b0) {
+                if (threadIdx.x == 0) atomicOr(A.status, kBadSeq);
+                rl[i] = 0;
+            }
+        }
+        rlmax = max(rlmax, rl[i]);
+    }
+    const int nvalid = max(0, min(S.chunk, rlmax - chunk0));
+    const int ntiles = (nvalid + 31) / 32;
+    const int npg = (nvalid + kPage - 1) / kPage;
+    const int row_end = chunk0 + nvalid;
+    for (int i = threadIdx.x; i < npg; i += NT) pages[i] = page_of(A, b0, chunk0 / kPage + i);
+    if constexpr (!SCORES)
+        for (int i = threadIdx.x; i < G * kCoarseBins; i += NT) hist_all[i] = 0u;
+    __syncthreads();
+    if (ntiles == 0) {
+        // nothing of this chunk is visible to any query of the group: an empty
+        // candidate set, or (single chunk) an all-padding output row
+        if constexpr (!SCORES) {
+            for (int i = 0; i < G; i++) {
+                const int jj = g * G + i;
+                if (jj >= A.num_q) break;
+                if (S.n_chunks == 1) {
+                    for (int r = threadIdx.x; r < S.topk; r += NT) {
+                        S.out_idx[(int64_t)jj * S.topk + r] = -1;
+                        if (S.out_score) S.out_score[(int64_t)jj * S.topk + r] = -INFINITY;
+                    }
+                } else if (threadIdx.x == 0) {
+                    S.cand_cnt[(int64_t)jj * S.n_chunks + c] = 0;
+                }
+            }
+        }
+        return;   // uniform over the workgroup
+    }
+
+    const int my_rl = rl[qi];
+    const int j = g * G + qi;
+    // query registers first (unconditionally: a clamped index keeps the load in
+    // bounds), and all of them in before the copy pipeline starts, so that the
+    // only vector-memory operations in flight in the loop are the ring copies
+    IdxQuery<MB, D> q;
+    load_query<MB, D>(A, min(j, A.num_q - 1), q);
+    wait_vmcnt<0>();
+
+    auto ring = [&](int u) -> uint8_t* {
+        return (u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3) + w * GM::TILE;
+    };
+    auto scl = [&](int u) -> float* { return (u == 0 ? scl0 : u == 1 ? scl1 : u == 2 ? scl2 : scl3) + w * 32; };
+    // copy tile ti (a tile past the end copies a dummy row) into this wave's slot
+    auto issue = [&](int ti, uint8_t* slot, float* sslot) {
+        const int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npg - 1)]);
+#pragma unroll
+        for (int r = 0; r < GM::DMA; r++) {
+            const int gi = r * kWave + l;
+            const int row = gi / CPR, cc = gi % CPR;
+            const int pos = chunk0 + ti * 32 + row;
+            const bool ok = page >= 0 && pos < row_end;
+            const int64_t grow = ok ? (int64_t)page * kPage + (pos & 63) : 0;
+            const uint8_t* src = A.rows + grow * R + ((cc ^ (row & GM::SWZ)) * 16);
+            __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)(slot + r * 1024), 16, 0, 0);
+        }
+        if constexpr (FP8) {
+            const int pos = chunk0 + ti * 32 + 4 * min(l, 7);
+            const bool ok = page >= 0 && pos < row_end;
+            const float* src = A.scale + (ok ? (int64_t)page * kPage + (pos & 63) : 0);
+            if (l < 8) __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)sslot, 16, 0, 0);
+        }
+    };
+    // operand reads of tile ti from its slot
+    auto fetch = [&](int ti, const uint8_t* slot, const float* sslot, KTile<D, FP8>& t) {
+        const int row = l & 31;
+        const int pos = chunk0 + ti * 32 + row;
+        const int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npg - 1)]);
+        constexpr int HALF = CPR / 2;                 // chunks per half row
+        // the scale is read first: the wait for the row data that the MFMAs need
+        // then also covers it, before the slot is refilled
+        if constexpr (FP8) t.sc = sslot[row];
+        else t.sc = 1.f;
+#pragma unroll
+        for (int i = 0; i < KTile<D, FP8>::NV; i++) {
+            const int cc = half * HALF + i;
+            t.v[i] = *reinterpret_cast<const u32x4*>(slot + row * R + ((cc ^ (row & GM::SWZ)) * 16));
+        }
+        t.ok = page >= 0 && pos < row_end && pos < my_rl;
+    };
+    auto finish = [&](int ti, const f32x16 (&acc)[MB], float tsc, bool tok) {
+        const float sc = tile_epilogue<MB, D, FP8>(q, acc, tsc);
+        const int i = ti * 32 + (l & 31);
+        const int pos = chunk0 + i;
+        if constexpr (SCORES) {
+            if (l < 32 && tok) S.scores[(int64_t)j * S.ld + pos] = sc;
+        } else {
+            // the key goes to LDS and into the coarse histogram of its query
+            const uint32_t k = (l < 32 && tok) ? score_key(sc) : 0u;
+            if (l < 32) keys_all[qi * S.chunk + i] = k;
+            if (k != 0u) atomicAdd(&hist_all[qi * kCoarseBins + coarse_bin(k)], 1u);
+        }
+    };
+
+    const bool active = my_rl > chunk0 && sub < ntiles;
+    if (active) {
+        // this wave's tiles: sub + k * WPQ; slot of the k-th: k % NS
+#pragma unroll
+        for (int u = 0; u < NS - 1; u++) issue(sub + u * WPQ, ring(u), scl(u));
+        f32x16 acc0[MB], acc1[MB];
+        float sc0 = 0.f, sc1 = 0.f;
+        bool ok0 = false, ok1 = false;
+        int prev = -1;
+        for (int k0 = 0; sub + k0 * WPQ < ntiles; k0 += 2 * NS) {
+#pragma unroll
+            for (int u = 0; u < 2 * NS; u++) {
+                const int ti = sub + (k0 + u) * WPQ;
+                if (ti < ntiles) {
+                    issue(ti + (NS - 1) * WPQ, ring((u + NS - 1) % NS), scl((u + NS - 1) % NS));
+                    wait_vmcnt<(NS - 1) * GM::PER_TILE>();   // this tile's copies have landed
+                    KTile<D, FP8> t;
+                    fetch(ti, ring(u % NS), scl(u % NS), t);
+                    // MFMAs of this tile, then the vector epilogue of the previous one
+                    if (u % 2 == 0) {
+                        tile_mfma<MB, D, FP8>(q, t, acc0);
+                        sc0 = t.sc; ok0 = t.ok;
+                        if (prev >= 0) finish(prev, acc1, sc1, ok1);
+                    } else {
+                        tile_mfma<MB, D, FP8>(q, t, acc1);
+                        sc1 = t.sc; ok1 = t.ok;
+                        finish(prev, acc0, sc0, ok0);
+                    }
+                    prev = ti;
+                }
+            }
+        }
+        // epilogue of the last tile: its parity is the count of tiles of this wave
+        const int count = (ntiles - sub + WPQ - 1) / WPQ;
+        if (count % 2 == 1) finish(prev, acc0, sc0, ok0);
+        else finish(prev, acc1, sc1, ok1);
+    } else if constexpr (!SCORES) {
+        // a query that sees nothing of this chunk still needs zero keys
+        for (int i = sub * kWave + l; i < ntiles * 32; i += WPQ * kWave) keys_all[qi * S.chunk + i] = 0u;
+    }
+    wait_vmcnt<0>();
     if constexpr (SCORES) return;
     else {
         __syncthreads();
         // ---- per-query selection over the chunk
-        for (int q2 = 0; q2 < G; q2++) {
-            const int j2 = g * G + q2;
-            if (j2 >= A.num_q) break;
-            int b2;
-            const int rl = visible_len(A, j2, b2);
-            const int nvalid = max(0, min(S.chunk, rl - chunk0));
-            const int nscan = (nvalid + 31) / 32 * 32;
-            const uint32_t* keys = keys_all + q2 * S.chunk;
+        const int nscan = ntiles * 32;
+#pragma unroll
+        for (int i = 0; i < G; i++) {
+            const int jj = g * G + i;
+            if (jj >= A.num_q) break;
+            const uint32_t* keys = keys_all + i * S.chunk;
+            const uint32_t* hist = hist_all + i * kCoarseBins;
             if (S.n_chunks == 1) {
-                int32_t* oi = S.out_idx + (int64_t)j2 * S.topk;
-                float* os = S.out_score ? S.out_score + (int64_t)j2 * S.topk : nullptr;
-                const int m = select_emit<kSplitThreads>(keys, nscan, S.topk, sel,
-                                                         EmitFinal{oi, os, chunk0});
-                for (int r = m + threadIdx.x; r < S.topk; r += kSplitThreads) {
+                int32_t* oi = S.out_idx + (int64_t)jj * S.topk;
+                float* os = S.out_score ? S.out_score + (int64_t)jj * S.topk : nullptr;
+                const int m = select_emit_coarse<NT>(keys, nscan, hist, S.topk, sel, EmitFinal{oi, os, chunk0});
+                for (int r = m + threadIdx.x; r < S.topk; r += NT) {
                     oi[r] = -1;
                     if (os) os[r] = -INFINITY;
                 }
             } else {
-                const int64_t slot = (int64_t)j2 * S.n_chunks + c;
-                const int m = select_emit<kSplitThreads>(
-                    keys, nscan, S.kc, sel,
+                const int64_t slot = (int64_t)jj * S.n_chunks + c;
+                const int m = select_emit_coarse<NT>(
+                    keys, nscan, hist, S.kc, sel,
                     EmitCand{S.cand_key + slot * S.kc, S.cand_pos + slot * S.kc, chunk0});
                 if (threadIdx.x == 0) S.cand_cnt[slot] = m;
             }
             __syncthreads();
         }
     }
+}
+
+// Largest chunk (power of two, <= 16384) whose LDS fits next to the ring.
+template <int MB, int D, bool FP8, int G>
+static int split_chunk_cap() {
+    using GM = SplitGeom<D, FP8, G>;
+    for (int chunk = 16384; chunk >= 64; chunk >>= 1) {
+        const size_t dyn = split_pages_bytes(chunk) + (size_t)G * (chunk + kCoarseBins) * 4 + sizeof(SelScratch);
+        if (GM::STATIC_LDS + dyn + 256 <= kMaxLds) return chunk;
+    }
+    return 64;
 }
 
 // ------------------------------------------------------------ selection from given scores
@@ -365,6 +649,15 @@ __global__ __launch_bounds__(kSplitThreads) void topk_from_scores_kernel(FromSco
 
 // ------------------------------------------------------------ merge
 
+// Rank -> candidate index, kept in LDS; positions are gathered afterwards in
+// one parallel pass instead of one dependent load per compaction round.
+struct EmitRank {
+    int32_t* rank_idx;
+    __device__ void prefetch(int, u32x4, uint32_t) {}
+    __device__ void prefetch2(int, u32x4, uint32_t) {}
+    __device__ void operator()(int rank, int i, int, uint32_t) const { rank_idx[rank] = i; }
+};
+
 __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs M) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
@@ -373,27 +666,63 @@ __global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs M) 
     const int s0 = o * M.fan_in;
     const int nsets = min(M.fan_in, M.n_in - s0);
     const int n = nsets * M.kc_in;
-    SelScratch* sel = reinterpret_cast<SelScratch*>(smem + (size_t)M.fan_in * M.kc_in * 4);
+    uint32_t* hist = keys + (size_t)M.fan_in * M.kc_in;
+    int32_t* rank_idx = reinterpret_cast<int32_t*>(hist + kCoarseBins);     // [topk]
+    int* cnt = rank_idx + M.topk;                                          // [fan_in]
+    SelScratch* sel = reinterpret_cast<SelScratch*>(cnt + (M.fan_in + 3) / 4 * 4);
     const int64_t set0 = (int64_t)q * M.n_in + s0;
-    for (int i = threadIdx.x; i < n; i += kMergeThreads) {
-        const int set = i / M.kc_in, off = i - set * M.kc_in;
-        keys[i] = off < M.in_cnt[set0 + set] ? M.in_key[set0 * M.kc_in + i] : 0u;
+    for (int i = threadIdx.x; i < kCoarseBins; i += kMergeThreads) hist[i] = 0u;
+    for (int i = threadIdx.x; i < nsets; i += kMergeThreads) cnt[i] = M.in_cnt[set0 + i];
+    __syncthreads();
+    // candidate keys: independent loads, several in flight per thread
+    const uint32_t* src = M.in_key + set0 * M.kc_in;
+    constexpr int U = 32;
+    for (int i0 = threadIdx.x; i0 < n; i0 += kMergeThreads * U) {
+        uint32_t k[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int i = i0 + u * kMergeThreads;
+            const int set = i / M.kc_in;
+            k[u] = (i < n && i - set * M.kc_in < cnt[min(set, nsets - 1)]) ? src[i] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int i = i0 + u * kMergeThreads;
+            if (i < n) keys[i] = k[u];
+        }
     }
+    __syncthreads();
+    for (int i = threadIdx.x * 4; i < n; i += kMergeThreads * 4) {
+        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) hist_add(hist, coarse_bin(k4[e]), i + e < n && k4[e] != 0u);
+    }
+    __syncthreads();
+    const int m = select_emit_coarse<kMergeThreads>(keys, n, hist, M.topk, sel, EmitRank{rank_idx});
     __syncthreads();
     const int32_t* src_pos = M.in_pos + set0 * M.kc_in;
     if (M.out_idx) {
         int32_t* oi = M.out_idx + (int64_t)q * M.topk;
         float* os = M.out_score ? M.out_score + (int64_t)q * M.topk : nullptr;
-        const int m = select_emit<kMergeThreads>(keys, n, M.topk, sel, EmitFinalPos{src_pos, oi, os});
-        for (int r = m + threadIdx.x; r < M.topk; r += kMergeThreads) {
-            oi[r] = -1;
-            if (os) os[r] = -INFINITY;
+        for (int r = threadIdx.x; r < M.topk; r += kMergeThreads) {
+            if (r < m) {
+                const int i = rank_idx[r];
+                oi[r] = src_pos[i];
+                if (os) os[r] = key_score(keys[i]);
+            } else {
+                oi[r] = -1;
+                if (os) os[r] = -INFINITY;
+            }
         }
     } else {
         const int64_t slot = (int64_t)q * M.n_out + o;
-        const int m = select_emit<kMergeThreads>(
-            keys, n, M.topk, sel,
-            EmitCandPos{src_pos, M.out_key + slot * M.topk, M.out_pos + slot * M.topk});
+        uint32_t* ok = M.out_key + slot * M.topk;
+        int32_t* op = M.out_pos + slot * M.topk;
+        for (int r = threadIdx.x; r < m; r += kMergeThreads) {
+            const int i = rank_idx[r];
+            ok[r] = keys[i];
+            op[r] = src_pos[i];
+        }
         if (threadIdx.x == 0) M.out_cnt[slot] = m;
     }
 }
@@ -407,10 +736,9 @@ struct WaveBuf {
 };
 
 template <int MB, int D, bool FP8>
-__device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, WaveBuf B) {
+__device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, int rl, const int* pages,
+                             WaveBuf B) {
     const int l = lane_id();
-    int b;
-    const int rl = visible_len(A, j, b);
     int32_t* oi = S.out_idx + (int64_t)j * S.topk;
     float* os = S.out_score ? S.out_score + (int64_t)j * S.topk : nullptr;
     int cnt = 0;
@@ -419,13 +747,15 @@ __device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, WaveB
     if (ntiles > 0) {
         IdxQuery<MB, D> q;
         load_query<MB, D>(A, j, q);
-        KTile<D, FP8> cur, nxt;
-        load_ktile<D, FP8>(A, b, 0, rl, cur);
-        for (int t = 0; t < ntiles; t++) {
-            if (t + 1 < ntiles) load_ktile<D, FP8>(A, b, (t + 1) * 32, rl, nxt);
-            const float s = tile_scores<MB, D, FP8>(q, cur);
-            const int p = t * 32 + (l & 31);
-            const uint32_t k = (l < 32 && p < rl) ? score_key(s) : 0u;
+        const int npages = (rl + kPage - 1) / kPage;
+        auto fetch = [&](KTile<D, FP8>& t, int ti) {   // ti past the end: dummy row
+            const int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npages - 1)]);
+            load_ktile<D, FP8>(A, page, ti * 32, ti < ntiles ? rl : 0, t);
+        };
+        auto consume = [&](const KTile<D, FP8>& t, int ti) {
+            const float sc = tile_scores<MB, D, FP8>(q, t);
+            const int p = ti * 32 + (l & 31);
+            const uint32_t k = (l < 32 && t.ok) ? score_key(sc) : 0u;
             const bool take = k > tau;
             const uint64_t mask = __ballot(take);
             if (take) {
@@ -434,7 +764,6 @@ __device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, WaveB
                 B.pos[at] = p;
             }
             cnt += __popcll(mask);
-            cur = nxt;
             if (cnt > S.cap - 32) {
                 // keep exactly the Top-K seen so far; later ties of T lose to them
                 wave_sync();
@@ -443,12 +772,27 @@ __device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, WaveB
                 for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
                 wave_sync();
                 const uint32_t T = radix_threshold<kWave>(B.key, n4, S.topk, B.sel, ties);
-                ordered_compact<kWave>(B.key, n4, T, ties, B.sel, EmitInPlace{B.key, B.pos, {}});
+                ordered_compact<kWave, true>(B.key, n4, T, ties, B.sel, EmitInPlace{B.key, B.pos, {}});
                 cnt = S.topk;
                 tau = T;
                 wave_sync();
             }
+        };
+        constexpr int kPrefetch = 4;   // K tiles in flight per wave
+        KTile<D, FP8> buf[kPrefetch];
+#pragma unroll
+        for (int d = 0; d < kPrefetch; d++) fetch(buf[d], d);
+        int t = 0;
+        for (; t + kPrefetch - 1 < ntiles; t += kPrefetch) {
+#pragma unroll
+            for (int d = 0; d < kPrefetch; d++) {
+                consume(buf[d], t + d);
+                fetch(buf[d], t + d + kPrefetch);
+            }
         }
+#pragma unroll
+        for (int d = 0; d < kPrefetch - 1; d++)
+            if (t + d < ntiles) consume(buf[d], t + d);
     }
     wave_sync();
     const int n4 = (cnt + 3) & ~3;
@@ -462,19 +806,46 @@ __device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, WaveB
     wave_sync();
 }
 
+__host__ __device__ inline size_t stream_wave_bytes(int cap) { return (size_t)cap * 8 + sizeof(SelScratch); }
+__host__ __device__ inline size_t stream_smem_bytes(int cap, int max_visible) {
+    return 4 * stream_wave_bytes(cap) + ((size_t)(max_visible + kPage - 1) / kPage * 4 + 15) / 16 * 16;
+}
+
 template <int MB, int D, bool FP8>
 __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs A, StreamArgs S) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int next_tile;
+    __shared__ int tile_seq, tile_rows;
+    constexpr int QPT = kStreamThreads / kWave;   // queries per tile, one per wave
     const int w = threadIdx.x / kWave;
-    const size_t per_wave = (size_t)S.cap * 8 + sizeof(SelScratch);
-    uint8_t* base = smem + w * per_wave;
+    uint8_t* base = smem + w * stream_wave_bytes(S.cap);
     WaveBuf B{reinterpret_cast<uint32_t*>(base), reinterpret_cast<int32_t*>(base + (size_t)S.cap * 4),
               reinterpret_cast<SelScratch*>(base + (size_t)S.cap * 8)};
-    constexpr int QPT = kStreamThreads / kWave;   // queries per tile
+    int* pages = reinterpret_cast<int*>(smem + QPT * stream_wave_bytes(S.cap));
+
+    // One tile: four consecutive queries of one sequence. Their page ids are staged
+    // once in LDS; a query of another sequence is dropped (status bit).
     auto run_tile = [&](int tile) {
         const int j = tile * QPT + w;
-        if (j < A.num_q) stream_query<MB, D, FP8>(A, S, j, B);
+        int b = 0, rl = 0;
+        if (j < A.num_q) rl = visible_len(A, j, b);
+        if (w == 0 && lane_id() == 0) tile_seq = b;
+        __syncthreads();
+        const int b0 = tile_seq;
+        if (j < A.num_q && b != b0) {
+            if (lane_id() == 0) atomicOr(A.status, kBadSeq);
+            rl = 0;
+        }
+        // longest row of the tile
+        if (w == 0 && lane_id() == 0) tile_rows = 0;
+        __syncthreads();
+        if (lane_id() == 0) atomicMax(&tile_rows, rl);
+        __syncthreads();
+        const int npg = (tile_rows + kPage - 1) / kPage;
+        for (int i = threadIdx.x; i < npg; i += kStreamThreads) pages[i] = page_of(A, b0, i);
+        __syncthreads();
+        if (j < A.num_q) stream_query<MB, D, FP8>(A, S, j, rl, pages, B);
+        __syncthreads();
     };
     if (S.sched == 0) {
         run_tile(blockIdx.x);
@@ -513,12 +884,14 @@ static hipError_t set_smem(K kernel, size_t bytes) {
 
 template <int MB, int D, bool FP8, int G, bool SC>
 static hipError_t split_launch(const IdxArgs& a, const SplitArgs& s, hipStream_t st) {
+    constexpr int NT = SplitGeom<D, FP8, G>::NT;
     const int groups = (a.num_q + G - 1) / G;
-    const size_t smem = SC ? 16 : (size_t)G * s.chunk * 4 + sizeof(SelScratch);
+    const size_t smem = split_pages_bytes(s.chunk) +
+                        (SC ? 0 : (size_t)G * (s.chunk + kCoarseBins) * 4 + sizeof(SelScratch));
     auto k = indexer_split_kernel<MB, D, FP8, G, SC>;
     hipError_t e = set_smem(k, smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(groups * s.n_chunks), dim3(kSplitThreads), smem, st, a, s);
+    hipLaunchKernelGGL(k, dim3(groups * s.n_chunks), dim3(NT), smem, st, a, s);
     return hipGetLastError();
 }
 
@@ -530,6 +903,16 @@ static hipError_t split_launch2(const IdxArgs& a, const SplitArgs& s, bool sc, h
 template <int MB, int D, bool FP8>
 static hipError_t split_launch3(const IdxArgs& a, const SplitArgs& s, int g, bool sc, hipStream_t st) {
     return g == 2 ? split_launch2<MB, D, FP8, 2>(a, s, sc, st) : split_launch2<MB, D, FP8, 1>(a, s, sc, st);
+}
+
+int indexer_split_chunk_cap(int mb, int dim, bool fp8, int group) {
+#define SIA_CAP(MBv, Dv, F8)                                                              \
+    if (mb == MBv && dim == Dv && fp8 == F8)                                              \
+        return group == 2 ? split_chunk_cap<MBv, Dv, F8, 2>() : split_chunk_cap<MBv, Dv, F8, 1>();
+    SIA_CAP(1, 64, false) SIA_CAP(1, 64, true) SIA_CAP(1, 128, false) SIA_CAP(1, 128, true)
+    SIA_CAP(2, 64, false) SIA_CAP(2, 64, true) SIA_CAP(2, 128, false) SIA_CAP(2, 128, true)
+#undef SIA_CAP
+    return 2048;
 }
 
 hipError_t launch_indexer_split(const IdxArgs& a, const SplitArgs& s, int mb, int dim, bool fp8,
@@ -553,19 +936,18 @@ hipError_t launch_topk_from_scores(const FromScoresArgs& f, const SplitArgs& s, 
 }
 
 hipError_t launch_topk_merge(const MergeArgs& m, hipStream_t st) {
-    const size_t smem = (size_t)m.fan_in * m.kc_in * 4 + sizeof(SelScratch);
+    const size_t smem = ((size_t)m.fan_in * m.kc_in + kCoarseBins + m.topk + (m.fan_in + 3) / 4 * 4) * 4 +
+                        sizeof(SelScratch);
     hipError_t e = set_smem(topk_merge_kernel, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_merge_kernel, dim3(m.num_q * m.n_out), dim3(kMergeThreads), smem, st, m);
     return hipGetLastError();
 }
 
-static size_t stream_smem(int cap) { return 4 * ((size_t)cap * 8 + sizeof(SelScratch)); }
-
 template <int MB, int D, bool FP8>
 static hipError_t stream_launch(const IdxArgs& a, const StreamArgs& s, int grid, hipStream_t st) {
     auto k = indexer_stream_kernel<MB, D, FP8>;
-    const size_t smem = stream_smem(s.cap);
+    const size_t smem = stream_smem_bytes(s.cap, a.max_visible);
     hipError_t e = set_smem(k, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kStreamThreads), smem, st, a, s);
@@ -573,9 +955,9 @@ static hipError_t stream_launch(const IdxArgs& a, const StreamArgs& s, int grid,
 }
 
 template <int MB, int D, bool FP8>
-static int stream_occupancy(int cap) {
+static int stream_occupancy(int cap, int max_visible) {
     auto k = indexer_stream_kernel<MB, D, FP8>;
-    const size_t smem = stream_smem(cap);
+    const size_t smem = stream_smem_bytes(cap, max_visible);
     if (set_smem(k, smem) != hipSuccess) return 1;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k),
@@ -594,9 +976,11 @@ hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, 
     return hipErrorInvalidValue;
 }
 
-int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap) {
+size_t indexer_stream_smem(int cap, int max_visible) { return stream_smem_bytes(cap, max_visible); }
+
+int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap, int max_visible) {
 #define SIA_OCC(MBv, Dv, F8) \
-    if (mb == MBv && dim == Dv && fp8 == F8) return stream_occupancy<MBv, Dv, F8>(cap);
+    if (mb == MBv && dim == Dv && fp8 == F8) return stream_occupancy<MBv, Dv, F8>(cap, max_visible);
     SIA_OCC(1, 64, false) SIA_OCC(1, 64, true) SIA_OCC(1, 128, false) SIA_OCC(1, 128, true)
     SIA_OCC(2, 64, false) SIA_OCC(2, 64, true) SIA_OCC(2, 128, false) SIA_OCC(2, 128, true)
 #undef SIA_OCC

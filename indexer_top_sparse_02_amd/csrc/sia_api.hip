@@ -124,7 +124,9 @@ void plan_merge(IndexerPlan& p, int64_t num_q, int topk, size_t cand_key, size_t
         MergeLevel L;
         L.n_in = n_in;
         L.kc_in = kc_in;
-        L.fan_in = std::max(1, std::min(n_in, sia::kMergeCap / kc_in));
+        // keys of fan_in candidate sets, the coarse histogram and the rank list share LDS
+        const int cap_keys = (int)((sia::kMaxLds - 4 * (size_t)sia::kCoarseBinsHost - 4 * (size_t)topk - 4096) / 4);
+        L.fan_in = std::max(2, std::min(n_in, std::min(sia::kMergeCap, cap_keys) / kc_in));
         L.n_out = (int)ceil_div(n_in, L.fan_in);
         L.in_key = ik; L.in_pos = ip; L.in_cnt = ic;
         L.out_key = L.out_pos = L.out_cnt = 0;
@@ -141,22 +143,21 @@ void plan_merge(IndexerPlan& p, int64_t num_q, int topk, size_t cand_key, size_t
     }
 }
 
-void plan_split(IndexerPlan& p, int64_t num_q, int max_visible, int topk, int group_cap) {
+void plan_split(IndexerPlan& p, int64_t num_q, int max_visible, int topk, int group_cap, int chunk_max) {
     p.group = group_cap;
     const int64_t n_groups = ceil_div(num_q, p.group);
-    const int chunk_max = p.group == 2 ? 8192 : 16384;   // 64 KB of keys per workgroup
     int chunk;
     const int forced = env_int("SIA_SPLIT_CHUNK", 0);
     if (forced > 0) {
-        chunk = std::max(32, std::min(chunk_max, forced / 32 * 32));
+        chunk = std::max(64, std::min(chunk_max, forced / 64 * 64));
     } else if (max_visible <= 4096) {
-        chunk = std::max(32, (max_visible + 31) / 32 * 32);
+        chunk = std::max(64, std::min(chunk_max, (max_visible + 63) / 64 * 64));
     } else {
         const int64_t target = ceil_div((int64_t)max_visible * n_groups, 1024);
         chunk = std::max(2048, std::min(chunk_max, round_up_pow2(target)));
     }
     p.n_chunks = (int)std::max<int64_t>(1, ceil_div(std::max(max_visible, 1), chunk));
-    if (p.n_chunks == 1) chunk = std::max(32, std::min(chunk_max, (max_visible + 31) / 32 * 32));
+    if (p.n_chunks == 1) chunk = std::max(64, std::min(chunk_max, (max_visible + 63) / 64 * 64));
     p.chunk = chunk;
     p.kc = std::min(topk, chunk);
     if (p.n_chunks > 1) {
@@ -168,7 +169,7 @@ void plan_split(IndexerPlan& p, int64_t num_q, int max_visible, int topk, int gr
     }
 }
 
-IndexerPlan plan_indexer(const sia_queries* qs, int topk) {
+IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bool fp8) {
     IndexerPlan p;
     const int mode = env_int("SIA_INDEXER_PATH", 0);   // 0 auto, 1 split, 2 stream
     const bool stream_ok = topk <= 2048 && qs->group % 4 == 0;
@@ -176,11 +177,16 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk) {
     if (mode == 1) stream = false;
     if (mode == 2) stream = stream_ok;
     if (stream) {
-        p.stream = true;
-        p.cap = std::min(4096, std::max(1024, 2 * topk));
-        return p;
+        const int cap = std::min(4096, std::max(1024, 2 * topk));
+        // the candidate buffers and the staged page ids must fit in LDS
+        if (sia::indexer_stream_smem(cap, qs->max_visible) + 64 <= sia::kMaxLds) {
+            p.stream = true;
+            p.cap = cap;
+            return p;
+        }
     }
-    plan_split(p, qs->num_q, qs->max_visible, topk, qs->group % 2 == 0 ? 2 : 1);
+    const int g = qs->group % 2 == 0 ? 2 : 1;
+    plan_split(p, qs->num_q, qs->max_visible, topk, g, sia::indexer_split_chunk_cap(heads > 32 ? 2 : 1, dim, fp8, g));
     return p;
 }
 
@@ -256,9 +262,9 @@ extern "C" {
 size_t sia_indexer_workspace_size(const sia_page_table* pt, const sia_paged_cache* index_k,
                                   const sia_queries* qs, int32_t heads, int32_t topk) {
     if (check_page_table(pt) != SIA_OK || check_index_cache(index_k) != SIA_OK ||
-        check_queries(qs, pt) != SIA_OK || heads < 1 || heads > 64 || topk < 1 || topk > 16384)
+        check_queries(qs, pt) != SIA_OK || heads < 1 || heads > 64 || topk < 1 || topk > 8192)
         return 0;
-    return plan_indexer(qs, topk).total;
+    return plan_indexer(qs, topk, heads, index_k->dim, index_k->dtype == SIA_FP8_E4M3FN).total;
 }
 
 int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
@@ -267,10 +273,10 @@ int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k
                         size_t workspace_bytes, void* stream) {
     int rc = check_indexer_common(pt, index_k, qs, q_idx, w, heads);
     if (rc != SIA_OK) return rc;
-    if (topk < 1 || topk > 16384) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..16384", topk);
+    if (topk < 1 || topk > 8192) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..8192", topk);
     if (qs->num_q > 0 && !out_idx) return fail(SIA_ERR_INVALID_ARG, "out_idx is NULL");
     if (sched < -1 || sched > 2) return fail(SIA_ERR_INVALID_ARG, "sched %d", sched);
-    const IndexerPlan p = plan_indexer(qs, topk);
+    const IndexerPlan p = plan_indexer(qs, topk, heads, index_k->dim, index_k->dtype == SIA_FP8_E4M3FN);
     if ((rc = check_workspace(workspace, workspace_bytes, p.total)) != SIA_OK) return rc;
     if (qs->num_q == 0) return SIA_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -294,7 +300,7 @@ int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k
         if (s.sched == 1) {
             e = sia::launch_fill_u32(s.counter, 0u, 1, st);
             if (e != hipSuccess) return hip_fail(e, "counter reset");
-            const int occ = sia::indexer_stream_blocks_per_cu(mb, index_k->dim, fp8, p.cap);
+            const int occ = sia::indexer_stream_blocks_per_cu(mb, index_k->dim, fp8, p.cap, qs->max_visible);
             grid = std::min<int64_t>(s.n_tiles, (int64_t)occ * device_cus());
         }
         e = sia::launch_indexer_stream(a, s, mb, index_k->dim, fp8, grid, st);
@@ -348,9 +354,9 @@ int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index
 }
 
 size_t sia_topk_workspace_size(int32_t num_q, int32_t max_row_len, int32_t topk) {
-    if (num_q < 0 || max_row_len < 0 || topk < 1 || topk > 16384) return 0;
+    if (num_q < 0 || max_row_len < 0 || topk < 1 || topk > 8192) return 0;
     IndexerPlan p;
-    plan_split(p, num_q, max_row_len, topk, 1);
+    plan_split(p, num_q, max_row_len, topk, 1, 16384);
     return p.total;
 }
 
@@ -359,10 +365,10 @@ int sparse_topk_from_scores(const float* scores, int64_t ld, const int32_t* row_
                             void* workspace, size_t workspace_bytes, void* stream) {
     if (num_q < 0) return fail(SIA_ERR_INVALID_ARG, "num_q %d < 0", num_q);
     if (num_q > 0 && (!scores || !row_len || !out_idx)) return fail(SIA_ERR_INVALID_ARG, "NULL pointer");
-    if (topk < 1 || topk > 16384) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..16384", topk);
+    if (topk < 1 || topk > 8192) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..8192", topk);
     if (max_row_len < 0 || ld < max_row_len) return fail(SIA_ERR_INVALID_ARG, "need 0 <= max_row_len <= ld");
     IndexerPlan p;
-    plan_split(p, num_q, max_row_len, topk, 1);
+    plan_split(p, num_q, max_row_len, topk, 1, 16384);
     int rc = check_workspace(workspace, workspace_bytes, p.total);
     if (rc != SIA_OK) return rc;
     if (num_q == 0) return SIA_OK;

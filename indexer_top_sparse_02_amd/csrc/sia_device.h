@@ -35,18 +35,21 @@ __device__ __forceinline__ uint32_t pack_hi16(float x0, float x1) {
     return (__float_as_uint(x0) >> 16) | (__float_as_uint(x1) & 0xffff0000u);
 }
 
-// Eight OCP e4m3fn codes (bytes of lo, then hi) -> eight bf16. Exact: every
-// e4m3fn value, subnormals included, is a bf16 value.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Eight OCP e4m3fn codes (bytes of lo, then hi) -> eight bf16, two per
+// instruction (scale 1.0). Exact: every e4m3fn value, subnormals included, is a
+// bf16 value.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-    f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-    f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
     u32x4 r;
-    r[0] = pack_hi16(a[0], a[1]);
-    r[1] = pack_hi16(b[0], b[1]);
-    r[2] = pack_hi16(c[0], c[1]);
-    r[3] = pack_hi16(d[0], d[1]);
+    r[0] = __builtin_bit_cast(uint32_t, a);
+    r[1] = __builtin_bit_cast(uint32_t, b);
+    r[2] = __builtin_bit_cast(uint32_t, c);
+    r[3] = __builtin_bit_cast(uint32_t, d);
     return as_bf16x8(r);
 }
 
@@ -87,14 +90,16 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP lane moves (no LDS
+// round trips): shifts by 1, 2, 4, 8 within each row of 16 lanes, then the last
+// lane of row 0 is added to rows 1 and 3 and the last lane of row 1 to rows 2, 3.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-    const int l = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int o = __shfl_up(v, d, kWave);
-        if (l >= d) v += o;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
     return v;
 }
 
@@ -140,6 +145,31 @@ __device__ __forceinline__ void scan2(int a, int b, int& a_pre, int& b_pre, int&
         int exc = before + inc - v;
         a_pre = exc & 0xffff; b_pre = exc >> 16;
         a_tot = tot & 0xffff; b_tot = tot >> 16;
+    }
+}
+
+// Exclusive prefix sum of one counter over NT threads (same conventions as scan2).
+template <int NT>
+__device__ __forceinline__ void scan1(int v, int& pre, int& tot, int* scratch) {
+    const int inc = wave_incl_scan(v);
+    if constexpr (NT == kWave) {
+        tot = __shfl(inc, kWave - 1, kWave);
+        pre = inc - v;
+    } else {
+        constexpr int NW = NT / kWave;
+        const int w = threadIdx.x / kWave;
+        if (lane_id() == kWave - 1) scratch[w] = inc;
+        __syncthreads();
+        int before = 0, t = 0;
+#pragma unroll
+        for (int i = 0; i < NW; i++) {
+            const int x = scratch[i];
+            before += (i < w) ? x : 0;
+            t += x;
+        }
+        __syncthreads();
+        pre = before + inc - v;
+        tot = t;
     }
 }
 

@@ -66,16 +66,21 @@ struct StreamArgs {
 // Launchers; return hipSuccess or the launch error. `mb` = ceil(heads / 32).
 hipError_t launch_indexer_split(const IdxArgs& a, const SplitArgs& s, int mb, int dim, bool fp8,
                                 int group, bool scores_mode, hipStream_t st);
+// Largest chunk the split kernel's LDS holds for this instantiation.
+int indexer_split_chunk_cap(int mb, int dim, bool fp8, int group);
 hipError_t launch_topk_from_scores(const FromScoresArgs& f, const SplitArgs& s, hipStream_t st);
 hipError_t launch_topk_merge(const MergeArgs& m, hipStream_t st);
 hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, bool fp8,
                                  int grid, hipStream_t st);
-int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap);
+int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap, int max_visible);
+size_t indexer_stream_smem(int cap, int max_visible);
+constexpr size_t kMaxLds = 160 * 1024;
+constexpr int kCoarseBinsHost = 2048;   // = kCoarseBins of the selection code
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
 
-constexpr int kSplitThreads = 256;
+constexpr int kSplitThreads = 512;   // eight waves: two per SIMD
 constexpr int kMergeThreads = 512;
-constexpr int kMergeCap = 32768;       // keys one merge workgroup holds in LDS
+constexpr int kMergeCap = 32768;       // keys one merge workgroup holds in LDS (128 KB)
 constexpr int kStreamThreads = 256;    // four waves, one query each
 
 // Attention.

@@ -37,25 +37,33 @@ __device__ __forceinline__ int sel_tid() {
     else return threadIdx.x;
 }
 
-// Step 1. keys: LDS, readable in groups of four (16-byte aligned; entries past n
-// may hold anything). Returns T; `ties` = number of key == T elements to keep.
+// hist[digit] += 1 for every active lane (LDS atomics; digits of the coarse
+// and refinement passes are spread enough that conflicts stay low).
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t digit, bool active) {
+    if (active) atomicAdd(&hist[digit], 1u);
+}
+
+// Step 1, refinement: the bits above `lowbit` are settled (`prefix` under
+// `pmask`) and `rem` elements matching the prefix are still to be taken. Finds
+// the remaining low bits in passes of up to 8 bits. keys: LDS, readable in
+// groups of four (16-byte aligned; entries past n may hold anything). Returns
+// T; `ties` = number of key == T elements to keep.
 template <int NT>
-__device__ uint32_t radix_threshold(const uint32_t* keys, int n, int m, SelScratch* s,
-                                    int& ties) {
+__device__ uint32_t radix_refine(const uint32_t* keys, int n, uint32_t prefix, uint32_t pmask,
+                                 int rem, int lowbit, SelScratch* s, int& ties) {
     const int tid = sel_tid<NT>();
-    uint32_t prefix = 0, pmask = 0;
-    int rem = m;
-    for (int pass = 0; pass < 4; pass++) {
-        const int shift = 24 - 8 * pass;
+    while (lowbit > 0) {
+        const int width = lowbit < 8 ? lowbit : 8;
+        const int shift = lowbit - width;
+        const uint32_t dmask = (1u << width) - 1u;
         for (int i = tid; i < 256; i += NT) s->hist[i] = 0;
         sel_sync<NT>();
         for (int i = tid * 4; i < n; i += NT * 4) {
             u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
 #pragma unroll
             for (int e = 0; e < 4; e++) {
-                uint32_t k = k4[e];
-                if (i + e < n && (k & pmask) == prefix)
-                    atomicAdd(&s->hist[(k >> shift) & 255u], 1u);
+                const uint32_t k = k4[e];
+                hist_add(s->hist, (k >> shift) & dmask, i + e < n && k != 0u && (k & pmask) == prefix);
             }
         }
         sel_sync<NT>();
@@ -80,51 +88,100 @@ __device__ uint32_t radix_threshold(const uint32_t* keys, int n, int m, SelScrat
         const int digit = s->bcast[0];
         const int above = s->bcast[1];
         prefix |= (uint32_t)digit << shift;
-        pmask |= 255u << shift;
+        pmask |= dmask << shift;
         rem -= above;
+        lowbit = shift;
         sel_sync<NT>();
     }
     ties = rem;
     return prefix;
 }
 
-// Step 2. Calls emit(rank, index, key) for each kept element, ranks 0..m-1 in
-// ascending index. `keys` may be compacted in place by emit (emit may only write
-// at index rank <= index, and reads of a round happen before its writes).
-template <int NT, typename Emit>
+// Step 1 from scratch: all 32 bits.
+template <int NT>
+__device__ uint32_t radix_threshold(const uint32_t* keys, int n, int m, SelScratch* s, int& ties) {
+    return radix_refine<NT>(keys, n, 0u, 0u, m, 32, s, ties);
+}
+
+// Top bits of a key used for the coarse histogram (11 bits: sign, exponent and
+// two mantissa bits of the score, i.e. quarter-octave bins).
+constexpr int kCoarseBits = 11;
+constexpr int kCoarseBins = 1 << kCoarseBits;
+__device__ __forceinline__ uint32_t coarse_bin(uint32_t key) { return key >> (32 - kCoarseBits); }
+
+// From a coarse histogram of the candidate keys (kCoarseBins counters in LDS),
+// find the bin that holds the m-th largest key. Returns the bin; `above` = keys
+// in higher bins, `total` = all counted keys. Block-wide (NT threads).
+template <int NT>
+__device__ int coarse_select(const uint32_t* hist, int m, SelScratch* s, int& above, int& total) {
+    constexpr int PER = kCoarseBins / NT;   // bins per thread, descending
+    const int tid = sel_tid<NT>();
+    int c[PER];
+    int sum = 0;
+#pragma unroll
+    for (int e = 0; e < PER; e++) { c[e] = (int)hist[kCoarseBins - 1 - (PER * tid + e)]; sum += c[e]; }
+    int pre, tot;
+    scan1<NT>(sum, pre, tot, s->scan);
+    if (tid == 0) s->bcast[2] = -1;
+    sel_sync<NT>();
+    int run = pre;
+#pragma unroll
+    for (int e = 0; e < PER; e++) {
+        if (run < m && run + c[e] >= m) {
+            s->bcast[2] = kCoarseBins - 1 - (PER * tid + e);
+            s->bcast[3] = run;
+        }
+        run += c[e];
+    }
+    sel_sync<NT>();
+    const int bin = s->bcast[2];
+    above = s->bcast[3];
+    total = tot;
+    sel_sync<NT>();
+    return bin;
+}
+
+// Step 2. Calls emit(rank, index, e, key) for each kept element, ranks 0..m-1 in
+// ascending index. Each thread takes 8 consecutive keys per round. With
+// InPlace, emit may overwrite keys/positions at index rank <= index: every read
+// of a round (keys here, emit.prefetch) happens before the round's writes.
+template <int NT, bool InPlace = false, typename Emit>
 __device__ void ordered_compact(const uint32_t* keys, int n, uint32_t T, int ties,
                                 SelScratch* s, Emit&& emit) {
+    constexpr int EPT = 8;
     const int tid = sel_tid<NT>();
     int run_gt = 0, run_eq = 0;
-    for (int base = 0; base < n; base += NT * 4) {
-        const int i = base + tid * 4;
-        u32x4 k4 = {0u, 0u, 0u, 0u};
-        if (i < n) k4 = *reinterpret_cast<const u32x4*>(keys + i);
+    for (int base = 0; base < n; base += NT * EPT) {
+        const int i = base + tid * EPT;
+        u32x4 ka = {0u, 0u, 0u, 0u}, kb = {0u, 0u, 0u, 0u};
+        if (i < n) ka = *reinterpret_cast<const u32x4*>(keys + i);
+        if (i + 4 < n) kb = *reinterpret_cast<const u32x4*>(keys + i + 4);
         int gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            if (i + e >= n) k4[e] = 0u;
-            gt += k4[e] > T;
-            eq += k4[e] == T;
+            if (i + e >= n) ka[e] = 0u;
+            if (i + 4 + e >= n) kb[e] = 0u;
+            gt += (ka[e] > T) + (kb[e] > T);
+            eq += (ka[e] == T) + (kb[e] == T);
         }
+        // index-based reads of the elements that may be kept start before the
+        // scan, so their latency overlaps it
+        emit.prefetch(i, ka, T);
+        emit.prefetch2(i + 4, kb, T);
         int gpre, epre, gtot, etot;
         scan2<NT>(gt, eq, gpre, epre, gtot, etot, s->scan);
         int eq_before = run_eq + epre;
         int rank = run_gt + gpre + min(eq_before, ties);
-        // positions of this round are read (by emit through its own state) before
-        // any write of this round: emit is given the key, and index-based reads
-        // are done by the caller's prefetch hook below.
-        emit.prefetch(i, k4);
-        sel_sync<NT>();
+        if constexpr (InPlace) sel_sync<NT>();
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            uint32_t k = k4[e];
+        for (int e = 0; e < 8; e++) {
+            const uint32_t k = e < 4 ? ka[e] : kb[e - 4];
             bool take = false;
             if (k > T) take = true;
             else if (k == T) { take = eq_before < ties; eq_before++; }
             if (take) emit(rank++, i + e, e, k);
         }
-        sel_sync<NT>();
+        if constexpr (InPlace) sel_sync<NT>();
         run_gt += gtot;
         run_eq += etot;
     }
@@ -152,6 +209,26 @@ __device__ int count_nonzero(const uint32_t* keys, int n, SelScratch* s) {
         __syncthreads();
         return tot;
     }
+}
+
+// Select the top min(m_cap, nonzero) of keys[0..n) given `hist`, the coarse
+// histogram of exactly the nonzero keys, and emit them in index order.
+template <int NT, typename Emit>
+__device__ int select_emit_coarse(const uint32_t* keys, int n, const uint32_t* hist, int m_cap,
+                                  SelScratch* s, Emit&& emit) {
+    int above, total;
+    const int bin = coarse_select<NT>(hist, m_cap, s, above, total);
+    const int m = min(m_cap, total);
+    if (m <= 0) return 0;
+    if (m == total) {
+        ordered_compact<NT>(keys, n, 0u, 0, s, emit);   // every nonzero key
+        return m;
+    }
+    int ties;
+    const uint32_t T = radix_refine<NT>(keys, n, (uint32_t)bin << (32 - kCoarseBits),
+                                        ~0u << (32 - kCoarseBits), m - above, 32 - kCoarseBits, s, ties);
+    ordered_compact<NT>(keys, n, T, ties, s, emit);
+    return m;
 }
 
 }  // namespace sia

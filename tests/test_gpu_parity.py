@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads as W
-from _paths import (check_attention, check_band, check_scores, env, gpu_attention, gpu_scores,
+from _paths import (check_attention, check_band, check_scores, env, gpu_attention, gpu_scores, group_of,
                     gpu_topk, oracle_topk_of, row_lengths, score_tol)
 
 pytestmark = pytest.mark.gpu
@@ -128,6 +128,32 @@ def test_split_and_stream_paths_agree():
     with env(SIA_INDEXER_PATH=2):
         b, _ = gpu_topk(wl)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("chunk", [0, 256, 1024])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_split_path_causal_rows_exact(chunk, fp8):
+    """Split path on causal rows: with the library's chunk choice (which must
+    respect the LDS bound of the bf16 rows) and with forced chunks that leave
+    late chunks invisible to early queries. The workspace starts as garbage, so
+    a candidate count that is never written would show."""
+    import indexer_top_sparse_02_amd as sia
+    s = W.spec("prefill_16k", ctx_lo=1800, ctx_hi=1800, topk=256, idx_fp8=fp8)
+    wl = W.make(s, device="cuda")
+    sc = gpu_scores(wl)
+    rl = row_lengths(wl)
+    kw = dict(SIA_INDEXER_PATH=1)
+    if chunk:
+        kw["SIA_SPLIT_CHUNK"] = chunk
+    with env(**kw):
+        need = sia.indexer_workspace_size(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq,
+                                          wl.q_pos, s.heads_idx, s.topk, group=group_of(wl))
+        ws = sia.new_workspace(need, "cuda")
+        ws.fill_(0x5a)
+        ws[:256].zero_()   # the status word starts clear
+        got, _ = gpu_topk(wl, workspace=ws)
+    ref, _ = oracle_topk_of(sc, rl, s.topk)
+    assert np.array_equal(got.cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("sched", [0, 1, 2])
