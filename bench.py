@@ -29,7 +29,63 @@ def _args():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="spec_decode_128k")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="instead of the path, run a plain device copy of this many bytes "
+                        "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
+
+
+# Sources of the kernels the roofline line reports on: a traffic figure taken
+# from hardware counters is only valid for the code it was measured on.
+KERNEL_SOURCES = ["indexer.hip", "sia_device.h", "sia_select.h", "sia_kernels.h", "sia_sched.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_traffic_spec_decode_128k.md")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space removed, so that
+    only a change of the code itself invalidates a counter figure."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "indexer_top_sparse_02_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(ln.strip() for ln in text.splitlines() if ln.strip()).encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per indexer call from the committed counter summary, or None
+    when there is none for this workload or the kernels changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("workload") != workload or fields.get("kernel source hash") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm bytes per call"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int):
+    """A plain device-to-device copy of nbytes, five times: the bytes a perfect
+    counter would report per dispatch are nbytes read and nbytes written."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda:0").fill_(7)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "dispatches": 5}))
 
 
 def algorithmic_bytes(wl, idx):
@@ -59,28 +115,36 @@ def algorithmic_bytes(wl, idx):
                 + Q * s.topk * 4)
 
 
-def cpu_baseline(wl_gpu, s):
-    """The oracle on a bounded sample of the same workload (one sequence)."""
+def cpu_baseline(wl_gpu, s, budget_s: float = 12.0):
+    """The oracle on a bounded sample of the same workload: whole sequences,
+    taken in order until about budget_s seconds of CPU work are done."""
     import oracle
     import workloads as W
-    seq = 0
-    sub = W.subset(wl_gpu, [seq], device="cpu")
     oracle.build(force=False)
-    t0 = time.perf_counter()
-    oracle.run(sub, attention=True)
-    dt = time.perf_counter() - t0
-    nq = sub.num_q
+    nq, dt, seqs = 0, 0.0, 0
+    for seq in range(int(wl_gpu.seq_lens.numel())):
+        sub = W.subset(wl_gpu, [seq], device="cpu")
+        t0 = time.perf_counter()
+        oracle.run(sub, attention=True)
+        dt += time.perf_counter() - t0
+        nq += sub.num_q
+        seqs += 1
+        if dt >= budget_s:
+            break
     return {"value": nq / dt, "unit": "query tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{nq} query tokens (sequence {seq}, {int(sub.seq_lens[0])} positions) of "
-                      f"{s.name}: indexer, Top-K and attention, {dt:.2f} s"}
+            "sample": f"{nq} query tokens of {seqs} sequences ({s.ctx_hi} positions each) of "
+                      f"{s.name}: indexer, Top-K and attention, {dt:.1f} s"}
 
 
 def main():
     a = _args()
+    if a.copy_bytes:
+        copy_calibration(a.copy_bytes)
+        return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
-                          "n_gpus": a.gpus}))
+        print(json.dumps({"error": "this implementation runs on one GPU (no sharding or "
+                                   "collectives); --gpus must be 1", "n_gpus": a.gpus}))
         sys.exit(2)
     import torch
 
@@ -139,12 +203,14 @@ def main():
     step_gbs = by["total"] / (ms * 1e-3) / 1e9
     idx_gbs = by["indexer"] / (idx_ms * 1e-3) / 1e9
     line = {
-        "metric": "decode query tokens/s at 128K context (indexer + Top-K + sparse MLA attention)",
+        "metric": "decode queries/s and HBM GB/s at 128K ctx; prefill tokens/s (indexer+TopK+sparse attn)",
         "value": wl.num_q / (ms * 1e-3),
         "unit": "query tokens/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8-e4m3fn index cache, bf16 MFMA (fp32 accumulate), bf16 latent KV",
+        "dtype": "bf16",
+        "dtype_detail": "fp8 e4m3fn index cache widened exactly to bf16; bf16 MFMA with fp32 "
+                        "accumulate; bf16 latent KV; fp32 softmax",
         "data": "synthetic (seeded N(0,1) caches and queries, shuffled page tables)",
         "config": {"workload": s.name, "batch": s.batch, "context": s.ctx_hi,
                    "query_tokens": wl.num_q, "indexer_heads": s.heads_idx, "index_dim": s.dim_idx,
@@ -152,9 +218,12 @@ def main():
         "hbm_gbs_step": step_gbs,
         "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
         "algorithmic_bytes": by,
-        "roofline": {"bound": "hbm", "kernel": "sparse_indexer_topk (indexer split + top-k merge)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "sparse_indexer_topk call (indexer_split_kernel + topk_merge_kernel)",
                      "achieved": idx_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": idx_gbs / PEAK_HBM_GBS, "traffic": None},
+                     "frac": idx_gbs / PEAK_HBM_GBS, "traffic": measured_traffic(s.name),
+                     "algorithmic_bytes_per_call": by["indexer"],
+                     "call_ms": idx_ms},
     }
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, s)

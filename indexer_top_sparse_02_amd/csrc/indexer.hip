@@ -4,9 +4,10 @@
 //
 // The q . k products of one query against 32 positions are one MFMA tile:
 // heads are the M dimension (32 per block), positions the N dimension, the
-// index dim the K dimension. Queries sit in registers for the whole pass; each
-// lane streams its position's half-row of index-K straight from the paged pool
-// (fp8 rows are widened to bf16 exactly in registers). The accumulator puts 16
+// index dim the K dimension. Queries sit in registers for the whole pass; a
+// lane supplies its position's half-row of index-K (fp8 rows are widened to bf16
+// exactly in registers), staged through LDS by the split kernel and loaded
+// straight from the paged pool by the stream kernel. The accumulator puts 16
 // heads of one position in each lane, so the ReLU, the head weights and the head
 // sum stay in registers with a single cross-lane add, and sigma_s multiplies the
 // sum. Only the selected positions ever reach memory ("Rapid Adaptation and

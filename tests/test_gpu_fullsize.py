@@ -1,0 +1,106 @@
+"""Parity at the workloads' full sizes, in the launch configuration the benchmark
+times (fused Top-K call with the sequence's draft tokens grouped, then sparse
+attention on its output). The oracle cannot compute a full step in seconds, so
+sampled queries are compared one by one:
+
+* scores of the sampled rows (scores hook) against the oracle, within tolerance;
+* the fused Top-K bit-exact against the oracle's selection on the GPU's scores;
+* the fused Top-K against the oracle's own set by the boundary-band rule;
+* attention rows against the oracle on the GPU's indices.
+"""
+from __future__ import annotations
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import indexer_top_sparse_02_amd as sia
+import oracle
+import workloads as W
+from _paths import check_attention, check_band, check_scores, score_tol
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_path(wl, group, queries=None):
+    """Fused Top-K (+ scores) and attention for all queries (or a query range)."""
+    w = wl if queries is None else wl.queries(*queries)
+    s = wl.spec
+    maxv = int(torch.minimum(w.q_pos.long() + 1, w.seq_lens.long()[w.q_seq.long()]).max())
+    idx, top = sia.sparse_indexer_topk(w.page_table, w.seq_lens, w.idx_k, w.idx_scale, w.q_seq,
+                                       w.q_pos, w.q_idx, w.w, s.topk, group=group,
+                                       max_visible=maxv, want_score=True)
+    out, lse = sia.sparse_mla_attention(w.page_table, w.seq_lens, w.kv, w.q_seq, w.q_attn, idx,
+                                        s.sm_scale, want_lse=True)
+    scores = sia.sparse_indexer_scores(w.page_table, w.seq_lens, w.idx_k, w.idx_scale, w.q_seq,
+                                       w.q_pos, w.q_idx, w.w, group=group, max_visible=maxv)
+    torch.cuda.synchronize()
+    return w, idx, top, out, lse, scores
+
+
+def _check_rows(s, wl_ref, gpu_rows, idx, top, out, lse, scores, row_len):
+    """Compare GPU results on query rows `gpu_rows` with the oracle run on
+    `wl_ref` (a CPU workload holding exactly those queries, in order)."""
+    ref = oracle.run(wl_ref, attention=False)
+    g_scores = scores[gpu_rows].cpu().numpy()
+    ref_scores = np.full(g_scores.shape, -np.inf)
+    ref_scores[:, :ref.scores.shape[1]] = ref.scores[:, :g_scores.shape[1]]
+    tol = 3e-2 if s.idx_fp8 else 1e-2
+    check_scores(g_scores, ref_scores, row_len, tol)
+    g_idx = idx[gpu_rows].cpu().numpy()
+    sel, sel_sc = oracle.topk(g_scores.astype(np.float64), row_len, s.topk)
+    assert np.array_equal(g_idx, sel)
+    g_top = top[gpu_rows].cpu().numpy().astype(np.float64)
+    assert np.array_equal(g_top[g_idx >= 0], sel_sc[g_idx >= 0])
+    check_band(g_idx, ref.idx, ref_scores, tol)
+    o_ref, lse_ref = oracle.sparse_mla(wl_ref.q_seq, int(wl_ref.seq_lens.numel()), wl_ref.page_table,
+                                       wl_ref.kv, wl_ref.q_attn, g_idx, s.sm_scale)
+    return check_attention(out[gpu_rows], o_ref, lse[gpu_rows], lse_ref)
+
+
+@pytest.mark.parametrize("name", ["spec_decode_128k", "decode_b32"])
+def test_full_size_decode_sampled_sequences(name):
+    s = W.spec(name)
+    wl = W.make(s, device="cuda", poison=True)
+    _, idx, top, out, lse, scores = _gpu_path(wl, group=s.q_per_seq)
+    q_seq = wl.q_seq.cpu().numpy()
+    lens = wl.seq_lens.cpu().numpy()
+    for seq in (0, s.batch // 2, s.batch - 1):
+        rows = np.flatnonzero(q_seq == seq)
+        sub = W.subset(wl, [seq], device="cpu")
+        rl = np.minimum(wl.q_pos.cpu().numpy()[rows] + 1, lens[seq]).astype(np.int32)
+        print(f"{name}: sequence {seq}, {len(rows)} queries, {lens[seq]} positions", flush=True)
+        _check_rows(s, sub, rows, idx, top, out, lse, scores, rl)
+
+
+def _sampled_cpu(wl, rows):
+    """CPU copy of a one-sequence workload's caches with only query rows `rows`."""
+    r = torch.as_tensor(rows, dtype=torch.long, device=wl.q_idx.device)
+    cpu = lambda t: None if t is None else t.cpu()
+    return replace(wl, seq_lens=cpu(wl.seq_lens), page_table=cpu(wl.page_table),
+                   idx_k=cpu(wl.idx_k), idx_scale=cpu(wl.idx_scale), kv=cpu(wl.kv),
+                   q_idx=wl.q_idx[r].cpu(), w=wl.w[r].cpu(), q_attn=wl.q_attn[r].cpu(),
+                   q_seq=wl.q_seq[r].cpu(), q_pos=wl.q_pos[r].cpu())
+
+
+def test_full_size_prefill_16k_sampled_queries():
+    s = W.spec("prefill_16k")
+    wl = W.make(s, device="cuda", poison=True)
+    _, idx, top, out, lse, scores = _gpu_path(wl, group=wl.num_q)
+    rows = np.array([0, 1, 2046, 2047, 2048, 2049, 9001, 16382, 16383])
+    rl = (rows + 1).astype(np.int32)
+    print(f"prefill_16k: queries {rows.tolist()}", flush=True)
+    _check_rows(s, _sampled_cpu(wl, rows), rows, idx, top, out, lse, scores, rl)
+
+
+def test_full_size_chunked_prefill_last_chunk_sampled_queries():
+    s = W.spec("chunked_prefill_128k")
+    wl = W.make(s, device="cuda", poison=True)
+    start = wl.num_q - s.chunk
+    w, idx, top, out, lse, scores = _gpu_path(wl, group=s.chunk, queries=(start, wl.num_q))
+    local = np.array([0, 1, 4095, 8190, 8191])
+    rl = (start + local + 1).astype(np.int32)
+    print(f"chunked_prefill_128k: last chunk, queries {(start + local).tolist()}", flush=True)
+    _check_rows(s, _sampled_cpu(w, local), local, idx, top, out, lse, scores, rl)
