@@ -316,16 +316,6 @@ __device__ int select_emit(const uint32_t* keys, int n, int m_cap, SelScratch* s
 
 // ------------------------------------------------------------ split kernel
 
-#define SIA_LDS __attribute__((address_space(3)))
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits 3:0
-// and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // MFMA half of a tile: the raw q.k products of one query against 32
 // positions (heads x positions accumulators). The K tile is widened here.
 template <int MB, int D, bool FP8>

@@ -400,10 +400,14 @@ static int attn_plan(const sia_queries* qs, int heads, int topk, int& hb, int& n
                      size_t& total) {
     hb = heads % 64 == 0 ? 64 : heads % 32 == 0 ? 32 : 16;
     const int64_t base = (int64_t)qs->num_q * (heads / hb);
+    // one workgroup per CU is resident (LDS); split the rows only as far as it
+    // takes to give every CU one, keeping at least two tiles per slice and at
+    // most the slice length the kernel's row list holds
     int ns = env_int("SIA_ATTN_SPLIT", 0);
-    if (ns <= 0) ns = (int)std::max<int64_t>(1, ceil_div(1024, std::max<int64_t>(1, base)));
-    const int max_split = std::max(1, (int)ceil_div(topk, 128));
-    ns = std::min(ns, max_split);
+    if (ns <= 0) ns = (int)std::max<int64_t>(1, ceil_div(256, std::max<int64_t>(1, base)));
+    const int max_split = std::max(1, (int)ceil_div(topk, 64));
+    const int min_split = (int)ceil_div(topk, sia::kAttnMaxSliceRows);
+    ns = std::max(min_split, std::min(ns, max_split));
     rows_per_split = (int)ceil_div(ceil_div(topk, ns), 32) * 32;
     n_split = (int)ceil_div(topk, rows_per_split);
     total = kHeader;

@@ -78,6 +78,32 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+#define SIA_LDS __attribute__((address_space(3)))
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt in 6:4, lgkmcnt in 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then all waves meet. Unlike __syncthreads() it does not wait for
+// outstanding global -> LDS copies (whose completion is waited for explicitly
+// with counted vmcnt waits); the clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// D[16x16] += A[16x32] * B[32x16], bf16 in, fp32 accumulate.
+// Lane l holds A row l%16, k = 8*(l/16)+i; B column l%16, k = 8*(l/16)+i;
+// accumulator register r holds D[4*(l/16) + r][l%16].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

@@ -106,6 +106,7 @@ struct AttnArgs {
 };
 
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st);
+constexpr int kAttnMaxSliceRows = 2048;   // selected rows one attention workgroup takes at most
 hipError_t launch_mla_combine(const AttnArgs& a, hipStream_t st);
 
 }  // namespace sia
