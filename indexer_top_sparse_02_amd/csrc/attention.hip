@@ -65,19 +65,24 @@ __device__ __forceinline__ void lds_wait(u32x2 (&a)[4], u32x2 (&b)[4]) {
 // by r within aligned groups of eight).
 __device__ __forceinline__ int tile_off(int r, int c) { return r * kRowB + ((c ^ (r & 7)) << 4); }
 
-// Max / sum over the 16 lanes of a DPP row (lanes 16g .. 16g+15).
+// Max / sum over the 16 lanes of a DPP row (lanes 16g .. 16g+15), by rotations
+// of the row by 8, 4, 2 and 1 lanes.
+template <int N>
+__device__ __forceinline__ float dpp_ror(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x120 + N, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false)));
+    v = __builtin_fmaxf(v, dpp_ror<8>(v));
+    v = __builtin_fmaxf(v, dpp_ror<4>(v));
+    v = __builtin_fmaxf(v, dpp_ror<2>(v));
+    v = __builtin_fmaxf(v, dpp_ror<1>(v));
     return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+    v += dpp_ror<8>(v);
+    v += dpp_ror<4>(v);
+    v += dpp_ror<2>(v);
+    v += dpp_ror<1>(v);
     return v;
 }
 
@@ -263,11 +268,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
                 asm volatile("" : "+v"(voff[e][v]));
             }
 
-        // ---- partial logits of 16 heads x 32 rows over this wave's half row
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int k0 = 0; k0 < kQKHalf; k0 += 3) {
-            u32x4 kb[2][3];
+        // ---- partial logits of 16 heads x 32 rows over this wave's half row;
+        // the key reads of the next three steps are in flight during the MFMAs
+        auto kload = [&](u32x4 (&kb)[2][3], int k0) {
 #pragma unroll
             for (int i = 0; i < 3; i++) {
                 const int ks = k0 + i;
@@ -275,11 +278,24 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
                 for (int c = 0; c < 2; c++)
                     kb[c][i] = *reinterpret_cast<const u32x4*>(buf + koff[c][ks & 1] + ((4 * rb + 4 * ks) >> 3) * 128);
             }
+        };
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        u32x4 kb[2][3];
+        kload(kb, 0);
+#pragma unroll
+        for (int k0 = 0; k0 < kQKHalf; k0 += 3) {
+            u32x4 kn[2][3];
+            if (k0 + 3 < kQKHalf) kload(kn, k0 + 3);
 #pragma unroll
             for (int i = 0; i < 3; i++)
 #pragma unroll
                 for (int c = 0; c < 2; c++) acc[c] = mfma16(qa[k0 + i], as_bf16x8(kb[c][i]), acc[c]);
-            __builtin_amdgcn_sched_barrier(0);
+            if (k0 + 3 < kQKHalf) {
+#pragma unroll
+                for (int c = 0; c < 2; c++)
+#pragma unroll
+                    for (int i = 0; i < 3; i++) kb[c][i] = kn[c][i];
+            }
         }
         // the flag of tile t+1 is cleared now: every read of it (tile t-1) is done
         if (tid == 0) rescale[(t + 1) & 1] = 0;
@@ -299,18 +315,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         for (int r = 0; r < 4; r++) {
             const float x0 = v0 ? s0[r] * scale_log2 : -INFINITY;
             const float x1 = v1 ? s1[r] * scale_log2 : -INFINITY;
-            const float tm = row16_max(fmaxf(x0, x1));
-            al[r] = 1.f;
-            if (tm > m_ref[r] + kLazyMax) {   // also when m_ref is still -inf
-                al[r] = exp2f(m_ref[r] - tm);
-                m_ref[r] = tm;
-                moved = true;
-            }
-            const float p0 = exp2f(x0 - m_ref[r]), p1 = exp2f(x1 - m_ref[r]);
+            const float tm = row16_max(__builtin_fmaxf(x0, x1));
+            const bool mv = tm > m_ref[r] + kLazyMax;   // also when m_ref is still -inf
+            al[r] = mv ? __builtin_amdgcn_exp2f(m_ref[r] - tm) : 1.f;
+            m_ref[r] = mv ? tm : m_ref[r];
+            moved |= mv;
+            const float p0 = __builtin_amdgcn_exp2f(x0 - m_ref[r]), p1 = __builtin_amdgcn_exp2f(x1 - m_ref[r]);
             l_run[r] = l_run[r] * al[r] + (p0 + p1);
-            const float pm = rb ? p1 : p0;   // this wave writes P of its row block
-            *reinterpret_cast<uint16_t*>(pbuf + (hh + r) * kPStride + (rb * 16 + jl) * 2) =
-                (uint16_t)f32_to_bf16_rne(pm);
+            const __bf16 pm = static_cast<__bf16>(rb ? p1 : p0);   // this wave writes P of its row block
+            *reinterpret_cast<__bf16*>(pbuf + (hh + r) * kPStride + (rb * 16 + jl) * 2) = pm;
         }
         if (rb == 0 && jl == 0) *reinterpret_cast<f32x4*>(&alpha_s[hh]) = f32x4{al[0], al[1], al[2], al[3]};
         if (moved) rescale[t & 1] = 1;
