@@ -9,19 +9,21 @@
 // Workgroup = (query, block of HB heads, slice of the selected rows), with
 // 2*HB/16 waves. At the start the slice's indices are validated, mapped through
 // the page table and compacted (skipped entries removed, order kept) into a
-// list of physical row ids in LDS. Then, per tile of 32 rows:
-//   copy     the tile's rows go from HBM straight into an LDS ring slot (36 KB,
-//            three slots, direct global -> LDS copies issued two tiles ahead),
-//            row-major, with the 16-byte chunks of a row XOR-swizzled by the row
-//            index so that both operand reads below are free of bank conflicts
-//   Q K^T    wave (hb, rb) computes logits of its 16 heads x 16 rows with
-//            16x16x32 MFMAs over all 576 columns; its Q slice stays in registers
-//   softmax  online, per head: the two row-block waves of a head block exchange
-//            their tile maxima through LDS; P goes to LDS as bf16
+// list of physical row ids in LDS. Tiles of 32 rows go from HBM straight into a
+// three-slot LDS ring (direct global -> LDS copies), row-major, with the 16-byte
+// chunks of a row XOR-swizzled by the row index so that the operand reads below
+// are free of bank conflicts. Wave (hb, rb) owns 16 heads and the 16-row half rb
+// of every tile:
+//   Q K^T    16x16x32 MFMAs over all 576 columns; its Q slice stays in registers
+//   softmax  online, per head; the two row halves of a head block exchange only
+//            their per-head tile maxima through LDS; P goes to LDS as bf16
 //   P V      wave w owns output columns [w*512/NW, (w+1)*512/NW) of all heads;
 //            the value operand is read from the same row-major tile with
 //            transposing LDS reads (ds_read_b64_tr_b16), so no transposed copy
 //            of the values is ever made
+// The loop is software-pipelined: between two barriers, iteration t runs the
+// Q K^T of tile t+1 next to the softmax of tile t, then P V of tile t; the copy of
+// tile t+2 goes out as soon as the slot of tile t-1 is free.
 // Slices of one query are merged afterwards by log-sum-exp.
 #include "sia_device.h"
 #include "sia_kernels.h"
@@ -36,7 +38,6 @@ constexpr int kTileB = kTR * kRowB;         // 36864
 constexpr int kTileCopies = kTileB / 1024;  // 36 copies of 64 lanes x 16 bytes
 constexpr int kPStride = kTR * 2 + 16;      // bytes per head of P (padded: no bank conflicts)
 constexpr int kMaxSliceRows = kAttnMaxSliceRows;
-constexpr int kQKHalf = kDK / 64;           // 32-column MFMA steps over half a row (9)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -98,30 +99,35 @@ struct MlaGeom {
     static constexpr int SPLIT = kTileCopies % NW;
 };
 
+// Wave (hb, rb) owns 16 heads
+// and the 16-row half rb of every tile: it computes that block's logits over all
+// 576 columns (its Q slice, 72 registers, stays in registers), so the two halves
+// of a tile only exchange per-head tile maxima. Iteration t runs, between two
+// barriers, the Q K^T MFMAs of tile t+1 next to the softmax of tile t (vector
+// work), then P V of tile t. The copy of tile t+2 is issued as soon as tile t-1's
+// slot is free (right after the first barrier).
 template <int HB>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_kernel(AttnArgs A) {
     using GM = MlaGeom<HB>;
     constexpr int NHB = GM::NHB, NW = GM::NW, NT = GM::NT, CPW = GM::CPW, NCB = GM::NCB;
+    constexpr int KS = kDK / 32;   // 18 MFMA steps over a full row
     __shared__ __attribute__((aligned(16))) uint8_t ring0[kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t ring2[kTileB];
     __shared__ __attribute__((aligned(16))) uint32_t rows[kMaxSliceRows];
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[HB * kPStride];
-    __shared__ __attribute__((aligned(16))) f32x4 sx[NW][2][kWave];   // partial logits, lane layout
-    __shared__ __attribute__((aligned(16))) float alpha_s[HB];
-    __shared__ __attribute__((aligned(16))) float lsum[HB];
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][HB * kPStride];   // by tile parity
+    __shared__ __attribute__((aligned(16))) float mx[2][2][HB];                // [parity][row half][head]
+    __shared__ __attribute__((aligned(16))) float alpha_s[2][HB];
+    __shared__ __attribute__((aligned(16))) float lsum[2][HB];
     __shared__ __attribute__((aligned(16))) float mfin[HB];
     __shared__ int scan_s[16];
-    __shared__ int rescale[2];   // by tile parity: some head's reference max moved
+    __shared__ __attribute__((aligned(16))) int moved_w[2][NW];   // [parity][wave]: a reference max moved
 
     const int tid = threadIdx.x, l = lane_id();
-    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int g = l >> 4, jl = l & 15;
     const int n_hb = A.heads / HB;
 
-    // XCD-aware block order: the head blocks of one (query, slice) pair get block
-    // ids 8 apart, which the dispatcher places on the same XCD (shared L2), so the
-    // second copy of the pair's rows is served from L2.
     const int bid = blockIdx.x;
     const int xcd = bid & 7, slot = bid >> 3;
     const int num_pairs = A.num_q * A.n_split;
@@ -142,15 +148,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     const int r0 = sp * A.rows_per_split;
     const int r1 = seq_ok ? min(A.topk, r0 + A.rows_per_split) : r0;
 
-    // ---- Q slice of this wave in registers (issued first, waited for below):
-    // its 16 heads, columns [288 rb, 288 rb + 288)
+    // ---- Q of this wave's 16 heads, all 576 columns
     const int hb = w % NHB, rb = w / NHB;
-    bf16x8 qa[kQKHalf];
+    bf16x8 qa[KS];
     {
-        const uint16_t* qrow = A.q + ((int64_t)j * A.heads + head0 + hb * 16 + jl) * kDK + rb * (kDK / 2) + g * 8;
+        const uint16_t* qrow = A.q + ((int64_t)j * A.heads + head0 + hb * 16 + jl) * kDK + g * 8;
 #pragma unroll
-        for (int ks = 0; ks < kQKHalf; ks++)
-            qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + ks * 32));
+        for (int ks = 0; ks < KS; ks++) qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + ks * 32));
     }
 
     // ---- validated, compacted physical row ids of the slice
@@ -182,62 +186,50 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     }
     __syncthreads();
     const int ntiles = (nr + kTR - 1) / kTR;
-    wait_vmcnt<0>();   // Q is in; from here on only tile copies are in flight
+    wait_vmcnt<0>();
 
-    // copies of tile t into `dst`: copy i covers tile bytes [1024 i, 1024 i + 1024);
-    // rows past the end repeat the last kept row (finite data, masked out below)
-    auto issue = [&](int t, uint8_t* dst) {
+    auto slot_of = [&](int t) -> uint8_t* {
+        const int u = t % 3;
+        return u == 0 ? ring0 : u == 1 ? ring1 : ring2;
+    };
+    // copies of tile t: copy i (= w + NW k) covers tile bytes [1024 i, 1024 i + 1024);
+    // all row ids are read from LDS before the first copy is issued
+    constexpr int CPMAX = GM::CP_LO + (GM::SPLIT ? 1 : 0);
+    const int ncp = GM::CP_LO + (w < GM::SPLIT ? 1 : 0);
+    auto issue = [&](int t) {
+        uint8_t* dst = slot_of(t);
+        // copy k of this wave is tile copy w + NW k; a wave with one copy fewer
+        // repeats its last one (same bytes to the same place), so that every wave
+        // runs the same branch-free sequence. Row ids are read in groups of up to
+        // six before the group's copies go out.
+        constexpr int GRP = CPMAX < 6 ? CPMAX : 6;
 #pragma unroll
-        for (int i = w; i < kTileCopies; i += NW) {
-            const int q = i * 64 + l;
-            const int rr = q / kRowChunks, c = q % kRowChunks;
-            const uint32_t row = rows[min(t * kTR + rr, nr - 1)];
-            const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row * kRowB +
-                                 ((c ^ (rr & 7)) << 4);
-            __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)(dst + i * 1024), 16, 0, 0);
+        for (int k0 = 0; k0 < CPMAX; k0 += GRP) {
+            uint32_t row[GRP];
+#pragma unroll
+            for (int k = k0; k < k0 + GRP && k < CPMAX; k++) {
+                const int i = w + NW * (k < ncp ? k : ncp - 1);
+                const int q = i * 64 + l;
+                row[k - k0] = rows[min(t * kTR + q / kRowChunks, nr - 1)];
+            }
+#pragma unroll
+            for (int k = k0; k < k0 + GRP && k < CPMAX; k++) {
+                const int i = w + NW * (k < ncp ? k : ncp - 1);
+                const int q = i * 64 + l;
+                const int rr = q / kRowChunks, c = q % kRowChunks;
+                const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row[k - k0] * kRowB +
+                                     ((c ^ (rr & 7)) << 4);
+                __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)(dst + i * 1024), 16, 0, 0);
+            }
         }
     };
-    // this wave's own copies of the tile after t have landed or not been issued
-    auto wait_tile = [&](int t) {
-        if (t + 1 < ntiles) {
-            if (w < GM::SPLIT) wait_vmcnt<GM::CP_LO + 1>();
-            else wait_vmcnt<GM::CP_LO>();
-        } else {
-            wait_vmcnt<0>();
-        }
-    };
 
-    const float scale_log2 = A.sm_scale * 1.4426950408889634f;
-    // Online softmax with a lazily moved reference max: p = 2^(x - m_ref) where
-    // m_ref only moves when a head's running max exceeds it by more than
-    // kLazyMax (log2 units), so p <= 2^kLazyMax and O, l are rescaled only then.
-    // O / l and the log-sum-exp are unchanged in exact arithmetic.
-    constexpr float kLazyMax = 8.f;
-    float m_ref[4], l_run[4];
+    // key rows rb*16 + jl, chunks 4 ks + g = 8 (ks / 2) + (4 (ks % 2) + g)
+    const int kn = rb * 16 + jl;
+    int koffL[2];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        m_ref[r] = -INFINITY;
-        l_run[r] = 0.f;
-    }
-    f32x4 o[NHB][NCB];
-#pragma unroll
-    for (int h = 0; h < NHB; h++)
-#pragma unroll
-        for (int cb = 0; cb < NCB; cb++) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tid < 2) rescale[tid] = 0;
-
-    // Per-lane byte offsets inside a tile (chunk 8a + b of row r sits at
-    // r*1152 + 128a + ((b ^ (r & 7)) << 4)):
-    //  keys: rows jl and 16 + jl, chunks 36 rb + 4 ks + g of this wave's half row
-    //  values: rows 8g + jl/4 (and +4), columns w*CPW + 16 cb + 4*(jl%4) .. +3
-    int koffL[2][2], voffL[2][4];
-#pragma unroll
-    for (int c = 0; c < 2; c++) {
-        const int kn = c * 16 + jl;
-#pragma unroll
-        for (int e = 0; e < 2; e++)
-            koffL[c][e] = kn * kRowB + (((((rb + e) & 1) << 2 | g) ^ (kn & 7)) << 4) + ((rb * 36) & ~7) * 16;
-    }
+    for (int e = 0; e < 2; e++) koffL[e] = kn * kRowB + ((((e << 2) | g) ^ (kn & 7)) << 4);
+    int voffL[2][4];
     {
         const int h = (jl >> 1) & 1, half8 = (jl & 1) << 3;
         const int base = (w * CPW / 8) << 4;
@@ -249,152 +241,177 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         }
     }
 
-    auto tile = [&](int t, const uint8_t* buf) {
-        // The slot's addresses are formed here from opaque copies of the lane
-        // offsets, so that they are not kept live per slot across the loop.
-        int koff[2][2], voff[2][4];
-#pragma unroll
-        for (int c = 0; c < 2; c++)
-#pragma unroll
-            for (int e = 0; e < 2; e++) {
-                koff[c][e] = koffL[c][e];
-                asm volatile("" : "+v"(koff[c][e]));
-            }
-#pragma unroll
-        for (int e = 0; e < 2; e++)
-#pragma unroll
-            for (int v = 0; v < 4; v++) {
-                voff[e][v] = voffL[e][v];
-                asm volatile("" : "+v"(voff[e][v]));
-            }
-
-        // ---- partial logits of 16 heads x 32 rows over this wave's half row;
-        // the key reads of the next three steps are in flight during the MFMAs
-        auto kload = [&](u32x4 (&kb)[2][3], int k0) {
-#pragma unroll
-            for (int i = 0; i < 3; i++) {
-                const int ks = k0 + i;
-#pragma unroll
-                for (int c = 0; c < 2; c++)
-                    kb[c][i] = *reinterpret_cast<const u32x4*>(buf + koff[c][ks & 1] + ((4 * rb + 4 * ks) >> 3) * 128);
-            }
+    // logits of this wave's 16 heads x 16 rows of the tile in `buf`
+    auto qk = [&](const uint8_t* buf) -> f32x4 {
+        const int koff[2] = {koffL[0], koffL[1]};
+        // the key operands of the next DEPTH steps are in flight during each MFMA
+        constexpr int DEPTH = 6;
+        auto kread = [&](int ks) -> u32x4 {
+            return *reinterpret_cast<const u32x4*>(buf + koff[ks & 1] + (ks >> 1) * 128);
         };
-        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        u32x4 kb[2][3];
-        kload(kb, 0);
+        u32x4 kb[DEPTH];
 #pragma unroll
-        for (int k0 = 0; k0 < kQKHalf; k0 += 3) {
-            u32x4 kn[2][3];
-            if (k0 + 3 < kQKHalf) kload(kn, k0 + 3);
+        for (int i = 0; i < DEPTH; i++) kb[i] = kread(i);
+        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 3; i++)
-#pragma unroll
-                for (int c = 0; c < 2; c++) acc[c] = mfma16(qa[k0 + i], as_bf16x8(kb[c][i]), acc[c]);
-            if (k0 + 3 < kQKHalf) {
-#pragma unroll
-                for (int c = 0; c < 2; c++)
-#pragma unroll
-                    for (int i = 0; i < 3; i++) kb[c][i] = kn[c][i];
-            }
+        for (int ks = 0; ks < KS; ks++) {
+            const u32x4 kv = kb[ks % DEPTH];
+            if (ks + DEPTH < KS) kb[ks % DEPTH] = kread(ks + DEPTH);
+            if (ks & 1) a1 = mfma16(qa[ks], as_bf16x8(kv), a1);
+            else a0 = mfma16(qa[ks], as_bf16x8(kv), a0);
         }
-        // the flag of tile t+1 is cleared now: every read of it (tile t-1) is done
-        if (tid == 0) rescale[(t + 1) & 1] = 0;
-        // the two half-row partials of the head block meet in LDS; both waves then
-        // hold the full logits (a + b = b + a bit for bit) and run the same softmax
-        sx[w][0][l] = acc[0];
-        sx[w][1][l] = acc[1];
-        lds_barrier();
-        const int pw = w ^ NHB;   // partner wave: same head block, other half
-        const f32x4 s0 = acc[0] + sx[pw][0][l];
-        const f32x4 s1 = acc[1] + sx[pw][1][l];
-        const bool v0 = t * kTR + jl < nr, v1 = t * kTR + 16 + jl < nr;
-        const int hh = hb * 16 + 4 * g;   // first of this lane's four heads
-        float al[4];
-        bool moved = false;
+        // schedule: DEPTH reads, then (MFMA, read) pairs, then the last MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, DEPTH, 0);
+#pragma unroll
+        for (int i = 0; i < KS - DEPTH; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, DEPTH, 0);
+        return a0 + a1;
+    };
+    const float scale_log2 = A.sm_scale * 1.4426950408889634f;
+    constexpr float kLazyMax = 8.f;
+    // per-head maxima of this wave's 16 rows (scaled, masked); lane group g holds heads 4g..4g+3
+    auto tile_max = [&](int t, const f32x4& sv, float (&x)[4], float (&tm)[4]) {
+        const bool valid = t * kTR + kn < nr;
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const float x0 = v0 ? s0[r] * scale_log2 : -INFINITY;
-            const float x1 = v1 ? s1[r] * scale_log2 : -INFINITY;
-            const float tm = row16_max(__builtin_fmaxf(x0, x1));
-            const bool mv = tm > m_ref[r] + kLazyMax;   // also when m_ref is still -inf
-            al[r] = mv ? __builtin_amdgcn_exp2f(m_ref[r] - tm) : 1.f;
-            m_ref[r] = mv ? tm : m_ref[r];
-            moved |= mv;
-            const float p0 = __builtin_amdgcn_exp2f(x0 - m_ref[r]), p1 = __builtin_amdgcn_exp2f(x1 - m_ref[r]);
-            l_run[r] = l_run[r] * al[r] + (p0 + p1);
-            const __bf16 pm = static_cast<__bf16>(rb ? p1 : p0);   // this wave writes P of its row block
-            *reinterpret_cast<__bf16*>(pbuf + (hh + r) * kPStride + (rb * 16 + jl) * 2) = pm;
-        }
-        if (rb == 0 && jl == 0) *reinterpret_cast<f32x4*>(&alpha_s[hh]) = f32x4{al[0], al[1], al[2], al[3]};
-        if (moved) rescale[t & 1] = 1;
-        lds_barrier();
-
-        // ---- O = alpha * O + P V over this wave's columns
-        if (__builtin_amdgcn_readfirstlane(rescale[t & 1])) {
-#pragma unroll
-            for (int h = 0; h < NHB; h++) {
-                const f32x4 a4 = *reinterpret_cast<const f32x4*>(&alpha_s[h * 16 + 4 * g]);
-#pragma unroll
-                for (int cb = 0; cb < NCB; cb++)
-#pragma unroll
-                    for (int r = 0; r < 4; r++) o[h][cb][r] *= a4[r];
-            }
-        }
-        bf16x8 pa[NHB];
-#pragma unroll
-        for (int h = 0; h < NHB; h++)
-            pa[h] = as_bf16x8(*reinterpret_cast<const u32x4*>(pbuf + (h * 16 + jl) * kPStride + g * 16));
-#pragma unroll
-        for (int c0 = 0; c0 < NCB; c0 += 4) {
-            u32x2 va[4], vb2[4];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const int cst = ((c0 + q) >> 2) * 128;
-                va[q] = ds_read_tr16(buf + voff[0][q] + cst);
-                vb2[q] = ds_read_tr16(buf + voff[1][q] + cst);
-            }
-            lds_wait(va, vb2);
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const bf16x8 vb = as_bf16x8(u32x4{va[q][0], va[q][1], vb2[q][0], vb2[q][1]});
-#pragma unroll
-                for (int h = 0; h < NHB; h++) o[h][c0 + q] = mfma16(pa[h], vb, o[h][c0 + q]);
-            }
+            x[r] = valid ? sv[r] * scale_log2 : -INFINITY;
+            tm[r] = row16_max(x[r]);
         }
     };
 
+    float m_ref[4], l_run[4];
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        m_ref[r] = -INFINITY;
+        l_run[r] = 0.f;
+    }
+    f32x4 o[NHB][NCB];
+#pragma unroll
+    for (int h = 0; h < NHB; h++)
+#pragma unroll
+        for (int cb = 0; cb < NCB; cb++) o[h][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int hh = hb * 16 + 4 * g;   // first of this lane's four heads
+
     if (ntiles > 0) {
-        issue(0, ring0);
-        if (ntiles > 1) issue(1, ring1);
+        issue(0);
+        if (ntiles > 1) issue(1);
+        if (ntiles > 1) wait_vmcnt<CPMAX>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        float x[4], tm[4];
+        {
+            const f32x4 sv = qk(ring0);
+            tile_max(0, sv, x, tm);
+        }
+        *reinterpret_cast<f32x4*>(&mx[0][rb][hh]) = f32x4{tm[0], tm[1], tm[2], tm[3]};
+
         for (int t = 0; t < ntiles; t++) {
-            const int u = t % 3;
-            wait_tile(t);
+            const int par = t & 1;
+            // B1: tile t+1 has landed, the maxima of tile t are visible, the slot of
+            // tile t-1 is free
+            if (t + 1 < ntiles) wait_vmcnt<0>();
             lds_barrier();
-            if (t + 2 < ntiles) issue(t + 2, u == 0 ? ring2 : u == 1 ? ring0 : ring1);
-            tile(t, u == 0 ? ring0 : u == 1 ? ring1 : ring2);
+            // ---- Q K^T of tile t+1 (matrix cores) ...
+            f32x4 sn = {0.f, 0.f, 0.f, 0.f};
+            if (t + 1 < ntiles) sn = qk(slot_of(t + 1));
+            // (the copy of tile t+2 goes out after the key reads: the compiler counts
+            // global -> LDS copies against the LDS counter, which would otherwise
+            // turn every wait on a key read into a full drain)
+            if (t + 2 < ntiles) issue(t + 2);
+            // ... next to the softmax of tile t (vector units)
+            {
+                const f32x4 pm = *reinterpret_cast<const f32x4*>(&mx[par][rb ^ 1][hh]);
+                float al[4];
+                bool moved = false;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float tmax = __builtin_fmaxf(tm[r], pm[r]);
+                    const bool mv = tmax > m_ref[r] + kLazyMax;
+                    al[r] = mv ? __builtin_amdgcn_exp2f(m_ref[r] - tmax) : 1.f;
+                    m_ref[r] = mv ? tmax : m_ref[r];
+                    moved |= mv;
+                    const float p = __builtin_amdgcn_exp2f(x[r] - m_ref[r]);
+                    l_run[r] = l_run[r] * al[r] + p;
+                    *reinterpret_cast<__bf16*>(&pbuf[par][(hh + r) * kPStride + kn * 2]) = static_cast<__bf16>(p);
+                }
+                // both row halves compute the same alpha: every lane stores it
+                *reinterpret_cast<f32x4*>(&alpha_s[par][hh]) = f32x4{al[0], al[1], al[2], al[3]};
+                moved_w[par][w] = __ballot(moved) != 0ull;
+            }
+            if (t + 1 < ntiles) {
+                tile_max(t + 1, sn, x, tm);
+                *reinterpret_cast<f32x4*>(&mx[par ^ 1][rb][hh]) = f32x4{tm[0], tm[1], tm[2], tm[3]};
+            }
+            // B2: P and alpha of tile t are visible
+            lds_barrier();
+            // ---- O = alpha * O + P V of tile t over this wave's columns
+            const int4 mv0 = *reinterpret_cast<const int4*>(&moved_w[par][0]);
+            int any = mv0.x | mv0.y | mv0.z | mv0.w;
+            if constexpr (NW > 4) {
+                const int4 mv1 = *reinterpret_cast<const int4*>(&moved_w[par][4]);
+                any |= mv1.x | mv1.y | mv1.z | mv1.w;
+            } else if constexpr (NW > 2) {
+                any |= moved_w[par][2] | moved_w[par][3];
+            }
+            if (__builtin_amdgcn_readfirstlane(any)) {
+#pragma unroll
+                for (int h = 0; h < NHB; h++) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&alpha_s[par][h * 16 + 4 * g]);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; cb++)
+#pragma unroll
+                        for (int r = 0; r < 4; r++) o[h][cb][r] *= a4[r];
+                }
+            }
+            bf16x8 pa[NHB];
+#pragma unroll
+            for (int h = 0; h < NHB; h++)
+                pa[h] = as_bf16x8(*reinterpret_cast<const u32x4*>(&pbuf[par][(h * 16 + jl) * kPStride + g * 16]));
+            const uint8_t* buf = slot_of(t);
+            const int(&voff)[2][4] = voffL;
+#pragma unroll
+            for (int c0 = 0; c0 < NCB; c0 += 4) {
+                u32x2 va[4], vb2[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const int cst = ((c0 + q) >> 2) * 128;
+                    va[q] = ds_read_tr16(buf + voff[0][q] + cst);
+                    vb2[q] = ds_read_tr16(buf + voff[1][q] + cst);
+                }
+                lds_wait(va, vb2);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const bf16x8 vb = as_bf16x8(u32x4{va[q][0], va[q][1], vb2[q][0], vb2[q][1]});
+#pragma unroll
+                    for (int h = 0; h < NHB; h++) o[h][c0 + q] = mfma16(pa[h], vb, o[h][c0 + q]);
+                }
+            }
         }
     }
     wait_vmcnt<0>();
 
-    // ---- finalize: per-head sums, normalize and write
-    if (rb == 0) {
-        const int hh = hb * 16 + 4 * g;
+    // ---- finalize: per-head sums of both row halves, normalize and write
+    {
         float ls[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) ls[r] = row16_sum(l_run[r]);
         if (jl == 0) {
-            *reinterpret_cast<f32x4*>(&lsum[hh]) = f32x4{ls[0], ls[1], ls[2], ls[3]};
-            *reinterpret_cast<f32x4*>(&mfin[hh]) = f32x4{m_ref[0], m_ref[1], m_ref[2], m_ref[3]};
+            *reinterpret_cast<f32x4*>(&lsum[rb][hh]) = f32x4{ls[0], ls[1], ls[2], ls[3]};
+            if (rb == 0) *reinterpret_cast<f32x4*>(&mfin[hh]) = f32x4{m_ref[0], m_ref[1], m_ref[2], m_ref[3]};
         }
     }
     __syncthreads();
     const bool split = A.n_split > 1;
 #pragma unroll
     for (int h = 0; h < NHB; h++) {
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lsum[h * 16 + 4 * g]);
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(&lsum[0][h * 16 + 4 * g]);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(&lsum[1][h * 16 + 4 * g]);
 #pragma unroll
         for (int r = 0; r < 4; r++) {
-            const float lt = l0[r];
+            const float lt = l0[r] + l1[r];
             const float inv = lt > 0.f ? 1.f / lt : 0.f;
             const int64_t head = head0 + h * 16 + 4 * g + r;
 #pragma unroll
@@ -409,7 +426,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         }
     }
     if (tid < HB) {
-        const float lt = lsum[tid];
+        const float lt = lsum[0][tid] + lsum[1][tid];
         const float lse = lt > 0.f ? (mfin[tid] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
         if (split)
             A.part_lse[((int64_t)j * A.n_split + sp) * A.heads + head0 + tid] = lse;
