@@ -35,36 +35,138 @@ static_assert(kCoarseBins == kCoarseBinsHost, "host and device histogram sizes d
 
 // ------------------------------------------------------------ score tile
 
+// A query's indexer heads in MFMA operand layout. The bf16 form feeds
+// 32x32x16 bf16 MFMAs (fp8 keys are widened to bf16). The fp8 form feeds
+// 32x32x64 fp8 MFMAs on the raw e4m3 key bytes: q * 2^s is split into an e4m3
+// high part and an e4m3 residual times 2^4 (one exponent s per query, chosen so
+// that max|q| * 2^s < 256), and the two products are summed with MFMA scales
+// 2^-s and 2^-(s+4). The split is exact for every element above 2^-21 of the
+// query's largest element (below that the residual underflows), so the scores
+// equal those of the bf16 form up to rounding order.
+template <int MB, int D, bool FP8>
+struct IdxQuery;
+
 template <int MB, int D>
-struct IdxQuery {
+struct IdxQuery<MB, D, false> {
     static constexpr int KS = D / 16;
     bf16x8 a[MB][KS];
     float w[MB][16];
 };
 
 template <int MB, int D>
-__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D>& q) {
+struct IdxQuery<MB, D, true> {
+    static constexpr int KS = D / 64;
+    i32x8 hi[MB][KS], lo[MB][KS];
+    int sh, sl;   // E8M0 scales of the two parts
+    float w[MB][16];
+};
+
+template <int MB, int D>
+__device__ __forceinline__ void load_weights(const IdxArgs& A, int j, float (&w)[MB][16]) {
+    const int half = lane_id() >> 5;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int h = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            w[mb][r] = h < A.heads ? A.w[(int64_t)j * A.heads + h] : 0.f;
+        }
+}
+
+template <int MB, int D>
+__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, false>& q) {
     const int l = lane_id(), m = l & 31, half = l >> 5;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
         const int head = mb * 32 + m;
 #pragma unroll
-        for (int ks = 0; ks < IdxQuery<MB, D>::KS; ks++) {
+        for (int ks = 0; ks < IdxQuery<MB, D, false>::KS; ks++) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (head < A.heads)
                 v = *reinterpret_cast<const u32x4*>(
                     A.q_idx + ((int64_t)j * A.heads + head) * D + half * (D / 2) + ks * 8);
             q.a[mb][ks] = as_bf16x8(v);
         }
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int h = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            q.w[mb][r] = h < A.heads ? A.w[(int64_t)j * A.heads + h] : 0.f;
-        }
     }
+    load_weights<MB, D>(A, j, q.w);
+}
+
+template <int MB, int D>
+__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, true>& q) {
+    constexpr int KS = IdxQuery<MB, D, true>::KS;
+    const int l = lane_id(), m = l & 31, half = l >> 5;
+    // lane l holds head mb*32 + l%32 and dims 64 ks + 32 (l/32) .. +31 of each step;
+    // the query is read twice (the second time from cache): once for its largest
+    // magnitude, once to split it
+    auto ld = [&](int mb, int ks, int c) -> u32x4 {
+        const int head = mb * 32 + m;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (head < A.heads)
+            v = *reinterpret_cast<const u32x4*>(
+                A.q_idx + ((int64_t)j * A.heads + head) * D + ks * 64 + half * 32 + c * 8);
+        return v;
+    };
+    float amax = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const u32x4 v = ld(mb, ks, c);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    amax = fmaxf(amax, fabsf(__uint_as_float(v[e] << 16)));
+                    amax = fmaxf(amax, fabsf(__uint_as_float(v[e] & 0xffff0000u)));
+                }
+            }
+    amax = wave_max_f(amax);
+    // exponent s with amax * 2^s in [128, 256) (0 for an all-zero query)
+    int s = 0;
+    if (amax > 0.f) {
+        int e;
+        frexpf(amax, &e);   // amax = f * 2^e, f in [0.5, 1)
+        s = min(max(8 - e, -120), 120);
+    }
+    const float f = ldexpf(1.f, s);
+    q.sh = 127 - s;
+    q.sl = 127 - s - 4;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                const u32x4 v = ld(mb, ks, c);
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    // four bf16 -> one dword of e4m3 (high part) and one of e4m3 (residual)
+                    float x[4];
+                    x[0] = __uint_as_float(v[e] << 16) * f;
+                    x[1] = __uint_as_float(v[e] & 0xffff0000u) * f;
+                    x[2] = __uint_as_float(v[e + 1] << 16) * f;
+                    x[3] = __uint_as_float(v[e + 1] & 0xffff0000u) * f;
+                    int h = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    h = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h, true);
+                    float r[4];
+                    r[0] = (x[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0)) * 16.f;
+                    r[1] = (x[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1)) * 16.f;
+                    r[2] = (x[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2)) * 16.f;
+                    r[3] = (x[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3)) * 16.f;
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lo, true);
+                    q.hi[mb][ks][c * 2 + e / 2] = h;
+                    q.lo[mb][ks][c * 2 + e / 2] = lo;
+                }
+            }
+        }
+    load_weights<MB, D>(A, j, q.w);
 }
 
 // One lane's share of a 32-position tile: half a row of index-K (+ its scale).
+// bf16: lane half h holds the row's chunks h*CPR/2 .. (16-byte chunks, the
+// 32x32x16 operand layout); fp8: for each 64-byte MFMA step ks it holds the 32
+// bytes 64 ks + 32 h .. (chunks 4 ks + 2 h and 4 ks + 2 h + 1).
 template <int D, bool FP8>
 struct KTile {
     static constexpr int BYTES = (D / 2) * (FP8 ? 1 : 2);
@@ -72,6 +174,11 @@ struct KTile {
     u32x4 v[NV];
     float sc;
     bool ok;      // this lane's position is visible and its page id valid
+    // 16-byte chunk of the row held in v[i] by lane half h
+    static __device__ __forceinline__ int chunk(int i, int h) {
+        if constexpr (FP8) return 4 * (i >> 1) + 2 * h + (i & 1);
+        else return h * NV + i;
+    }
 };
 
 // Visible row length of query j (clamped; flags bad input).
@@ -119,9 +226,10 @@ __device__ __forceinline__ void load_ktile(const IdxArgs& A, int page, int pos0,
     const int p = pos0 + (l & 31);
     t.ok = page >= 0 && p < row_len;
     const int64_t row = t.ok ? (int64_t)page * kPage + (p & 63) : 0;
-    const uint8_t* src = A.rows + row * (D * (FP8 ? 1 : 2)) + half * KTile<D, FP8>::BYTES;
+    const uint8_t* src = A.rows + row * (D * (FP8 ? 1 : 2));
 #pragma unroll
-    for (int i = 0; i < KTile<D, FP8>::NV; i++) t.v[i] = reinterpret_cast<const u32x4*>(src)[i];
+    for (int i = 0; i < KTile<D, FP8>::NV; i++)
+        t.v[i] = reinterpret_cast<const u32x4*>(src)[KTile<D, FP8>::chunk(i, half)];
     if constexpr (FP8) t.sc = A.scale[row];
     else t.sc = 1.f;
 }
@@ -139,59 +247,68 @@ __device__ __forceinline__ float add_halves(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Scores of the tile's 32 positions for G queries that share it; lanes l and
-// l+32 both get the score of position pos0 + l%32 (undefined where the tile
-// lane is not ok). The tile is widened once and feeds every query's MFMAs. Per
-// query the operation order is fixed and independent of G, so every kernel
-// that uses this produces the same bits for the same query and position.
-template <int MB, int D, bool FP8, int G>
-__device__ __forceinline__ void tile_scores(const IdxQuery<MB, D> (&q)[G], const KTile<D, FP8>& t,
-                                            float (&s)[G]) {
-    constexpr int KS = D / 16;
-    f32x16 acc[G][MB];
+// MFMA half of a tile: the raw q.k products of one query against 32
+// positions (heads x positions accumulators).
+template <int MB, int D, bool FP8>
+__device__ __forceinline__ void tile_mfma(const IdxQuery<MB, D, FP8>& q, const KTile<D, FP8>& t,
+                                          f32x16 (&acc)[MB]) {
 #pragma unroll
-    for (int g = 0; g < G; g++)
+    for (int mb = 0; mb < MB; mb++) acc[mb] = f32x16{};
+    if constexpr (FP8) {
+        constexpr int KS = D / 64;
 #pragma unroll
-        for (int mb = 0; mb < MB; mb++) acc[g][mb] = f32x16{};
+        for (int ks = 0; ks < KS; ks++) {
+            const u32x4 v0 = t.v[2 * ks], v1 = t.v[2 * ks + 1];
+            const i32x8 b = {(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                             (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-        bf16x8 bk;
-        if constexpr (FP8) {
-            const u32x4 vv = t.v[ks >> 1];
-            bk = e4m3x8_to_bf16x8(vv[(ks & 1) * 2], vv[(ks & 1) * 2 + 1]);
-        } else {
-            bk = as_bf16x8(t.v[ks]);
-        }
-#pragma unroll
-        for (int g = 0; g < G; g++)
-#pragma unroll
-            for (int mb = 0; mb < MB; mb++) acc[g][mb] = mfma32(q[g].a[mb][ks], bk, acc[g][mb]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; g++) {
-        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < MB; mb++) {
-#pragma unroll
-            for (int r = 0; r < 16; r += 4) {
-                p0 = fmaf(q[g].w[mb][r + 0], relu(acc[g][mb][r + 0]), p0);
-                p1 = fmaf(q[g].w[mb][r + 1], relu(acc[g][mb][r + 1]), p1);
-                p2 = fmaf(q[g].w[mb][r + 2], relu(acc[g][mb][r + 2]), p2);
-                p3 = fmaf(q[g].w[mb][r + 3], relu(acc[g][mb][r + 3]), p3);
+            for (int mb = 0; mb < MB; mb++) {
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.hi[mb][ks], b, acc[mb], 0, 0, 0,
+                                                                          q.sh, 0, 127);
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.lo[mb][ks], b, acc[mb], 0, 0, 0,
+                                                                          q.sl, 0, 127);
             }
         }
-        float v = add_halves((p0 + p1) + (p2 + p3));
-        if constexpr (FP8) v = v * t.sc;
-        s[g] = v;
+    } else {
+        constexpr int KS = D / 16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const bf16x8 bk = as_bf16x8(t.v[ks]);
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++) acc[mb] = mfma32(q.a[mb][ks], bk, acc[mb]);
+        }
     }
 }
 
+// Vector half: ReLU, head weights, head sum, token scale.
 template <int MB, int D, bool FP8>
-__device__ __forceinline__ float tile_scores(const IdxQuery<MB, D>& q, const KTile<D, FP8>& t) {
-    const IdxQuery<MB, D> qq[1] = {q};
-    float s[1];
-    tile_scores<MB, D, FP8, 1>(qq, t, s);
-    return s[0];
+__device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D, FP8>& q, const f32x16 (&acc)[MB],
+                                               float tsc) {
+    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+            p0 = fmaf(q.w[mb][r + 0], relu(acc[mb][r + 0]), p0);
+            p1 = fmaf(q.w[mb][r + 1], relu(acc[mb][r + 1]), p1);
+            p2 = fmaf(q.w[mb][r + 2], relu(acc[mb][r + 2]), p2);
+            p3 = fmaf(q.w[mb][r + 3], relu(acc[mb][r + 3]), p3);
+        }
+    }
+    float v = add_halves((p0 + p1) + (p2 + p3));
+    if constexpr (FP8) v = v * tsc;
+    return v;
+}
+
+// Scores of the tile's 32 positions for one query; lanes l and l+32 both get
+// the score of position pos0 + l%32 (undefined where the tile lane is not ok).
+// Every kernel scores through tile_mfma + tile_epilogue, so a query and position
+// give the same bits in each of them.
+template <int MB, int D, bool FP8>
+__device__ __forceinline__ float tile_scores(const IdxQuery<MB, D, FP8>& q, const KTile<D, FP8>& t) {
+    f32x16 acc[MB];
+    tile_mfma<MB, D, FP8>(q, t, acc);
+    return tile_epilogue<MB, D, FP8>(q, acc, t.sc);
 }
 
 // ------------------------------------------------------------ emitters
@@ -316,47 +433,6 @@ __device__ int select_emit(const uint32_t* keys, int n, int m_cap, SelScratch* s
 
 // ------------------------------------------------------------ split kernel
 
-// MFMA half of a tile: the raw q.k products of one query against 32
-// positions (heads x positions accumulators). The K tile is widened here.
-template <int MB, int D, bool FP8>
-__device__ __forceinline__ void tile_mfma(const IdxQuery<MB, D>& q, const KTile<D, FP8>& t, f32x16 (&acc)[MB]) {
-    constexpr int KS = D / 16;
-#pragma unroll
-    for (int mb = 0; mb < MB; mb++) acc[mb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-        bf16x8 bk;
-        if constexpr (FP8) {
-            const u32x4 vv = t.v[ks >> 1];
-            bk = e4m3x8_to_bf16x8(vv[(ks & 1) * 2], vv[(ks & 1) * 2 + 1]);
-        } else {
-            bk = as_bf16x8(t.v[ks]);
-        }
-#pragma unroll
-        for (int mb = 0; mb < MB; mb++) acc[mb] = mfma32(q.a[mb][ks], bk, acc[mb]);
-    }
-}
-
-// Vector half: ReLU, head weights, head sum, token scale. Same operation order
-// as tile_scores.
-template <int MB, int D, bool FP8>
-__device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D>& q, const f32x16 (&acc)[MB], float tsc) {
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < MB; mb++) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-            p0 = fmaf(q.w[mb][r + 0], relu(acc[mb][r + 0]), p0);
-            p1 = fmaf(q.w[mb][r + 1], relu(acc[mb][r + 1]), p1);
-            p2 = fmaf(q.w[mb][r + 2], relu(acc[mb][r + 2]), p2);
-            p3 = fmaf(q.w[mb][r + 3], relu(acc[mb][r + 3]), p3);
-        }
-    }
-    float v = add_halves((p0 + p1) + (p2 + p3));
-    if constexpr (FP8) v = v * tsc;
-    return v;
-}
-
 // Geometry of the split kernel. Eight waves; wave w scores query w / (8/G)
 // against its tiles sub, sub + 8/G, ... (sub = w % (8/G)) of 32 positions.
 // Each wave streams its tiles through a private ring of NS LDS slots filled by
@@ -372,15 +448,20 @@ struct SplitGeom {
     static constexpr int R = D * (FP8 ? 1 : 2);          // bytes per row
     static constexpr int CPR = R / 16;                   // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
-    static constexpr int NWV = 8;                        // waves per workgroup
+    // two queries: eight waves and most of the LDS (one workgroup per CU); one
+    // query: four waves and at most half the LDS, so that two workgroups share a
+    // CU and one's setup and selection overlap the other's streaming
+    static constexpr int NWV = G == 2 ? 8 : 4;           // waves per workgroup
     static constexpr int NT = NWV * kWave;
     static constexpr int WPQ = NWV / G;                  // waves per query
     static constexpr int TILE = 32 * R;                  // bytes of one tile
-    static constexpr int NS_RAW = 98304 / (NWV * TILE);
+    static constexpr size_t LDS_BUDGET = G == 2 ? kMaxLds : kMaxLds / 2;
+    static constexpr int NRING = NWV;                    // one ring per wave
+    static constexpr int NS_RAW = (G == 2 ? 98304 : 49152) / (NRING * TILE);
     static constexpr int NS = NS_RAW < 2 ? 2 : (NS_RAW > 4 ? 4 : NS_RAW);   // ring depth
     static constexpr int DMA = TILE / 1024;              // 1 KB copies per tile
     static constexpr int PER_TILE = DMA + (FP8 ? 1 : 0); // copies per tile (+ scales)
-    static constexpr size_t STATIC_LDS = (size_t)NS * NWV * (TILE + (FP8 ? 128 : 0));
+    static constexpr size_t STATIC_LDS = (size_t)NS * NRING * (TILE + (FP8 ? 128 : 0));
 };
 
 __host__ __device__ inline size_t split_pages_bytes(int chunk) {
@@ -391,15 +472,17 @@ template <int MB, int D, bool FP8, int G, bool SCORES>
 __global__ __launch_bounds__(512) void indexer_split_kernel(IdxArgs A, SplitArgs S) {
     using GM = SplitGeom<D, FP8, G>;
     constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NWV = GM::NWV, NT = GM::NT, WPQ = GM::WPQ;
-    static_assert(NT == 512, "launch bounds assume eight waves");
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[NWV * GM::TILE];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[NWV * GM::TILE];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS > 2 ? NWV * GM::TILE : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS > 3 ? NWV * GM::TILE : 16];
-    __shared__ __attribute__((aligned(16))) float scl0[FP8 ? NWV * 32 : 4];
-    __shared__ __attribute__((aligned(16))) float scl1[FP8 ? NWV * 32 : 4];
-    __shared__ __attribute__((aligned(16))) float scl2[FP8 && NS > 2 ? NWV * 32 : 4];
-    __shared__ __attribute__((aligned(16))) float scl3[FP8 && NS > 3 ? NWV * 32 : 4];
+    constexpr int NRING = GM::NRING, RB = NRING * GM::TILE, SB = FP8 ? NRING * 32 : 4;
+    // one static array per ring slot: every LDS access names its slot, which lets
+    // the compiler wait for exactly the copies that wrote it
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[RB];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[RB];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS > 2 ? RB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS > 3 ? RB : 16];
+    __shared__ __attribute__((aligned(16))) float scl0[SB];
+    __shared__ __attribute__((aligned(16))) float scl1[SB];
+    __shared__ __attribute__((aligned(16))) float scl2[NS > 2 ? SB : 4];
+    __shared__ __attribute__((aligned(16))) float scl3[NS > 3 ? SB : 4];
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int* pages = reinterpret_cast<int*>(smem);
     uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem + split_pages_bytes(S.chunk));
@@ -464,7 +547,7 @@ __global__ __launch_bounds__(512) void indexer_split_kernel(IdxArgs A, SplitArgs
     // query registers first (unconditionally: a clamped index keeps the load in
     // bounds), and all of them in before the copy pipeline starts, so that the
     // only vector-memory operations in flight in the loop are the ring copies
-    IdxQuery<MB, D> q;
+    IdxQuery<MB, D, FP8> q;
     load_query<MB, D>(A, min(j, A.num_q - 1), q);
     wait_vmcnt<0>();
 
@@ -497,14 +580,13 @@ __global__ __launch_bounds__(512) void indexer_split_kernel(IdxArgs A, SplitArgs
         const int row = l & 31;
         const int pos = chunk0 + ti * 32 + row;
         const int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npg - 1)]);
-        constexpr int HALF = CPR / 2;                 // chunks per half row
         // the scale is read first: the wait for the row data that the MFMAs need
         // then also covers it, before the slot is refilled
         if constexpr (FP8) t.sc = sslot[row];
         else t.sc = 1.f;
 #pragma unroll
         for (int i = 0; i < KTile<D, FP8>::NV; i++) {
-            const int cc = half * HALF + i;
+            const int cc = KTile<D, FP8>::chunk(i, half);
             t.v[i] = *reinterpret_cast<const u32x4*>(slot + row * R + ((cc ^ (row & GM::SWZ)) * 16));
         }
         t.ok = page >= 0 && pos < row_end && pos < my_rl;
@@ -601,7 +683,7 @@ static int split_chunk_cap() {
     using GM = SplitGeom<D, FP8, G>;
     for (int chunk = 16384; chunk >= 64; chunk >>= 1) {
         const size_t dyn = split_pages_bytes(chunk) + (size_t)G * (chunk + kCoarseBins) * 4 + sizeof(SelScratch);
-        if (GM::STATIC_LDS + dyn + 256 <= kMaxLds) return chunk;
+        if (GM::STATIC_LDS + dyn + 256 <= GM::LDS_BUDGET) return chunk;
     }
     return 64;
 }
@@ -736,7 +818,7 @@ __device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, int r
     uint32_t tau = 0u;
     const int ntiles = (rl + 31) / 32;
     if (ntiles > 0) {
-        IdxQuery<MB, D> q;
+        IdxQuery<MB, D, FP8> q;
         load_query<MB, D>(A, j, q);
         const int npages = (rl + kPage - 1) / kPage;
         auto fetch = [&](KTile<D, FP8>& t, int ti) {   // ti past the end: dummy row

@@ -185,7 +185,8 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bo
             return p;
         }
     }
-    const int g = qs->group % 2 == 0 ? 2 : 1;
+    int g = qs->group % 2 == 0 ? 2 : 1;
+    if (env_int("SIA_SPLIT_GROUP", 0) == 1) g = 1;
     plan_split(p, qs->num_q, qs->max_visible, topk, g, sia::indexer_split_chunk_cap(heads > 32 ? 2 : 1, dim, fp8, g));
     return p;
 }
