@@ -471,7 +471,7 @@ __host__ __device__ inline size_t split_pages_bytes(int chunk) {
 template <int MB, int D, bool FP8, int G, bool SCORES>
 __global__ __launch_bounds__(512) void indexer_split_kernel(IdxArgs A, SplitArgs S) {
     using GM = SplitGeom<D, FP8, G>;
-    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NWV = GM::NWV, NT = GM::NT, WPQ = GM::WPQ;
+    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NT = GM::NT, WPQ = GM::WPQ;
     constexpr int NRING = GM::NRING, RB = NRING * GM::TILE, SB = FP8 ? NRING * 32 : 4;
     // one static array per ring slot: every LDS access names its slot, which lets
     // the compiler wait for exactly the copies that wrote it
@@ -555,53 +555,63 @@ __global__ __launch_bounds__(512) void indexer_split_kernel(IdxArgs A, SplitArgs
         return (u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3) + w * GM::TILE;
     };
     auto scl = [&](int u) -> float* { return (u == 0 ? scl0 : u == 1 ? scl1 : u == 2 ? scl2 : scl3) + w * 32; };
-    // copy tile ti (a tile past the end copies a dummy row) into this wave's slot
+    // Loop-invariant per-lane offsets. A tile (32 positions, 32-aligned) lies in
+    // one page, so its rows are contiguous: copy r of a tile moves the 16-byte
+    // piece gi = 64 r + lane, i.e. row gi / CPR, chunk gi % CPR, stored at the
+    // chunk's swizzled place in the slot.
+    const int frow = l & 31;   // the tile row (position) this lane reads
+    int lds_off[KTile<D, FP8>::NV];
+#pragma unroll
+    for (int i = 0; i < KTile<D, FP8>::NV; i++) {
+        const int cc = KTile<D, FP8>::chunk(i, half);
+        lds_off[i] = frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
+    }
+    // positions [0, lim) of the chunk are visible to this wave's query
+    const int lim = min(row_end, my_rl) - chunk0;
+
+    // copy tile ti into this wave's slot (a tile past the end repeats the last
+    // page; rows past the visible end are read from the same, valid, page and
+    // masked out when scored)
     auto issue = [&](int ti, uint8_t* slot, float* sslot) {
-        const int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npg - 1)]);
+        int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npg - 1)]);
+        page = page < 0 ? 0 : page;
+        const int64_t row0 = (int64_t)page * kPage + (ti & 1) * 32;
+        const uint8_t* base = A.rows + row0 * R;
 #pragma unroll
         for (int r = 0; r < GM::DMA; r++) {
             const int gi = r * kWave + l;
             const int row = gi / CPR, cc = gi % CPR;
-            const int pos = chunk0 + ti * 32 + row;
-            const bool ok = page >= 0 && pos < row_end;
-            const int64_t grow = ok ? (int64_t)page * kPage + (pos & 63) : 0;
-            const uint8_t* src = A.rows + grow * R + ((cc ^ (row & GM::SWZ)) * 16);
+            // (the source goes through a named pointer: written inline in the call,
+            // the host compile drops the kernel's launch stub)
+            const uint8_t* src = base + row * R + ((cc ^ (row & GM::SWZ)) << 4);
             __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)(slot + r * 1024), 16, 0, 0);
         }
         if constexpr (FP8) {
-            const int pos = chunk0 + ti * 32 + 4 * min(l, 7);
-            const bool ok = page >= 0 && pos < row_end;
-            const float* src = A.scale + (ok ? (int64_t)page * kPage + (pos & 63) : 0);
-            if (l < 8) __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)sslot, 16, 0, 0);
+            const float* ssrc = A.scale + row0 + 4 * l;
+            if (l < 8) __builtin_amdgcn_global_load_lds(ssrc, (SIA_LDS void*)sslot, 16, 0, 0);
         }
     };
     // operand reads of tile ti from its slot
     auto fetch = [&](int ti, const uint8_t* slot, const float* sslot, KTile<D, FP8>& t) {
-        const int row = l & 31;
-        const int pos = chunk0 + ti * 32 + row;
-        const int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npg - 1)]);
         // the scale is read first: the wait for the row data that the MFMAs need
         // then also covers it, before the slot is refilled
-        if constexpr (FP8) t.sc = sslot[row];
+        if constexpr (FP8) t.sc = sslot[frow];
         else t.sc = 1.f;
 #pragma unroll
-        for (int i = 0; i < KTile<D, FP8>::NV; i++) {
-            const int cc = KTile<D, FP8>::chunk(i, half);
-            t.v[i] = *reinterpret_cast<const u32x4*>(slot + row * R + ((cc ^ (row & GM::SWZ)) * 16));
-        }
-        t.ok = page >= 0 && pos < row_end && pos < my_rl;
+        for (int i = 0; i < KTile<D, FP8>::NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + lds_off[i]);
+        t.ok = frow < lim - ti * 32;   // a tile whose page id is invalid has no visible position
     };
     auto finish = [&](int ti, const f32x16 (&acc)[MB], float tsc, bool tok) {
         const float sc = tile_epilogue<MB, D, FP8>(q, acc, tsc);
-        const int i = ti * 32 + (l & 31);
-        const int pos = chunk0 + i;
+        const int i = ti * 32 + frow;
         if constexpr (SCORES) {
-            if (l < 32 && tok) S.scores[(int64_t)j * S.ld + pos] = sc;
+            if (l < 32 && tok) S.scores[(int64_t)j * S.ld + chunk0 + i] = sc;
         } else {
-            // the key goes to LDS and into the coarse histogram of its query
-            const uint32_t k = (l < 32 && tok) ? score_key(sc) : 0u;
-            if (l < 32) keys_all[qi * S.chunk + i] = k;
-            if (k != 0u) atomicAdd(&hist_all[qi * kCoarseBins + coarse_bin(k)], 1u);
+            // the key goes to LDS (both lane halves hold the same key and store
+            // it to the same place) and into the coarse histogram of its query
+            const uint32_t k = tok ? score_key(sc) : 0u;
+            keys_all[qi * S.chunk + i] = k;
+            if (l < 32 && k != 0u) atomicAdd(&hist_all[qi * kCoarseBins + coarse_bin(k)], 1u);
         }
     };
 
