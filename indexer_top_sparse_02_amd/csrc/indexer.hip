@@ -313,66 +313,19 @@ __device__ __forceinline__ float tile_scores(const IdxQuery<MB, D, FP8>& q, cons
 
 // ------------------------------------------------------------ emitters
 
+// Output rows hold `cap` entries; a rank past them (only possible if a row's
+// histogram and keys disagreed) is dropped rather than written out of bounds.
 struct EmitFinal {
     int32_t* idx;
     float* score;
     int base;        // position of key index 0
+    int cap;
     __device__ void prefetch(int, u32x4, uint32_t) {}
     __device__ void prefetch2(int, u32x4, uint32_t) {}
     __device__ void operator()(int rank, int i, int, uint32_t k) const {
+        if (rank >= cap) return;
         idx[rank] = base + i;
         if (score) score[rank] = key_score(k);
-    }
-};
-
-struct EmitCand {
-    uint32_t* key;
-    int32_t* pos;
-    int base;
-    __device__ void prefetch(int, u32x4, uint32_t) {}
-    __device__ void prefetch2(int, u32x4, uint32_t) {}
-    __device__ void operator()(int rank, int i, int, uint32_t k) const {
-        key[rank] = k;
-        pos[rank] = base + i;
-    }
-};
-
-// Positions come from a parallel array in global memory (merge inputs).
-struct EmitFinalPos {
-    const int32_t* src_pos;
-    int32_t* idx;
-    float* score;
-    int32_t p4[8];
-    __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) p4[e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
-    }
-    __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
-    }
-    __device__ void operator()(int rank, int, int e, uint32_t k) const {
-        idx[rank] = p4[e];
-        if (score) score[rank] = key_score(k);
-    }
-};
-
-struct EmitCandPos {
-    const int32_t* src_pos;
-    uint32_t* key;
-    int32_t* pos;
-    int32_t p4[8];
-    __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) p4[e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
-    }
-    __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? src_pos[i + e] : 0;
-    }
-    __device__ void operator()(int rank, int, int e, uint32_t k) const {
-        key[rank] = k;
-        pos[rank] = p4[e];
     }
 };
 
@@ -400,6 +353,7 @@ struct EmitFinalBuf {
     const int32_t* pos;
     int32_t* idx;
     float* score;
+    int cap;
     int32_t p4[8];
     __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
 #pragma unroll
@@ -410,6 +364,7 @@ struct EmitFinalBuf {
         for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
     }
     __device__ void operator()(int rank, int, int e, uint32_t k) const {
+        if (rank >= cap) return;
         idx[rank] = p4[e];
         if (score) score[rank] = key_score(k);
     }
@@ -431,382 +386,364 @@ __device__ int select_emit(const uint32_t* keys, int n, int m_cap, SelScratch* s
     return m;
 }
 
-// ------------------------------------------------------------ split kernel
+// ------------------------------------------------------------ score pass (decode)
 
-// Geometry of the split kernel. Eight waves; wave w scores query w / (8/G)
-// against its tiles sub, sub + 8/G, ... (sub = w % (8/G)) of 32 positions.
-// Each wave streams its tiles through a private ring of NS LDS slots filled by
-// direct global -> LDS copies, 16 bytes per lane and eight lanes per 128-byte
-// row (coalesced), with the 16-byte chunks of a row XOR-swizzled by the row
-// index so that the MFMA operand reads spread over the LDS banks. A wave only
-// waits on its own copies (no barrier in the streaming loop), and issues the
-// MFMAs of tile k before the vector epilogue of tile k-1, so both pipes stay
-// busy. With two queries the waves of a pair copy the same rows; the second
-// copy is served from L2.
+// Geometry of the score pass. Eight waves; the waves of query qi (8/G of them)
+// split the part's tiles of 32 positions into contiguous runs, one run per
+// wave. Each wave streams its run through a private ring of NS LDS slots filled
+// by direct global -> LDS copies, 16 bytes per lane and eight lanes per
+// 128-byte row (coalesced), with the 16-byte chunks of a row XOR-swizzled by
+// the row index so that the MFMA operand reads spread over the LDS banks. The
+// copies are addressed from scalar registers (page base) plus a loop-invariant
+// lane offset. A wave only waits on its own copies (no barrier in the loop);
+// it issues the MFMAs of tile k, the copy of tile k + NS - 1, the vector
+// epilogue of tile k - 1, then reads tile k + 1's operands, so the matrix pipe,
+// the vector pipe and the copies overlap. With two queries the waves of a pair
+// copy the same rows at about the same time; the second copy is served from L2.
 template <int D, bool FP8, int G>
-struct SplitGeom {
+struct RowsGeom {
     static constexpr int R = D * (FP8 ? 1 : 2);          // bytes per row
     static constexpr int CPR = R / 16;                   // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
-    // two queries: eight waves and most of the LDS (one workgroup per CU); one
-    // query: four waves and at most half the LDS, so that two workgroups share a
-    // CU and one's setup and selection overlap the other's streaming
-    static constexpr int NWV = G == 2 ? 8 : 4;           // waves per workgroup
-    static constexpr int NT = NWV * kWave;
+    static constexpr int NWV = kRowsThreads / kWave;
     static constexpr int WPQ = NWV / G;                  // waves per query
     static constexpr int TILE = 32 * R;                  // bytes of one tile
-    static constexpr size_t LDS_BUDGET = G == 2 ? kMaxLds : kMaxLds / 2;
-    static constexpr int NRING = NWV;                    // one ring per wave
-    static constexpr int NS_RAW = (G == 2 ? 98304 : 49152) / (NRING * TILE);
-    static constexpr int NS = NS_RAW < 2 ? 2 : (NS_RAW > 4 ? 4 : NS_RAW);   // ring depth
     static constexpr int DMA = TILE / 1024;              // 1 KB copies per tile
     static constexpr int PER_TILE = DMA + (FP8 ? 1 : 0); // copies per tile (+ scales)
-    static constexpr size_t STATIC_LDS = (size_t)NS * NRING * (TILE + (FP8 ? 128 : 0));
+    static constexpr int SLOT = TILE + (FP8 ? 256 : 0);  // (+ the scales of the tile's page)
+    static constexpr size_t FIXED = (size_t)G * kCoarseBins * 4 + kMaxPartPages * 4 + 512;
+    static constexpr int NS_FIT = (int)((kMaxLds - FIXED) / ((size_t)NWV * SLOT));
+    static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;   // ring depth
+    static constexpr int U = NS % 2 == 0 ? NS : 2 * NS;  // unroll: static slot and accumulator
+    static_assert(NS >= 2, "the ring needs two slots per wave");
 };
 
-__host__ __device__ inline size_t split_pages_bytes(int chunk) {
-    return ((size_t)(chunk / kPage) * 4 + 15) / 16 * 16;
-}
-
 template <int MB, int D, bool FP8, int G, bool SCORES>
-__global__ __launch_bounds__(512) void indexer_split_kernel(IdxArgs A, SplitArgs S) {
-    using GM = SplitGeom<D, FP8, G>;
-    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NT = GM::NT, WPQ = GM::WPQ;
-    constexpr int NRING = GM::NRING, RB = NRING * GM::TILE, SB = FP8 ? NRING * 32 : 4;
-    // one static array per ring slot: every LDS access names its slot, which lets
-    // the compiler wait for exactly the copies that wrote it
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[RB];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[RB];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[NS > 2 ? RB : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[NS > 3 ? RB : 16];
-    __shared__ __attribute__((aligned(16))) float scl0[SB];
-    __shared__ __attribute__((aligned(16))) float scl1[SB];
-    __shared__ __attribute__((aligned(16))) float scl2[NS > 2 ? SB : 4];
-    __shared__ __attribute__((aligned(16))) float scl3[NS > 3 ? SB : 4];
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    int* pages = reinterpret_cast<int*>(smem);
-    uint32_t* keys_all = reinterpret_cast<uint32_t*>(smem + split_pages_bytes(S.chunk));
-    uint32_t* hist_all = keys_all + (size_t)G * S.chunk;          // [G][kCoarseBins]
-    SelScratch* sel = reinterpret_cast<SelScratch*>(hist_all + (SCORES ? 0 : G * kCoarseBins));
+__global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, RowsArgs S) {
+    using GM = RowsGeom<D, FP8, G>;
+    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NWV = GM::NWV, WPQ = GM::WPQ, U = GM::U;
+    constexpr int SLOT = GM::SLOT, NV = KTile<D, FP8>::NV;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NWV * SLOT];
+    __shared__ int pages[kMaxPartPages];
+    __shared__ uint32_t hist[SCORES ? 1 : G * kCoarseBins];
 
-    const int g = blockIdx.x / S.n_chunks;
-    const int c = blockIdx.x % S.n_chunks;
-    const int w = threadIdx.x / kWave, l = lane_id(), half = l >> 5;
+    const int g = blockIdx.x / S.n_parts;
+    const int part = blockIdx.x % S.n_parts;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int l = lane_id(), half = l >> 5, frow = l & 31;
     const int qi = w / WPQ, sub = w % WPQ;
-    const int chunk0 = c * S.chunk;
+    const int pos0 = part * S.part;
 
     // The group's queries share one sequence; a query naming another sequence is
     // dropped (status bit) rather than scored against the wrong cache.
-    int rl[G];
-    int b0 = 0, rlmax = 0;
+    int b0 = 0, rlmax = 0, my_rl = 0;
 #pragma unroll
     for (int i = 0; i < G; i++) {
-        const int j = g * G + i;
-        rl[i] = 0;
-        if (j < A.num_q) {
+        const int jj = g * G + i;
+        int r = 0;
+        if (jj < A.num_q) {
             int b;
-            rl[i] = visible_len(A, j, b);
+            r = visible_len(A, jj, b);
             if (i == 0) b0 = b;
             else if (b != b0) {
                 if (threadIdx.x == 0) atomicOr(A.status, kBadSeq);
-                rl[i] = 0;
+                r = 0;
             }
+            if (!SCORES && part == 0 && threadIdx.x == 0) S.row_len[jj] = r;
         }
-        rlmax = max(rlmax, rl[i]);
+        rlmax = max(rlmax, r);
+        if (i == qi) my_rl = r;
     }
-    const int nvalid = max(0, min(S.chunk, rlmax - chunk0));
-    const int ntiles = (nvalid + 31) / 32;
+    // wave-uniform (the copies are addressed from scalar registers)
+    b0 = __builtin_amdgcn_readfirstlane(b0);
+    rlmax = __builtin_amdgcn_readfirstlane(rlmax);
+    my_rl = __builtin_amdgcn_readfirstlane(my_rl);
+    const int nvalid = max(0, min(S.part, rlmax - pos0));
     const int npg = (nvalid + kPage - 1) / kPage;
-    const int row_end = chunk0 + nvalid;
-    for (int i = threadIdx.x; i < npg; i += NT) pages[i] = page_of(A, b0, chunk0 / kPage + i);
+    for (int i = threadIdx.x; i < npg; i += kRowsThreads) pages[i] = page_of(A, b0, pos0 / kPage + i);
     if constexpr (!SCORES)
-        for (int i = threadIdx.x; i < G * kCoarseBins; i += NT) hist_all[i] = 0u;
+        for (int i = threadIdx.x; i < G * kCoarseBins; i += kRowsThreads) hist[i] = 0u;
     __syncthreads();
-    if (ntiles == 0) {
-        // nothing of this chunk is visible to any query of the group: an empty
-        // candidate set, or (single chunk) an all-padding output row
-        if constexpr (!SCORES) {
-            for (int i = 0; i < G; i++) {
-                const int jj = g * G + i;
-                if (jj >= A.num_q) break;
-                if (S.n_chunks == 1) {
-                    for (int r = threadIdx.x; r < S.topk; r += NT) {
-                        S.out_idx[(int64_t)jj * S.topk + r] = -1;
-                        if (S.out_score) S.out_score[(int64_t)jj * S.topk + r] = -INFINITY;
-                    }
-                } else if (threadIdx.x == 0) {
-                    S.cand_cnt[(int64_t)jj * S.n_chunks + c] = 0;
-                }
-            }
-        }
-        return;   // uniform over the workgroup
-    }
 
-    const int my_rl = rl[qi];
+    // this wave's run: tiles t0 .. t0 + n - 1 of the part (an even count per wave,
+    // so that a run starts on a page)
     const int j = g * G + qi;
-    // query registers first (unconditionally: a clamped index keeps the load in
-    // bounds), and all of them in before the copy pipeline starts, so that the
-    // only vector-memory operations in flight in the loop are the ring copies
-    IdxQuery<MB, D, FP8> q;
-    load_query<MB, D>(A, min(j, A.num_q - 1), q);
-    wait_vmcnt<0>();
+    const int my_valid = max(0, min(S.part, my_rl - pos0));
+    const int my_tiles = (my_valid + 31) / 32;
+    const int tpw = ((my_tiles + WPQ - 1) / WPQ + 1) & ~1;
+    const int t0 = sub * tpw;
+    const int n = max(0, min(tpw, my_tiles - t0));
+    const int64_t rowbase = (int64_t)j * S.ld + pos0;
 
-    auto ring = [&](int u) -> uint8_t* {
-        return (u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3) + w * GM::TILE;
-    };
-    auto scl = [&](int u) -> float* { return (u == 0 ? scl0 : u == 1 ? scl1 : u == 2 ? scl2 : scl3) + w * 32; };
-    // Loop-invariant per-lane offsets. A tile (32 positions, 32-aligned) lies in
-    // one page, so its rows are contiguous: copy r of a tile moves the 16-byte
-    // piece gi = 64 r + lane, i.e. row gi / CPR, chunk gi % CPR, stored at the
-    // chunk's swizzled place in the slot.
-    const int frow = l & 31;   // the tile row (position) this lane reads
-    int lds_off[KTile<D, FP8>::NV];
-#pragma unroll
-    for (int i = 0; i < KTile<D, FP8>::NV; i++) {
-        const int cc = KTile<D, FP8>::chunk(i, half);
-        lds_off[i] = frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
-    }
-    // positions [0, lim) of the chunk are visible to this wave's query
-    const int lim = min(row_end, my_rl) - chunk0;
-
-    // copy tile ti into this wave's slot (a tile past the end repeats the last
-    // page; rows past the visible end are read from the same, valid, page and
-    // masked out when scored)
-    auto issue = [&](int ti, uint8_t* slot, float* sslot) {
-        int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npg - 1)]);
-        page = page < 0 ? 0 : page;
-        const int64_t row0 = (int64_t)page * kPage + (ti & 1) * 32;
-        const uint8_t* base = A.rows + row0 * R;
+    if (n > 0) {
+        // copy r of a tile moves the 16-byte piece gi = 64 r + lane: row gi / CPR,
+        // chunk gi % CPR, stored at the chunk's swizzled place in the slot
+        uint32_t voff[GM::DMA];
 #pragma unroll
         for (int r = 0; r < GM::DMA; r++) {
             const int gi = r * kWave + l;
             const int row = gi / CPR, cc = gi % CPR;
-            // (the source goes through a named pointer: written inline in the call,
-            // the host compile drops the kernel's launch stub)
-            const uint8_t* src = base + row * R + ((cc ^ (row & GM::SWZ)) << 4);
-            __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)(slot + r * 1024), 16, 0, 0);
+            voff[r] = row * R + ((cc ^ (row & GM::SWZ)) << 4);
         }
-        if constexpr (FP8) {
-            const float* ssrc = A.scale + row0 + 4 * l;
-            if (l < 8) __builtin_amdgcn_global_load_lds(ssrc, (SIA_LDS void*)sslot, 16, 0, 0);
-        }
-    };
-    // operand reads of tile ti from its slot
-    auto fetch = [&](int ti, const uint8_t* slot, const float* sslot, KTile<D, FP8>& t) {
-        // the scale is read first: the wait for the row data that the MFMAs need
-        // then also covers it, before the slot is refilled
-        if constexpr (FP8) t.sc = sslot[frow];
-        else t.sc = 1.f;
+        // operand reads: lane half `half` of row frow
+        uint32_t roff[NV];
 #pragma unroll
-        for (int i = 0; i < KTile<D, FP8>::NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + lds_off[i]);
-        t.ok = frow < lim - ti * 32;   // a tile whose page id is invalid has no visible position
-    };
-    auto finish = [&](int ti, const f32x16 (&acc)[MB], float tsc, bool tok) {
-        const float sc = tile_epilogue<MB, D, FP8>(q, acc, tsc);
-        const int i = ti * 32 + frow;
-        if constexpr (SCORES) {
-            if (l < 32 && tok) S.scores[(int64_t)j * S.ld + chunk0 + i] = sc;
-        } else {
-            // the key goes to LDS (both lane halves hold the same key and store
-            // it to the same place) and into the coarse histogram of its query
-            const uint32_t k = tok ? score_key(sc) : 0u;
-            keys_all[qi * S.chunk + i] = k;
-            if (l < 32 && k != 0u) atomicAdd(&hist_all[qi * kCoarseBins + coarse_bin(k)], 1u);
+        for (int i = 0; i < NV; i++) {
+            const int cc = KTile<D, FP8>::chunk(i, half);
+            roff[i] = w * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
         }
-    };
+        const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring)) +
+                                  w * SLOT;
+        // copy the wave's k-th tile (clamped to its last) into slot s
+        auto issue = [&](int k, int s) {
+            const int t = t0 + min(k, n - 1);
+            const int page = max(__builtin_amdgcn_readfirstlane(pages[t >> 1]), 0);
+            const int64_t row0 = (int64_t)page * kPage + (t & 1) * 32;
+            const uint8_t* base = A.rows + row0 * R;
+            const uint32_t dst = ring_lds + s * (NWV * SLOT);
+#pragma unroll
+            for (int r = 0; r < GM::DMA; r++) dma16_s(base, voff[r], dst + r * 1024);
+            if constexpr (FP8) {
+                // the 64 scales of the page, 4 bytes per lane (no lane mask, so
+                // that the loop body stays one basic block)
+                const float* sbase = A.scale + (int64_t)page * kPage;
+                dma4_s(sbase, 4 * l, dst + GM::TILE);
+            }
+        };
+        // operand reads of the wave's k-th tile from slot s
+        auto fetch = [&](int k, int s, KTile<D, FP8>& t) {
+            const uint8_t* slot = ring + s * (NWV * SLOT);
+#pragma unroll
+            for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
+            if constexpr (FP8)
+                t.sc = *reinterpret_cast<const float*>(slot + w * SLOT + GM::TILE + 4 * (((t0 + k) & 1) * 32 + frow));
+            else t.sc = 1.f;
+            // (positions on a page whose id is out of range are scored from page 0;
+            // the call reports the bad id through the status word)
+            t.ok = (t0 + k) * 32 + frow < my_valid;
+        };
+        // Epilogue of the wave's kk-th tile. kk outside [0, n) is a padding step
+        // (the last tile again, or the step before the first): its keys go to the
+        // row's spare tail and count nowhere. Without branches, so that the
+        // compiler keeps the MFMAs where they are issued instead of sinking them
+        // into a store branch next to this epilogue.
+        auto finish = [&](int kk, const f32x16 (&acc)[MB], float tsc, bool tok, const IdxQuery<MB, D, FP8>& q) {
+            const float sc = tile_epilogue<MB, D, FP8>(q, acc, tsc);
+            const bool valid = kk >= 0 && kk < n;
+            if constexpr (SCORES) {
+                asm volatile("" ::"v"(sc));
+                if (l < 32 && tok && valid) S.scores[rowbase + (t0 + kk) * 32 + frow] = sc;
+            } else {
+                const uint32_t key = tok && valid ? score_key(sc) : 0u;
+                const int64_t o = valid ? rowbase + (t0 + kk) * 32 + frow : (int64_t)j * S.ld + S.ld - 64 + frow;
+                S.keys[o] = key;   // both lane halves hold the same key
+                // lanes 32..63 add 0 to distinct bins (no conflicts)
+                atomicAdd(&hist[qi * kCoarseBins + (l < 32 ? coarse_bin(key) : (uint32_t)l)],
+                          (l < 32 && key != 0u) ? 1u : 0u);
+            }
+        };
 
-    const bool active = my_rl > chunk0 && sub < ntiles;
-    if (active) {
-        // this wave's tiles: sub + k * WPQ; slot of the k-th: k % NS
+        // the first copies go out before the query is read, so that both latencies overlap
 #pragma unroll
-        for (int u = 0; u < NS - 1; u++) issue(sub + u * WPQ, ring(u), scl(u));
+        for (int u = 0; u < NS - 1; u++) issue(u, u);
+        IdxQuery<MB, D, FP8> q;
+        load_query<MB, D>(A, j, q);
+        wait_vmcnt_mem<0>();
+        KTile<D, FP8> t;
+        fetch(0, 0, t);
         f32x16 acc0[MB], acc1[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) acc1[mb] = f32x16{};
         float sc0 = 0.f, sc1 = 0.f;
         bool ok0 = false, ok1 = false;
-        int prev = -1;
-        for (int k0 = 0; sub + k0 * WPQ < ntiles; k0 += 2 * NS) {
+        // the run is padded to a multiple of the unroll with repeats of its last
+        // tile (scored, never stored), so the loop body has no branches
+        for (int k0 = 0; k0 < n; k0 += U) {
 #pragma unroll
-            for (int u = 0; u < 2 * NS; u++) {
-                const int ti = sub + (k0 + u) * WPQ;
-                if (ti < ntiles) {
-                    issue(ti + (NS - 1) * WPQ, ring((u + NS - 1) % NS), scl((u + NS - 1) % NS));
-                    wait_vmcnt<(NS - 1) * GM::PER_TILE>();   // this tile's copies have landed
-                    KTile<D, FP8> t;
-                    fetch(ti, ring(u % NS), scl(u % NS), t);
-                    // MFMAs of this tile, then the vector epilogue of the previous one
-                    if (u % 2 == 0) {
-                        tile_mfma<MB, D, FP8>(q, t, acc0);
-                        sc0 = t.sc; ok0 = t.ok;
-                        if (prev >= 0) finish(prev, acc1, sc1, ok1);
-                    } else {
-                        tile_mfma<MB, D, FP8>(q, t, acc1);
-                        sc1 = t.sc; ok1 = t.ok;
-                        finish(prev, acc0, sc0, ok0);
-                    }
-                    prev = ti;
+            for (int u = 0; u < U; u++) {
+                const int k = k0 + u;
+                if (u % 2 == 0) {
+                    tile_mfma<MB, D, FP8>(q, t, acc0);
+                    sc0 = t.sc; ok0 = t.ok;
+                } else {
+                    tile_mfma<MB, D, FP8>(q, t, acc1);
+                    sc1 = t.sc; ok1 = t.ok;
                 }
+                __builtin_amdgcn_sched_barrier(0);   // the MFMAs go out before the epilogue below
+                issue(k + NS - 1, (u + NS - 1) % NS);   // refills the slot of tile k - 1
+                if (u % 2 == 0) finish(k - 1, acc1, sc1, ok1, q);
+                else finish(k - 1, acc0, sc0, ok0, q);
+                wait_vmcnt_mem<(NS - 2) * GM::PER_TILE>();   // tile k + 1 has landed
+                fetch(min(k + 1, n - 1), (u + 1) % NS, t);
             }
         }
-        // epilogue of the last tile: its parity is the count of tiles of this wave
-        const int count = (ntiles - sub + WPQ - 1) / WPQ;
-        if (count % 2 == 1) finish(prev, acc0, sc0, ok0);
-        else finish(prev, acc1, sc1, ok1);
-    } else if constexpr (!SCORES) {
-        // a query that sees nothing of this chunk still needs zero keys
-        for (int i = sub * kWave + l; i < ntiles * 32; i += WPQ * kWave) keys_all[qi * S.chunk + i] = 0u;
+        // last step of the padded run: its parity is that of U (even)
+        finish(((n + U - 1) / U) * U - 1, acc1, sc1, ok1, q);
+        wait_vmcnt_mem<0>();
     }
-    wait_vmcnt<0>();
-    if constexpr (SCORES) return;
-    else {
+    if constexpr (!SCORES) {
         __syncthreads();
-        // ---- per-query selection over the chunk
-        const int nscan = ntiles * 32;
-#pragma unroll
         for (int i = 0; i < G; i++) {
             const int jj = g * G + i;
             if (jj >= A.num_q) break;
-            const uint32_t* keys = keys_all + i * S.chunk;
-            const uint32_t* hist = hist_all + i * kCoarseBins;
-            if (S.n_chunks == 1) {
-                int32_t* oi = S.out_idx + (int64_t)jj * S.topk;
-                float* os = S.out_score ? S.out_score + (int64_t)jj * S.topk : nullptr;
-                const int m = select_emit_coarse<NT>(keys, nscan, hist, S.topk, sel, EmitFinal{oi, os, chunk0});
-                for (int r = m + threadIdx.x; r < S.topk; r += NT) {
-                    oi[r] = -1;
-                    if (os) os[r] = -INFINITY;
+            uint32_t* dst = S.hist + ((int64_t)jj * S.n_parts + part) * kCoarseBins;
+            for (int b = threadIdx.x; b < kCoarseBins; b += kRowsThreads) dst[b] = hist[i * kCoarseBins + b];
+        }
+    }
+}
+
+// ------------------------------------------------------------ keys from given scores
+
+__global__ __launch_bounds__(kRowsThreads) void keys_from_scores_kernel(KeysFromScoresArgs K) {
+    __shared__ uint32_t hist[kCoarseBins];
+    const int j = blockIdx.x / K.n_parts;
+    const int part = blockIdx.x % K.n_parts;
+    for (int b = threadIdx.x; b < kCoarseBins; b += kRowsThreads) hist[b] = 0u;
+    __syncthreads();
+    int rl = K.row_len[j];
+    if (rl < 0 || rl > K.max_len) {
+        if (threadIdx.x == 0) atomicOr(K.status, kRowTooLong);
+        rl = max(0, min(rl, K.max_len));
+    }
+    const int p0 = part * K.part;
+    const int p1 = min(p0 + K.part, rl);
+    for (int p = p0 + threadIdx.x; p < p1; p += kRowsThreads) {
+        const uint32_t key = score_key(K.scores[(int64_t)j * K.ld_in + p]);
+        K.keys[(int64_t)j * K.ld + p] = key;
+        atomicAdd(&hist[coarse_bin(key)], 1u);
+    }
+    __syncthreads();
+    uint32_t* dst = K.hist + ((int64_t)j * K.n_parts + part) * kCoarseBins;
+    for (int b = threadIdx.x; b < kCoarseBins; b += kRowsThreads) dst[b] = hist[b];
+}
+
+// ------------------------------------------------------------ selection pass
+
+// Appends every key >= lo of keys[0..n) (global) and its position to the LDS
+// arrays ckey / cpos, in position order. Wave w takes a contiguous segment;
+// within it, 16 steps of 256 keys (4 per lane) are in flight at once, and each
+// step's candidates are placed by a wave prefix sum. Returns the count.
+__device__ int filter_candidates(const uint32_t* keys, int n, uint32_t lo, uint32_t* ckey, int32_t* cpos,
+                                 int* wtot) {
+    constexpr int NW = kSelThreads / kWave, STEPS = 16, SPAN = STEPS * 256;
+    const int w = threadIdx.x / kWave, l = lane_id();
+    const int seg = ((n + NW - 1) / NW + SPAN - 1) / SPAN * SPAN;
+    const int s0 = w * seg, s1 = min(s0 + seg, n);
+    // pass 1: count
+    int cnt = 0;
+    for (int b = s0; b < s1; b += SPAN) {
+        u32x4 k4[STEPS];
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            const int i = b + s * 256 + 4 * l;
+            k4[s] = i < s1 ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            const int i = b + s * 256 + 4 * l;
+#pragma unroll
+            for (int e = 0; e < 4; e++) cnt += (i + e < s1 && k4[s][e] >= lo);
+        }
+    }
+    cnt = wave_sum(cnt);
+    if (l == 0) wtot[w] = cnt;
+    __syncthreads();
+    int off = 0, total = 0;
+    for (int i = 0; i < NW; i++) {
+        const int c = wtot[i];
+        off += i < w ? c : 0;
+        total += c;
+    }
+    // pass 2: place (the segment is read again, from cache)
+    for (int b = s0; b < s1; b += SPAN) {
+        u32x4 k4[STEPS];
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            const int i = b + s * 256 + 4 * l;
+            k4[s] = i < s1 ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            const int i = b + s * 256 + 4 * l;
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) c += (i + e < s1 && k4[s][e] >= lo);
+            const int inc = wave_incl_scan(c);
+            int at = off + inc - c;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if (i + e < s1 && k4[s][e] >= lo) {
+                    if (at < kSelCap) {   // (the caller checked the count; this only guards LDS)
+                        ckey[at] = k4[s][e];
+                        cpos[at] = i + e;
+                    }
+                    at++;
                 }
-            } else {
-                const int64_t slot = (int64_t)jj * S.n_chunks + c;
-                const int m = select_emit_coarse<NT>(
-                    keys, nscan, hist, S.kc, sel,
-                    EmitCand{S.cand_key + slot * S.kc, S.cand_pos + slot * S.kc, chunk0});
-                if (threadIdx.x == 0) S.cand_cnt[slot] = m;
             }
+            off += __shfl(inc, kWave - 1, kWave);
+        }
+    }
+    __syncthreads();
+    return total;
+}
+
+// One workgroup per query: the coarse histogram (sum of the parts') gives the
+// bin of the K-th largest key; every key at or above that bin is gathered into
+// LDS in position order, the exact threshold is refined there, and the ordered
+// compaction emits the Top-K ascending in position. A row whose candidates do
+// not fit in LDS is refined and compacted straight from global memory.
+__global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
+    __shared__ uint32_t hist[kCoarseBins];
+    __shared__ __attribute__((aligned(16))) uint32_t ckey[kSelCap];
+    __shared__ __attribute__((aligned(16))) int32_t cpos[kSelCap];
+    __shared__ SelScratch sel;
+    __shared__ int wtot[kSelThreads / kWave];
+    const int j = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int rl = max(0, min(S.row_len[j], S.max_len));
+    int32_t* oi = S.out_idx + (int64_t)j * S.topk;
+    float* os = S.out_score ? S.out_score + (int64_t)j * S.topk : nullptr;
+    for (int b = tid; b < kCoarseBins; b += kSelThreads) {
+        uint32_t c = 0;
+        for (int p = 0; p < S.n_parts; p++) c += S.hist[((int64_t)j * S.n_parts + p) * kCoarseBins + b];
+        hist[b] = c;
+    }
+    __syncthreads();
+    int above, total;
+    const int bin = coarse_select<kSelThreads>(hist, S.topk, &sel, above, total);
+    const int m = min(S.topk, total);
+    if (m > 0) {
+        const uint32_t* keys = S.keys + (int64_t)j * S.ld;
+        const bool all = m == total;
+        const uint32_t bin_lo = (uint32_t)bin << (32 - kCoarseBits);
+        const uint32_t lo = all ? 1u : max(bin_lo, 1u);
+        const int ncand = all ? total : above + (int)hist[bin];
+        if (ncand <= kSelCap) {
+            const int got = filter_candidates(keys, rl, lo, ckey, cpos, wtot);
+            // (got == ncand: the histogram counted exactly these keys)
+            const int nc = min(got, kSelCap);
+            for (int i = nc + tid; i < (nc + 7) / 8 * 8; i += kSelThreads) ckey[i] = 0u;
             __syncthreads();
-        }
-    }
-}
-
-// Largest chunk (power of two, <= 16384) whose LDS fits next to the ring.
-template <int MB, int D, bool FP8, int G>
-static int split_chunk_cap() {
-    using GM = SplitGeom<D, FP8, G>;
-    for (int chunk = 16384; chunk >= 64; chunk >>= 1) {
-        const size_t dyn = split_pages_bytes(chunk) + (size_t)G * (chunk + kCoarseBins) * 4 + sizeof(SelScratch);
-        if (GM::STATIC_LDS + dyn + 256 <= GM::LDS_BUDGET) return chunk;
-    }
-    return 64;
-}
-
-// ------------------------------------------------------------ selection from given scores
-
-__global__ __launch_bounds__(kSplitThreads) void topk_from_scores_kernel(FromScoresArgs F, SplitArgs S) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
-    SelScratch* sel = reinterpret_cast<SelScratch*>(smem + (size_t)S.chunk * 4);
-    const int j = blockIdx.x / S.n_chunks;
-    const int c = blockIdx.x % S.n_chunks;
-    const int chunk0 = c * S.chunk;
-    const int rl = F.row_len[j];
-    const int nvalid = max(0, min(S.chunk, rl - chunk0));
-    const int nscan = (nvalid + 3) / 4 * 4;
-    for (int i = threadIdx.x; i < nscan; i += kSplitThreads)
-        keys[i] = i < nvalid ? score_key(F.scores[(int64_t)j * F.ld + chunk0 + i]) : 0u;
-    __syncthreads();
-    if (S.n_chunks == 1) {
-        int32_t* oi = S.out_idx + (int64_t)j * S.topk;
-        float* os = S.out_score ? S.out_score + (int64_t)j * S.topk : nullptr;
-        const int m = select_emit<kSplitThreads>(keys, nscan, S.topk, sel, EmitFinal{oi, os, chunk0});
-        for (int r = m + threadIdx.x; r < S.topk; r += kSplitThreads) {
-            oi[r] = -1;
-            if (os) os[r] = -INFINITY;
-        }
-    } else {
-        const int64_t slot = (int64_t)j * S.n_chunks + c;
-        const int m = select_emit<kSplitThreads>(
-            keys, nscan, S.kc, sel,
-            EmitCand{S.cand_key + slot * S.kc, S.cand_pos + slot * S.kc, chunk0});
-        if (threadIdx.x == 0) S.cand_cnt[slot] = m;
-    }
-}
-
-// ------------------------------------------------------------ merge
-
-// Rank -> candidate index, kept in LDS; positions are gathered afterwards in
-// one parallel pass instead of one dependent load per compaction round.
-struct EmitRank {
-    int32_t* rank_idx;
-    __device__ void prefetch(int, u32x4, uint32_t) {}
-    __device__ void prefetch2(int, u32x4, uint32_t) {}
-    __device__ void operator()(int rank, int i, int, uint32_t) const { rank_idx[rank] = i; }
-};
-
-__global__ __launch_bounds__(kMergeThreads) void topk_merge_kernel(MergeArgs M) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint32_t* keys = reinterpret_cast<uint32_t*>(smem);
-    const int q = blockIdx.x / M.n_out;
-    const int o = blockIdx.x % M.n_out;
-    const int s0 = o * M.fan_in;
-    const int nsets = min(M.fan_in, M.n_in - s0);
-    const int n = nsets * M.kc_in;
-    uint32_t* hist = keys + (size_t)M.fan_in * M.kc_in;
-    int32_t* rank_idx = reinterpret_cast<int32_t*>(hist + kCoarseBins);     // [topk]
-    int* cnt = rank_idx + M.topk;                                          // [fan_in]
-    SelScratch* sel = reinterpret_cast<SelScratch*>(cnt + (M.fan_in + 3) / 4 * 4);
-    const int64_t set0 = (int64_t)q * M.n_in + s0;
-    for (int i = threadIdx.x; i < kCoarseBins; i += kMergeThreads) hist[i] = 0u;
-    for (int i = threadIdx.x; i < nsets; i += kMergeThreads) cnt[i] = M.in_cnt[set0 + i];
-    __syncthreads();
-    // candidate keys: independent loads, several in flight per thread
-    const uint32_t* src = M.in_key + set0 * M.kc_in;
-    constexpr int U = 32;
-    for (int i0 = threadIdx.x; i0 < n; i0 += kMergeThreads * U) {
-        uint32_t k[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int i = i0 + u * kMergeThreads;
-            const int set = i / M.kc_in;
-            k[u] = (i < n && i - set * M.kc_in < cnt[min(set, nsets - 1)]) ? src[i] : 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int i = i0 + u * kMergeThreads;
-            if (i < n) keys[i] = k[u];
-        }
-    }
-    __syncthreads();
-    for (int i = threadIdx.x * 4; i < n; i += kMergeThreads * 4) {
-        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
-#pragma unroll
-        for (int e = 0; e < 4; e++) hist_add(hist, coarse_bin(k4[e]), i + e < n && k4[e] != 0u);
-    }
-    __syncthreads();
-    const int m = select_emit_coarse<kMergeThreads>(keys, n, hist, M.topk, sel, EmitRank{rank_idx});
-    __syncthreads();
-    const int32_t* src_pos = M.in_pos + set0 * M.kc_in;
-    if (M.out_idx) {
-        int32_t* oi = M.out_idx + (int64_t)q * M.topk;
-        float* os = M.out_score ? M.out_score + (int64_t)q * M.topk : nullptr;
-        for (int r = threadIdx.x; r < M.topk; r += kMergeThreads) {
-            if (r < m) {
-                const int i = rank_idx[r];
-                oi[r] = src_pos[i];
-                if (os) os[r] = key_score(keys[i]);
+            if (all) {
+                ordered_compact<kSelThreads>(ckey, nc, 0u, 0, &sel, EmitFinalBuf{cpos, oi, os, S.topk, {}});
             } else {
-                oi[r] = -1;
-                if (os) os[r] = -INFINITY;
+                int ties;
+                const uint32_t T = radix_refine<kSelThreads>(ckey, nc, bin_lo, ~0u << (32 - kCoarseBits),
+                                                             m - above, 32 - kCoarseBits, &sel, ties);
+                ordered_compact<kSelThreads>(ckey, nc, T, ties, &sel, EmitFinalBuf{cpos, oi, os, S.topk, {}});
             }
+        } else if (all) {
+            ordered_compact<kSelThreads>(keys, rl, 0u, 0, &sel, EmitFinal{oi, os, 0, S.topk});
+        } else {
+            int ties;
+            const uint32_t T = radix_refine<kSelThreads>(keys, rl, bin_lo, ~0u << (32 - kCoarseBits), m - above,
+                                                         32 - kCoarseBits, &sel, ties);
+            ordered_compact<kSelThreads>(keys, rl, T, ties, &sel, EmitFinal{oi, os, 0, S.topk});
         }
-    } else {
-        const int64_t slot = (int64_t)q * M.n_out + o;
-        uint32_t* ok = M.out_key + slot * M.topk;
-        int32_t* op = M.out_pos + slot * M.topk;
-        for (int r = threadIdx.x; r < m; r += kMergeThreads) {
-            const int i = rank_idx[r];
-            ok[r] = keys[i];
-            op[r] = src_pos[i];
-        }
-        if (threadIdx.x == 0) M.out_cnt[slot] = m;
+    }
+    for (int r = m + tid; r < S.topk; r += kSelThreads) {
+        oi[r] = -1;
+        if (os) os[r] = -INFINITY;
     }
 }
 
@@ -881,7 +818,7 @@ __device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, int r
     const int n4 = (cnt + 3) & ~3;
     for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
     wave_sync();
-    const int m = select_emit<kWave>(B.key, n4, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, {}});
+    const int m = select_emit<kWave>(B.key, n4, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}});
     for (int r = m + l; r < S.topk; r += kWave) {
         oi[r] = -1;
         if (os) os[r] = -INFINITY;
@@ -966,64 +903,37 @@ static hipError_t set_smem(K kernel, size_t bytes) {
 }
 
 template <int MB, int D, bool FP8, int G, bool SC>
-static hipError_t split_launch(const IdxArgs& a, const SplitArgs& s, hipStream_t st) {
-    constexpr int NT = SplitGeom<D, FP8, G>::NT;
+static hipError_t rows_launch(const IdxArgs& a, const RowsArgs& r, hipStream_t st) {
     const int groups = (a.num_q + G - 1) / G;
-    const size_t smem = split_pages_bytes(s.chunk) +
-                        (SC ? 0 : (size_t)G * (s.chunk + kCoarseBins) * 4 + sizeof(SelScratch));
-    auto k = indexer_split_kernel<MB, D, FP8, G, SC>;
-    hipError_t e = set_smem(k, smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(groups * s.n_chunks), dim3(NT), smem, st, a, s);
+    hipLaunchKernelGGL((indexer_rows_kernel<MB, D, FP8, G, SC>), dim3(groups * r.n_parts), dim3(kRowsThreads), 0,
+                       st, a, r);
     return hipGetLastError();
-}
-
-template <int MB, int D, bool FP8, int G>
-static hipError_t split_launch2(const IdxArgs& a, const SplitArgs& s, bool sc, hipStream_t st) {
-    return sc ? split_launch<MB, D, FP8, G, true>(a, s, st) : split_launch<MB, D, FP8, G, false>(a, s, st);
 }
 
 template <int MB, int D, bool FP8>
-static hipError_t split_launch3(const IdxArgs& a, const SplitArgs& s, int g, bool sc, hipStream_t st) {
-    return g == 2 ? split_launch2<MB, D, FP8, 2>(a, s, sc, st) : split_launch2<MB, D, FP8, 1>(a, s, sc, st);
+static hipError_t rows_launch3(const IdxArgs& a, const RowsArgs& r, int g, bool sc, hipStream_t st) {
+    if (g == 2) return sc ? rows_launch<MB, D, FP8, 2, true>(a, r, st) : rows_launch<MB, D, FP8, 2, false>(a, r, st);
+    return sc ? rows_launch<MB, D, FP8, 1, true>(a, r, st) : rows_launch<MB, D, FP8, 1, false>(a, r, st);
 }
 
-int indexer_split_chunk_cap(int mb, int dim, bool fp8, int group) {
-#define SIA_CAP(MBv, Dv, F8)                                                              \
-    if (mb == MBv && dim == Dv && fp8 == F8)                                              \
-        return group == 2 ? split_chunk_cap<MBv, Dv, F8, 2>() : split_chunk_cap<MBv, Dv, F8, 1>();
-    SIA_CAP(1, 64, false) SIA_CAP(1, 64, true) SIA_CAP(1, 128, false) SIA_CAP(1, 128, true)
-    SIA_CAP(2, 64, false) SIA_CAP(2, 64, true) SIA_CAP(2, 128, false) SIA_CAP(2, 128, true)
-#undef SIA_CAP
-    return 2048;
-}
-
-hipError_t launch_indexer_split(const IdxArgs& a, const SplitArgs& s, int mb, int dim, bool fp8,
-                                int group, bool scores_mode, hipStream_t st) {
-#define SIA_SPLIT(MBv, Dv, F8)                                                  \
-    if (mb == MBv && dim == Dv && fp8 == F8)                                   \
-        return split_launch3<MBv, Dv, F8>(a, s, group, scores_mode, st);
-    SIA_SPLIT(1, 64, false) SIA_SPLIT(1, 64, true) SIA_SPLIT(1, 128, false) SIA_SPLIT(1, 128, true)
-    SIA_SPLIT(2, 64, false) SIA_SPLIT(2, 64, true) SIA_SPLIT(2, 128, false) SIA_SPLIT(2, 128, true)
-#undef SIA_SPLIT
+hipError_t launch_indexer_rows(const IdxArgs& a, const RowsArgs& r, int mb, int dim, bool fp8, int group,
+                               bool scores_mode, hipStream_t st) {
+#define SIA_ROWS(MBv, Dv, F8)                                                  \
+    if (mb == MBv && dim == Dv && fp8 == F8)                                  \
+        return rows_launch3<MBv, Dv, F8>(a, r, group, scores_mode, st);
+    SIA_ROWS(1, 64, false) SIA_ROWS(1, 64, true) SIA_ROWS(1, 128, false) SIA_ROWS(1, 128, true)
+    SIA_ROWS(2, 64, false) SIA_ROWS(2, 64, true) SIA_ROWS(2, 128, false) SIA_ROWS(2, 128, true)
+#undef SIA_ROWS
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_topk_from_scores(const FromScoresArgs& f, const SplitArgs& s, hipStream_t st) {
-    const size_t smem = (size_t)s.chunk * 4 + sizeof(SelScratch);
-    hipError_t e = set_smem(topk_from_scores_kernel, smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_from_scores_kernel, dim3(f.num_q * s.n_chunks), dim3(kSplitThreads), smem,
-                       st, f, s);
+hipError_t launch_keys_from_scores(const KeysFromScoresArgs& k, hipStream_t st) {
+    hipLaunchKernelGGL(keys_from_scores_kernel, dim3(k.num_q * k.n_parts), dim3(kRowsThreads), 0, st, k);
     return hipGetLastError();
 }
 
-hipError_t launch_topk_merge(const MergeArgs& m, hipStream_t st) {
-    const size_t smem = ((size_t)m.fan_in * m.kc_in + kCoarseBins + m.topk + (m.fan_in + 3) / 4 * 4) * 4 +
-                        sizeof(SelScratch);
-    hipError_t e = set_smem(topk_merge_kernel, smem);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(m.num_q * m.n_out), dim3(kMergeThreads), smem, st, m);
+hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st) {
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(s.num_q), dim3(kSelThreads), 0, st, s);
     return hipGetLastError();
 }
 

@@ -99,79 +99,38 @@ int check_index_cache(const sia_paged_cache* c) {
 
 // ------------------------------------------------------------ indexer plan
 
-struct MergeLevel {
-    int n_in, kc_in, fan_in, n_out;
-    size_t in_key, in_pos, in_cnt;     // workspace offsets of the level's inputs
-    size_t out_key, out_pos, out_cnt;  // intermediate outputs (unused on the last level)
-};
-
 struct IndexerPlan {
     bool stream = false;
-    int group = 1;               // queries per split workgroup (1 or 2)
-    int chunk = 0, n_chunks = 0, kc = 0;
+    int group = 1;               // queries per score-pass workgroup (1 or 2)
+    int part = 0, n_parts = 0;   // score-pass parts of each row
+    int64_t ld = 0;              // key row stride
+    size_t keys = 0, hist = 0, rlen = 0;   // workspace offsets
     int cap = 0;                 // stream buffer capacity
-    int n_levels = 0;
-    MergeLevel lv[8];
     size_t total = kHeader;
 };
 
-void plan_merge(IndexerPlan& p, int64_t num_q, int topk, size_t cand_key, size_t cand_pos,
-                size_t cand_cnt) {
-    int n_in = p.n_chunks, kc_in = p.kc;
-    size_t ik = cand_key, ip = cand_pos, ic = cand_cnt;
-    p.n_levels = 0;
-    while (n_in > 1 && p.n_levels < 8) {
-        MergeLevel L;
-        L.n_in = n_in;
-        L.kc_in = kc_in;
-        // keys of fan_in candidate sets, the coarse histogram and the rank list share LDS
-        const int cap_keys = (int)((sia::kMaxLds - 4 * (size_t)sia::kCoarseBinsHost - 4 * (size_t)topk - 4096) / 4);
-        L.fan_in = std::max(2, std::min(n_in, std::min(sia::kMergeCap, cap_keys) / kc_in));
-        L.n_out = (int)ceil_div(n_in, L.fan_in);
-        L.in_key = ik; L.in_pos = ip; L.in_cnt = ic;
-        L.out_key = L.out_pos = L.out_cnt = 0;
-        if (L.n_out > 1) {
-            const size_t nset = (size_t)num_q * L.n_out;
-            L.out_key = p.total; p.total += align_up(nset * topk * 4);
-            L.out_pos = p.total; p.total += align_up(nset * topk * 4);
-            L.out_cnt = p.total; p.total += align_up(nset * 4);
-        }
-        p.lv[p.n_levels++] = L;
-        ik = L.out_key; ip = L.out_pos; ic = L.out_cnt;
-        n_in = L.n_out;
-        kc_in = topk;
-    }
-}
-
-void plan_split(IndexerPlan& p, int64_t num_q, int max_visible, int topk, int group_cap, int chunk_max) {
-    p.group = group_cap;
-    const int64_t n_groups = ceil_div(num_q, p.group);
-    int chunk;
-    const int forced = env_int("SIA_SPLIT_CHUNK", 0);
-    if (forced > 0) {
-        chunk = std::max(64, std::min(chunk_max, forced / 64 * 64));
-    } else if (max_visible <= 4096) {
-        chunk = std::max(64, std::min(chunk_max, (max_visible + 63) / 64 * 64));
-    } else {
-        const int64_t target = ceil_div((int64_t)max_visible * n_groups, 1024);
-        chunk = std::max(2048, std::min(chunk_max, round_up_pow2(target)));
-    }
-    p.n_chunks = (int)std::max<int64_t>(1, ceil_div(std::max(max_visible, 1), chunk));
-    if (p.n_chunks == 1) chunk = std::max(64, std::min(chunk_max, (max_visible + 63) / 64 * 64));
-    p.chunk = chunk;
-    p.kc = std::min(topk, chunk);
-    if (p.n_chunks > 1) {
-        const size_t nset = (size_t)num_q * p.n_chunks;
-        const size_t ck = p.total; p.total += align_up(nset * p.kc * 4);
-        const size_t cp = p.total; p.total += align_up(nset * p.kc * 4);
-        const size_t cc = p.total; p.total += align_up(nset * 4);
-        plan_merge(p, num_q, topk, ck, cp, cc);
-    }
+// Score pass + selection pass. One score workgroup is resident per CU, so a row
+// is cut into enough parts to give every CU one (parts of 2048 to 65536
+// positions); the selection pass reads the key rows and per-part histograms.
+void plan_rows(IndexerPlan& p, int64_t num_q, int max_visible, int group) {
+    p.group = group;
+    const int64_t n_groups = std::max<int64_t>(1, ceil_div(num_q, group));
+    const int64_t mv = std::max(max_visible, 1);
+    const int forced = env_int("SIA_ROWS_PARTS", 0);
+    int64_t np = forced > 0 ? forced : std::max<int64_t>(1, ceil_div(device_cus(), n_groups));
+    if (forced <= 0) np = std::min<int64_t>(np, std::max<int64_t>(1, ceil_div(mv, 2048)));
+    np = std::max<int64_t>(np, ceil_div(mv, 64 * (int64_t)sia::kMaxPartPages));
+    p.part = (int)(ceil_div(ceil_div(mv, np), 64) * 64);
+    p.n_parts = (int)ceil_div(mv, p.part);
+    p.ld = ceil_div(mv, 64) * 64 + 64;   // (+ a spare tail that padding steps write)
+    p.keys = p.total; p.total += align_up((size_t)num_q * p.ld * 4);
+    p.hist = p.total; p.total += align_up((size_t)num_q * p.n_parts * sia::kCoarseBinsHost * 4);
+    p.rlen = p.total; p.total += align_up((size_t)num_q * 4);
 }
 
 IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bool fp8) {
     IndexerPlan p;
-    const int mode = env_int("SIA_INDEXER_PATH", 0);   // 0 auto, 1 split, 2 stream
+    const int mode = env_int("SIA_INDEXER_PATH", 0);   // 0 auto, 1 score + select passes, 2 stream
     const bool stream_ok = topk <= 2048 && qs->group % 4 == 0;
     bool stream = stream_ok && qs->num_q >= 256 && qs->max_visible > 2 * topk;
     if (mode == 1) stream = false;
@@ -185,9 +144,10 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bo
             return p;
         }
     }
+    (void)heads; (void)dim; (void)fp8;
     int g = qs->group % 2 == 0 ? 2 : 1;
-    if (env_int("SIA_SPLIT_GROUP", 0) == 1) g = 1;
-    plan_split(p, qs->num_q, qs->max_visible, topk, g, sia::indexer_split_chunk_cap(heads > 32 ? 2 : 1, dim, fp8, g));
+    if (env_int("SIA_ROWS_GROUP", 0) == 1) g = 1;
+    plan_rows(p, qs->num_q, qs->max_visible, g);
     return p;
 }
 
@@ -210,32 +170,6 @@ sia::IdxArgs idx_args(const sia_page_table* pt, const sia_paged_cache* c, const 
     a.heads = heads;
     a.status = static_cast<uint32_t*>(ws);
     return a;
-}
-
-hipError_t run_merges(const IndexerPlan& p, uint8_t* ws, int num_q, int topk, int32_t* out_idx,
-                      float* out_score, hipStream_t st) {
-    for (int i = 0; i < p.n_levels; i++) {
-        const MergeLevel& L = p.lv[i];
-        sia::MergeArgs m;
-        m.num_q = num_q;
-        m.n_in = L.n_in;
-        m.kc_in = L.kc_in;
-        m.fan_in = L.fan_in;
-        m.n_out = L.n_out;
-        m.topk = topk;
-        m.in_key = reinterpret_cast<const uint32_t*>(ws + L.in_key);
-        m.in_pos = reinterpret_cast<const int32_t*>(ws + L.in_pos);
-        m.in_cnt = reinterpret_cast<const int32_t*>(ws + L.in_cnt);
-        const bool last = L.n_out == 1;
-        m.out_key = last ? nullptr : reinterpret_cast<uint32_t*>(ws + L.out_key);
-        m.out_pos = last ? nullptr : reinterpret_cast<int32_t*>(ws + L.out_pos);
-        m.out_cnt = last ? nullptr : reinterpret_cast<int32_t*>(ws + L.out_cnt);
-        m.out_idx = last ? out_idx : nullptr;
-        m.out_score = last ? out_score : nullptr;
-        hipError_t e = sia::launch_topk_merge(m, st);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
 }
 
 int check_workspace(void* ws, size_t have, size_t need) {
@@ -308,22 +242,19 @@ int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k
         if (e != hipSuccess) return hip_fail(e, "indexer stream launch");
         return SIA_OK;
     }
-    sia::SplitArgs s{};
-    s.chunk = p.chunk;
-    s.n_chunks = p.n_chunks;
-    s.topk = topk;
-    s.kc = p.kc;
-    s.out_idx = out_idx;
-    s.out_score = out_score;
-    if (p.n_chunks > 1) {
-        s.cand_key = reinterpret_cast<uint32_t*>(ws + p.lv[0].in_key);
-        s.cand_pos = reinterpret_cast<int32_t*>(ws + p.lv[0].in_pos);
-        s.cand_cnt = reinterpret_cast<int32_t*>(ws + p.lv[0].in_cnt);
-    }
-    e = sia::launch_indexer_split(a, s, mb, index_k->dim, fp8, p.group, false, st);
-    if (e != hipSuccess) return hip_fail(e, "indexer split launch");
-    e = run_merges(p, ws, qs->num_q, topk, out_idx, out_score, st);
-    if (e != hipSuccess) return hip_fail(e, "top-k merge launch");
+    sia::RowsArgs r{};
+    r.part = p.part;
+    r.n_parts = p.n_parts;
+    r.ld = p.ld;
+    r.keys = reinterpret_cast<uint32_t*>(ws + p.keys);
+    r.hist = reinterpret_cast<uint32_t*>(ws + p.hist);
+    r.row_len = reinterpret_cast<int32_t*>(ws + p.rlen);
+    e = sia::launch_indexer_rows(a, r, mb, index_k->dim, fp8, p.group, false, st);
+    if (e != hipSuccess) return hip_fail(e, "indexer score launch");
+    const sia::SelectArgs sel{r.keys, r.ld, r.hist, r.n_parts, r.row_len, qs->max_visible, qs->num_q, topk,
+                              out_idx, out_score};
+    e = sia::launch_topk_rows(sel, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k selection launch");
     return SIA_OK;
 }
 
@@ -341,15 +272,15 @@ int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index
                                         (int64_t)qs->num_q * ld, st);
     if (e != hipSuccess) return hip_fail(e, "scores fill");
     const sia::IdxArgs a = idx_args(pt, index_k, qs, q_idx, w, heads, workspace);
-    sia::SplitArgs s{};
-    s.chunk = 8192;
-    s.n_chunks = (int)std::max<int64_t>(1, ceil_div(std::max(qs->max_visible, 1), s.chunk));
-    s.topk = 1;
-    s.kc = 1;
-    s.scores = scores;
-    s.ld = ld;
-    e = sia::launch_indexer_split(a, s, heads > 32 ? 2 : 1, index_k->dim,
-                                  index_k->dtype == SIA_FP8_E4M3FN, 1, true, st);
+    IndexerPlan p;
+    plan_rows(p, qs->num_q, qs->max_visible, qs->group % 2 == 0 ? 2 : 1);
+    sia::RowsArgs r{};
+    r.part = p.part;
+    r.n_parts = p.n_parts;
+    r.ld = ld;
+    r.scores = scores;
+    e = sia::launch_indexer_rows(a, r, heads > 32 ? 2 : 1, index_k->dim, index_k->dtype == SIA_FP8_E4M3FN,
+                                 p.group, true, st);
     if (e != hipSuccess) return hip_fail(e, "indexer scores launch");
     return SIA_OK;
 }
@@ -357,7 +288,7 @@ int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index
 size_t sia_topk_workspace_size(int32_t num_q, int32_t max_row_len, int32_t topk) {
     if (num_q < 0 || max_row_len < 0 || topk < 1 || topk > 8192) return 0;
     IndexerPlan p;
-    plan_split(p, num_q, max_row_len, topk, 1, 16384);
+    plan_rows(p, num_q, max_row_len, 1);
     return p.total;
 }
 
@@ -369,29 +300,30 @@ int sparse_topk_from_scores(const float* scores, int64_t ld, const int32_t* row_
     if (topk < 1 || topk > 8192) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..8192", topk);
     if (max_row_len < 0 || ld < max_row_len) return fail(SIA_ERR_INVALID_ARG, "need 0 <= max_row_len <= ld");
     IndexerPlan p;
-    plan_split(p, num_q, max_row_len, topk, 1, 16384);
+    plan_rows(p, num_q, max_row_len, 1);
     int rc = check_workspace(workspace, workspace_bytes, p.total);
     if (rc != SIA_OK) return rc;
     if (num_q == 0) return SIA_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    sia::FromScoresArgs f{scores, ld, row_len, num_q, reinterpret_cast<uint32_t*>(ws)};
-    sia::SplitArgs s{};
-    s.chunk = p.chunk;
-    s.n_chunks = p.n_chunks;
-    s.topk = topk;
-    s.kc = p.kc;
-    s.out_idx = out_idx;
-    s.out_score = out_score;
-    if (p.n_chunks > 1) {
-        s.cand_key = reinterpret_cast<uint32_t*>(ws + p.lv[0].in_key);
-        s.cand_pos = reinterpret_cast<int32_t*>(ws + p.lv[0].in_pos);
-        s.cand_cnt = reinterpret_cast<int32_t*>(ws + p.lv[0].in_cnt);
-    }
-    hipError_t e = sia::launch_topk_from_scores(f, s, st);
-    if (e != hipSuccess) return hip_fail(e, "top-k from scores launch");
-    e = run_merges(p, ws, num_q, topk, out_idx, out_score, st);
-    if (e != hipSuccess) return hip_fail(e, "top-k merge launch");
+    sia::KeysFromScoresArgs k{};
+    k.scores = scores;
+    k.ld_in = ld;
+    k.row_len = row_len;
+    k.num_q = num_q;
+    k.max_len = max_row_len;
+    k.part = p.part;
+    k.n_parts = p.n_parts;
+    k.ld = p.ld;
+    k.keys = reinterpret_cast<uint32_t*>(ws + p.keys);
+    k.hist = reinterpret_cast<uint32_t*>(ws + p.hist);
+    k.status = reinterpret_cast<uint32_t*>(ws);
+    hipError_t e = sia::launch_keys_from_scores(k, st);
+    if (e != hipSuccess) return hip_fail(e, "score keys launch");
+    const sia::SelectArgs sel{k.keys, k.ld, k.hist, k.n_parts, row_len, max_row_len, num_q, topk, out_idx,
+                              out_score};
+    e = sia::launch_topk_rows(sel, st);
+    if (e != hipSuccess) return hip_fail(e, "top-k selection launch");
     return SIA_OK;
 }
 

@@ -89,6 +89,39 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt vmcnt(N) that is also a compiler memory barrier: no memory access
+// moves across it. Pairs with dma16, whose copies the compiler does not see.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_mem() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Global -> LDS copy of 16 bytes per active lane: lane i's bytes land at
+// lds + 16 i (lds must be wave-uniform). Written as inline assembly so that the
+// compiler neither counts nor waits for it (its own tracking of such copies
+// falls back to draining every copy in flight before unrelated LDS accesses).
+// The copy completes in order with the wave's other vector-memory loads: a
+// reader of the destination waits with wait_vmcnt_mem<number of loads issued
+// after it>.
+__device__ __forceinline__ void dma16(const void* src, SIA_LDS void* lds) {
+    const uint32_t m = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m) : "memory");
+}
+
+// The same copy addressed as a wave-uniform base (SGPRs) plus a per-lane byte
+// offset, to the LDS byte address `lds` (wave-uniform): no per-copy vector
+// address arithmetic.
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
+// 4 bytes per lane from base + voff to lds + 4 * lane (same conventions).
+__device__ __forceinline__ void dma4_s(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+
 // Workgroup barrier for LDS traffic only: this wave's LDS operations are
 // complete, then all waves meet. Unlike __syncthreads() it does not wait for
 // outstanding global -> LDS copies (whose completion is waited for explicitly

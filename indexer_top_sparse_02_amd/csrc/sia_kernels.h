@@ -23,36 +23,38 @@ struct IdxArgs {
     uint32_t* status;          // device status word
 };
 
-// Split-context pass: a workgroup scores `chunk` positions for `group` queries.
-struct SplitArgs {
-    int32_t chunk, n_chunks, topk, kc;   // kc = candidates kept per chunk
-    int32_t* out_idx;                    // final output when n_chunks == 1
-    float* out_score;
-    uint32_t* cand_key;                  // [num_q, n_chunks, kc]
-    int32_t* cand_pos;
-    int32_t* cand_cnt;                   // [num_q, n_chunks]
-    float* scores;                       // scores hook: [num_q, ld]
-    int64_t ld;
+// Score pass: a workgroup scores one part (`part` consecutive positions, a
+// multiple of the page size) of the rows of one or two queries.
+struct RowsArgs {
+    int32_t part, n_parts;
+    int64_t ld;                // row stride of keys / scores
+    uint32_t* keys;            // [num_q, ld] score keys (0: not a candidate)
+    uint32_t* hist;            // [num_q, n_parts, kCoarseBins] per-part coarse histograms
+    int32_t* row_len;          // [num_q] visible row length (written by part 0)
+    float* scores;             // scores mode: [num_q, ld]
 };
 
-// Selection directly from a score matrix (test hook).
-struct FromScoresArgs {
+// Keys and per-part histograms from a given score matrix (test hook).
+struct KeysFromScoresArgs {
     const float* scores;
-    int64_t ld;
+    int64_t ld_in;
     const int32_t* row_len;
-    int32_t num_q;
+    int32_t num_q, max_len, part, n_parts;
+    int64_t ld;
+    uint32_t* keys;
+    uint32_t* hist;
     uint32_t* status;
 };
 
-struct MergeArgs {
-    int32_t num_q, n_in, kc_in, fan_in, n_out, topk;
-    const uint32_t* in_key;
-    const int32_t* in_pos;
-    const int32_t* in_cnt;
-    uint32_t* out_key;      // intermediate level (capacity topk per set)
-    int32_t* out_pos;
-    int32_t* out_cnt;
-    int32_t* out_idx;       // final level
+// Selection pass: exact Top-K of each key row.
+struct SelectArgs {
+    const uint32_t* keys;
+    int64_t ld;
+    const uint32_t* hist;
+    int32_t n_parts;
+    const int32_t* row_len;    // clamped to [0, max_len]
+    int32_t max_len, num_q, topk;
+    int32_t* out_idx;
     float* out_score;
 };
 
@@ -64,12 +66,10 @@ struct StreamArgs {
 };
 
 // Launchers; return hipSuccess or the launch error. `mb` = ceil(heads / 32).
-hipError_t launch_indexer_split(const IdxArgs& a, const SplitArgs& s, int mb, int dim, bool fp8,
-                                int group, bool scores_mode, hipStream_t st);
-// Largest chunk the split kernel's LDS holds for this instantiation.
-int indexer_split_chunk_cap(int mb, int dim, bool fp8, int group);
-hipError_t launch_topk_from_scores(const FromScoresArgs& f, const SplitArgs& s, hipStream_t st);
-hipError_t launch_topk_merge(const MergeArgs& m, hipStream_t st);
+hipError_t launch_indexer_rows(const IdxArgs& a, const RowsArgs& r, int mb, int dim, bool fp8, int group,
+                               bool scores_mode, hipStream_t st);
+hipError_t launch_keys_from_scores(const KeysFromScoresArgs& k, hipStream_t st);
+hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st);
 hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, bool fp8,
                                  int grid, hipStream_t st);
 int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap, int max_visible);
@@ -78,9 +78,10 @@ constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kCoarseBinsHost = 2048;   // = kCoarseBins of the selection code
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
 
-constexpr int kSplitThreads = 512;   // eight waves: two per SIMD
-constexpr int kMergeThreads = 512;
-constexpr int kMergeCap = 32768;       // keys one merge workgroup holds in LDS (128 KB)
+constexpr int kRowsThreads = 512;      // eight waves: two per SIMD
+constexpr int kMaxPartPages = 1024;    // a score-pass part spans at most 65536 positions
+constexpr int kSelThreads = 1024;
+constexpr int kSelCap = 16384;         // candidates the selection pass holds in LDS
 constexpr int kStreamThreads = 256;    // four waves, one query each
 
 // Attention.

@@ -120,7 +120,7 @@ def test_attention_matches_oracle(case):
 
 # ------------------------------------------------------------------ invariants
 
-def test_split_and_stream_paths_agree():
+def test_row_and_stream_paths_agree():
     s = W.spec("prefill_16k", ctx_lo=1800, ctx_hi=1800, topk=256)
     wl = W.make(s, device="cuda")
     with env(SIA_INDEXER_PATH=1):
@@ -130,21 +130,22 @@ def test_split_and_stream_paths_agree():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("chunk", [0, 256, 1024])
+@pytest.mark.parametrize("parts", [0, 3, 7])
 @pytest.mark.parametrize("fp8", [False, True])
-def test_split_path_causal_rows_exact(chunk, fp8):
-    """Split path on causal rows: with the library's chunk choice (which must
-    respect the LDS bound of the bf16 rows) and with forced chunks that leave
-    late chunks invisible to early queries. The workspace starts as garbage, so
-    a candidate count that is never written would show."""
+def test_row_path_causal_rows_exact(parts, fp8):
+    """Score + selection passes on causal rows: with the library's part choice
+    and with forced part counts that leave late parts invisible to early
+    queries (ragged parts, and parts whose waves have no tiles). The workspace
+    starts as garbage, so a key, histogram or row length that is never written
+    would show."""
     import indexer_top_sparse_02_amd as sia
     s = W.spec("prefill_16k", ctx_lo=1800, ctx_hi=1800, topk=256, idx_fp8=fp8)
     wl = W.make(s, device="cuda")
     sc = gpu_scores(wl)
     rl = row_lengths(wl)
     kw = dict(SIA_INDEXER_PATH=1)
-    if chunk:
-        kw["SIA_SPLIT_CHUNK"] = chunk
+    if parts:
+        kw["SIA_ROWS_PARTS"] = parts
     with env(**kw):
         need = sia.indexer_workspace_size(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq,
                                           wl.q_pos, s.heads_idx, s.topk, group=group_of(wl))
@@ -196,14 +197,27 @@ def test_repeated_runs_are_bit_identical():
         assert torch.equal(i0, i1) and torch.equal(s0, s1) and torch.equal(o0, o1)
 
 
-def test_multi_level_merge_matches_oracle_selection():
+def test_many_parts_match_oracle_selection():
     s = W.spec("decode_b32", batch=2, ctx_lo=40000, ctx_hi=41000, heads_idx=16, topk=2048)
     wl = W.make(s, device="cuda")
-    with env(SIA_SPLIT_CHUNK=2048):      # 20 chunks of candidates -> two merge levels
+    with env(SIA_ROWS_PARTS=20):      # 20 per-part histograms per row
         idx, _ = gpu_topk(wl)
     sc = gpu_scores(wl)
     ref, _ = oracle_topk_of(sc, row_lengths(wl), s.topk)
     assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_selection_beyond_lds_candidates_uses_global_keys():
+    """Every score equal (zero queries): the threshold bin holds the whole row,
+    more candidates than the selection keeps in LDS, so the threshold and the
+    ordered compaction run over the key rows in global memory; ties go to the
+    lowest positions."""
+    s = W.spec("decode_b32", batch=2, ctx_lo=20000, ctx_hi=30000, topk=3000)
+    wl = W.make(s, device="cuda")
+    wl.q_idx.zero_()
+    idx, top = gpu_topk(wl)
+    assert torch.equal(idx, torch.arange(3000, dtype=torch.int32, device="cuda").expand(2, 3000))
+    assert torch.all(top == 0)
 
 
 # ------------------------------------------------------------------ edge cases
