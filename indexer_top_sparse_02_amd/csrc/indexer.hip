@@ -534,9 +534,10 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
                 asm volatile("" ::"v"(sc));
                 if (l < 32 && tok && valid) S.scores[rowbase + (t0 + kk) * 32 + frow] = sc;
             } else {
-                const uint32_t key = tok && valid ? score_key(sc) : 0u;
-                const int64_t o = valid ? rowbase + (t0 + kk) * 32 + frow : (int64_t)j * S.ld + S.ld - 64 + frow;
-                S.keys[o] = key;   // both lane halves hold the same key
+                const uint32_t key = score_key(sc) & (0u - (uint32_t)(tok && valid));
+                // (a scalar select of the row base: no branch in the loop body)
+                const int64_t base = valid ? rowbase + (t0 + kk) * 32 : (int64_t)j * S.ld + S.ld - 64;
+                S.keys[base + frow] = key;   // both lane halves hold the same key
                 // lanes 32..63 add 0 to distinct bins (no conflicts)
                 atomicAdd(&hist[qi * kCoarseBins + (l < 32 ? coarse_bin(key) : (uint32_t)l)],
                           (l < 32 && key != 0u) ? 1u : 0u);
@@ -588,6 +589,243 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
             if (jj >= A.num_q) break;
             uint32_t* dst = S.hist + ((int64_t)jj * S.n_parts + part) * kCoarseBins;
             for (int b = threadIdx.x; b < kCoarseBins; b += kRowsThreads) dst[b] = hist[i * kCoarseBins + b];
+        }
+    }
+}
+
+// ------------------------------------------------------------ score pass, query pairs
+
+// Two queries of one sequence (draft tokens) read the same index-K rows. Here
+// every wave scores both against its run of tiles, so each row is copied from
+// HBM once for the pair. Four waves (one per SIMD) with twice the registers;
+// the ring is deeper (up to eight slots per wave). A wave keeps the matrix and
+// vector pipes busy on its own: the MFMAs of one query are interleaved with
+// the vector epilogue of the other, whose accumulators were issued a full MFMA
+// group earlier, so no epilogue waits for the MFMAs it follows. Keys are staged
+// in LDS and written 8 tiles at a time (1 KB per query, 16 bytes per lane):
+// single-dword stores after every tile hold up the copy stream.
+constexpr int kPairFlush = 8;           // tiles per key flush (= the loop unroll)
+constexpr int kPairPartPages = 512;     // a pair part spans at most 32768 positions
+
+template <int D, bool FP8>
+struct PairGeom {
+    static constexpr int R = D * (FP8 ? 1 : 2);
+    static constexpr int CPR = R / 16;
+    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;
+    static constexpr int NWV = kPairThreads / kWave;
+    static constexpr int TILE = 32 * R;
+    static constexpr int DMA = TILE / 1024;
+    static constexpr int PER_TILE = DMA + (FP8 ? 1 : 0);
+    static constexpr int SLOT = TILE + (FP8 ? 256 : 0);
+    static constexpr int STAGE = 3 * kPairFlush * 32;    // keys staged per wave
+    static constexpr size_t FIXED = kCoarseBins * 4 + kPairPartPages * 4 + (size_t)NWV * STAGE * 4 + 512;
+    static constexpr int NS_FIT = (int)((kMaxLds - FIXED) / ((size_t)NWV * SLOT));
+    static constexpr int NS = NS_FIT >= 8 ? 8 : (NS_FIT >= 4 ? 4 : 2);   // divides the unroll
+    static_assert(NS_FIT >= 4, "the pair ring needs four slots per wave at least");
+};
+
+// Scheduling hint for a step: each of the query's MFMAs followed by the vector
+// instructions that fit in its shadow.
+template <int NMFMA>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+    for (int i = 0; i < NMFMA; i++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // then up to sixteen VALU (its shadow)
+    }
+}
+
+template <int MB, int D, bool FP8, bool SCORES>
+__global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
+    using GM = PairGeom<D, FP8>;
+    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NWV = GM::NWV, U = kPairFlush;
+    constexpr int SLOT = GM::SLOT, NV = KTile<D, FP8>::NV;
+    constexpr int NMFMA = MB * (FP8 ? 2 * (D / 64) : D / 16);   // MFMAs per query and tile
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NWV * SLOT];
+    __shared__ int pages[kPairPartPages];
+    // the part's coarse histograms, query 0 in the low and query 1 in the high
+    // 16 bits of each counter (a part has at most 32768 positions)
+    __shared__ uint32_t hist[SCORES ? 1 : kCoarseBins];
+    // per wave: query 0's keys of two 8-tile blocks, query 1's of one
+    __shared__ __attribute__((aligned(16))) uint32_t stage[SCORES ? 4 : NWV * GM::STAGE];
+
+    const int g = blockIdx.x / S.n_parts;
+    const int part = blockIdx.x % S.n_parts;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int l = lane_id(), half = l >> 5, frow = l & 31;
+    const int pos0 = part * S.part;
+    const int j0 = 2 * g, j1 = 2 * g + 1;
+
+    // both queries must name one sequence; a second query naming another is
+    // dropped (status bit)
+    int b0 = 0, rl0 = 0, rl1 = 0;
+    if (j0 < A.num_q) rl0 = visible_len(A, j0, b0);
+    if (j1 < A.num_q) {
+        int b1;
+        rl1 = visible_len(A, j1, b1);
+        if (b1 != b0) {
+            if (threadIdx.x == 0) atomicOr(A.status, kBadSeq);
+            rl1 = 0;
+        }
+    }
+    if (!SCORES && part == 0 && threadIdx.x == 0) {
+        if (j0 < A.num_q) S.row_len[j0] = rl0;
+        if (j1 < A.num_q) S.row_len[j1] = rl1;
+    }
+    b0 = __builtin_amdgcn_readfirstlane(b0);
+    rl0 = __builtin_amdgcn_readfirstlane(rl0);
+    rl1 = __builtin_amdgcn_readfirstlane(rl1);
+    const int valid0 = max(0, min(S.part, rl0 - pos0));
+    const int valid1 = max(0, min(S.part, rl1 - pos0));
+    const int nvalid = max(valid0, valid1);
+    const int npg = (nvalid + kPage - 1) / kPage;
+    for (int i = threadIdx.x; i < npg; i += kPairThreads) pages[i] = page_of(A, b0, pos0 / kPage + i);
+    if constexpr (!SCORES)
+        for (int i = threadIdx.x; i < kCoarseBins; i += kPairThreads) hist[i] = 0u;
+    __syncthreads();
+
+    // this wave's run of tiles (an even count, so that a run starts on a page)
+    const int ntiles = (nvalid + 31) / 32;
+    const int tpw = ((ntiles + NWV - 1) / NWV + 1) & ~1;
+    const int t0 = w * tpw;
+    const int n = max(0, min(tpw, ntiles - t0));
+
+    if (n > 0) {
+        uint32_t voff[GM::DMA];
+#pragma unroll
+        for (int r = 0; r < GM::DMA; r++) {
+            const int gi = r * kWave + l;
+            const int row = gi / CPR, cc = gi % CPR;
+            voff[r] = row * R + ((cc ^ (row & GM::SWZ)) << 4);
+        }
+        uint32_t roff[NV];
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int cc = KTile<D, FP8>::chunk(i, half);
+            roff[i] = w * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
+        }
+        const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring)) +
+                                  w * SLOT;
+        // copy the wave's k-th tile (clamped to its last) into slot s
+        auto issue = [&](int k, int s) {
+            const int t = t0 + min(k, n - 1);
+            const int page = max(__builtin_amdgcn_readfirstlane(pages[t >> 1]), 0);
+            const int64_t row0 = (int64_t)page * kPage + (t & 1) * 32;
+            const uint8_t* base = A.rows + row0 * R;
+            const uint32_t dst = ring_lds + s * (NWV * SLOT);
+#pragma unroll
+            for (int r = 0; r < GM::DMA; r++) dma16_s(base, voff[r], dst + r * 1024);
+            if constexpr (FP8) {
+                // the 64 scales of the page, 4 bytes per lane (no lane mask)
+                const float* sbase = A.scale + (int64_t)page * kPage;
+                dma4_s(sbase, 4 * l, dst + GM::TILE);
+            }
+        };
+        auto fetch = [&](int k, int s, KTile<D, FP8>& t) {
+            const uint8_t* slot = ring + s * (NWV * SLOT);
+#pragma unroll
+            for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
+            if constexpr (FP8)
+                t.sc = *reinterpret_cast<const float*>(slot + w * SLOT + GM::TILE + 4 * (((t0 + k) & 1) * 32 + frow));
+            else t.sc = 1.f;
+        };
+        // Key of query qq on the wave's kk-th tile: 0 where the position is not
+        // visible or kk is a padding step (outside [0, n)). Branch-free, so that
+        // the MFMAs stay where they are issued.
+        auto key_of = [&](int qq, int kk, const f32x16 (&acc)[MB], float tsc,
+                          const IdxQuery<MB, D, FP8>& q) -> uint32_t {
+            const float sc = tile_epilogue<MB, D, FP8>(q, acc, tsc);
+            const bool tok = kk >= 0 && kk < n && (t0 + kk) * 32 + frow < (qq ? valid1 : valid0);
+            if constexpr (SCORES) {
+                asm volatile("" ::"v"(sc));
+                if (l < 32 && tok) S.scores[(int64_t)(qq ? j1 : j0) * S.ld + pos0 + (t0 + kk) * 32 + frow] = sc;
+                return 0u;
+            } else {
+                return score_key(sc) & (0u - (uint32_t)tok);
+            }
+        };
+        uint32_t* st0 = stage + w * GM::STAGE;   // [2][U][32]: query 0, block parity
+        uint32_t* st1 = st0 + 2 * U * 32;        // [U][32]: query 1
+        // query 0's key of tile k (lanes 0..31) and query 1's of tile k - 1
+        // (lanes 32..63): one LDS atomic and one LDS write for both
+        auto record = [&](int k, uint32_t key0, uint32_t key1) {
+            if constexpr (!SCORES) {
+                const uint32_t key = half ? key1 : key0;
+                atomicAdd(&hist[coarse_bin(key)], key == 0u ? 0u : (half ? 0x10000u : 1u));
+                uint32_t* dst = half ? st1 + ((k - 1) & (U - 1)) * 32 : st0 + (k & (2 * U - 1)) * 32;
+                dst[frow] = key;
+            }
+        };
+        // the wave's tiles [kb, kb + U) of query qq from its staging: 1 KB, 16
+        // bytes per lane; lanes whose tile is outside the run write the row's
+        // spare tail instead
+        auto flush = [&](int qq, int kb, const uint32_t* src) {
+            if constexpr (!SCORES) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * l);
+                const int64_t row = (int64_t)(qq ? j1 : j0) * S.ld;
+                const int tile = kb + (l >> 3);
+                const bool ok = tile >= 0 && tile < n;
+                const int64_t o = ok ? row + pos0 + (t0 + kb) * 32 + 4 * l : row + S.ld - 64 + 4 * (l & 15);
+                *reinterpret_cast<u32x4*>(S.keys + o) = v;
+            }
+        };
+
+        // the first copies go out before the queries are read, so that both
+        // latencies overlap
+#pragma unroll
+        for (int u = 0; u < NS - 1; u++) issue(u, u);
+        IdxQuery<MB, D, FP8> q0, q1;
+        load_query<MB, D>(A, min(j0, A.num_q - 1), q0);
+        load_query<MB, D>(A, min(j1, A.num_q - 1), q1);
+        wait_vmcnt_mem<0>();
+        KTile<D, FP8> t;
+        fetch(0, 0, t);
+        f32x16 a0[MB], a1[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; mb++) a1[mb] = f32x16{};
+        float sc_prev = 0.f;
+        // the run is padded to a multiple of U with repeats of its last tile
+        // (scored, never stored), so the loop body has no branches
+        for (int k0 = 0; k0 < n; k0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int k = k0 + u;
+                // query 0 on tile k, beside query 1's epilogue of tile k - 1
+                tile_mfma<MB, D, FP8>(q0, t, a0);
+                const uint32_t key1 = key_of(1, k - 1, a1, sc_prev, q1);
+                interleave_mfma_valu<NMFMA>();
+                // query 1 on tile k, beside query 0's epilogue of tile k
+                tile_mfma<MB, D, FP8>(q1, t, a1);
+                const uint32_t key0 = key_of(0, k, a0, t.sc, q0);
+                interleave_mfma_valu<NMFMA>();
+                record(k, key0, key1);
+                if (u == 0) {
+                    // the previous block is complete for both queries (at k0 == 0
+                    // these write the spare tail)
+                    flush(0, k0 - U, st0 + (((k0 / U) - 1) & 1) * U * 32);
+                    flush(1, k0 - U, st1);
+                }
+                sc_prev = t.sc;
+                issue(k + NS - 1, (u + NS - 1) % NS);   // refills the slot of tile k - 1
+                wait_vmcnt_mem<(NS - 2) * GM::PER_TILE>();   // tile k + 1 has landed
+                fetch(min(k + 1, n - 1), (u + 1) % NS, t);
+            }
+        }
+        const int np = ((n + U - 1) / U) * U;
+        record(np, 0u, key_of(1, np - 1, a1, sc_prev, q1));
+        flush(0, np - U, st0 + (((np / U) - 1) & 1) * U * 32);
+        flush(1, np - U, st1);
+        wait_vmcnt_mem<0>();
+    }
+    if constexpr (!SCORES) {
+        __syncthreads();
+        for (int i = 0; i < 2; i++) {
+            const int jj = 2 * g + i;
+            if (jj >= A.num_q) break;
+            uint32_t* dst = S.hist + ((int64_t)jj * S.n_parts + part) * kCoarseBins;
+            for (int b = threadIdx.x; b < kCoarseBins; b += kPairThreads)
+                dst[b] = i ? hist[b] >> 16 : hist[b] & 0xffffu;
         }
     }
 }
@@ -910,9 +1148,17 @@ static hipError_t rows_launch(const IdxArgs& a, const RowsArgs& r, hipStream_t s
     return hipGetLastError();
 }
 
+template <int MB, int D, bool FP8, bool SC>
+static hipError_t pair_launch(const IdxArgs& a, const RowsArgs& r, hipStream_t st) {
+    const int pairs = (a.num_q + 1) / 2;
+    hipLaunchKernelGGL((indexer_pair_kernel<MB, D, FP8, SC>), dim3(pairs * r.n_parts), dim3(kPairThreads), 0, st,
+                       a, r);
+    return hipGetLastError();
+}
+
 template <int MB, int D, bool FP8>
 static hipError_t rows_launch3(const IdxArgs& a, const RowsArgs& r, int g, bool sc, hipStream_t st) {
-    if (g == 2) return sc ? rows_launch<MB, D, FP8, 2, true>(a, r, st) : rows_launch<MB, D, FP8, 2, false>(a, r, st);
+    if (g == 2) return sc ? pair_launch<MB, D, FP8, true>(a, r, st) : pair_launch<MB, D, FP8, false>(a, r, st);
     return sc ? rows_launch<MB, D, FP8, 1, true>(a, r, st) : rows_launch<MB, D, FP8, 1, false>(a, r, st);
 }
 

@@ -119,7 +119,9 @@ void plan_rows(IndexerPlan& p, int64_t num_q, int max_visible, int group) {
     const int forced = env_int("SIA_ROWS_PARTS", 0);
     int64_t np = forced > 0 ? forced : std::max<int64_t>(1, ceil_div(device_cus(), n_groups));
     if (forced <= 0) np = std::min<int64_t>(np, std::max<int64_t>(1, ceil_div(mv, 2048)));
-    np = std::max<int64_t>(np, ceil_div(mv, 64 * (int64_t)sia::kMaxPartPages));
+    // (a pair part keeps 16-bit histogram counters: at most 32768 positions)
+    const int64_t max_part = group == 2 ? 32768 : 64 * (int64_t)sia::kMaxPartPages;
+    np = std::max<int64_t>(np, ceil_div(mv, max_part));
     p.part = (int)(ceil_div(ceil_div(mv, np), 64) * 64);
     p.n_parts = (int)ceil_div(mv, p.part);
     p.ld = ceil_div(mv, 64) * 64 + 64;   // (+ a spare tail that padding steps write)

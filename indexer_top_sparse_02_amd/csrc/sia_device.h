@@ -65,10 +65,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // Order-preserving key of a score: larger score <=> larger key. -0 and +0 map
 // to one key; NaN maps to 1, below every number; 0 marks "no candidate".
 __device__ __forceinline__ uint32_t score_key(float f) {
+    // (selects only: callers inside software-pipelined loops need it branch-free)
     uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return 1u;
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    u = u == 0x80000000u ? 0u : u;
+    const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (u & 0x7fffffffu) > 0x7f800000u ? 1u : k;
 }
 
 __device__ __forceinline__ float key_score(uint32_t k) {
