@@ -1,26 +1,25 @@
-// Fused lightweight indexer + exact Top-K for gfx950.
+// Lightweight indexer + exact Top-K for gfx950.
 //
 // score[j,s] = sigma_s * sum_h w[j,h] * max(0, q[j,h,:] . k_s)
 //
 // The q . k products of one query against 32 positions are one MFMA tile:
 // heads are the M dimension (32 per block), positions the N dimension, the
 // index dim the K dimension. Queries sit in registers for the whole pass; a
-// lane supplies its position's half-row of index-K (fp8 rows are widened to bf16
-// exactly in registers), staged through LDS by the split kernel and loaded
-// straight from the paged pool by the stream kernel. The accumulator puts 16
-// heads of one position in each lane, so the ReLU, the head weights and the head
-// sum stay in registers with a single cross-lane add, and sigma_s multiplies the
-// sum. Only the selected positions ever reach memory ("Rapid Adaptation and
-// Inference Optimization", section 4.1 "Indexer Fusion").
+// lane supplies its position's half-row of index-K, staged through LDS by the
+// decode score passes and loaded straight from the paged pool by the stream
+// kernel. The accumulator puts 16 heads of one position in each lane, so the
+// ReLU, the head weights and the head sum stay in registers with a single
+// cross-lane add, and sigma_s multiplies the sum ("Rapid Adaptation and
+// Inference Optimization", section 4.1 "Indexer Fusion": the indexer reads the
+// paged K cache directly and hands on only the selection).
 //
-// Two launch shapes share that score code and the exact selection of
-// sia_select.h, so they return identical indices:
-//  * split: a workgroup scores a chunk of one sequence's positions for one or two
-//    queries (decode, draft tokens), keeps the chunk's scores in LDS, selects the
-//    chunk's Top-K and writes those candidates; a merge pass selects the final
-//    Top-K from the candidates of all chunks. The global Top-K is a subset of the
-//    union of per-chunk Top-Ks under the same total order, so this is exact.
-//  * stream: one wave walks one query's whole causal row (prefill), appending
+// Launch shapes (all score through tile_mfma + tile_epilogue, so a query and a
+// position give the same bits everywhere, and all select with sia_select.h):
+//  * decode, score pass + selection pass: the score pass streams parts of the
+//    rows (two draft tokens of a sequence share every copy) and writes one
+//    4-byte order-preserving key per visible position plus a coarse histogram
+//    per part; the selection pass takes each row's exact Top-K from its keys.
+//  * prefill, stream: one wave walks one query's whole causal row, appending
 //    positions that beat the current threshold to an LDS buffer kept in position
 //    order, and re-selecting the Top-K when the buffer fills. A position that
 //    ties the threshold arrives after every kept one, so it can be dropped.
