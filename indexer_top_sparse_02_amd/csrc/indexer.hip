@@ -60,24 +60,25 @@ struct IdxQuery<MB, D, true> {
     float w[MB][16];
 };
 
+// hb0: first head block (of 32 heads) held, for waves that split a query's heads.
 template <int MB, int D>
-__device__ __forceinline__ void load_weights(const IdxArgs& A, int j, float (&w)[MB][16]) {
+__device__ __forceinline__ void load_weights(const IdxArgs& A, int j, float (&w)[MB][16], int hb0 = 0) {
     const int half = lane_id() >> 5;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-            const int h = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const int h = (hb0 + mb) * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
             w[mb][r] = h < A.heads ? A.w[(int64_t)j * A.heads + h] : 0.f;
         }
 }
 
 template <int MB, int D>
-__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, false>& q) {
+__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, false>& q, int hb0 = 0) {
     const int l = lane_id(), m = l & 31, half = l >> 5;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
-        const int head = mb * 32 + m;
+        const int head = (hb0 + mb) * 32 + m;
 #pragma unroll
         for (int ks = 0; ks < IdxQuery<MB, D, false>::KS; ks++) {
             u32x4 v = {0u, 0u, 0u, 0u};
@@ -87,18 +88,19 @@ __device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB,
             q.a[mb][ks] = as_bf16x8(v);
         }
     }
-    load_weights<MB, D>(A, j, q.w);
+    load_weights<MB, D>(A, j, q.w, hb0);
 }
 
 template <int MB, int D>
-__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, true>& q) {
+__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, true>& q, int hb0 = 0) {
     constexpr int KS = IdxQuery<MB, D, true>::KS;
     const int l = lane_id(), m = l & 31, half = l >> 5;
-    // lane l holds head mb*32 + l%32 and dims 64 ks + 32 (l/32) .. +31 of each step;
-    // the query is read twice (the second time from cache): once for its largest
-    // magnitude, once to split it
-    auto ld = [&](int mb, int ks, int c) -> u32x4 {
-        const int head = mb * 32 + m;
+    // lane l holds head (hb0 + mb)*32 + l%32 and dims 64 ks + 32 (l/32) .. +31 of
+    // each step; the query is read twice (the second time from cache): once for
+    // the largest magnitude over all its heads (one exponent per query, whatever
+    // share of the heads a wave holds), once to split it
+    auto ld = [&](int blk, int ks, int c) -> u32x4 {
+        const int head = blk * 32 + m;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (head < A.heads)
             v = *reinterpret_cast<const u32x4*>(
@@ -107,12 +109,12 @@ __device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB,
     };
     float amax = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < MB; mb++)
+    for (int blk = 0; blk < 2; blk++)   // every head block (64 heads at most)
 #pragma unroll
         for (int ks = 0; ks < KS; ks++)
 #pragma unroll
             for (int c = 0; c < 4; c++) {
-                const u32x4 v = ld(mb, ks, c);
+                const u32x4 v = ld(blk, ks, c);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     amax = fmaxf(amax, fabsf(__uint_as_float(v[e] << 16)));
@@ -136,7 +138,7 @@ __device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB,
         for (int ks = 0; ks < KS; ks++) {
 #pragma unroll
             for (int c = 0; c < 4; c++) {
-                const u32x4 v = ld(mb, ks, c);
+                const u32x4 v = ld(hb0 + mb, ks, c);
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
                     // four bf16 -> one dword of e4m3 (high part) and one of e4m3 (residual)
@@ -159,7 +161,7 @@ __device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB,
                 }
             }
         }
-    load_weights<MB, D>(A, j, q.w);
+    load_weights<MB, D>(A, j, q.w, hb0);
 }
 
 // One lane's share of a 32-position tile: half a row of index-K (+ its scale).
@@ -279,13 +281,16 @@ __device__ __forceinline__ void tile_mfma(const IdxQuery<MB, D, FP8>& q, const K
     }
 }
 
-// Vector half: ReLU, head weights, head sum, token scale.
+// Vector half: ReLU, head weights and head sum, block by block: each block of 32
+// heads is summed on its own and the block sums are added in block order, so a
+// wave holding one block of a query gives the same bits once its partner's block
+// sum is added.
 template <int MB, int D, bool FP8>
-__device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D, FP8>& q, const f32x16 (&acc)[MB],
-                                               float tsc) {
-    float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
+__device__ __forceinline__ float tile_head_sum(const IdxQuery<MB, D, FP8>& q, const f32x16 (&acc)[MB]) {
+    float v = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
+        float p0 = 0.f, p1 = 0.f, p2 = 0.f, p3 = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 4) {
             p0 = fmaf(q.w[mb][r + 0], relu(acc[mb][r + 0]), p0);
@@ -293,10 +298,18 @@ __device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D, FP8>& q, co
             p2 = fmaf(q.w[mb][r + 2], relu(acc[mb][r + 2]), p2);
             p3 = fmaf(q.w[mb][r + 3], relu(acc[mb][r + 3]), p3);
         }
+        const float b = add_halves((p0 + p1) + (p2 + p3));
+        v = mb == 0 ? b : v + b;
     }
-    float v = add_halves((p0 + p1) + (p2 + p3));
-    if constexpr (FP8) v = v * tsc;
     return v;
+}
+
+// ... times the token scale.
+template <int MB, int D, bool FP8>
+__device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D, FP8>& q, const f32x16 (&acc)[MB],
+                                               float tsc) {
+    const float v = tile_head_sum<MB, D, FP8>(q, acc);
+    return FP8 ? v * tsc : v;
 }
 
 // Scores of the tile's 32 positions for one query; lanes l and l+32 both get
@@ -594,16 +607,21 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
 
 // ------------------------------------------------------------ score pass, query pairs
 
-// Two queries of one sequence (draft tokens) read the same index-K rows. Here
-// every wave scores both against its run of tiles, so each row is copied from
-// HBM once for the pair. Four waves (one per SIMD) with twice the registers;
-// the ring is deeper (up to eight slots per wave). A wave keeps the matrix and
-// vector pipes busy on its own: the MFMAs of one query are interleaved with
-// the vector epilogue of the other, whose accumulators were issued a full MFMA
-// group earlier, so no epilogue waits for the MFMAs it follows. Keys are staged
-// in LDS and written 8 tiles at a time (1 KB per query, 16 bytes per lane):
-// single-dword stores after every tile hold up the copy stream.
-constexpr int kPairFlush = 8;           // tiles per key flush (= the loop unroll)
+// Two queries of one sequence (draft tokens) read the same index-K rows, so a
+// workgroup scores a part of both rows and copies every row once for the pair.
+// Eight waves form four teams; a team is the two waves of one SIMD (w and w + 4)
+// with one ring of LDS slots and one contiguous run of tiles:
+//   copier (w < 4):    copies the team's tiles, scores heads 0..31 of both
+//                      queries and hands its block sums over through LDS;
+//   finisher (w >= 4): scores heads 32..63 of both queries, adds the copier's
+//                      block sums (block order kept), applies the token scale,
+//                      writes keys and histogram counts.
+// Each wave holds one head block of both queries (about 200 registers), so two
+// waves share a SIMD and each hides the other's vector work behind its MFMAs.
+// One workgroup barrier per tile orders the copies, the hand-over and the reuse
+// of ring slots. Within a wave the MFMAs of one query are interleaved with the
+// vector epilogue of the other, whose accumulators were issued a group earlier.
+constexpr int kPairUnroll = 8;          // loop unroll (ring slots are static per step)
 constexpr int kPairPartPages = 512;     // a pair part spans at most 32768 positions
 
 template <int D, bool FP8>
@@ -611,16 +629,15 @@ struct PairGeom {
     static constexpr int R = D * (FP8 ? 1 : 2);
     static constexpr int CPR = R / 16;
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;
-    static constexpr int NWV = kPairThreads / kWave;
+    static constexpr int NTEAM = kPairThreads / kWave / 2;
     static constexpr int TILE = 32 * R;
     static constexpr int DMA = TILE / 1024;
     static constexpr int PER_TILE = DMA + (FP8 ? 1 : 0);
     static constexpr int SLOT = TILE + (FP8 ? 256 : 0);
-    static constexpr int STAGE = 3 * kPairFlush * 32;    // keys staged per wave
-    static constexpr size_t FIXED = kCoarseBins * 4 + kPairPartPages * 4 + (size_t)NWV * STAGE * 4 + 512;
-    static constexpr int NS_FIT = (int)((kMaxLds - FIXED) / ((size_t)NWV * SLOT));
+    static constexpr size_t FIXED = kCoarseBins * 4 + kPairPartPages * 4 + 2 * NTEAM * kWave * 4 + 512;
+    static constexpr int NS_FIT = (int)((kMaxLds - FIXED) / ((size_t)NTEAM * SLOT));
     static constexpr int NS = NS_FIT >= 8 ? 8 : (NS_FIT >= 4 ? 4 : 2);   // divides the unroll
-    static_assert(NS_FIT >= 4, "the pair ring needs four slots per wave at least");
+    static_assert(NS_FIT >= 4, "the pair ring needs four slots per team at least");
 };
 
 // Scheduling hint for a step: each of the query's MFMAs followed by the vector
@@ -634,24 +651,23 @@ __device__ __forceinline__ void interleave_mfma_valu() {
     }
 }
 
-template <int MB, int D, bool FP8, bool SCORES>
-__global__ __launch_bounds__(kPairThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
+template <int D, bool FP8, bool SCORES>
+__global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
     using GM = PairGeom<D, FP8>;
-    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NWV = GM::NWV, U = kPairFlush;
+    constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NTEAM = GM::NTEAM, U = kPairUnroll;
     constexpr int SLOT = GM::SLOT, NV = KTile<D, FP8>::NV;
-    constexpr int NMFMA = MB * (FP8 ? 2 * (D / 64) : D / 16);   // MFMAs per query and tile
-    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NWV * SLOT];
+    constexpr int NMFMA = FP8 ? 2 * (D / 64) : D / 16;   // MFMAs per query, tile and head block
+    __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NTEAM * SLOT];
     __shared__ int pages[kPairPartPages];
     // the part's coarse histograms, query 0 in the low and query 1 in the high
     // 16 bits of each counter (a part has at most 32768 positions)
     __shared__ uint32_t hist[SCORES ? 1 : kCoarseBins];
-    // per wave: query 0's keys of two 8-tile blocks, query 1's of one
-    __shared__ __attribute__((aligned(16))) uint32_t stage[SCORES ? 4 : NWV * GM::STAGE];
+    __shared__ float xch[2][NTEAM][kWave];   // copier block sums, by step parity
 
     const int g = blockIdx.x / S.n_parts;
     const int part = blockIdx.x % S.n_parts;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int team = w % NTEAM, hb = w / NTEAM;   // hb = 0: copier, 1: finisher
     const int l = lane_id(), half = l >> 5, frow = l & 31;
     const int pos0 = part * S.part;
     const int j0 = 2 * g, j1 = 2 * g + 1;
@@ -684,13 +700,16 @@ void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
         for (int i = threadIdx.x; i < kCoarseBins; i += kPairThreads) hist[i] = 0u;
     __syncthreads();
 
-    // this wave's run of tiles (an even count, so that a run starts on a page)
+    // the team's run of tiles (an even count, so that a run starts on a page);
+    // every wave takes the same number of steps (the longest run, padded to the
+    // unroll), so that the barriers match
     const int ntiles = (nvalid + 31) / 32;
-    const int tpw = ((ntiles + NWV - 1) / NWV + 1) & ~1;
-    const int t0 = w * tpw;
+    const int tpw = ((ntiles + NTEAM - 1) / NTEAM + 1) & ~1;
+    const int t0 = team * tpw;
     const int n = max(0, min(tpw, ntiles - t0));
+    const int nloop = (min(tpw, ntiles) + U - 1) / U * U;
 
-    if (n > 0) {
+    if (nloop > 0) {
         uint32_t voff[GM::DMA];
 #pragma unroll
         for (int r = 0; r < GM::DMA; r++) {
@@ -702,17 +721,19 @@ void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int cc = KTile<D, FP8>::chunk(i, half);
-            roff[i] = w * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
+            roff[i] = team * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring)) +
-                                  w * SLOT;
-        // copy the wave's k-th tile (clamped to its last) into slot s
-        auto issue = [&](int k, int s) {
-            const int t = t0 + min(k, n - 1);
+                                  team * SLOT;
+        // tile of the team's k-th step: clamped into the run (a padding step
+        // repeats the last tile; a team without tiles reads the part's last one)
+        auto tile_of = [&](int k) { return min(t0 + max(min(k, n - 1), 0), ntiles - 1); };
+        auto issue = [&](int k, int s) {   // copier only
+            const int t = tile_of(k);
             const int page = max(__builtin_amdgcn_readfirstlane(pages[t >> 1]), 0);
             const int64_t row0 = (int64_t)page * kPage + (t & 1) * 32;
             const uint8_t* base = A.rows + row0 * R;
-            const uint32_t dst = ring_lds + s * (NWV * SLOT);
+            const uint32_t dst = ring_lds + s * (NTEAM * SLOT);
 #pragma unroll
             for (int r = 0; r < GM::DMA; r++) dma16_s(base, voff[r], dst + r * 1024);
             if constexpr (FP8) {
@@ -722,99 +743,78 @@ void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
             }
         };
         auto fetch = [&](int k, int s, KTile<D, FP8>& t) {
-            const uint8_t* slot = ring + s * (NWV * SLOT);
+            const uint8_t* slot = ring + s * (NTEAM * SLOT);
 #pragma unroll
             for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
             if constexpr (FP8)
-                t.sc = *reinterpret_cast<const float*>(slot + w * SLOT + GM::TILE + 4 * (((t0 + k) & 1) * 32 + frow));
+                t.sc = *reinterpret_cast<const float*>(slot + team * SLOT + GM::TILE +
+                                                       4 * ((tile_of(k) & 1) * 32 + frow));
             else t.sc = 1.f;
         };
-        // Key of query qq on the wave's kk-th tile: 0 where the position is not
-        // visible or kk is a padding step (outside [0, n)). Branch-free, so that
-        // the MFMAs stay where they are issued.
-        auto key_of = [&](int qq, int kk, const f32x16 (&acc)[MB], float tsc,
-                          const IdxQuery<MB, D, FP8>& q) -> uint32_t {
-            const float sc = tile_epilogue<MB, D, FP8>(q, acc, tsc);
-            const bool tok = kk >= 0 && kk < n && (t0 + kk) * 32 + frow < (qq ? valid1 : valid0);
+        // finisher: lanes 0..31 hold query 0 of step kq, lanes 32..63 query 1 of
+        // step kq - 1; padding steps go to the key row's spare tail
+        auto finish = [&](int kq, float v, float tsc) {
+            const float sc = FP8 ? v * tsc : v;
+            const int kk = half ? kq - 1 : kq;
+            const bool in_run = kk >= 0 && kk < n;
+            const bool tok = in_run && (t0 + kk) * 32 + frow < (half ? valid1 : valid0);
+            const int64_t row = (int64_t)(half ? j1 : j0) * S.ld;
             if constexpr (SCORES) {
-                asm volatile("" ::"v"(sc));
-                if (l < 32 && tok) S.scores[(int64_t)(qq ? j1 : j0) * S.ld + pos0 + (t0 + kk) * 32 + frow] = sc;
-                return 0u;
+                if (tok) S.scores[row + pos0 + (t0 + kk) * 32 + frow] = sc;
             } else {
-                return score_key(sc) & (0u - (uint32_t)tok);
-            }
-        };
-        uint32_t* st0 = stage + w * GM::STAGE;   // [2][U][32]: query 0, block parity
-        uint32_t* st1 = st0 + 2 * U * 32;        // [U][32]: query 1
-        // query 0's key of tile k (lanes 0..31) and query 1's of tile k - 1
-        // (lanes 32..63): one LDS atomic and one LDS write for both
-        auto record = [&](int k, uint32_t key0, uint32_t key1) {
-            if constexpr (!SCORES) {
-                const uint32_t key = half ? key1 : key0;
+                const uint32_t key = score_key(sc) & (0u - (uint32_t)tok);
+                const int64_t o = in_run ? row + pos0 + (t0 + kk) * 32 + frow : row + S.ld - 64 + frow;
+                S.keys[o] = key;
                 atomicAdd(&hist[coarse_bin(key)], key == 0u ? 0u : (half ? 0x10000u : 1u));
-                uint32_t* dst = half ? st1 + ((k - 1) & (U - 1)) * 32 : st0 + (k & (2 * U - 1)) * 32;
-                dst[frow] = key;
-            }
-        };
-        // the wave's tiles [kb, kb + U) of query qq from its staging: 1 KB, 16
-        // bytes per lane; lanes whose tile is outside the run write the row's
-        // spare tail instead
-        auto flush = [&](int qq, int kb, const uint32_t* src) {
-            if constexpr (!SCORES) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * l);
-                const int64_t row = (int64_t)(qq ? j1 : j0) * S.ld;
-                const int tile = kb + (l >> 3);
-                const bool ok = tile >= 0 && tile < n;
-                const int64_t o = ok ? row + pos0 + (t0 + kb) * 32 + 4 * l : row + S.ld - 64 + 4 * (l & 15);
-                *reinterpret_cast<u32x4*>(S.keys + o) = v;
             }
         };
 
-        // the first copies go out before the queries are read, so that both
-        // latencies overlap
+        if (hb == 0) {
 #pragma unroll
-        for (int u = 0; u < NS - 1; u++) issue(u, u);
-        IdxQuery<MB, D, FP8> q0, q1;
-        load_query<MB, D>(A, min(j0, A.num_q - 1), q0);
-        load_query<MB, D>(A, min(j1, A.num_q - 1), q1);
+            for (int u = 0; u < NS - 1; u++) issue(u, u);
+        }
+        IdxQuery<1, D, FP8> q0, q1;
+        load_query<1, D>(A, min(j0, A.num_q - 1), q0, hb);
+        load_query<1, D>(A, min(j1, A.num_q - 1), q1, hb);
         wait_vmcnt_mem<0>();
+        __syncthreads();   // the first copies have landed
         KTile<D, FP8> t;
         fetch(0, 0, t);
-        f32x16 a0[MB], a1[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; mb++) a1[mb] = f32x16{};
+        f32x16 a0[1], a1[1];
+        a1[0] = f32x16{};
         float sc_prev = 0.f;
-        // the run is padded to a multiple of U with repeats of its last tile
-        // (scored, never stored), so the loop body has no branches
-        for (int k0 = 0; k0 < n; k0 += U) {
+        for (int k0 = 0; k0 < nloop; k0 += U) {
 #pragma unroll
             for (int u = 0; u < U; u++) {
                 const int k = k0 + u;
-                // query 0 on tile k, beside query 1's epilogue of tile k - 1
-                tile_mfma<MB, D, FP8>(q0, t, a0);
-                const uint32_t key1 = key_of(1, k - 1, a1, sc_prev, q1);
+                // query 0 on tile k, beside query 1's block sum of tile k - 1
+                tile_mfma<1, D, FP8>(q0, t, a0);
+                const float h1 = tile_head_sum<1, D, FP8>(q1, a1);
                 interleave_mfma_valu<NMFMA>();
-                // query 1 on tile k, beside query 0's epilogue of tile k
-                tile_mfma<MB, D, FP8>(q1, t, a1);
-                const uint32_t key0 = key_of(0, k, a0, t.sc, q0);
+                // query 1 on tile k, beside query 0's block sum of tile k
+                tile_mfma<1, D, FP8>(q1, t, a1);
+                const float h0 = tile_head_sum<1, D, FP8>(q0, a0);
                 interleave_mfma_valu<NMFMA>();
-                record(k, key0, key1);
-                if (u == 0) {
-                    // the previous block is complete for both queries (at k0 == 0
-                    // these write the spare tail)
-                    flush(0, k0 - U, st0 + (((k0 / U) - 1) & 1) * U * 32);
-                    flush(1, k0 - U, st1);
-                }
+                const float mine = half ? h1 : h0;
+                const float tsc = half ? sc_prev : t.sc;
                 sc_prev = t.sc;
-                issue(k + NS - 1, (u + NS - 1) % NS);   // refills the slot of tile k - 1
-                wait_vmcnt_mem<(NS - 2) * GM::PER_TILE>();   // tile k + 1 has landed
-                fetch(min(k + 1, n - 1), (u + 1) % NS, t);
+                if (hb == 0) {
+                    xch[k & 1][team][l] = mine;
+                    issue(k + NS - 1, (u + NS - 1) % NS);   // refills the slot of tile k - 1
+                    wait_vmcnt_mem<(NS - 2) * GM::PER_TILE>();   // tile k + 1 has landed
+                }
+                lds_barrier();
+                if (hb == 1) finish(k, xch[k & 1][team][l] + mine, tsc);
+                fetch(k + 1, (u + 1) % NS, t);
             }
         }
-        const int np = ((n + U - 1) / U) * U;
-        record(np, 0u, key_of(1, np - 1, a1, sc_prev, q1));
-        flush(0, np - U, st0 + (((np / U) - 1) & 1) * U * 32);
-        flush(1, np - U, st1);
+        // query 1 of the last step
+        {
+            const float h1 = tile_head_sum<1, D, FP8>(q1, a1);
+            if (hb == 0) xch[nloop & 1][team][l] = h1;
+            lds_barrier();
+            if (hb == 1) finish(nloop, xch[nloop & 1][team][l] + h1, sc_prev);
+        }
         wait_vmcnt_mem<0>();
     }
     if constexpr (!SCORES) {
@@ -1147,17 +1147,17 @@ static hipError_t rows_launch(const IdxArgs& a, const RowsArgs& r, hipStream_t s
     return hipGetLastError();
 }
 
-template <int MB, int D, bool FP8, bool SC>
+template <int D, bool FP8, bool SC>
 static hipError_t pair_launch(const IdxArgs& a, const RowsArgs& r, hipStream_t st) {
     const int pairs = (a.num_q + 1) / 2;
-    hipLaunchKernelGGL((indexer_pair_kernel<MB, D, FP8, SC>), dim3(pairs * r.n_parts), dim3(kPairThreads), 0, st,
-                       a, r);
+    hipLaunchKernelGGL((indexer_pair_kernel<D, FP8, SC>), dim3(pairs * r.n_parts), dim3(kPairThreads), 0, st, a,
+                       r);
     return hipGetLastError();
 }
 
 template <int MB, int D, bool FP8>
 static hipError_t rows_launch3(const IdxArgs& a, const RowsArgs& r, int g, bool sc, hipStream_t st) {
-    if (g == 2) return sc ? pair_launch<MB, D, FP8, true>(a, r, st) : pair_launch<MB, D, FP8, false>(a, r, st);
+    if (g == 2) return sc ? pair_launch<D, FP8, true>(a, r, st) : pair_launch<D, FP8, false>(a, r, st);
     return sc ? rows_launch<MB, D, FP8, 1, true>(a, r, st) : rows_launch<MB, D, FP8, 1, false>(a, r, st);
 }
 

@@ -79,7 +79,7 @@ constexpr int kCoarseBinsHost = 2048;   // = kCoarseBins of the selection code
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
 
 constexpr int kRowsThreads = 512;      // eight waves: two per SIMD
-constexpr int kPairThreads = 256;      // four waves (one per SIMD), each scoring a query pair
+constexpr int kPairThreads = 512;      // four teams of two waves (one team per SIMD) per query pair
 constexpr int kMaxPartPages = 1024;    // a score-pass part spans at most 65536 positions
 constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 16384;         // candidates the selection pass holds in LDS
