@@ -20,6 +20,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 
 
 def _args():
@@ -29,6 +30,8 @@ def _args():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", default="spec_decode_128k")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="leave out the 16K causal prefill figures")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead of the path, run a plain device copy of this many bytes "
                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -137,27 +140,15 @@ def cpu_baseline(wl_gpu, s, budget_s: float = 12.0):
                       f"{s.name}: indexer, Top-K and attention, {dt:.1f} s"}
 
 
-def main():
-    a = _args()
-    if a.copy_bytes:
-        copy_calibration(a.copy_bytes)
-        return
-    if a.gpus != 1:
-        print(json.dumps({"error": "this implementation runs on one GPU (no sharding or "
-                                   "collectives); --gpus must be 1", "n_gpus": a.gpus}))
-        sys.exit(2)
+METRIC = "decode queries/s and HBM GB/s at 128K ctx; prefill tokens/s (indexer+TopK+sparse attn)"
+
+
+def time_path(sia, wl, s, group, steps, warmup):
+    """Times `steps` passes of the whole path (indexer + Top-K, then sparse
+    attention) with HIP events on the stream the library runs on. Returns the
+    indices of the last pass, ms per step and ms per phase."""
     import torch
-
-    import indexer_top_sparse_02_amd as sia
-    import workloads as W
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    s = W.spec(a.config)
-    if s.prefill:
-        raise SystemExit("bench times the decode workloads; prefill is timed by tests")
-    wl = W.make(s, device=dev)
-    group = s.q_per_seq
+    dev = wl.q_idx.device
     maxv = int(torch.minimum(wl.q_pos.long() + 1, wl.seq_lens.long()[wl.q_seq.long()]).max())
     ws_i = sia.new_workspace(sia.indexer_workspace_size(wl.page_table, wl.seq_lens, wl.idx_k,
                                                         wl.idx_scale, wl.q_seq, wl.q_pos,
@@ -177,12 +168,12 @@ def main():
         sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx,
                                  s.sm_scale, out=out, lse=lse, workspace=ws_a)
 
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         indexer()
         attention()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -195,15 +186,84 @@ def main():
         e2.record()
     t_end.record()
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / a.steps
-    idx_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / a.steps
-    att_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / a.steps
+    ms = t_start.elapsed_time(t_end) / steps
+    idx_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / steps
+    att_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / steps
+    return idx, ms, idx_ms, att_ms
+
+
+def prefill_flops(s, wl):
+    """Algorithmic flops of one causal prefill pass: 2*H_I*d_I per visible
+    (query, position) for the indexer, 2*H_A*(576 + 512) per selected
+    (query, row) for attention."""
+    t = wl.q_pos.long().cpu() + 1
+    vis = float(t.sum())
+    sel = float(torch_min(t, s.topk).sum())
+    return 2.0 * s.heads_idx * s.dim_idx * vis, 2.0 * s.heads_attn * (576 + 512) * sel
+
+
+def torch_min(t, k):
+    import torch
+    return torch.clamp(t, max=k)
+
+
+def prefill_line(wl, s, steps, warmup):
+    """Causal prefill: every position of the sequence is a query that sees
+    positions 0..t. Reports tokens/s and MFMA throughput of each phase."""
+    import indexer_top_sparse_02_amd as sia
+    idx, ms, idx_ms, att_ms = time_path(sia, wl, s, wl.num_q, steps, warmup)
+    f_idx, f_att = prefill_flops(s, wl)
+    ti, ta = f_idx / (idx_ms * 1e-3) / 1e12, f_att / (att_ms * 1e-3) / 1e12
+    dominant = ("sparse_mla_attention call (sparse_mla_kernel)", ta, f_att, att_ms) \
+        if att_ms >= idx_ms else ("sparse_indexer_topk call (indexer_stream_kernel)", ti, f_idx, idx_ms)
+    return {
+        "metric": METRIC, "value": wl.num_q / (ms * 1e-3), "unit": "prefill tokens/s",
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) caches and queries, shuffled page table)",
+        "config": {"workload": s.name, "tokens": wl.num_q, "indexer_heads": s.heads_idx,
+                   "index_dim": s.dim_idx, "topk": s.topk, "attention_heads": s.heads_attn,
+                   "page_size": 64},
+        "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
+        "algorithmic_tflop": {"indexer": f_idx / 1e12, "attention": f_att / 1e12},
+        "phase_tflops": {"indexer": ti, "attention": ta},
+        "mfma_frac_step": (f_idx + f_att) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": dominant[0], "achieved": dominant[1],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dominant[1] / PEAK_BF16_TFLOPS,
+                     "traffic": None, "algorithmic_tflop_per_call": dominant[2] / 1e12,
+                     "call_ms": dominant[3]},
+    }
+
+
+def main():
+    a = _args()
+    if a.copy_bytes:
+        copy_calibration(a.copy_bytes)
+        return
+    if a.gpus != 1:
+        print(json.dumps({"error": "this implementation runs on one GPU (no sharding or "
+                                   "collectives); --gpus must be 1", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+
+    import indexer_top_sparse_02_amd as sia
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = W.spec(a.config)
+    if s.prefill:
+        line = prefill_line(W.make(s, device=dev), s, a.steps, a.warmup)
+        line.update({"n_gpus": 1, "steps": a.steps, "warmup": a.warmup})
+        print(json.dumps(line))
+        return
+    wl = W.make(s, device=dev)
+    group = s.q_per_seq
+    idx, ms, idx_ms, att_ms = time_path(sia, wl, s, group, a.steps, a.warmup)
     by = algorithmic_bytes(wl, idx)
     step_gbs = by["total"] / (ms * 1e-3) / 1e9
     idx_gbs = by["indexer"] / (idx_ms * 1e-3) / 1e9
     line = {
-        "metric": "decode queries/s and HBM GB/s at 128K ctx; prefill tokens/s (indexer+TopK+sparse attn)",
+        "metric": METRIC,
         "value": wl.num_q / (ms * 1e-3),
         "unit": "query tokens/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
@@ -220,14 +280,22 @@ def main():
         "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
         "algorithmic_bytes": by,
         "roofline": {"bound": "hbm",
-                     "kernel": "sparse_indexer_topk call (indexer_rows_kernel + topk_rows_kernel)",
+                     "kernel": "sparse_indexer_topk call (indexer_pair_kernel score pass + "
+                               "topk_rows_kernel selection pass)",
                      "achieved": idx_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": idx_gbs / PEAK_HBM_GBS, "traffic": measured_traffic(s.name),
                      "algorithmic_bytes_per_call": by["indexer"],
                      "call_ms": idx_ms},
     }
+    del wl, idx
+    torch.cuda.empty_cache()
+    if not a.no_prefill:
+        ps = W.spec("prefill_16k")
+        line["prefill"] = prefill_line(W.make(ps, device=dev), ps, max(2, a.steps // 4),
+                                       max(1, a.warmup))
+        torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, s)
+        line["cpu_baseline"] = cpu_baseline(W.make(s, device=dev), s)
     print(json.dumps(line))
 
 
