@@ -10,7 +10,7 @@
 // 2*HB/16 waves. At the start the slice's indices are validated, mapped through
 // the page table and compacted (skipped entries removed, order kept) into a
 // list of physical row ids in LDS. Tiles of 32 rows go from HBM straight into a
-// three-slot LDS ring (direct global -> LDS copies), row-major, with the 16-byte
+// four-slot LDS ring (direct global -> LDS copies), row-major, with the 16-byte
 // chunks of a row XOR-swizzled by the row index so that the operand reads below
 // are free of bank conflicts. Wave (hb, rb) owns 16 heads and the 16-row half rb
 // of every tile:
@@ -22,8 +22,10 @@
 //            transposing LDS reads (ds_read_b64_tr_b16), so no transposed copy
 //            of the values is ever made
 // The loop is software-pipelined: between two barriers, iteration t runs the
-// Q K^T of tile t+1 next to the softmax of tile t, then P V of tile t; the copy of
-// tile t+2 goes out as soon as the slot of tile t-1 is free.
+// Q K^T of tile t+1 next to the softmax of tile t, then P V of tile t. The copy of
+// tile t+3 goes out as soon as the slot of tile t-1 is free, so two tiles (72 KB)
+// are in flight while one is consumed: a gathered row takes microseconds to
+// arrive, longer than the arithmetic on one tile.
 // Slices of one query are merged afterwards by log-sum-exp.
 #include "sia_device.h"
 #include "sia_kernels.h"
@@ -104,8 +106,11 @@ struct MlaGeom {
 // 576 columns (its Q slice, 72 registers, stays in registers), so the two halves
 // of a tile only exchange per-head tile maxima. Iteration t runs, between two
 // barriers, the Q K^T MFMAs of tile t+1 next to the softmax of tile t (vector
-// work), then P V of tile t. The copy of tile t+2 is issued as soon as tile t-1's
-// slot is free (right after the first barrier).
+// work), then P V of tile t. The copy of tile t+3 is issued as soon as tile t-1's
+// slot is free (right after the first barrier). The copies are inline assembly
+// (dma16): the compiler neither sees nor waits for them, and each wave waits for
+// its own copies of a tile with a counted vmcnt wait before the barrier that
+// publishes the tile to the other waves.
 template <int HB>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_kernel(AttnArgs A) {
     using GM = MlaGeom<HB>;
@@ -114,14 +119,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     __shared__ __attribute__((aligned(16))) uint8_t ring0[kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t ring1[kTileB];
     __shared__ __attribute__((aligned(16))) uint8_t ring2[kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[kTileB];
     __shared__ __attribute__((aligned(16))) uint32_t rows[kMaxSliceRows];
-    __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][HB * kPStride];   // by tile parity
+    // P, alpha and the moved flags of tile t are written after the first barrier
+    // of iteration t and read after its second; the next writes come after the
+    // first barrier of iteration t+1, which every wave passes only once its reads
+    // of tile t are done: one buffer each suffices. The tile maxima of tile t+1
+    // are written in iteration t while those of tile t are still read, so they
+    // alternate by tile parity.
+    __shared__ __attribute__((aligned(16))) uint8_t pbuf[HB * kPStride];
     __shared__ __attribute__((aligned(16))) float mx[2][2][HB];                // [parity][row half][head]
-    __shared__ __attribute__((aligned(16))) float alpha_s[2][HB];
+    __shared__ __attribute__((aligned(16))) float alpha_s[HB];
     __shared__ __attribute__((aligned(16))) float lsum[2][HB];
     __shared__ __attribute__((aligned(16))) float mfin[HB];
     __shared__ int scan_s[16];
-    __shared__ __attribute__((aligned(16))) int moved_w[2][NW];   // [parity][wave]: a reference max moved
+    __shared__ __attribute__((aligned(16))) int moved_w[NW];   // [wave]: a reference max moved
 
     const int tid = threadIdx.x, l = lane_id();
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -189,8 +201,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     wait_vmcnt<0>();
 
     auto slot_of = [&](int t) -> uint8_t* {
-        const int u = t % 3;
-        return u == 0 ? ring0 : u == 1 ? ring1 : ring2;
+        const int u = t & 3;
+        return u == 0 ? ring0 : u == 1 ? ring1 : u == 2 ? ring2 : ring3;
     };
     // copies of tile t: copy i (= w + NW k) covers tile bytes [1024 i, 1024 i + 1024);
     // all row ids are read from LDS before the first copy is issued
@@ -219,7 +231,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
                 const int rr = q / kRowChunks, c = q % kRowChunks;
                 const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row[k - k0] * kRowB +
                                      ((c ^ (rr & 7)) << 4);
-                __builtin_amdgcn_global_load_lds(src, (SIA_LDS void*)(dst + i * 1024), 16, 0, 0);
+                dma16(src, (SIA_LDS void*)(dst + i * 1024));
             }
         }
     };
@@ -296,10 +308,14 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     const int hh = hb * 16 + 4 * g;   // first of this lane's four heads
 
     if (ntiles > 0) {
+        // every wave issues exactly CPMAX copies per tile, so "tile t landed" is
+        // "at most CPMAX copies per later tile still outstanding"
         issue(0);
         if (ntiles > 1) issue(1);
-        if (ntiles > 1) wait_vmcnt<CPMAX>();
-        else wait_vmcnt<0>();
+        if (ntiles > 2) issue(2);
+        if (ntiles > 2) wait_vmcnt_mem<2 * CPMAX>();
+        else if (ntiles > 1) wait_vmcnt_mem<CPMAX>();
+        else wait_vmcnt_mem<0>();
         lds_barrier();
         float x[4], tm[4];
         {
@@ -310,17 +326,15 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
 
         for (int t = 0; t < ntiles; t++) {
             const int par = t & 1;
-            // B1: tile t+1 has landed, the maxima of tile t are visible, the slot of
-            // tile t-1 is free
-            if (t + 1 < ntiles) wait_vmcnt<0>();
+            // B1: tile t+1 has landed (only tile t+2's copies may still be in
+            // flight), the maxima of tile t are visible, the slot of tile t-1 is free
+            if (t + 2 < ntiles) wait_vmcnt_mem<CPMAX>();
+            else wait_vmcnt_mem<0>();
             lds_barrier();
+            if (t + 3 < ntiles) issue(t + 3);
             // ---- Q K^T of tile t+1 (matrix cores) ...
             f32x4 sn = {0.f, 0.f, 0.f, 0.f};
             if (t + 1 < ntiles) sn = qk(slot_of(t + 1));
-            // (the copy of tile t+2 goes out after the key reads: the compiler counts
-            // global -> LDS copies against the LDS counter, which would otherwise
-            // turn every wait on a key read into a full drain)
-            if (t + 2 < ntiles) issue(t + 2);
             // ... next to the softmax of tile t (vector units)
             {
                 const f32x4 pm = *reinterpret_cast<const f32x4*>(&mx[par][rb ^ 1][hh]);
@@ -335,11 +349,11 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
                     moved |= mv;
                     const float p = __builtin_amdgcn_exp2f(x[r] - m_ref[r]);
                     l_run[r] = l_run[r] * al[r] + p;
-                    *reinterpret_cast<__bf16*>(&pbuf[par][(hh + r) * kPStride + kn * 2]) = static_cast<__bf16>(p);
+                    *reinterpret_cast<__bf16*>(&pbuf[(hh + r) * kPStride + kn * 2]) = static_cast<__bf16>(p);
                 }
                 // both row halves compute the same alpha: every lane stores it
-                *reinterpret_cast<f32x4*>(&alpha_s[par][hh]) = f32x4{al[0], al[1], al[2], al[3]};
-                moved_w[par][w] = __ballot(moved) != 0ull;
+                *reinterpret_cast<f32x4*>(&alpha_s[hh]) = f32x4{al[0], al[1], al[2], al[3]};
+                moved_w[w] = __ballot(moved) != 0ull;
             }
             if (t + 1 < ntiles) {
                 tile_max(t + 1, sn, x, tm);
@@ -348,18 +362,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             // B2: P and alpha of tile t are visible
             lds_barrier();
             // ---- O = alpha * O + P V of tile t over this wave's columns
-            const int4 mv0 = *reinterpret_cast<const int4*>(&moved_w[par][0]);
-            int any = mv0.x | mv0.y | mv0.z | mv0.w;
-            if constexpr (NW > 4) {
-                const int4 mv1 = *reinterpret_cast<const int4*>(&moved_w[par][4]);
-                any |= mv1.x | mv1.y | mv1.z | mv1.w;
-            } else if constexpr (NW > 2) {
-                any |= moved_w[par][2] | moved_w[par][3];
+            int any = 0;
+            if constexpr (NW >= 4) {
+                const int4 mv0 = *reinterpret_cast<const int4*>(&moved_w[0]);
+                any = mv0.x | mv0.y | mv0.z | mv0.w;
+                if constexpr (NW > 4) {
+                    const int4 mv1 = *reinterpret_cast<const int4*>(&moved_w[4]);
+                    any |= mv1.x | mv1.y | mv1.z | mv1.w;
+                }
+            } else {
+                any = moved_w[0] | moved_w[1];
             }
             if (__builtin_amdgcn_readfirstlane(any)) {
 #pragma unroll
                 for (int h = 0; h < NHB; h++) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&alpha_s[par][h * 16 + 4 * g]);
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&alpha_s[h * 16 + 4 * g]);
 #pragma unroll
                     for (int cb = 0; cb < NCB; cb++)
 #pragma unroll
@@ -369,7 +386,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             bf16x8 pa[NHB];
 #pragma unroll
             for (int h = 0; h < NHB; h++)
-                pa[h] = as_bf16x8(*reinterpret_cast<const u32x4*>(&pbuf[par][(h * 16 + jl) * kPStride + g * 16]));
+                pa[h] = as_bf16x8(*reinterpret_cast<const u32x4*>(&pbuf[(h * 16 + jl) * kPStride + g * 16]));
             const uint8_t* buf = slot_of(t);
             const int(&voff)[2][4] = voffL;
 #pragma unroll
