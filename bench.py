@@ -143,10 +143,11 @@ def cpu_baseline(wl_gpu, s, budget_s: float = 12.0):
 METRIC = "decode queries/s and HBM GB/s at 128K ctx; prefill tokens/s (indexer+TopK+sparse attn)"
 
 
-def time_path(sia, wl, s, group, steps, warmup):
+def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True):
     """Times `steps` passes of the whole path (indexer + Top-K, then sparse
     attention) with HIP events on the stream the library runs on. Returns the
-    indices of the last pass, ms per step and ms per phase."""
+    indices of the last pass, ms per step and ms per phase. `sched` picks the
+    causal prefill tile schedule (-1: the library's default)."""
     import torch
     dev = wl.q_idx.device
     maxv = int(torch.minimum(wl.q_pos.long() + 1, wl.seq_lens.long()[wl.q_seq.long()]).max())
@@ -162,11 +163,12 @@ def time_path(sia, wl, s, group, steps, warmup):
     def indexer():
         sia.sparse_indexer_topk(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq,
                                 wl.q_pos, wl.q_idx, wl.w, s.topk, group=group, max_visible=maxv,
-                                out_idx=idx, workspace=ws_i)
+                                out_idx=idx, workspace=ws_i, sched=sched)
 
     def attention():
-        sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx,
-                                 s.sm_scale, out=out, lse=lse, workspace=ws_a)
+        if attention_too:
+            sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx,
+                                     s.sm_scale, out=out, lse=lse, workspace=ws_a)
 
     for _ in range(warmup):
         indexer()
@@ -213,6 +215,11 @@ def prefill_line(wl, s, steps, warmup):
     import indexer_top_sparse_02_amd as sia
     idx, ms, idx_ms, att_ms = time_path(sia, wl, s, wl.num_q, steps, warmup)
     f_idx, f_att = prefill_flops(s, wl)
+    # the causal tile schedules of the fused indexer, timed alone (same results)
+    sched_ms = {}
+    for name, code in (("naive", 0), ("heavy_first", 1), ("zigzag", 2)):
+        sched_ms[name] = time_path(sia, wl, s, wl.num_q, max(2, steps // 2), 1, sched=code,
+                                   attention_too=False)[2]
     ti, ta = f_idx / (idx_ms * 1e-3) / 1e12, f_att / (att_ms * 1e-3) / 1e12
     dominant = ("sparse_mla_attention call (sparse_mla_kernel)", ta, f_att, att_ms) \
         if att_ms >= idx_ms else ("sparse_indexer_topk call (indexer_stream_kernel)", ti, f_idx, idx_ms)
@@ -224,6 +231,7 @@ def prefill_line(wl, s, steps, warmup):
                    "index_dim": s.dim_idx, "topk": s.topk, "attention_heads": s.heads_attn,
                    "page_size": 64},
         "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
+        "indexer_schedule_ms": sched_ms,
         "algorithmic_tflop": {"indexer": f_idx / 1e12, "attention": f_att / 1e12},
         "phase_tflops": {"indexer": ti, "attention": ta},
         "mfma_frac_step": (f_idx + f_att) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -231,6 +239,52 @@ def prefill_line(wl, s, steps, warmup):
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dominant[1] / PEAK_BF16_TFLOPS,
                      "traffic": None, "algorithmic_tflop_per_call": dominant[2] / 1e12,
                      "call_ms": dominant[3]},
+    }
+
+
+def chunked_line(wl, s, steps, warmup):
+    """Chunked causal prefill: the sequence's queries in chunks of s.chunk, each
+    chunk one indexer call and one attention call against the paged caches
+    (a chunk's queries see positions 0..t, so later rows already in the cache
+    stay invisible, as in a cache that grows chunk by chunk). Reports the time
+    of every chunk: the causal work grows linearly with the chunk index."""
+    import indexer_top_sparse_02_amd as sia
+    n_chunks = wl.num_q // s.chunk
+    chunks = []
+    tot_ms = tot_i = tot_a = f_i_all = f_a_all = 0.0
+    for c in range(n_chunks):
+        sub = wl.queries(c * s.chunk, (c + 1) * s.chunk)
+        _, ms, i_ms, a_ms = time_path(sia, sub, s, s.chunk, steps, warmup)
+        f_i, f_a = prefill_flops(s, sub)
+        chunks.append({"chunk": c, "ms": ms, "indexer_ms": i_ms, "attention_ms": a_ms,
+                       "indexer_tflops": f_i / (i_ms * 1e-3) / 1e12,
+                       "attention_tflops": f_a / (a_ms * 1e-3) / 1e12})
+        print(f"chunk {c}: {ms:.3f} ms (indexer {i_ms:.3f}, attention {a_ms:.3f})", file=sys.stderr,
+              flush=True)
+        tot_ms += ms
+        tot_i += i_ms
+        tot_a += a_ms
+        f_i_all += f_i
+        f_a_all += f_a
+    dominant = ("sparse_indexer_topk calls (indexer_stream_kernel)", f_i_all / (tot_i * 1e-3) / 1e12,
+                f_i_all, tot_i) if tot_i >= tot_a else \
+        ("sparse_mla_attention calls (sparse_mla_kernel)", f_a_all / (tot_a * 1e-3) / 1e12, f_a_all, tot_a)
+    return {
+        "metric": METRIC, "value": wl.num_q / (tot_ms * 1e-3), "unit": "prefill tokens/s",
+        "ms_per_step": tot_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded fp8 index-K with per-token scales, N(0,1) "
+                                 "latent KV and queries, shuffled page table)",
+        "config": {"workload": s.name, "tokens": wl.num_q, "chunk": s.chunk, "indexer_heads": s.heads_idx,
+                   "index_dim": s.dim_idx, "topk": s.topk, "attention_heads": s.heads_attn,
+                   "page_size": 64},
+        "phases_ms": {"indexer_topk": tot_i, "attention": tot_a},
+        "algorithmic_tflop": {"indexer": f_i_all / 1e12, "attention": f_a_all / 1e12},
+        "mfma_frac_step": (f_i_all + f_a_all) / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "chunks": chunks,
+        "roofline": {"bound": "mfma", "kernel": dominant[0], "achieved": dominant[1],
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": dominant[1] / PEAK_BF16_TFLOPS,
+                     "traffic": None, "algorithmic_tflop_per_call": dominant[2] / 1e12 / n_chunks,
+                     "call_ms": dominant[3] / n_chunks},
     }
 
 
@@ -252,7 +306,10 @@ def main():
     torch.cuda.set_device(dev)
     s = W.spec(a.config)
     if s.prefill:
-        line = prefill_line(W.make(s, device=dev), s, a.steps, a.warmup)
+        if s.chunk:
+            line = chunked_line(W.make(s, device=dev), s, max(1, a.steps // 4), max(1, a.warmup))
+        else:
+            line = prefill_line(W.make(s, device=dev), s, a.steps, a.warmup)
         line.update({"n_gpus": 1, "steps": a.steps, "warmup": a.warmup})
         print(json.dumps(line))
         return
