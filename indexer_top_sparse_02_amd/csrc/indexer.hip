@@ -992,22 +992,91 @@ struct WaveBuf {
     SelScratch* sel;
 };
 
+// Geometry of the K ring the four waves of a stream workgroup share: every
+// 32-position tile of index-K is copied once from global memory into LDS and
+// read there by all four queries of the workgroup (consecutive positions of one
+// sequence walk almost the same causal rows).
+template <int D, bool FP8>
+struct StreamGeom {
+    static constexpr int R = D * (FP8 ? 1 : 2);            // bytes per row
+    static constexpr int CPR = R / 16;                      // 16-byte chunks per row
+    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;     // chunk swizzle mask
+    static constexpr int TILE = 32 * R;
+    static constexpr int DMA = TILE / 1024;                 // 1 KB copies per tile
+    static constexpr int QPT = kStreamThreads / kWave;      // waves (= queries) per workgroup
+    static constexpr int CPW = (DMA + QPT - 1) / QPT;       // copies per wave and tile
+    static constexpr int PER_TILE = CPW + (FP8 ? 1 : 0);    // (+ the page's 64 scales)
+    static constexpr int SLOT = TILE + (FP8 ? 256 : 0);
+    static constexpr int NS = TILE <= 4096 ? 8 : 4;         // ring slots
+    static constexpr int RING = NS * SLOT;
+    static_assert(DMA >= 1 && (NS - 1) * PER_TILE < 64, "stream ring geometry");
+};
+
+__host__ __device__ inline size_t stream_ring_bytes(int dim, bool fp8) {
+    const size_t tile = 32 * (size_t)dim * (fp8 ? 1 : 2);
+    return (tile <= 4096 ? 8 : 4) * (tile + (fp8 ? 256 : 0));
+}
+
+// One workgroup's four queries j (one per wave; rl = its visible length, rl_max
+// the longest of the four) walked tile by tile over the shared K ring. Each
+// wave keeps the keys that beat its threshold tau in its own LDS candidate
+// buffer and re-selects inside it when the buffer fills, then emits its Top-K.
+// Called by all four waves (the ring needs one barrier per tile).
 template <int MB, int D, bool FP8>
-__device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, int rl, const int* pages,
-                             WaveBuf B) {
-    const int l = lane_id();
-    int32_t* oi = S.out_idx + (int64_t)j * S.topk;
-    float* os = S.out_score ? S.out_score + (int64_t)j * S.topk : nullptr;
+__device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int rl, int rl_max,
+                             const int* pages, WaveBuf B, uint8_t* ring) {
+    using SG = StreamGeom<D, FP8>;
+    constexpr int NS = SG::NS, R = SG::R, NV = KTile<D, FP8>::NV;
+    const int l = lane_id(), half = l >> 5, frow = l & 31;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const bool live = j < A.num_q;
     int cnt = 0;
     uint32_t tau = 0u;
-    const int ntiles = (rl + 31) / 32;
-    if (ntiles > 0) {
+    const int nt = (rl_max + 31) / 32;
+    if (nt > 0) {
         IdxQuery<MB, D, FP8> q;
-        load_query<MB, D>(A, j, q);
-        const int npages = (rl + kPage - 1) / kPage;
-        auto fetch = [&](KTile<D, FP8>& t, int ti) {   // ti past the end: dummy row
-            const int page = __builtin_amdgcn_readfirstlane(pages[min(ti >> 1, npages - 1)]);
-            load_ktile<D, FP8>(A, page, ti * 32, ti < ntiles ? rl : 0, t);
+        load_query<MB, D>(A, live ? j : A.num_q - 1, q);
+        // this wave's copies of a tile: tile bytes [1024 r, 1024 r + 1024) land
+        // linearly in the slot; lane l fetches the source chunk that belongs at
+        // slot byte 1024 r + 16 l (logical chunk c of a row sits at c ^ (row & SWZ))
+        uint32_t voff[SG::CPW];
+#pragma unroll
+        for (int c = 0; c < SG::CPW; c++) {
+            const int r = min(w * SG::CPW + c, SG::DMA - 1);
+            const int gi = r * 1024 + 16 * l;
+            const int row = gi / R, cc = (gi % R) / 16;
+            voff[c] = row * R + ((cc ^ (row & SG::SWZ)) << 4);
+        }
+        uint32_t roff[NV];
+#pragma unroll
+        for (int i = 0; i < NV; i++) {
+            const int cc = KTile<D, FP8>::chunk(i, half);
+            roff[i] = frow * R + ((cc ^ (frow & SG::SWZ)) << 4);
+        }
+        const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring));
+        // copies of tile k (clamped to the last tile, so that every wave issues
+        // the same count whatever k is; a clamped copy lands in a free slot)
+        auto issue = [&](int k) {
+            const int ti = min(k, nt - 1);
+            const int page = max(__builtin_amdgcn_readfirstlane(pages[ti >> 1]), 0);
+            const uint8_t* base = A.rows + ((int64_t)page * kPage + (ti & 1) * 32) * R;
+            const uint32_t dst = ring_lds + (k % NS) * SG::SLOT;
+#pragma unroll
+            for (int c = 0; c < SG::CPW; c++) {
+                const int r = min(w * SG::CPW + c, SG::DMA - 1);
+                dma16_s(base, voff[c], dst + r * 1024);
+            }
+            if constexpr (FP8) dma4_s(A.scale + (int64_t)page * kPage, 4 * l, dst + SG::TILE);
+        };
+        // operands of tile k (k may be nt: then the slot holds a clamped copy and
+        // no lane is ok; the page id is read only for visible positions)
+        auto fetch = [&](int k, KTile<D, FP8>& t) {
+            const uint8_t* slot = ring + (k % NS) * SG::SLOT;
+#pragma unroll
+            for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
+            if constexpr (FP8) t.sc = *reinterpret_cast<const float*>(slot + SG::TILE + 4 * ((k & 1) * 32 + frow));
+            else t.sc = 1.f;
+            t.ok = k * 32 + frow < rl && pages[k >> 1] >= 0;
         };
         auto consume = [&](const KTile<D, FP8>& t, int ti) {
             const float sc = tile_scores<MB, D, FP8>(q, t);
@@ -1035,37 +1104,53 @@ __device__ void stream_query(const IdxArgs& A, const StreamArgs& S, int j, int r
                 wave_sync();
             }
         };
-        constexpr int kPrefetch = 4;   // K tiles in flight per wave
-        KTile<D, FP8> buf[kPrefetch];
+        // Tiles 0 .. NS-1 go out first; iteration k scores tile k (its operands
+        // already in registers) while the operands of tile k+1 are read from LDS,
+        // and refills the slot of tile k, which every wave has read by then.
 #pragma unroll
-        for (int d = 0; d < kPrefetch; d++) fetch(buf[d], d);
-        int t = 0;
-        for (; t + kPrefetch - 1 < ntiles; t += kPrefetch) {
-#pragma unroll
-            for (int d = 0; d < kPrefetch; d++) {
-                consume(buf[d], t + d);
-                fetch(buf[d], t + d + kPrefetch);
-            }
+        for (int k = 0; k < NS; k++) issue(k);
+        wait_vmcnt_mem<(NS - 1) * SG::PER_TILE>();   // tile 0 has landed
+        lds_barrier();
+        KTile<D, FP8> t;
+        fetch(0, t);
+        for (int k = 0; k < nt; k++) {
+            // tile k+1 has landed (the copies of tiles k+2 .. k+NS-1 may still be
+            // in flight); after the barrier every wave's part of it is visible and
+            // every wave holds tile k in registers, so tile k's slot takes k+NS
+            wait_vmcnt_mem<(NS - 2) * SG::PER_TILE>();
+            lds_barrier();
+            issue(k + NS);
+            KTile<D, FP8> tn;
+            fetch(k + 1, tn);
+            consume(t, k);
+            t = tn;
         }
-#pragma unroll
-        for (int d = 0; d < kPrefetch - 1; d++)
-            if (t + d < ntiles) consume(buf[d], t + d);
+        wait_vmcnt_mem<0>();
     }
-    wave_sync();
-    const int n4 = (cnt + 3) & ~3;
-    for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
-    wave_sync();
-    const int m = select_emit<kWave>(B.key, n4, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}});
-    for (int r = m + l; r < S.topk; r += kWave) {
-        oi[r] = -1;
-        if (os) os[r] = -INFINITY;
+    if (live) {
+        int32_t* oi = S.out_idx + (int64_t)j * S.topk;
+        float* os = S.out_score ? S.out_score + (int64_t)j * S.topk : nullptr;
+        wave_sync();
+        const int n4 = (cnt + 3) & ~3;
+        for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
+        wave_sync();
+        const int m = select_emit<kWave>(B.key, n4, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}});
+        for (int r = m + l; r < S.topk; r += kWave) {
+            oi[r] = -1;
+            if (os) os[r] = -INFINITY;
+        }
+        wave_sync();
     }
-    wave_sync();
 }
 
 __host__ __device__ inline size_t stream_wave_bytes(int cap) { return (size_t)cap * 8 + sizeof(SelScratch); }
-__host__ __device__ inline size_t stream_smem_bytes(int cap, int max_visible) {
-    return 4 * stream_wave_bytes(cap) + ((size_t)(max_visible + kPage - 1) / kPage * 4 + 15) / 16 * 16;
+__host__ __device__ inline size_t stream_pages_offset(int cap) { return 4 * stream_wave_bytes(cap); }
+__host__ __device__ inline size_t stream_ring_offset(int cap, int max_visible) {
+    const size_t pages_end = stream_pages_offset(cap) + (size_t)(max_visible + kPage - 1) / kPage * 4;
+    return (pages_end + 255) / 256 * 256;
+}
+__host__ __device__ inline size_t stream_smem_bytes(int cap, int max_visible, int dim, bool fp8) {
+    return stream_ring_offset(cap, max_visible) + stream_ring_bytes(dim, fp8);
 }
 
 template <int MB, int D, bool FP8>
@@ -1078,7 +1163,8 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
     uint8_t* base = smem + w * stream_wave_bytes(S.cap);
     WaveBuf B{reinterpret_cast<uint32_t*>(base), reinterpret_cast<int32_t*>(base + (size_t)S.cap * 4),
               reinterpret_cast<SelScratch*>(base + (size_t)S.cap * 8)};
-    int* pages = reinterpret_cast<int*>(smem + QPT * stream_wave_bytes(S.cap));
+    int* pages = reinterpret_cast<int*>(smem + stream_pages_offset(S.cap));
+    uint8_t* ring = smem + stream_ring_offset(S.cap, A.max_visible);
 
     // One tile: four consecutive queries of one sequence. Their page ids are staged
     // once in LDS; a query of another sequence is dropped (status bit).
@@ -1098,10 +1184,11 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
         __syncthreads();
         if (lane_id() == 0) atomicMax(&tile_rows, rl);
         __syncthreads();
-        const int npg = (tile_rows + kPage - 1) / kPage;
+        const int rows = tile_rows;
+        const int npg = (rows + kPage - 1) / kPage;
         for (int i = threadIdx.x; i < npg; i += kStreamThreads) pages[i] = page_of(A, b0, i);
         __syncthreads();
-        if (j < A.num_q) stream_query<MB, D, FP8>(A, S, j, rl, pages, B);
+        stream_group<MB, D, FP8>(A, S, j, rl, rows, pages, B, ring);
         __syncthreads();
     };
     if (S.sched == 0) {
@@ -1185,7 +1272,7 @@ hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st) {
 template <int MB, int D, bool FP8>
 static hipError_t stream_launch(const IdxArgs& a, const StreamArgs& s, int grid, hipStream_t st) {
     auto k = indexer_stream_kernel<MB, D, FP8>;
-    const size_t smem = stream_smem_bytes(s.cap, a.max_visible);
+    const size_t smem = stream_smem_bytes(s.cap, a.max_visible, D, FP8);
     hipError_t e = set_smem(k, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kStreamThreads), smem, st, a, s);
@@ -1195,7 +1282,7 @@ static hipError_t stream_launch(const IdxArgs& a, const StreamArgs& s, int grid,
 template <int MB, int D, bool FP8>
 static int stream_occupancy(int cap, int max_visible) {
     auto k = indexer_stream_kernel<MB, D, FP8>;
-    const size_t smem = stream_smem_bytes(cap, max_visible);
+    const size_t smem = stream_smem_bytes(cap, max_visible, D, FP8);
     if (set_smem(k, smem) != hipSuccess) return 1;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k),
@@ -1214,7 +1301,9 @@ hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, 
     return hipErrorInvalidValue;
 }
 
-size_t indexer_stream_smem(int cap, int max_visible) { return stream_smem_bytes(cap, max_visible); }
+size_t indexer_stream_smem(int cap, int max_visible, int dim, bool fp8) {
+    return stream_smem_bytes(cap, max_visible, dim, fp8);
+}
 
 int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap, int max_visible) {
 #define SIA_OCC(MBv, Dv, F8) \

@@ -138,15 +138,20 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bo
     if (mode == 1) stream = false;
     if (mode == 2) stream = stream_ok;
     if (stream) {
-        const int cap = std::min(4096, std::max(1024, 2 * topk));
-        // the candidate buffers and the staged page ids must fit in LDS
-        if (sia::indexer_stream_smem(cap, qs->max_visible) + 64 <= sia::kMaxLds) {
+        // the candidate buffers, the staged page ids and the K ring must fit in
+        // LDS: the buffers shrink (down to K + 256 keys, which only makes the
+        // in-buffer re-selection more frequent) until they do
+        int cap = std::min(4096, std::max(1024, 2 * topk));
+        const int cap_min = std::max(1024, (topk + 256 + 63) / 64 * 64);
+        while (cap > cap_min && sia::indexer_stream_smem(cap, qs->max_visible, dim, fp8) + 64 > sia::kMaxLds)
+            cap = std::max(cap_min, cap - 256);
+        if (sia::indexer_stream_smem(cap, qs->max_visible, dim, fp8) + 64 <= sia::kMaxLds) {
             p.stream = true;
             p.cap = cap;
             return p;
         }
     }
-    (void)heads; (void)dim; (void)fp8;
+    (void)heads;
     int g = qs->group % 2 == 0 ? 2 : 1;
     if (env_int("SIA_ROWS_GROUP", 0) == 1) g = 1;
     plan_rows(p, qs->num_q, qs->max_visible, g);

@@ -73,7 +73,7 @@ hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st);
 hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, bool fp8,
                                  int grid, hipStream_t st);
 int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap, int max_visible);
-size_t indexer_stream_smem(int cap, int max_visible);
+size_t indexer_stream_smem(int cap, int max_visible, int dim, bool fp8);
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kCoarseBinsHost = 2048;   // = kCoarseBins of the selection code
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
