@@ -1009,7 +1009,7 @@ struct StreamGeom {
     static constexpr int SLOT = TILE + (FP8 ? 256 : 0);
     static constexpr int NS = TILE <= 4096 ? 8 : 4;         // ring slots
     static constexpr int RING = NS * SLOT;
-    static_assert(DMA >= 1 && (NS - 1) * PER_TILE < 64, "stream ring geometry");
+    static_assert(DMA >= 1 && NS >= 4 && (NS - 1) * PER_TILE < 64, "stream ring geometry");
 };
 
 __host__ __device__ inline size_t stream_ring_bytes(int dim, bool fp8) {
@@ -1054,11 +1054,13 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             roff[i] = frow * R + ((cc ^ (frow & SG::SWZ)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring));
-        // copies of tile k (clamped to the last tile, so that every wave issues
-        // the same count whatever k is; a clamped copy lands in a free slot)
-        auto issue = [&](int k) {
+        // page id of tile k's copy (clamped to the last tile, so that every wave
+        // issues the same count whatever k is; a clamped copy lands in a free slot)
+        auto copy_page = [&](int k) { return pages[min(k, nt - 1) >> 1]; };
+        // copies of tile k from physical page pg (its page id, read beforehand)
+        auto issue = [&](int k, int pg) {
             const int ti = min(k, nt - 1);
-            const int page = max(__builtin_amdgcn_readfirstlane(pages[ti >> 1]), 0);
+            const int page = max(__builtin_amdgcn_readfirstlane(pg), 0);
             const uint8_t* base = A.rows + ((int64_t)page * kPage + (ti & 1) * 32) * R;
             const uint32_t dst = ring_lds + (k % NS) * SG::SLOT;
 #pragma unroll
@@ -1068,28 +1070,34 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             }
             if constexpr (FP8) dma4_s(A.scale + (int64_t)page * kPage, 4 * l, dst + SG::TILE);
         };
-        // operands of tile k (k may be nt: then the slot holds a clamped copy and
-        // no lane is ok; the page id is read only for visible positions)
-        auto fetch = [&](int k, KTile<D, FP8>& t) {
+        // operands of tile k (k may be past the last tile: then the slot holds a
+        // clamped copy and no position is visible). t.ok is the visibility only;
+        // the page id `pg` is read without a branch and checked when the tile is
+        // scored, so nothing waits for these reads before then.
+        auto fetch = [&](int k, KTile<D, FP8>& t, int& pg) {
             const uint8_t* slot = ring + (k % NS) * SG::SLOT;
 #pragma unroll
             for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
             if constexpr (FP8) t.sc = *reinterpret_cast<const float*>(slot + SG::TILE + 4 * ((k & 1) * 32 + frow));
             else t.sc = 1.f;
-            t.ok = k * 32 + frow < rl && pages[k >> 1] >= 0;
+            t.ok = k * 32 + frow < rl;
+            pg = pages[min(k, nt - 1) >> 1];
         };
-        auto consume = [&](const KTile<D, FP8>& t, int ti) {
-            const float sc = tile_scores<MB, D, FP8>(q, t);
+        // appends the key of position ti*32 + l (score sc, lanes 0..31) if it beats
+        // tau. Branch-free: a lane that does not take writes to its own spare entry
+        // past the buffer (so the MFMAs issued before it stay where they are).
+        auto append = [&](float sc, bool ok, int ti) {
             const int p = ti * 32 + (l & 31);
-            const uint32_t k = (l < 32 && t.ok) ? score_key(sc) : 0u;
+            const uint32_t k = score_key(sc) & (0u - (uint32_t)(l < 32 && ok));
             const bool take = k > tau;
             const uint64_t mask = __ballot(take);
-            if (take) {
-                const int at = cnt + lanes_below(mask);
-                B.key[at] = k;
-                B.pos[at] = p;
-            }
+            const int at = take ? cnt + lanes_below(mask) : S.cap + l;
+            B.key[at] = k;
+            B.pos[at] = p;
             cnt += __popcll(mask);
+        };
+        // re-selects inside the buffer once it may not take another tile
+        auto reselect = [&]() {
             if (cnt > S.cap - 32) {
                 // keep exactly the Top-K seen so far; later ties of T lose to them
                 wave_sync();
@@ -1104,26 +1112,52 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
                 wave_sync();
             }
         };
-        // Tiles 0 .. NS-1 go out first; iteration k scores tile k (its operands
-        // already in registers) while the operands of tile k+1 are read from LDS,
-        // and refills the slot of tile k, which every wave has read by then.
+        constexpr int NMFMA = MB * (FP8 ? 2 * (D / 64) : D / 16);   // MFMAs per tile
+        // Tiles 0 .. NS-1 go out first. Iteration k: the MFMAs of tile k+1 (its
+        // operands read from LDS one iteration earlier) run interleaved with the
+        // epilogue of tile k (ReLU, head weights, head sum, key, append), while the
+        // operands of tile k+2 are read; tile k's slot, read two iterations back,
+        // takes tile k+NS.
 #pragma unroll
-        for (int k = 0; k < NS; k++) issue(k);
-        wait_vmcnt_mem<(NS - 1) * SG::PER_TILE>();   // tile 0 has landed
+        for (int k = 0; k < NS; k++) issue(k, copy_page(k));
+        int pg_issue = copy_page(NS);                 // page of the next copy
+        wait_vmcnt_mem<(NS - 2) * SG::PER_TILE>();   // tiles 0 and 1 have landed
         lds_barrier();
-        KTile<D, FP8> t;
-        fetch(0, t);
-        for (int k = 0; k < nt; k++) {
-            // tile k+1 has landed (the copies of tiles k+2 .. k+NS-1 may still be
-            // in flight); after the barrier every wave's part of it is visible and
-            // every wave holds tile k in registers, so tile k's slot takes k+NS
-            wait_vmcnt_mem<(NS - 2) * SG::PER_TILE>();
+        // tb holds the operands of the next tile to multiply; A0 / A1 alternate as
+        // the accumulators of the tile being finished and of the tile being
+        // multiplied (two sets, so that the MFMAs never wait for the epilogue)
+        KTile<D, FP8> tb;
+        int pg_b;
+        f32x16 A0[MB], A1[MB];
+        fetch(0, tb, pg_b);
+        tile_mfma<MB, D, FP8>(q, tb, A0);
+        float sc_c = tb.sc;
+        bool ok_c = tb.ok;
+        int pg_c = pg_b;
+        fetch(1, tb, pg_b);
+        auto step = [&](int k, f32x16 (&cur)[MB], f32x16 (&nxt)[MB]) {
+            reselect();
+            // tile k+2 has landed (the copies of tiles k+3 .. k+NS-1 may still be in
+            // flight); after the barrier every wave's part of it is visible
+            wait_vmcnt_mem<(NS - 3) * SG::PER_TILE>();
             lds_barrier();
-            issue(k + NS);
-            KTile<D, FP8> tn;
-            fetch(k + 1, tn);
-            consume(t, k);
-            t = tn;
+            issue(k + NS, pg_issue);
+            pg_issue = copy_page(k + NS + 1);
+            tile_mfma<MB, D, FP8>(q, tb, nxt);   // tile k+1
+            const float sc_n = tb.sc;
+            const bool ok_n = tb.ok;
+            const int pg_n = pg_b;
+            fetch(k + 2, tb, pg_b);              // (after the MFMAs have read tb)
+            const float sc = tile_epilogue<MB, D, FP8>(q, cur, sc_c);
+            interleave_mfma_valu<NMFMA>();
+            append(sc, ok_c && pg_c >= 0, k);
+            sc_c = sc_n;
+            ok_c = ok_n;
+            pg_c = pg_n;
+        };
+        for (int k = 0; k < nt; k += 2) {
+            step(k, A0, A1);
+            if (k + 1 < nt) step(k + 1, A1, A0);
         }
         wait_vmcnt_mem<0>();
     }
@@ -1143,7 +1177,11 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
     }
 }
 
-__host__ __device__ inline size_t stream_wave_bytes(int cap) { return (size_t)cap * 8 + sizeof(SelScratch); }
+// a wave's candidate keys and positions (cap entries each, plus one spare entry
+// per lane for the branch-free append) and its selection scratch
+__host__ __device__ inline size_t stream_wave_bytes(int cap) {
+    return (size_t)(cap + kWave) * 8 + sizeof(SelScratch);
+}
 __host__ __device__ inline size_t stream_pages_offset(int cap) { return 4 * stream_wave_bytes(cap); }
 __host__ __device__ inline size_t stream_ring_offset(int cap, int max_visible) {
     const size_t pages_end = stream_pages_offset(cap) + (size_t)(max_visible + kPage - 1) / kPage * 4;
@@ -1161,8 +1199,8 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
     constexpr int QPT = kStreamThreads / kWave;   // queries per tile, one per wave
     const int w = threadIdx.x / kWave;
     uint8_t* base = smem + w * stream_wave_bytes(S.cap);
-    WaveBuf B{reinterpret_cast<uint32_t*>(base), reinterpret_cast<int32_t*>(base + (size_t)S.cap * 4),
-              reinterpret_cast<SelScratch*>(base + (size_t)S.cap * 8)};
+    WaveBuf B{reinterpret_cast<uint32_t*>(base), reinterpret_cast<int32_t*>(base + (size_t)(S.cap + kWave) * 4),
+              reinterpret_cast<SelScratch*>(base + (size_t)(S.cap + kWave) * 8)};
     int* pages = reinterpret_cast<int*>(smem + stream_pages_offset(S.cap));
     uint8_t* ring = smem + stream_ring_offset(S.cap, A.max_visible);
 
