@@ -169,32 +169,45 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         for (int ks = 0; ks < KS; ks++) qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + ks * 32));
     }
 
-    // ---- validated, compacted physical row ids of the slice
+    // ---- validated, compacted physical row ids of the slice. Thread t owns the
+    // RPT consecutive entries r0 + RPT t ..: all index loads go out together,
+    // then all page-table loads, then one prefix sum places the kept rows in
+    // order (one round trip of each kind instead of one per NT entries).
+    constexpr int RPT = kMaxSliceRows / NT;
     int nr = 0;
-    for (int base = r0; base < r1; base += NT) {
-        const int r = base + tid;
-        uint32_t row = 0u;
+    {
+        int sidx[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int r = r0 + tid * RPT + i;
+            sidx[i] = r < r1 ? A.idx[(int64_t)j * A.topk + r] : -1;
+        }
+        int pg[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
+            const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
+            pg[i] = in ? A.page_table[(int64_t)b * A.max_pages + (s >> 6)] : -1;
+            if (s >= 0 && !in) atomicOr(A.status, kBadIndex);
+        }
+        uint32_t row[RPT];
         int keep = 0;
-        if (r < r1) {
-            const int s = A.idx[(int64_t)j * A.topk + r];
-            if (s >= 0) {
-                if (s >= n_b || s >= A.max_pages * kPage) {
-                    atomicOr(A.status, kBadIndex);
-                } else {
-                    const int page = A.page_table[(int64_t)b * A.max_pages + (s >> 6)];
-                    if (page >= 0 && page < A.num_pages) {
-                        row = (uint32_t)page * kPage + (uint32_t)(s & 63);
-                        keep = 1;
-                    } else {
-                        atomicOr(A.status, kBadPage);
-                    }
-                }
-            }
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
+            const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
+            const bool ok = in && pg[i] >= 0 && pg[i] < A.num_pages;
+            if (in && !ok) atomicOr(A.status, kBadPage);
+            row[i] = ok ? (uint32_t)pg[i] * kPage + (uint32_t)(s & 63) : 0xffffffffu;
+            keep += ok;
         }
         int pre, tot;
         scan1<NT>(keep, pre, tot, scan_s);
-        if (keep) rows[nr + pre] = row;
-        nr += tot;
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            if (row[i] != 0xffffffffu) rows[pre++] = row[i];
+        }
+        nr = tot;
     }
     __syncthreads();
     const int ntiles = (nr + kTR - 1) / kTR;
