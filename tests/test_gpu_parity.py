@@ -157,6 +157,44 @@ def test_row_path_causal_rows_exact(parts, fp8):
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("layout", ["causal", "scattered"])
+@pytest.mark.parametrize("dim,fp8,heads", [(128, False, 64), (128, True, 64), (64, False, 32),
+                                          (64, True, 32), (64, True, 64), (128, True, 32)])
+def test_stream_path_exact_selection(dim, fp8, heads, layout):
+    """The fused streaming Top-K (the four queries of a workgroup share one LDS
+    ring of K tiles) against the oracle's selection on the GPU's own scores,
+    bit for bit, for every index row shape it is built for (64 or 128 wide,
+    bf16 or fp8; 32 or 64 heads). Rows are longer than the candidate buffer, so
+    the in-buffer re-selection runs. "scattered" gives the four queries of a
+    workgroup very different row lengths (a workgroup walks its longest row;
+    shorter rows must ignore the tiles past their end)."""
+    import dataclasses
+    s = W.spec("prefill_16k", ctx_lo=2600, ctx_hi=2600, topk=256, idx_fp8=fp8, dim_idx=dim,
+               heads_idx=heads, heads_attn=16)
+    wl = W.make(s, device="cuda", poison=True)
+    if layout == "scattered":
+        g = torch.Generator().manual_seed(7)
+        perm = torch.randperm(wl.num_q, generator=g).to(wl.q_pos.device)
+        wl = dataclasses.replace(wl, q_pos=wl.q_pos[perm].contiguous())
+    sc = gpu_scores(wl)
+    rl = row_lengths(wl)
+    # the scores themselves, on a few rows, against the oracle
+    rows = [0, 3, 1001, wl.num_q - 1]
+    cpu = wl.to("cpu")
+    ref_rows = [oracle.run(cpu.queries(r, r + 1), attention=False).scores[0] for r in rows]
+    ref_scores = np.full((len(rows), sc.shape[1]), -np.inf)
+    for i, r in enumerate(ref_rows):
+        ref_scores[i, :r.shape[0]] = r[:sc.shape[1]]
+    check_scores(sc.cpu().numpy()[rows], ref_scores, rl[rows], score_tol(wl))
+    with env(SIA_INDEXER_PATH=2):
+        got, top = gpu_topk(wl)
+    ref, ref_sc = oracle_topk_of(sc, rl, s.topk)
+    g_idx = got.cpu().numpy()
+    assert np.array_equal(g_idx, ref)
+    g_top = top.cpu().numpy().astype(np.float64)
+    assert np.array_equal(g_top[g_idx >= 0], ref_sc[g_idx >= 0])
+
+
 @pytest.mark.parametrize("sched", [0, 1, 2])
 def test_prefill_schedules_agree(sched):
     s = W.spec("prefill_16k", ctx_lo=1500, ctx_hi=1500, topk=128, idx_fp8=True)
