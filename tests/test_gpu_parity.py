@@ -204,6 +204,33 @@ def test_prefill_schedules_agree(sched):
     assert torch.equal(ref, got)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_chunked_prefill_equals_single_shot(fp8):
+    """A causal prefill run as three chunks of queries (each chunk one indexer
+    call and one attention call against the full caches, seeing positions 0..t)
+    gives the same indices and the same attention output bits as one call over
+    all queries: a query's result depends only on its own row."""
+    s = W.spec("prefill_16k", ctx_lo=3000, ctx_hi=3000, topk=256, idx_fp8=fp8, heads_attn=32)
+    wl = W.make(s, device="cuda", poison=True)
+    import indexer_top_sparse_02_amd as sia
+    idx_all, _ = sia.sparse_indexer_topk(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq,
+                                         wl.q_pos, wl.q_idx, wl.w, s.topk, group=wl.num_q)
+    out_all, lse_all = gpu_attention(wl, idx_all)
+    parts_idx, parts_out, parts_lse = [], [], []
+    for a, b in ((0, 1024), (1024, 2048), (2048, wl.num_q)):
+        c = wl.queries(a, b)
+        i, _ = sia.sparse_indexer_topk(c.page_table, c.seq_lens, c.idx_k, c.idx_scale, c.q_seq, c.q_pos,
+                                       c.q_idx, c.w, s.topk, group=b - a)
+        o, l = gpu_attention(c, i)
+        parts_idx.append(i)
+        parts_out.append(o)
+        parts_lse.append(l)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(parts_idx), idx_all)
+    assert torch.equal(torch.cat(parts_out).view(torch.int16), out_all.view(torch.int16))
+    assert torch.equal(torch.cat(parts_lse), lse_all)
+
+
 def test_page_placement_does_not_change_results():
     s = W.spec("decode_b32", batch=3, ctx_lo=3000, ctx_hi=6000, topk=512, heads_attn=64)
     a = W.make(s, device="cuda", shuffle=False)
