@@ -124,11 +124,13 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     // P, alpha and the moved flags of tile t are written after the first barrier
     // of iteration t and read after its second; the next writes come after the
     // first barrier of iteration t+1, which every wave passes only once its reads
-    // of tile t are done: one buffer each suffices. The tile maxima of tile t+1
-    // are written in iteration t while those of tile t are still read, so they
-    // alternate by tile parity.
+    // of tile t are done: one buffer each suffices. The "reference moves" flags
+    // of tile t+1 are written in iteration t while those of tile t may still be
+    // read, so they alternate by tile parity; the tile maxima, exchanged only in
+    // an iteration that moves a reference (with a barrier of its own), need one.
     __shared__ __attribute__((aligned(16))) uint8_t pbuf[HB * kPStride];
-    __shared__ __attribute__((aligned(16))) float mx[2][2][HB];                // [parity][row half][head]
+    __shared__ __attribute__((aligned(16))) float mx[2][HB];                   // [row half][head]
+    __shared__ __attribute__((aligned(16))) int flg[2][NW < 4 ? 4 : NW];        // [parity][wave]
     __shared__ __attribute__((aligned(16))) float alpha_s[HB];
     __shared__ __attribute__((aligned(16))) float lsum[2][HB];
     __shared__ __attribute__((aligned(16))) float mfin[HB];
@@ -297,22 +299,43 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     };
     const float scale_log2 = A.sm_scale * 1.4426950408889634f;
     constexpr float kLazyMax = 8.f;
-    // per-head maxima of this wave's 16 rows (scaled, masked); lane group g holds heads 4g..4g+3
-    auto tile_max = [&](int t, const f32x4& sv, float (&x)[4], float (&tm)[4]) {
-        const bool valid = t * kTR + kn < nr;
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            x[r] = valid ? sv[r] * scale_log2 : -INFINITY;
-            tm[r] = row16_max(x[r]);
-        }
-    };
-
     float m_ref[4], l_run[4];
 #pragma unroll
     for (int r = 0; r < 4; r++) {
         m_ref[r] = -INFINITY;
         l_run[r] = 0.f;
     }
+    // Scaled, masked logits of this wave's 16 rows of tile t (lane group g holds
+    // heads 4g..4g+3), and whether any of them exceeds its head's reference
+    // maximum by more than kLazyMax: only then does the softmax of the tile need
+    // the exact tile maxima (and a reference may move). The flag goes to LDS for
+    // tile parity `par`, where every wave reads all of them after the next barrier.
+    auto tile_logits = [&](int t, const f32x4& sv, float (&x)[4], int par) {
+        const bool valid = t * kTR + kn < nr;
+        bool over = false;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            x[r] = valid ? sv[r] * scale_log2 : -INFINITY;
+            over |= x[r] > m_ref[r] + kLazyMax;
+        }
+        flg[par][w] = __ballot(over) != 0ull;
+    };
+    // any wave's flag for tile parity par (the same answer in every wave)
+    auto any_flag = [&](int par) -> bool {
+        int a;
+        if constexpr (NW >= 4) {
+            const int4 f0 = *reinterpret_cast<const int4*>(&flg[par][0]);
+            a = f0.x | f0.y | f0.z | f0.w;
+            if constexpr (NW > 4) {
+                const int4 f1 = *reinterpret_cast<const int4*>(&flg[par][4]);
+                a |= f1.x | f1.y | f1.z | f1.w;
+            }
+        } else {
+            a = flg[par][0] | flg[par][1];
+        }
+        return __builtin_amdgcn_readfirstlane(a) != 0;
+    };
+
     f32x4 o[NHB][NCB];
 #pragma unroll
     for (int h = 0; h < NHB; h++)
@@ -330,17 +353,16 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         else if (ntiles > 1) wait_vmcnt_mem<CPMAX>();
         else wait_vmcnt_mem<0>();
         lds_barrier();
-        float x[4], tm[4];
+        float x[4];
         {
             const f32x4 sv = qk(ring0);
-            tile_max(0, sv, x, tm);
+            tile_logits(0, sv, x, 0);
         }
-        *reinterpret_cast<f32x4*>(&mx[0][rb][hh]) = f32x4{tm[0], tm[1], tm[2], tm[3]};
 
         for (int t = 0; t < ntiles; t++) {
             const int par = t & 1;
             // B1: tile t+1 has landed (only tile t+2's copies may still be in
-            // flight), the maxima of tile t are visible, the slot of tile t-1 is free
+            // flight), the flags of tile t are visible, the slot of tile t-1 is free
             if (t + 2 < ntiles) wait_vmcnt_mem<CPMAX>();
             else wait_vmcnt_mem<0>();
             lds_barrier();
@@ -348,11 +370,20 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             // ---- Q K^T of tile t+1 (matrix cores) ...
             f32x4 sn = {0.f, 0.f, 0.f, 0.f};
             if (t + 1 < ntiles) sn = qk(slot_of(t + 1));
-            // ... next to the softmax of tile t (vector units)
-            {
-                const f32x4 pm = *reinterpret_cast<const f32x4*>(&mx[par][rb ^ 1][hh]);
-                float al[4];
+            // ... next to the softmax of tile t (vector units). A reference moves
+            // only when a head's tile maximum exceeds it by more than kLazyMax; the
+            // maxima are computed and exchanged between the row halves only in a
+            // tile where some wave flagged that (the same for all waves).
+            const bool rare = any_flag(par);
+            float al[4] = {1.f, 1.f, 1.f, 1.f};
+            if (rare) {
+                float tm[4];
                 bool moved = false;
+#pragma unroll
+                for (int r = 0; r < 4; r++) tm[r] = row16_max(x[r]);
+                *reinterpret_cast<f32x4*>(&mx[rb][hh]) = f32x4{tm[0], tm[1], tm[2], tm[3]};
+                lds_barrier();
+                const f32x4 pm = *reinterpret_cast<const f32x4*>(&mx[rb ^ 1][hh]);
 #pragma unroll
                 for (int r = 0; r < 4; r++) {
                     const float tmax = __builtin_fmaxf(tm[r], pm[r]);
@@ -360,31 +391,33 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
                     al[r] = mv ? __builtin_amdgcn_exp2f(m_ref[r] - tmax) : 1.f;
                     m_ref[r] = mv ? tmax : m_ref[r];
                     moved |= mv;
-                    const float p = __builtin_amdgcn_exp2f(x[r] - m_ref[r]);
-                    l_run[r] = l_run[r] * al[r] + p;
-                    *reinterpret_cast<__bf16*>(&pbuf[(hh + r) * kPStride + kn * 2]) = static_cast<__bf16>(p);
                 }
                 // both row halves compute the same alpha: every lane stores it
                 *reinterpret_cast<f32x4*>(&alpha_s[hh]) = f32x4{al[0], al[1], al[2], al[3]};
                 moved_w[w] = __ballot(moved) != 0ull;
             }
-            if (t + 1 < ntiles) {
-                tile_max(t + 1, sn, x, tm);
-                *reinterpret_cast<f32x4*>(&mx[par ^ 1][rb][hh]) = f32x4{tm[0], tm[1], tm[2], tm[3]};
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const float p = __builtin_amdgcn_exp2f(x[r] - m_ref[r]);
+                l_run[r] = __builtin_fmaf(l_run[r], al[r], p);
+                *reinterpret_cast<__bf16*>(&pbuf[(hh + r) * kPStride + kn * 2]) = static_cast<__bf16>(p);
             }
+            if (t + 1 < ntiles) tile_logits(t + 1, sn, x, par ^ 1);
             // B2: P and alpha of tile t are visible
             lds_barrier();
             // ---- O = alpha * O + P V of tile t over this wave's columns
             int any = 0;
-            if constexpr (NW >= 4) {
-                const int4 mv0 = *reinterpret_cast<const int4*>(&moved_w[0]);
-                any = mv0.x | mv0.y | mv0.z | mv0.w;
-                if constexpr (NW > 4) {
-                    const int4 mv1 = *reinterpret_cast<const int4*>(&moved_w[4]);
-                    any |= mv1.x | mv1.y | mv1.z | mv1.w;
+            if (rare) {
+                if constexpr (NW >= 4) {
+                    const int4 mv0 = *reinterpret_cast<const int4*>(&moved_w[0]);
+                    any = mv0.x | mv0.y | mv0.z | mv0.w;
+                    if constexpr (NW > 4) {
+                        const int4 mv1 = *reinterpret_cast<const int4*>(&moved_w[4]);
+                        any |= mv1.x | mv1.y | mv1.z | mv1.w;
+                    }
+                } else {
+                    any = moved_w[0] | moved_w[1];
                 }
-            } else {
-                any = moved_w[0] | moved_w[1];
             }
             if (__builtin_amdgcn_readfirstlane(any)) {
 #pragma unroll
