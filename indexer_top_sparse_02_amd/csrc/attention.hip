@@ -64,6 +64,29 @@ __device__ __forceinline__ void lds_wait(u32x2 (&a)[4], u32x2 (&b)[4]) {
                  : "memory");
 }
 
+// Eight transposing reads (as ds_read_tr16), then this wave's LDS operations
+// complete and the workgroup meets at a barrier, in one asm block: the results
+// are defined only when the block ends, after the wait, so no copy of a value
+// still in flight can be made. Used to start the value reads of P V before the
+// barrier that publishes P.
+__device__ __forceinline__ void ds_read_tr16x8_barrier(u32x2 (&a)[4], u32x2 (&b)[4], const uint32_t (&pa)[4],
+                                                       const uint32_t (&pb)[4]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\t"
+        "ds_read_b64_tr_b16 %1, %9\n\t"
+        "ds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\t"
+        "ds_read_b64_tr_b16 %4, %12\n\t"
+        "ds_read_b64_tr_b16 %5, %13\n\t"
+        "ds_read_b64_tr_b16 %6, %14\n\t"
+        "ds_read_b64_tr_b16 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)\n\t"
+        "s_barrier"
+        : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+        : "v"(pa[0]), "v"(pa[1]), "v"(pa[2]), "v"(pa[3]), "v"(pb[0]), "v"(pb[1]), "v"(pb[2]), "v"(pb[3])
+        : "memory");
+}
+
 // Byte offset of logical 16-byte chunk c of tile row r (chunks are XOR-swizzled
 // by r within aligned groups of eight).
 __device__ __forceinline__ int tile_off(int r, int c) { return r * kRowB + ((c ^ (r & 7)) << 4); }
@@ -268,8 +291,10 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         }
     }
 
-    // logits of this wave's 16 heads x 16 rows of the tile in `buf`
-    auto qk = [&](const uint8_t* buf) -> f32x4 {
+    // logits of this wave's 16 heads x 16 rows of the tile in `buf`, as two
+    // partial sums (even and odd steps) that the caller adds only where it needs
+    // them, so that the vector work in between runs while the MFMAs finish
+    auto qk = [&](const uint8_t* buf, f32x4& a0, f32x4& a1) {
         const int koff[2] = {koffL[0], koffL[1]};
         // the key operands of the next DEPTH steps are in flight during each MFMA
         constexpr int DEPTH = 6;
@@ -279,7 +304,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         u32x4 kb[DEPTH];
 #pragma unroll
         for (int i = 0; i < DEPTH; i++) kb[i] = kread(i);
-        f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        a0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        a1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
             const u32x4 kv = kb[ks % DEPTH];
@@ -295,7 +321,6 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, DEPTH, 0);
-        return a0 + a1;
     };
     const float scale_log2 = A.sm_scale * 1.4426950408889634f;
     constexpr float kLazyMax = 8.f;
@@ -355,8 +380,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         lds_barrier();
         float x[4];
         {
-            const f32x4 sv = qk(ring0);
-            tile_logits(0, sv, x, 0);
+            f32x4 s0, s1;
+            qk(ring0, s0, s1);
+            tile_logits(0, s0 + s1, x, 0);
         }
 
         for (int t = 0; t < ntiles; t++) {
@@ -368,8 +394,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             lds_barrier();
             if (t + 3 < ntiles) issue(t + 3);
             // ---- Q K^T of tile t+1 (matrix cores) ...
-            f32x4 sn = {0.f, 0.f, 0.f, 0.f};
-            if (t + 1 < ntiles) sn = qk(slot_of(t + 1));
+            f32x4 sn0 = {0.f, 0.f, 0.f, 0.f}, sn1 = {0.f, 0.f, 0.f, 0.f};
+            if (t + 1 < ntiles) qk(slot_of(t + 1), sn0, sn1);
             // ... next to the softmax of tile t (vector units). A reference moves
             // only when a head's tile maximum exceeds it by more than kLazyMax; the
             // maxima are computed and exchanged between the row halves only in a
@@ -402,9 +428,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
                 l_run[r] = __builtin_fmaf(l_run[r], al[r], p);
                 *reinterpret_cast<__bf16*>(&pbuf[(hh + r) * kPStride + kn * 2]) = static_cast<__bf16>(p);
             }
-            if (t + 1 < ntiles) tile_logits(t + 1, sn, x, par ^ 1);
-            // B2: P and alpha of tile t are visible
-            lds_barrier();
+            if (t + 1 < ntiles) tile_logits(t + 1, sn0 + sn1, x, par ^ 1);
+            // B2: P and alpha of tile t are visible. The values of the first four
+            // column blocks of tile t (in its slot since the previous iteration)
+            // are read on the way into the barrier.
+            u32x2 va0[4], vb0[4];
+            {
+                const uint32_t sb = (uint32_t)(uintptr_t)(const SIA_LDS uint8_t*)slot_of(t);
+                uint32_t pa_[4], pb_[4];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    pa_[q] = sb + voffL[0][q];
+                    pb_[q] = sb + voffL[1][q];
+                }
+                ds_read_tr16x8_barrier(va0, vb0, pa_, pb_);
+            }
             // ---- O = alpha * O + P V of tile t over this wave's columns
             int any = 0;
             if (rare) {
@@ -438,13 +476,21 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
 #pragma unroll
             for (int c0 = 0; c0 < NCB; c0 += 4) {
                 u32x2 va[4], vb2[4];
+                if (c0 == 0) {
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int cst = ((c0 + q) >> 2) * 128;
-                    va[q] = ds_read_tr16(buf + voff[0][q] + cst);
-                    vb2[q] = ds_read_tr16(buf + voff[1][q] + cst);
+                    for (int q = 0; q < 4; q++) {
+                        va[q] = va0[q];
+                        vb2[q] = vb0[q];
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const int cst = ((c0 + q) >> 2) * 128;
+                        va[q] = ds_read_tr16(buf + voff[0][q] + cst);
+                        vb2[q] = ds_read_tr16(buf + voff[1][q] + cst);
+                    }
+                    lds_wait(va, vb2);
                 }
-                lds_wait(va, vb2);
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
                     const bf16x8 vb = as_bf16x8(u32x4{va[q][0], va[q][1], vb2[q][0], vb2[q][1]});
