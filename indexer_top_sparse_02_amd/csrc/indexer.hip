@@ -859,9 +859,10 @@ __global__ __launch_bounds__(kRowsThreads) void keys_from_scores_kernel(KeysFrom
 // Appends every key >= lo of keys[0..n) (global) and its position to the LDS
 // arrays ckey / cpos, in position order. Wave w takes a contiguous segment;
 // within it, 16 steps of 256 keys (4 per lane) are in flight at once, and each
-// step's candidates are placed by a wave prefix sum. Returns the count.
-__device__ int filter_candidates(const uint32_t* keys, int n, uint32_t lo, uint32_t* ckey, int32_t* cpos,
-                                 int* wtot) {
+// step's candidates are placed by a wave prefix sum. Two passes over the keys:
+// count, then place. Returns the count.
+__device__ int filter_candidates_two_pass(const uint32_t* keys, int n, uint32_t lo, uint32_t* ckey,
+                                          int32_t* cpos, int* wtot) {
     constexpr int NW = kSelThreads / kWave, STEPS = 16, SPAN = STEPS * 256;
     const int w = threadIdx.x / kWave, l = lane_id();
     const int seg = ((n + NW - 1) / NW + SPAN - 1) / SPAN * SPAN;
@@ -918,6 +919,83 @@ __device__ int filter_candidates(const uint32_t* keys, int n, uint32_t lo, uint3
                 }
             }
             off += __shfl(inc, kWave - 1, kWave);
+        }
+    }
+    __syncthreads();
+    return total;
+}
+
+// The same result in one pass over the keys: wave w appends its segment's
+// candidates, in order, to its own region of kSelCap / NW entries; the regions
+// are then moved together in wave order (through registers, between two
+// barriers). If a segment holds more candidates than its region, the two-pass
+// form is used instead (the decision is the same in every wave).
+__device__ int filter_candidates(const uint32_t* keys, int n, uint32_t lo, uint32_t* ckey, int32_t* cpos,
+                                 int* wtot) {
+    constexpr int NW = kSelThreads / kWave, STEPS = 16, SPAN = STEPS * 256, RW = kSelCap / NW;
+    const int w = threadIdx.x / kWave, l = lane_id();
+    const int seg = ((n + NW - 1) / NW + SPAN - 1) / SPAN * SPAN;
+    const int s0 = w * seg, s1 = min(s0 + seg, n);
+    uint32_t* wk = ckey + w * RW;
+    int32_t* wp = cpos + w * RW;
+    int cnt = 0;
+    for (int b = s0; b < s1; b += SPAN) {
+        u32x4 k4[STEPS];
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            const int i = b + s * 256 + 4 * l;
+            k4[s] = i < s1 ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; s++) {
+            const int i = b + s * 256 + 4 * l;
+            int c = 0;
+#pragma unroll
+            for (int e = 0; e < 4; e++) c += (i + e < s1 && k4[s][e] >= lo);
+            const int inc = wave_incl_scan(c);
+            int at = cnt + inc - c;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                if (i + e < s1 && k4[s][e] >= lo) {
+                    if (at < RW) {
+                        wk[at] = k4[s][e];
+                        wp[at] = i + e;
+                    }
+                    at++;
+                }
+            }
+            cnt += __shfl(inc, kWave - 1, kWave);
+        }
+    }
+    if (l == 0) wtot[w] = cnt;
+    __syncthreads();
+    int off = 0, total = 0, over = 0;
+    for (int i = 0; i < NW; i++) {
+        const int c = wtot[i];
+        off += i < w ? c : 0;
+        total += c;
+        over |= c > RW;
+    }
+    if (over) {
+        __syncthreads();   // (every wave has read wtot)
+        return filter_candidates_two_pass(keys, n, lo, ckey, cpos, wtot);
+    }
+    constexpr int PER = RW / kWave;
+    uint32_t rk[PER];
+    int32_t rp[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int x = i * kWave + l;
+        rk[i] = x < cnt ? wk[x] : 0u;
+        rp[i] = x < cnt ? wp[x] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int x = i * kWave + l;
+        if (x < cnt) {
+            ckey[off + x] = rk[i];
+            cpos[off + x] = rp[i];
         }
     }
     __syncthreads();
