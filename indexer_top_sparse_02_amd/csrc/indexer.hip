@@ -925,11 +925,14 @@ __device__ int filter_candidates_two_pass(const uint32_t* keys, int n, uint32_t 
     return total;
 }
 
-// The same result in one pass over the keys: wave w appends its segment's
-// candidates, in order, to its own region of kSelCap / NW entries; the regions
-// are then moved together in wave order (through registers, between two
-// barriers). If a segment holds more candidates than its region, the two-pass
-// form is used instead (the decision is the same in every wave).
+// The same candidates in one pass over the keys: wave w appends its segment's
+// candidates, in order, to its own region of kSelCap / NW entries and clears the
+// rest of the region (key 0, which is never selected: every candidate key is at
+// least 1). The regions follow each other in wave order, so the kSelCap entries
+// list the candidates in position order with gaps; the refinement and the
+// ordered compaction skip the gaps. If a segment holds more candidates than its
+// region, the two-pass form (contiguous) is used instead; the decision is the
+// same in every wave. Returns the number of entries to scan.
 __device__ int filter_candidates(const uint32_t* keys, int n, uint32_t lo, uint32_t* ckey, int32_t* cpos,
                                  int* wtot) {
     constexpr int NW = kSelThreads / kWave, STEPS = 16, SPAN = STEPS * 256, RW = kSelCap / NW;
@@ -969,37 +972,15 @@ __device__ int filter_candidates(const uint32_t* keys, int n, uint32_t lo, uint3
     }
     if (l == 0) wtot[w] = cnt;
     __syncthreads();
-    int off = 0, total = 0, over = 0;
-    for (int i = 0; i < NW; i++) {
-        const int c = wtot[i];
-        off += i < w ? c : 0;
-        total += c;
-        over |= c > RW;
-    }
+    int over = 0;
+    for (int i = 0; i < NW; i++) over |= wtot[i] > RW;
     if (over) {
         __syncthreads();   // (every wave has read wtot)
         return filter_candidates_two_pass(keys, n, lo, ckey, cpos, wtot);
     }
-    constexpr int PER = RW / kWave;
-    uint32_t rk[PER];
-    int32_t rp[PER];
-#pragma unroll
-    for (int i = 0; i < PER; i++) {
-        const int x = i * kWave + l;
-        rk[i] = x < cnt ? wk[x] : 0u;
-        rp[i] = x < cnt ? wp[x] : 0;
-    }
+    for (int x = cnt + l; x < RW; x += kWave) wk[x] = 0u;
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PER; i++) {
-        const int x = i * kWave + l;
-        if (x < cnt) {
-            ckey[off + x] = rk[i];
-            cpos[off + x] = rp[i];
-        }
-    }
-    __syncthreads();
-    return total;
+    return NW * RW;
 }
 
 // One workgroup per query: the coarse histogram (sum of the parts') gives the
@@ -1034,8 +1015,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
         const uint32_t lo = all ? 1u : max(bin_lo, 1u);
         const int ncand = all ? total : above + (int)hist[bin];
         if (ncand <= kSelCap) {
+            // (the candidates are exactly the ncand keys the histogram counted,
+            // listed in position order within the first `got` entries)
             const int got = filter_candidates(keys, rl, lo, ckey, cpos, wtot);
-            // (got == ncand: the histogram counted exactly these keys)
             const int nc = min(got, kSelCap);
             for (int i = nc + tid; i < (nc + 7) / 8 * 8; i += kSelThreads) ckey[i] = 0u;
             __syncthreads();
