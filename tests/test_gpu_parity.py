@@ -231,6 +231,57 @@ def test_chunked_prefill_equals_single_shot(fp8):
     assert torch.equal(torch.cat(parts_lse), lse_all)
 
 
+@pytest.mark.parametrize("case", ["spec_decode", "decode_bf16", "prefill"])
+def test_graph_replay_matches_eager(case):
+    """The whole path (indexer + Top-K, then attention) captured in a HIP graph
+    and replayed several times, with eager work and synchronizations between the
+    replays: every replay reproduces the eager results bit for bit (the library
+    enqueues only its own kernels, including its counter and fill resets)."""
+    import indexer_top_sparse_02_amd as sia
+    s = _spec(case)
+    wl = W.make(s, device="cuda")
+    group = group_of(wl)
+    maxv = int(torch.minimum(wl.q_pos.long() + 1, wl.seq_lens.long()[wl.q_seq.long()]).max())
+    ws_i = sia.new_workspace(sia.indexer_workspace_size(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale,
+                                                        wl.q_seq, wl.q_pos, s.heads_idx, s.topk, group=group,
+                                                        max_visible=maxv), "cuda")
+    ws_a = sia.new_workspace(sia.mla_workspace_size(wl.num_q, s.heads_attn, s.topk), "cuda")
+    idx = torch.empty((wl.num_q, s.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.num_q, s.heads_attn, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((wl.num_q, s.heads_attn), dtype=torch.float32, device="cuda")
+
+    def step():
+        sia.sparse_indexer_topk(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq, wl.q_pos,
+                                wl.q_idx, wl.w, s.topk, group=group, max_visible=maxv, out_idx=idx,
+                                workspace=ws_i)
+        sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx, s.sm_scale,
+                                 out=out, lse=lse, workspace=ws_a)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (idx.clone(), out.clone(), lse.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        idx.fill_(-7)
+        out.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0])
+        assert torch.equal(out.view(torch.int16), ref[1].view(torch.int16))
+        assert torch.equal(lse, ref[2])
+
+
 def test_page_placement_does_not_change_results():
     s = W.spec("decode_b32", batch=3, ctx_lo=3000, ctx_hi=6000, topk=512, heads_attn=64)
     a = W.make(s, device="cuda", shuffle=False)
