@@ -32,6 +32,9 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true",
                    help="leave out the 16K causal prefill figures")
+    p.add_argument("--graph", action="store_true",
+                   help="replay every call from a HIP graph instead of launching it from the host "
+                        "(measured the same as host launches on this path)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead of the path, run a plain device copy of this many bytes "
                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -143,11 +146,17 @@ def cpu_baseline(wl_gpu, s, budget_s: float = 12.0):
 METRIC = "decode queries/s and HBM GB/s at 128K ctx; prefill tokens/s (indexer+TopK+sparse attn)"
 
 
+GRAPH = False   # replay each call from a HIP graph (set from --graph)
+
+
 def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True):
     """Times `steps` passes of the whole path (indexer + Top-K, then sparse
     attention) with HIP events on the stream the library runs on. Returns the
     indices of the last pass, ms per step and ms per phase. `sched` picks the
-    causal prefill tile schedule (-1: the library's default)."""
+    causal prefill tile schedule (-1: the library's default). With GRAPH, each
+    call is captured once into a HIP graph after the eager warmup and the timed
+    steps replay the graphs (the same kernels and arguments, without the host
+    launch path); the events sit between the replays."""
     import torch
     dev = wl.q_idx.device
     maxv = int(torch.minimum(wl.q_pos.long() + 1, wl.seq_lens.long()[wl.q_seq.long()]).max())
@@ -170,10 +179,25 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True):
             sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx,
                                      s.sm_scale, out=out, lse=lse, workspace=ws_a)
 
-    for _ in range(warmup):
+    for _ in range(max(1, warmup)):
         indexer()
         attention()
     torch.cuda.synchronize()
+    if GRAPH:
+        g_idx = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_idx):
+            indexer()
+        indexer = g_idx.replay
+        if attention_too:
+            g_att = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_att):
+                attention()
+            attention = g_att.replay
+        torch.cuda.synchronize()
+        for _ in range(max(1, warmup)):
+            indexer()
+            attention()
+        torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
@@ -229,7 +253,7 @@ def prefill_line(wl, s, steps, warmup):
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) caches and queries, shuffled page table)",
         "config": {"workload": s.name, "tokens": wl.num_q, "indexer_heads": s.heads_idx,
                    "index_dim": s.dim_idx, "topk": s.topk, "attention_heads": s.heads_attn,
-                   "page_size": 64},
+                   "page_size": 64, "launch": "hip graph per call" if GRAPH else "eager"},
         "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
         "indexer_schedule_ms": sched_ms,
         "algorithmic_tflop": {"indexer": f_idx / 1e12, "attention": f_att / 1e12},
@@ -276,7 +300,7 @@ def chunked_line(wl, s, steps, warmup):
                                  "latent KV and queries, shuffled page table)",
         "config": {"workload": s.name, "tokens": wl.num_q, "chunk": s.chunk, "indexer_heads": s.heads_idx,
                    "index_dim": s.dim_idx, "topk": s.topk, "attention_heads": s.heads_attn,
-                   "page_size": 64},
+                   "page_size": 64, "launch": "hip graph per call" if GRAPH else "eager"},
         "phases_ms": {"indexer_topk": tot_i, "attention": tot_a},
         "algorithmic_tflop": {"indexer": f_i_all / 1e12, "attention": f_a_all / 1e12},
         "mfma_frac_step": (f_i_all + f_a_all) / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -302,6 +326,8 @@ def main():
     import indexer_top_sparse_02_amd as sia
     import workloads as W
 
+    global GRAPH
+    GRAPH = a.graph
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     s = W.spec(a.config)
@@ -332,7 +358,8 @@ def main():
         "data": "synthetic (seeded N(0,1) caches and queries, shuffled page tables)",
         "config": {"workload": s.name, "batch": s.batch, "context": s.ctx_hi,
                    "query_tokens": wl.num_q, "indexer_heads": s.heads_idx, "index_dim": s.dim_idx,
-                   "topk": s.topk, "attention_heads": s.heads_attn, "page_size": 64},
+                   "topk": s.topk, "attention_heads": s.heads_attn, "page_size": 64,
+                   "launch": "hip graph per call" if GRAPH else "eager"},
         "hbm_gbs_step": step_gbs,
         "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
         "algorithmic_bytes": by,
