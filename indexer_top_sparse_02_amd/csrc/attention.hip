@@ -15,12 +15,15 @@
 // are free of bank conflicts. Wave (hb, rb) owns 16 heads and the 16-row half rb
 // of every tile:
 //   Q K^T    16x16x32 MFMAs over all 576 columns; its Q slice stays in registers
-//   softmax  online, per head; the two row halves of a head block exchange only
-//            their per-head tile maxima through LDS; P goes to LDS as bf16
+//   softmax  online, per head, against a reference maximum that moves only when
+//            a logit exceeds it by more than 2^8; only in such a tile do the two
+//            row halves of a head block compute and exchange per-head tile
+//            maxima through LDS; P goes to LDS as bf16
 //   P V      wave w owns output columns [w*512/NW, (w+1)*512/NW) of all heads;
 //            the value operand is read from the same row-major tile with
 //            transposing LDS reads (ds_read_b64_tr_b16), so no transposed copy
-//            of the values is ever made
+//            of the values is ever made; the first reads go out before the
+//            barrier that publishes P
 // The loop is software-pipelined: between two barriers, iteration t runs the
 // Q K^T of tile t+1 next to the softmax of tile t, then P V of tile t. The copy of
 // tile t+3 goes out as soon as the slot of tile t-1 is free, so two tiles (72 KB)

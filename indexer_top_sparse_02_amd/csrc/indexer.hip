@@ -5,9 +5,10 @@
 // The q . k products of one query against 32 positions are one MFMA tile:
 // heads are the M dimension (32 per block), positions the N dimension, the
 // index dim the K dimension. Queries sit in registers for the whole pass; a
-// lane supplies its position's half-row of index-K, staged through LDS by the
-// decode score passes and loaded straight from the paged pool by the stream
-// kernel. The accumulator puts 16 heads of one position in each lane, so the
+// lane supplies its position's half-row of index-K, staged through LDS by
+// direct global -> LDS copies (a private ring per team in the decode score pass,
+// one ring shared by the four queries of a workgroup in the stream kernel). The
+// accumulator puts 16 heads of one position in each lane, so the
 // ReLU, the head weights and the head sum stay in registers with a single
 // cross-lane add, and sigma_s multiplies the sum ("Rapid Adaptation and
 // Inference Optimization", section 4.1 "Indexer Fusion": the indexer reads the
@@ -19,10 +20,12 @@
 //    rows (two draft tokens of a sequence share every copy) and writes one
 //    4-byte order-preserving key per visible position plus a coarse histogram
 //    per part; the selection pass takes each row's exact Top-K from its keys.
-//  * prefill, stream: one wave walks one query's whole causal row, appending
-//    positions that beat the current threshold to an LDS buffer kept in position
-//    order, and re-selecting the Top-K when the buffer fills. A position that
-//    ties the threshold arrives after every kept one, so it can be dropped.
+//  * prefill, stream: one wave walks one query's whole causal row (the four
+//    waves of a workgroup walk four consecutive queries over one shared ring of
+//    K tiles), appending positions that beat the current threshold to an LDS
+//    buffer kept in position order, and re-selecting the Top-K when the buffer
+//    fills. A position that ties the threshold arrives after every kept one, so
+//    it can be dropped.
 #include "sia_device.h"
 #include "sia_kernels.h"
 #include "sia_sched.h"
