@@ -1176,14 +1176,16 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             }
         };
         constexpr int NMFMA = MB * (FP8 ? 2 * (D / 64) : D / 16);   // MFMAs per tile
-        // Tiles 0 .. NS-1 go out first. Iteration k: the MFMAs of tile k+1 (its
-        // operands read from LDS one iteration earlier) run interleaved with the
+        // Tiles 0 .. NS-1 go out first. Step k: the MFMAs of tile k+1 (its
+        // operands read from LDS one step earlier) run interleaved with the
         // epilogue of tile k (ReLU, head weights, head sum, key, append), while the
-        // operands of tile k+2 are read; tile k's slot, read two iterations back,
-        // takes tile k+NS.
+        // operands of tile k+2 are read. The waves meet every second step: at an
+        // even step k, tiles k+2 and k+3 have landed and become visible, and the
+        // slots of tiles k and k+1 (read at steps k-2 and k-1) take tiles k+NS and
+        // k+NS+1; each copy still goes out two steps before it is read.
 #pragma unroll
         for (int k = 0; k < NS; k++) issue(k, copy_page(k));
-        int pg_issue = copy_page(NS);                 // page of the next copy
+        int cp_a = copy_page(NS), cp_b = copy_page(NS + 1);   // pages of the next copies
         wait_vmcnt_mem<(NS - 2) * SG::PER_TILE>();   // tiles 0 and 1 have landed
         lds_barrier();
         // tb holds the operands of the next tile to multiply; A0 / A1 alternate as
@@ -1198,14 +1200,19 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         bool ok_c = tb.ok;
         int pg_c = pg_b;
         fetch(1, tb, pg_b);
-        auto step = [&](int k, f32x16 (&cur)[MB], f32x16 (&nxt)[MB]) {
+        auto step = [&](int k, f32x16 (&cur)[MB], f32x16 (&nxt)[MB], bool sync) {
             reselect();
-            // tile k+2 has landed (the copies of tiles k+3 .. k+NS-1 may still be in
-            // flight); after the barrier every wave's part of it is visible
-            wait_vmcnt_mem<(NS - 3) * SG::PER_TILE>();
-            lds_barrier();
-            issue(k + NS, pg_issue);
-            pg_issue = copy_page(k + NS + 1);
+            if (sync) {
+                // tiles k+2 and k+3 have landed (the copies of tiles k+4 .. k+NS-1
+                // may still be in flight); after the barrier every wave's part of
+                // them is visible
+                wait_vmcnt_mem<(NS - 4) * SG::PER_TILE>();
+                lds_barrier();
+                issue(k + NS, cp_a);
+                issue(k + NS + 1, cp_b);
+                cp_a = copy_page(k + NS + 2);
+                cp_b = copy_page(k + NS + 3);
+            }
             tile_mfma<MB, D, FP8>(q, tb, nxt);   // tile k+1
             const float sc_n = tb.sc;
             const bool ok_n = tb.ok;
@@ -1219,8 +1226,8 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             pg_c = pg_n;
         };
         for (int k = 0; k < nt; k += 2) {
-            step(k, A0, A1);
-            if (k + 1 < nt) step(k + 1, A1, A0);
+            step(k, A0, A1, true);
+            if (k + 1 < nt) step(k + 1, A1, A0, false);
         }
         wait_vmcnt_mem<0>();
     }
