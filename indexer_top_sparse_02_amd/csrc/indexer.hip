@@ -1162,16 +1162,42 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         // re-selects inside the buffer once it may not take another tile
         auto reselect = [&]() {
             if (cnt > S.cap - 32) {
-                // keep exactly the Top-K seen so far; later ties of T lose to them
+                // keep the Top-K seen so far (or a superset of it); later keys
+                // equal to the new threshold lose to the kept ones
                 wave_sync();
                 int ties;
                 const int n4 = (cnt + 3) & ~3;
                 for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
                 wave_sync();
-                const uint32_t T = radix_threshold<kWave>(B.key, n4, S.topk, B.sel, ties);
-                ordered_compact<kWave, true>(B.key, n4, T, ties, B.sel, EmitInPlace{B.key, B.pos, {}});
-                cnt = S.topk;
-                tau = T;
+                // After the first re-selection the buffered keys lie close
+                // together, and a superset of the Top-K is usually enough: every
+                // key >= L, L found in one histogram pass, with later keys appended
+                // only when above L (at least K kept keys >= L precede them). The
+                // exact threshold is taken on the first re-selection (keys spread
+                // over the whole score range) and when the superset would leave
+                // too little room.
+                bool done = false;
+                uint32_t T = 0u, pm = 0u;
+                int above = 0, low = 32;
+                if (tau != 0u) {
+                    int kept;
+                    const uint32_t L = wave_select_floor(B.key, n4, S.topk, B.sel, kept, pm, above, low);
+                    if (L != 0u && kept <= S.topk + (S.cap - S.topk) / 2) {
+                        ordered_compact<kWave, true>(B.key, n4, L, 0x7fffffff, B.sel, EmitInPlace{B.key, B.pos, {}});
+                        cnt = kept;
+                        tau = L;
+                        done = true;
+                    }
+                    T = L;
+                }
+                if (!done) {
+                    // exact: the bits under pm are settled (none on the first
+                    // re-selection), the rest is refined
+                    T = radix_refine<kWave>(B.key, n4, T, pm, S.topk - above, low, B.sel, ties);
+                    ordered_compact<kWave, true>(B.key, n4, T, ties, B.sel, EmitInPlace{B.key, B.pos, {}});
+                    cnt = S.topk;
+                    tau = T;
+                }
                 wave_sync();
             }
         };

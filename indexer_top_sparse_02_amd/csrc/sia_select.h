@@ -103,6 +103,82 @@ __device__ uint32_t radix_threshold(const uint32_t* keys, int n, int m, SelScrat
     return radix_refine<NT>(keys, n, 0u, 0u, m, 32, s, ties);
 }
 
+// One wave, a superset of the Top-m in one histogram pass. The leading bits on
+// which the AND and the OR of all nonzero keys agree are shared by every key; one
+// histogram of the (up to) 8 bits below them finds the digit b of the m-th largest
+// key. Every key whose digit is at least b, i.e. every key >= L = shared bits | b,
+// is at least as large as the m-th largest, so keeping them keeps the Top-m (and
+// at least m keys). Returns L (0 when all nonzero keys are to be kept) and sets
+// `kept` to the number of nonzero keys >= L. keys: LDS, readable in groups of four
+// (16-byte aligned, entries past n may hold anything); callers pass 1 <= m <= the
+// number of nonzero keys. For an exact threshold from there, `pmask_out` and
+// `above` give the settled bits and the number of keys above digit b, and `low`
+// the number of bits still open (the arguments radix_refine continues from).
+__device__ uint32_t wave_select_floor(const uint32_t* keys, int n, int m, SelScratch* s, int& kept,
+                                     uint32_t& pmask_out, int& above_out, int& low) {
+    const int l = lane_id();
+    uint32_t a = ~0u, o = 0u;
+    for (int i = l * 4; i < n; i += kWave * 4) {
+        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const uint32_t k = k4[e];
+            if (i + e < n && k != 0u) {
+                a &= k;
+                o |= k;
+            }
+        }
+    }
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1) {
+        a &= (uint32_t)__shfl_xor((int)a, d, kWave);
+        o |= (uint32_t)__shfl_xor((int)o, d, kWave);
+    }
+    const uint32_t diff = a ^ o;
+    const int lead = diff == 0u ? 32 : __builtin_clz(diff);   // shared leading bits
+    const int width = 32 - lead < 8 ? 32 - lead : 8;
+    const int shift = 32 - lead - width;
+    const uint32_t dmask = (1u << width) - 1u;   // (width 0: every key in digit 0)
+    const uint32_t pmask = lead == 0 ? 0u : ~0u << (32 - lead);
+    for (int i = l; i < 256; i += kWave) s->hist[i] = 0;
+    wave_sync();
+    for (int i = l * 4; i < n; i += kWave * 4) {
+        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const uint32_t k = k4[e];
+            hist_add(s->hist, (k >> shift) & dmask, i + e < n && k != 0u);
+        }
+    }
+    wave_sync();
+    {
+        // lane l owns bins 255-4l .. 252-4l (descending)
+        int c[4];
+        int tot = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) { c[e] = (int)s->hist[255 - (4 * l + e)]; tot += c[e]; }
+        const int inc = wave_incl_scan(tot);
+        int above = inc - tot;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            if (above < m && above + c[e] >= m) {
+                s->bcast[0] = 255 - (4 * l + e);
+                s->bcast[1] = above + c[e];
+                s->bcast[2] = above;
+            }
+            above += c[e];
+        }
+    }
+    wave_sync();
+    const uint32_t b = (uint32_t)s->bcast[0];
+    kept = s->bcast[1];
+    above_out = s->bcast[2];
+    wave_sync();
+    pmask_out = pmask | (dmask << shift);
+    low = shift;
+    return (a & pmask) | (b << shift);
+}
+
 // Top bits of a key used for the coarse histogram (11 bits: sign, exponent and
 // two mantissa bits of the score, i.e. quarter-octave bins).
 constexpr int kCoarseBits = 11;
