@@ -195,6 +195,47 @@ def test_stream_path_exact_selection(dim, fp8, heads, layout):
     assert np.array_equal(g_top[g_idx >= 0], ref_sc[g_idx >= 0])
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_stream_reselection_on_rising_scores(fp8):
+    """Scores that rise along the row (one head, q = e_0, the key's first element
+    rising in steps shared by seven positions) make every position beat the
+    running threshold of the streaming Top-K, so its candidate buffer fills and
+    is re-selected again and again, mostly by the one-pass superset rule, with
+    ties at every step. Indices and scores must be the oracle's selection of the
+    GPU's own scores, bit for bit, and the scores are exactly the key values."""
+    s = W.spec("prefill_16k", ctx_lo=6000, ctx_hi=6000, topk=256, idx_fp8=fp8, heads_attn=16)
+    wl = W.make(s, device="cuda", poison=True, with_attn=False)
+    n = 6000
+    pos = torch.arange(n, device="cuda")
+    val = (pos // 7).float() / 64.0 + 0.25
+    phys = wl.page_table[0].long()[pos // 64] * 64 + pos % 64
+    flat = wl.idx_k.view(-1, s.dim_idx)
+    row = torch.zeros((n, s.dim_idx), device="cuda", dtype=torch.float32)
+    row[:, 0] = val
+    if fp8:
+        flat[phys] = row.to(torch.float8_e4m3fn).view(torch.uint8)
+        wl.idx_scale.view(-1)[phys] = 1.0
+        key0 = row[:, 0].to(torch.float8_e4m3fn).float()
+    else:
+        flat[phys] = row.to(torch.bfloat16)
+        key0 = row[:, 0].to(torch.bfloat16).float()
+    wl.q_idx.zero_()
+    wl.q_idx[:, 0, 0] = 1.0
+    wl.w.zero_()
+    wl.w[:, 0] = 1.0
+    sc = gpu_scores(wl)
+    rl = row_lengths(wl)
+    last = sc[n - 1, :n].cpu()
+    assert torch.equal(last, key0.cpu())
+    with env(SIA_INDEXER_PATH=2):
+        got, top = gpu_topk(wl)
+    ref, ref_sc = oracle_topk_of(sc, rl, s.topk)
+    g_idx = got.cpu().numpy()
+    assert np.array_equal(g_idx, ref)
+    g_top = top.cpu().numpy().astype(np.float64)
+    assert np.array_equal(g_top[g_idx >= 0], ref_sc[g_idx >= 0])
+
+
 @pytest.mark.parametrize("sched", [0, 1, 2])
 def test_prefill_schedules_agree(sched):
     s = W.spec("prefill_16k", ctx_lo=1500, ctx_hi=1500, topk=128, idx_fp8=True)
