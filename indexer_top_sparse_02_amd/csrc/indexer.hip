@@ -385,10 +385,10 @@ struct EmitFinalBuf {
     }
 };
 
-// Select the top min(m_cap, nonzero) of keys[0..n) and emit them in index order.
+// Select the top min(m_cap, cnt) of keys[0..n) and emit them in index order;
+// cnt = the number of nonzero keys, known to the caller.
 template <int NT, typename Emit>
-__device__ int select_emit(const uint32_t* keys, int n, int m_cap, SelScratch* s, Emit&& emit) {
-    const int cnt = count_nonzero<NT>(keys, n, s);
+__device__ int select_emit(const uint32_t* keys, int n, int cnt, int m_cap, SelScratch* s, Emit&& emit) {
     const int m = min(m_cap, cnt);
     if (m <= 0) return 0;
     if (m == cnt) {
@@ -1264,7 +1264,9 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         const int n4 = (cnt + 3) & ~3;
         for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
         wave_sync();
-        const int m = select_emit<kWave>(B.key, n4, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}});
+        // (the buffer's first cnt entries are its nonzero keys: only keys above
+        // tau >= 0 are appended, and the re-selections keep nonzero keys)
+        const int m = select_emit<kWave>(B.key, n4, cnt, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}});
         for (int r = m + l; r < S.topk; r += kWave) {
             oi[r] = -1;
             if (os) os[r] = -INFINITY;

@@ -263,30 +263,6 @@ __device__ void ordered_compact(const uint32_t* keys, int n, uint32_t T, int tie
     }
 }
 
-// Count of nonzero keys among keys[0..n).
-template <int NT>
-__device__ int count_nonzero(const uint32_t* keys, int n, SelScratch* s) {
-    const int tid = sel_tid<NT>();
-    int c = 0;
-    for (int i = tid * 4; i < n; i += NT * 4) {
-        u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
-#pragma unroll
-        for (int e = 0; e < 4; e++) c += (i + e < n && k4[e] != 0u);
-    }
-    c = wave_sum(c);
-    if constexpr (NT == kWave) {
-        return c;
-    } else {
-        const int w = threadIdx.x / kWave;
-        if (lane_id() == 0) s->scan[w] = c;
-        __syncthreads();
-        int tot = 0;
-        for (int i = 0; i < NT / kWave; i++) tot += s->scan[i];
-        __syncthreads();
-        return tot;
-    }
-}
-
 // Select the top min(m_cap, nonzero) of keys[0..n) given `hist`, the coarse
 // histogram of exactly the nonzero keys, and emit them in index order.
 template <int NT, typename Emit>
