@@ -1002,10 +1002,32 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
     const int rl = max(0, min(S.row_len[j], S.max_len));
     int32_t* oi = S.out_idx + (int64_t)j * S.topk;
     float* os = S.out_score ? S.out_score + (int64_t)j * S.topk : nullptr;
-    for (int b = tid; b < kCoarseBins; b += kSelThreads) {
-        uint32_t c = 0;
-        for (int p = 0; p < S.n_parts; p++) c += S.hist[((int64_t)j * S.n_parts + p) * kCoarseBins + b];
-        hist[b] = c;
+    // the row's coarse histogram: the sum of its parts' (both bins of a thread,
+    // four parts at a time, so that the loads go out together)
+    static_assert(kCoarseBins == 2 * kSelThreads, "two coarse bins per thread");
+    {
+        const uint32_t* h = S.hist + (int64_t)j * S.n_parts * kCoarseBins + tid;
+        uint32_t c0 = 0, c1 = 0;
+        int p = 0;
+        for (; p + 4 <= S.n_parts; p += 4) {
+            uint32_t v[8];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                v[2 * i] = h[(int64_t)(p + i) * kCoarseBins];
+                v[2 * i + 1] = h[(int64_t)(p + i) * kCoarseBins + kSelThreads];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                c0 += v[2 * i];
+                c1 += v[2 * i + 1];
+            }
+        }
+        for (; p < S.n_parts; p++) {
+            c0 += h[(int64_t)p * kCoarseBins];
+            c1 += h[(int64_t)p * kCoarseBins + kSelThreads];
+        }
+        hist[tid] = c0;
+        hist[tid + kSelThreads] = c1;
     }
     __syncthreads();
     int above, total;
