@@ -8,12 +8,18 @@
  *   stage 1  sparse_indexer_topk   -- a lightweight indexer scores every visible
  *            historical position against the query by reading the paged index-K
  *            cache directly, combines its heads with per-token head weights and
- *            keeps the Top-K positions, all in one fused pass that writes only
- *            the selected indices ("Rapid Adaptation and Inference Optimization:
- *            Key Engineering Practices for Day0 LLM Support", section 4.1
- *            "Indexer Fusion"; "Day0 Inference Adaptation and Performance
- *            Optimization for New-Architecture LLMs", section 3.1 "Fused
- *            Indexer").
+ *            keeps the Top-K positions ("Rapid Adaptation and Inference
+ *            Optimization: Key Engineering Practices for Day0 LLM Support",
+ *            section 4.1 "Indexer Fusion"; "Day0 Inference Adaptation and
+ *            Performance Optimization for New-Architecture LLMs", section 3.1
+ *            "Fused Indexer"). No score ever reaches memory. Long causal rows
+ *            (prefill) take one fused pass that writes only the selected
+ *            indices. Decode rows, which a single workgroup cannot stream fast
+ *            enough, are split over workgroups: a scoring pass keeps, per part of
+ *            a row, only the positions whose score reaches a running floor (the
+ *            part's K-th largest so far, at coarse granularity) and appends them
+ *            with their keys to the workspace; a selection pass then takes the
+ *            exact Top-K of those candidates.
  *   stage 2  sparse_mla_attention -- gathers only the selected rows of the paged
  *            latent (MLA) KV cache and runs softmax attention over them
  *            ("Rapid Adaptation ...", section 4.2 "Sparse Attention
@@ -38,10 +44,14 @@
  *    argument returns a negative sia_status, sets sia_last_error() and launches
  *    nothing. A failed launch returns SIA_ERR_HIP.
  *  - Device data that the host cannot see (page ids, sequence ids of queries,
- *    positions) is bounds-checked by the kernels: an out-of-range page or
- *    sequence id is never dereferenced; the affected query yields -1 indices
- *    (stage 1) or a zero output (stage 2) and a bit is set in the status word
- *    at the start of the workspace, readable with sia_read_device_status().
+ *    positions, stage-2 indices) is bounds-checked by the kernels and never
+ *    dereferenced when out of range; a bit is set in the status word at the
+ *    start of the workspace, readable with sia_read_device_status():
+ *      - a query whose sequence id is outside [0, batch): stage 1 selects
+ *        nothing (all -1), stage 2 gives a zero output and lse = -inf;
+ *      - a page id outside [0, num_pages): stage 1 drops the positions on
+ *        that page (they are never selected), stage 2 skips the rows on it;
+ *      - a stage-2 index >= n_b: the entry is skipped.
  *  - Paged caches: row r of physical page p sits at
  *    rows + ((size_t)p * page_size + r) * dim * element_size; the page size is
  *    64. Logical position s of sequence b lives on physical page
@@ -133,8 +143,8 @@ size_t sia_indexer_workspace_size(const sia_page_table *pt, const sia_paged_cach
  *   out_idx   device int32 [num_q, topk]        selected logical positions, ascending, -1 padded
  *   out_score device fp32 [num_q, topk] or NULL scores of out_idx entries (-inf for padding)
  *   sched     sia_sched for long causal rows; results do not depend on it
- * Supported: heads in {4, 8, 16, 32, 64}, dim in {64, 128}, index_k dtype bf16 or
- * fp8 e4m3fn, page size 64.
+ * Supported: 1 <= heads <= 64, dim in {64, 128}, index_k dtype bf16 or fp8
+ * e4m3fn, page size 64.
  */
 int sparse_indexer_topk(const sia_page_table *pt, const sia_paged_cache *index_k,
                         const sia_queries *qs, const void *q_idx, const float *w,

@@ -17,9 +17,12 @@
 // Launch shapes (all score through tile_mfma + tile_epilogue, so a query and a
 // position give the same bits everywhere, and all select with sia_select.h):
 //  * decode, score pass + selection pass: the score pass streams parts of the
-//    rows (two draft tokens of a sequence share every copy) and writes one
-//    4-byte order-preserving key per visible position plus a coarse histogram
-//    per part; the selection pass takes each row's exact Top-K from its keys.
+//    rows (two draft tokens of a sequence share every copy). A position's
+//    order-preserving key is kept only if it reaches the part's running floor
+//    (the coarse bin of the part's K-th largest kept key, raised as the pass
+//    goes); kept keys and positions are appended to per-team candidate lists,
+//    with a coarse histogram per part. No per-position score or key is
+//    written. The selection pass takes each row's exact Top-K from its lists.
 //  * prefill, stream: one wave walks one query's whole causal row (the four
 //    waves of a workgroup walk four consecutive queries over one shared ring of
 //    K tiles), appending positions that beat the current threshold to an LDS
@@ -440,7 +443,8 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
     constexpr int SLOT = GM::SLOT, NV = KTile<D, FP8>::NV;
     __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NWV * SLOT];
     __shared__ int pages[kMaxPartPages];
-    __shared__ uint32_t hist[SCORES ? 1 : G * kCoarseBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[SCORES ? 4 : G * kCoarseBins];
+    __shared__ uint32_t floor_key[G];   // keys below it are not kept (>= 1)
 
     const int g = blockIdx.x / S.n_parts;
     const int part = blockIdx.x % S.n_parts;
@@ -476,8 +480,10 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
     const int nvalid = max(0, min(S.part, rlmax - pos0));
     const int npg = (nvalid + kPage - 1) / kPage;
     for (int i = threadIdx.x; i < npg; i += kRowsThreads) pages[i] = page_of(A, b0, pos0 / kPage + i);
-    if constexpr (!SCORES)
+    if constexpr (!SCORES) {
         for (int i = threadIdx.x; i < G * kCoarseBins; i += kRowsThreads) hist[i] = 0u;
+        if (threadIdx.x < G) floor_key[threadIdx.x] = 1u;
+    }
     __syncthreads();
 
     // this wave's run: tiles t0 .. t0 + n - 1 of the part (an even count per wave,
@@ -489,6 +495,8 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
     const int t0 = sub * tpw;
     const int n = max(0, min(tpw, my_tiles - t0));
     const int64_t rowbase = (int64_t)j * S.ld + pos0;
+    const int rbase = pos0 + t0 * 32;   // first entry of this wave's candidate region
+    int cnt = 0;                        // candidates appended
 
     if (n > 0) {
         // copy r of a tile moves the 16-byte piece gi = 64 r + lane: row gi / CPR,
@@ -533,9 +541,9 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
             if constexpr (FP8)
                 t.sc = *reinterpret_cast<const float*>(slot + w * SLOT + GM::TILE + 4 * (((t0 + k) & 1) * 32 + frow));
             else t.sc = 1.f;
-            // (positions on a page whose id is out of range are scored from page 0;
-            // the call reports the bad id through the status word)
-            t.ok = (t0 + k) * 32 + frow < my_valid;
+            // (a position on a page whose id is out of range was copied from page 0;
+            // it is not visible, and the call reports the bad id in the status word)
+            t.ok = (t0 + k) * 32 + frow < my_valid && pages[(t0 + k) >> 1] >= 0;
         };
         // Epilogue of the wave's kk-th tile. kk outside [0, n) is a padding step
         // (the last tile again, or the step before the first): its keys go to the
@@ -549,13 +557,20 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
                 asm volatile("" ::"v"(sc));
                 if (l < 32 && tok && valid) S.scores[rowbase + (t0 + kk) * 32 + frow] = sc;
             } else {
-                const uint32_t key = score_key(sc) & (0u - (uint32_t)(tok && valid));
-                // (a scalar select of the row base: no branch in the loop body)
-                const int64_t base = valid ? rowbase + (t0 + kk) * 32 : (int64_t)j * S.ld + S.ld - 64;
-                S.keys[base + frow] = key;   // both lane halves hold the same key
-                // lanes 32..63 add 0 to distinct bins (no conflicts)
-                atomicAdd(&hist[qi * kCoarseBins + (l < 32 ? coarse_bin(key) : (uint32_t)l)],
-                          (l < 32 && key != 0u) ? 1u : 0u);
+                // lanes 0..31 keep their position's key if it reaches the floor
+                // (lanes 32..63 hold the same keys and keep none); a lane that
+                // keeps nothing writes to the row's spare tail (no branch in the
+                // loop body)
+                const uint32_t key = score_key(sc) & (0u - (uint32_t)(tok && valid && l < 32));
+                const bool take = key >= floor_key[qi];
+                const uint64_t mask = __ballot(take);
+                const int64_t at = take ? (int64_t)j * S.ld + rbase + cnt + lanes_below(mask)
+                                        : (int64_t)j * S.ld + S.ld - 64 + frow;
+                S.cand_key[at] = key;
+                S.cand_pos[at] = pos0 + (t0 + kk) * 32 + frow;
+                // lanes that keep nothing add 0 to distinct bins (no conflicts)
+                atomicAdd(&hist[qi * kCoarseBins + (take ? coarse_bin(key) : (uint32_t)l)], take ? 1u : 0u);
+                cnt += __popcll(mask);
             }
         };
 
@@ -592,12 +607,21 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
                 wait_vmcnt_mem<(NS - 2) * GM::PER_TILE>();   // tile k + 1 has landed
                 fetch(min(k + 1, n - 1), (u + 1) % NS, t);
             }
+            if constexpr (!SCORES) {
+                // the waves take turns raising the floor from the part's histogram
+                if ((k0 / U) % WPQ == sub) {
+                    int b0, b1;
+                    coarse_floor<false>(hist + qi * kCoarseBins, S.topk, b0, b1);
+                    if (l == 0) floor_key[qi] = max((uint32_t)b0 << (32 - kCoarseBits), 1u);
+                }
+            }
         }
         // last step of the padded run: its parity is that of U (even)
         finish(((n + U - 1) / U) * U - 1, acc1, sc1, ok1, q);
         wait_vmcnt_mem<0>();
     }
     if constexpr (!SCORES) {
+        if (j < A.num_q && l == 0) S.reg[(int64_t)j * S.n_reg + part * WPQ + sub] = make_int2(rbase, cnt);
         __syncthreads();
         for (int i = 0; i < G; i++) {
             const int jj = g * G + i;
@@ -664,8 +688,9 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
     __shared__ int pages[kPairPartPages];
     // the part's coarse histograms, query 0 in the low and query 1 in the high
     // 16 bits of each counter (a part has at most 32768 positions)
-    __shared__ uint32_t hist[SCORES ? 1 : kCoarseBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[SCORES ? 4 : kCoarseBins];
     __shared__ float xch[2][NTEAM][kWave];   // copier block sums, by step parity
+    __shared__ uint32_t floor_key[2];        // per query: keys below it are not kept (>= 1)
 
     const int g = blockIdx.x / S.n_parts;
     const int part = blockIdx.x % S.n_parts;
@@ -674,6 +699,8 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
     const int l = lane_id(), half = l >> 5, frow = l & 31;
     const int pos0 = part * S.part;
     const int j0 = 2 * g, j1 = 2 * g + 1;
+    const int j1s = j1 < A.num_q ? j1 : j0;   // (an odd last query has no partner: its
+                                              // half of the work keeps nothing)
 
     // both queries must name one sequence; a second query naming another is
     // dropped (status bit)
@@ -699,8 +726,10 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
     const int nvalid = max(valid0, valid1);
     const int npg = (nvalid + kPage - 1) / kPage;
     for (int i = threadIdx.x; i < npg; i += kPairThreads) pages[i] = page_of(A, b0, pos0 / kPage + i);
-    if constexpr (!SCORES)
+    if constexpr (!SCORES) {
         for (int i = threadIdx.x; i < kCoarseBins; i += kPairThreads) hist[i] = 0u;
+        if (threadIdx.x < 2) floor_key[threadIdx.x] = 1u;
+    }
     __syncthreads();
 
     // the team's run of tiles (an even count, so that a run starts on a page);
@@ -711,6 +740,8 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
     const int t0 = team * tpw;
     const int n = max(0, min(tpw, ntiles - t0));
     const int nloop = (min(tpw, ntiles) + U - 1) / U * U;
+    const int rbase = pos0 + t0 * 32;   // first entry of the team's candidate regions
+    int cnt0 = 0, cnt1 = 0;             // candidates appended per query (finisher)
 
     if (nloop > 0) {
         uint32_t voff[GM::DMA];
@@ -755,20 +786,32 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             else t.sc = 1.f;
         };
         // finisher: lanes 0..31 hold query 0 of step kq, lanes 32..63 query 1 of
-        // step kq - 1; padding steps go to the key row's spare tail
+        // step kq - 1. A key that reaches its query's floor is appended to the
+        // query's candidate list of this team; a lane that keeps nothing (padding
+        // steps included) writes to the row's spare tail, so the loop body has no
+        // branch. Positions on a page whose id is out of range were copied from
+        // page 0 and are dropped.
         auto finish = [&](int kq, float v, float tsc) {
             const float sc = FP8 ? v * tsc : v;
             const int kk = half ? kq - 1 : kq;
             const bool in_run = kk >= 0 && kk < n;
-            const bool tok = in_run && (t0 + kk) * 32 + frow < (half ? valid1 : valid0);
-            const int64_t row = (int64_t)(half ? j1 : j0) * S.ld;
+            const int tpos = (t0 + kk) * 32 + frow;   // position within the part
+            const bool tok = in_run && tpos < (half ? valid1 : valid0) && pages[tile_of(kk) >> 1] >= 0;
+            const int64_t row = (int64_t)(half ? j1s : j0) * S.ld;
             if constexpr (SCORES) {
-                if (tok) S.scores[row + pos0 + (t0 + kk) * 32 + frow] = sc;
+                if (tok) S.scores[row + pos0 + tpos] = sc;
             } else {
                 const uint32_t key = score_key(sc) & (0u - (uint32_t)tok);
-                const int64_t o = in_run ? row + pos0 + (t0 + kk) * 32 + frow : row + S.ld - 64 + frow;
-                S.keys[o] = key;
-                atomicAdd(&hist[coarse_bin(key)], key == 0u ? 0u : (half ? 0x10000u : 1u));
+                const bool take = key >= floor_key[half];
+                const uint64_t mask = __ballot(take);
+                const uint32_t m0 = (uint32_t)mask, m1 = (uint32_t)(mask >> 32);
+                const int rank = (half ? cnt1 : cnt0) + __popc((half ? m1 : m0) & ((1u << frow) - 1u));
+                const int64_t at = take ? row + rbase + rank : row + S.ld - 64 + frow;
+                S.cand_key[at] = key;
+                S.cand_pos[at] = pos0 + tpos;
+                atomicAdd(&hist[take ? coarse_bin(key) : (uint32_t)l], take ? (half ? 0x10000u : 1u) : 0u);
+                cnt0 += __popc(m0);
+                cnt1 += __popc(m1);
             }
         };
 
@@ -808,6 +851,18 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
                 }
                 lds_barrier();
                 if (hb == 1) finish(k, xch[k & 1][team][l] + mine, tsc);
+                if constexpr (!SCORES) {
+                    // once per unrolled round, team 0's finisher raises both
+                    // queries' floors from the part's histogram
+                    if (u == U - 1 && hb == 1 && team == 0) {
+                        int b0, b1;
+                        coarse_floor<true>(hist, S.topk, b0, b1);
+                        if (l == 0) {
+                            floor_key[0] = max((uint32_t)b0 << (32 - kCoarseBits), 1u);
+                            floor_key[1] = max((uint32_t)b1 << (32 - kCoarseBits), 1u);
+                        }
+                    }
+                }
                 fetch(k + 1, (u + 1) % NS, t);
             }
         }
@@ -821,6 +876,10 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
         wait_vmcnt_mem<0>();
     }
     if constexpr (!SCORES) {
+        if (hb == 1 && l == 0) {
+            S.reg[(int64_t)j0 * S.n_reg + part * NTEAM + team] = make_int2(rbase, cnt0);
+            if (j1 < A.num_q) S.reg[(int64_t)j1 * S.n_reg + part * NTEAM + team] = make_int2(rbase, cnt1);
+        }
         __syncthreads();
         for (int i = 0; i < 2; i++) {
             const int jj = 2 * g + i;
@@ -834,6 +893,8 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
 
 // ------------------------------------------------------------ keys from given scores
 
+// Every key of a given score row becomes a candidate: part p of query j is one
+// region holding positions p * part .. in order.
 __global__ __launch_bounds__(kRowsThreads) void keys_from_scores_kernel(KeysFromScoresArgs K) {
     __shared__ uint32_t hist[kCoarseBins];
     const int j = blockIdx.x / K.n_parts;
@@ -849,9 +910,11 @@ __global__ __launch_bounds__(kRowsThreads) void keys_from_scores_kernel(KeysFrom
     const int p1 = min(p0 + K.part, rl);
     for (int p = p0 + threadIdx.x; p < p1; p += kRowsThreads) {
         const uint32_t key = score_key(K.scores[(int64_t)j * K.ld_in + p]);
-        K.keys[(int64_t)j * K.ld + p] = key;
+        K.cand_key[(int64_t)j * K.ld + p] = key;
+        K.cand_pos[(int64_t)j * K.ld + p] = p;
         atomicAdd(&hist[coarse_bin(key)], 1u);
     }
+    if (threadIdx.x == 0) K.reg[(int64_t)j * K.n_parts + part] = make_int2(p0, max(0, p1 - p0));
     __syncthreads();
     uint32_t* dst = K.hist + ((int64_t)j * K.n_parts + part) * kCoarseBins;
     for (int b = threadIdx.x; b < kCoarseBins; b += kRowsThreads) dst[b] = hist[b];
@@ -859,31 +922,39 @@ __global__ __launch_bounds__(kRowsThreads) void keys_from_scores_kernel(KeysFrom
 
 // ------------------------------------------------------------ selection pass
 
-// Appends every key >= lo of keys[0..n) (global) and its position to the LDS
-// arrays ckey / cpos, in position order. Wave w takes a contiguous segment;
-// within it, 16 steps of 256 keys (4 per lane) are in flight at once, and each
-// step's candidates are placed by a wave prefix sum. Two passes over the keys:
-// count, then place. Returns the count.
-__device__ int filter_candidates_two_pass(const uint32_t* keys, int n, uint32_t lo, uint32_t* ckey,
-                                          int32_t* cpos, int* wtot) {
-    constexpr int NW = kSelThreads / kWave, STEPS = 16, SPAN = STEPS * 256;
+// Gathers every candidate key >= lo of query j and its position into the LDS
+// arrays ckey / cpos, in position order (the regions are taken in order; wave w
+// takes a contiguous range of them). Two passes over the candidate keys: count
+// per wave, then place at the wave's offset. The caller knows that the count
+// fits (at most kSelCap). Returns the count.
+__device__ int gather_candidates(const SelectArgs& S, int j, uint32_t lo, uint32_t* ckey, int32_t* cpos,
+                                 int* wtot) {
+    constexpr int NW = kSelThreads / kWave, STEPS = 4;
     const int w = threadIdx.x / kWave, l = lane_id();
-    const int seg = ((n + NW - 1) / NW + SPAN - 1) / SPAN * SPAN;
-    const int s0 = w * seg, s1 = min(s0 + seg, n);
-    // pass 1: count
+    const int r0 = (int)((int64_t)w * S.n_reg / NW), r1 = (int)((int64_t)(w + 1) * S.n_reg / NW);
+    const int2* reg = S.reg + (int64_t)j * S.n_reg;
+    const uint32_t* krow = S.cand_key + (int64_t)j * S.ld;
+    const int32_t* prow = S.cand_pos + (int64_t)j * S.ld;
+    // keys e .. e+3 of chunk s of a region starting at entry `base` with `c` entries
+    auto load4 = [&](int base, int c, int i) -> u32x4 {
+        u32x4 k4 = {0u, 0u, 0u, 0u};
+        if (i < c) k4 = *reinterpret_cast<const u32x4*>(krow + base + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+            if (i + e >= c) k4[e] = 0u;
+        return k4;
+    };
     int cnt = 0;
-    for (int b = s0; b < s1; b += SPAN) {
-        u32x4 k4[STEPS];
+    for (int r = r0; r < r1; r++) {
+        const int2 rc = reg[r];
+        for (int b = 0; b < rc.y; b += STEPS * 256) {
+            u32x4 k4[STEPS];
 #pragma unroll
-        for (int s = 0; s < STEPS; s++) {
-            const int i = b + s * 256 + 4 * l;
-            k4[s] = i < s1 ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
-        }
+            for (int s = 0; s < STEPS; s++) k4[s] = load4(rc.x, rc.y, b + s * 256 + 4 * l);
 #pragma unroll
-        for (int s = 0; s < STEPS; s++) {
-            const int i = b + s * 256 + 4 * l;
+            for (int s = 0; s < STEPS; s++)
 #pragma unroll
-            for (int e = 0; e < 4; e++) cnt += (i + e < s1 && k4[s][e] >= lo);
+                for (int e = 0; e < 4; e++) cnt += k4[s][e] >= lo;
         }
     }
     cnt = wave_sum(cnt);
@@ -895,102 +966,48 @@ __device__ int filter_candidates_two_pass(const uint32_t* keys, int n, uint32_t 
         off += i < w ? c : 0;
         total += c;
     }
-    // pass 2: place (the segment is read again, from cache)
-    for (int b = s0; b < s1; b += SPAN) {
-        u32x4 k4[STEPS];
+    for (int r = r0; r < r1; r++) {
+        const int2 rc = reg[r];
+        for (int b = 0; b < rc.y; b += STEPS * 256) {
+            u32x4 k4[STEPS];
 #pragma unroll
-        for (int s = 0; s < STEPS; s++) {
-            const int i = b + s * 256 + 4 * l;
-            k4[s] = i < s1 ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
-        }
+            for (int s = 0; s < STEPS; s++) k4[s] = load4(rc.x, rc.y, b + s * 256 + 4 * l);
 #pragma unroll
-        for (int s = 0; s < STEPS; s++) {
-            const int i = b + s * 256 + 4 * l;
-            int c = 0;
+            for (int s = 0; s < STEPS; s++) {
+                const int i = b + s * 256 + 4 * l;
+                int c = 0;
 #pragma unroll
-            for (int e = 0; e < 4; e++) c += (i + e < s1 && k4[s][e] >= lo);
-            const int inc = wave_incl_scan(c);
-            int at = off + inc - c;
+                for (int e = 0; e < 4; e++) c += k4[s][e] >= lo;
+                // (positions of the four entries, read only where one is taken)
+                u32x4 p4 = {0u, 0u, 0u, 0u};
+                if (c > 0) p4 = *reinterpret_cast<const u32x4*>(prow + rc.x + i);
+                const int inc = wave_incl_scan(c);
+                int at = off + inc - c;
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                if (i + e < s1 && k4[s][e] >= lo) {
-                    if (at < kSelCap) {   // (the caller checked the count; this only guards LDS)
-                        ckey[at] = k4[s][e];
-                        cpos[at] = i + e;
+                for (int e = 0; e < 4; e++) {
+                    if (k4[s][e] >= lo) {
+                        if (at < kSelCap) {   // (the caller checked the count; this only guards LDS)
+                            ckey[at] = k4[s][e];
+                            cpos[at] = (int32_t)p4[e];
+                        }
+                        at++;
                     }
-                    at++;
                 }
+                off += __shfl(inc, kWave - 1, kWave);
             }
-            off += __shfl(inc, kWave - 1, kWave);
         }
     }
     __syncthreads();
     return total;
 }
 
-// The same candidates in one pass over the keys: wave w appends its segment's
-// candidates, in order, to its own region of kSelCap / NW entries and clears the
-// rest of the region (key 0, which is never selected: every candidate key is at
-// least 1). The regions follow each other in wave order, so the kSelCap entries
-// list the candidates in position order with gaps; the refinement and the
-// ordered compaction skip the gaps. If a segment holds more candidates than its
-// region, the two-pass form (contiguous) is used instead; the decision is the
-// same in every wave. Returns the number of entries to scan.
-__device__ int filter_candidates(const uint32_t* keys, int n, uint32_t lo, uint32_t* ckey, int32_t* cpos,
-                                 int* wtot) {
-    constexpr int NW = kSelThreads / kWave, STEPS = 16, SPAN = STEPS * 256, RW = kSelCap / NW;
-    const int w = threadIdx.x / kWave, l = lane_id();
-    const int seg = ((n + NW - 1) / NW + SPAN - 1) / SPAN * SPAN;
-    const int s0 = w * seg, s1 = min(s0 + seg, n);
-    uint32_t* wk = ckey + w * RW;
-    int32_t* wp = cpos + w * RW;
-    int cnt = 0;
-    for (int b = s0; b < s1; b += SPAN) {
-        u32x4 k4[STEPS];
-#pragma unroll
-        for (int s = 0; s < STEPS; s++) {
-            const int i = b + s * 256 + 4 * l;
-            k4[s] = i < s1 ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int s = 0; s < STEPS; s++) {
-            const int i = b + s * 256 + 4 * l;
-            int c = 0;
-#pragma unroll
-            for (int e = 0; e < 4; e++) c += (i + e < s1 && k4[s][e] >= lo);
-            const int inc = wave_incl_scan(c);
-            int at = cnt + inc - c;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                if (i + e < s1 && k4[s][e] >= lo) {
-                    if (at < RW) {
-                        wk[at] = k4[s][e];
-                        wp[at] = i + e;
-                    }
-                    at++;
-                }
-            }
-            cnt += __shfl(inc, kWave - 1, kWave);
-        }
-    }
-    if (l == 0) wtot[w] = cnt;
-    __syncthreads();
-    int over = 0;
-    for (int i = 0; i < NW; i++) over |= wtot[i] > RW;
-    if (over) {
-        __syncthreads();   // (every wave has read wtot)
-        return filter_candidates_two_pass(keys, n, lo, ckey, cpos, wtot);
-    }
-    for (int x = cnt + l; x < RW; x += kWave) wk[x] = 0u;
-    __syncthreads();
-    return NW * RW;
-}
-
 // One workgroup per query: the coarse histogram (sum of the parts') gives the
-// bin of the K-th largest key; every key at or above that bin is gathered into
-// LDS in position order, the exact threshold is refined there, and the ordered
-// compaction emits the Top-K ascending in position. A row whose candidates do
-// not fit in LDS is refined and compacted straight from global memory.
+// bin of the K-th largest key; every candidate at or above that bin is gathered
+// into LDS in position order, the exact threshold is refined there, and the
+// ordered compaction emits the Top-K ascending in position. A row whose
+// candidates at that bin do not fit in LDS (many equal scores) is first spread
+// into a dense key row in global memory (key 0 where there is none) and
+// selected there.
 __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
     __shared__ uint32_t hist[kCoarseBins];
     __shared__ __attribute__((aligned(16))) uint32_t ckey[kSelCap];
@@ -1030,19 +1047,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
         hist[tid + kSelThreads] = c1;
     }
     __syncthreads();
+    // (every key in the K-th bin or above was kept by the score pass: its floor
+    // never passes the row's K-th bin, so these counts are exact there)
     int above, total;
     const int bin = coarse_select<kSelThreads>(hist, S.topk, &sel, above, total);
     const int m = min(S.topk, total);
     if (m > 0) {
-        const uint32_t* keys = S.keys + (int64_t)j * S.ld;
         const bool all = m == total;
         const uint32_t bin_lo = (uint32_t)bin << (32 - kCoarseBits);
         const uint32_t lo = all ? 1u : max(bin_lo, 1u);
         const int ncand = all ? total : above + (int)hist[bin];
         if (ncand <= kSelCap) {
-            // (the candidates are exactly the ncand keys the histogram counted,
-            // listed in position order within the first `got` entries)
-            const int got = filter_candidates(keys, rl, lo, ckey, cpos, wtot);
+            const int got = gather_candidates(S, j, lo, ckey, cpos, wtot);
             const int nc = min(got, kSelCap);
             for (int i = nc + tid; i < (nc + 7) / 8 * 8; i += kSelThreads) ckey[i] = 0u;
             __syncthreads();
@@ -1054,13 +1070,35 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
                                                              m - above, 32 - kCoarseBits, &sel, ties);
                 ordered_compact<kSelThreads>(ckey, nc, T, ties, &sel, EmitFinalBuf{cpos, oi, os, S.topk, {}});
             }
-        } else if (all) {
-            ordered_compact<kSelThreads>(keys, rl, 0u, 0, &sel, EmitFinal{oi, os, 0, S.topk});
         } else {
-            int ties;
-            const uint32_t T = radix_refine<kSelThreads>(keys, rl, bin_lo, ~0u << (32 - kCoarseBits), m - above,
-                                                         32 - kCoarseBits, &sel, ties);
-            ordered_compact<kSelThreads>(keys, rl, T, ties, &sel, EmitFinal{oi, os, 0, S.topk});
+            // dense key row: clear it, spread the candidates at or above lo to
+            // their positions (distinct, below rl), then select in global memory
+            uint32_t* keys = S.keys + (int64_t)j * S.ld;
+            const int n8 = (rl + 7) / 8 * 8;   // (ld >= n8: the row has a spare tail)
+            for (int p = tid; p < n8; p += kSelThreads) keys[p] = 0u;
+            __threadfence();
+            __syncthreads();
+            const int2* reg = S.reg + (int64_t)j * S.n_reg;
+            const uint32_t* krow = S.cand_key + (int64_t)j * S.ld;
+            const int32_t* prow = S.cand_pos + (int64_t)j * S.ld;
+            for (int r = 0; r < S.n_reg; r++) {
+                const int2 rc = reg[r];
+                for (int i = tid; i < rc.y; i += kSelThreads) {
+                    const uint32_t k = krow[rc.x + i];
+                    const int p = prow[rc.x + i];
+                    if (k >= lo && p >= 0 && p < rl) keys[p] = k;
+                }
+            }
+            __threadfence();
+            __syncthreads();
+            if (all) {
+                ordered_compact<kSelThreads>(keys, rl, 0u, 0, &sel, EmitFinal{oi, os, 0, S.topk});
+            } else {
+                int ties;
+                const uint32_t T = radix_refine<kSelThreads>(keys, rl, bin_lo, ~0u << (32 - kCoarseBits),
+                                                             m - above, 32 - kCoarseBits, &sel, ties);
+                ordered_compact<kSelThreads>(keys, rl, T, ties, &sel, EmitFinal{oi, os, 0, S.topk});
+            }
         }
     }
     for (int r = m + tid; r < S.topk; r += kSelThreads) {

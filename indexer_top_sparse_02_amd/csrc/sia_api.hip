@@ -103,16 +103,21 @@ struct IndexerPlan {
     bool stream = false;
     int group = 1;               // queries per score-pass workgroup (1 or 2)
     int part = 0, n_parts = 0;   // score-pass parts of each row
-    int64_t ld = 0;              // key row stride
-    size_t keys = 0, hist = 0, rlen = 0;   // workspace offsets
+    int n_reg = 0;               // candidate regions per query
+    int64_t ld = 0;              // row stride of the candidate and key rows
+    size_t keys = 0, ckey = 0, cpos = 0, hist = 0, reg = 0, rlen = 0;   // workspace offsets
     int cap = 0;                 // stream buffer capacity
     size_t total = kHeader;
 };
 
 // Score pass + selection pass. One score workgroup is resident per CU, so a row
 // is cut into enough parts to give every CU one (parts of 2048 to 65536
-// positions); the selection pass reads the key rows and per-part histograms.
-void plan_rows(IndexerPlan& p, int64_t num_q, int max_visible, int group) {
+// positions); each part has `regs_per_part` candidate regions (one per team or
+// wave of the score pass). The selection pass reads the candidate regions and
+// the per-part histograms; the dense key rows are its scratch for rows whose
+// candidates do not fit in LDS. Every row holds room for all of its positions
+// plus a spare tail of 64 entries that non-keeping lanes write to.
+void plan_rows(IndexerPlan& p, int64_t num_q, int max_visible, int group, int regs_per_part) {
     p.group = group;
     const int64_t n_groups = std::max<int64_t>(1, ceil_div(num_q, group));
     const int64_t mv = std::max(max_visible, 1);
@@ -124,10 +129,23 @@ void plan_rows(IndexerPlan& p, int64_t num_q, int max_visible, int group) {
     np = std::max<int64_t>(np, ceil_div(mv, max_part));
     p.part = (int)(ceil_div(ceil_div(mv, np), 64) * 64);
     p.n_parts = (int)ceil_div(mv, p.part);
-    p.ld = ceil_div(mv, 64) * 64 + 64;   // (+ a spare tail that padding steps write)
-    p.keys = p.total; p.total += align_up((size_t)num_q * p.ld * 4);
+    p.n_reg = p.n_parts * regs_per_part;
+    p.ld = ceil_div(mv, 64) * 64 + 64;
+    const size_t row_bytes = align_up((size_t)num_q * p.ld * 4);
+    p.keys = p.total; p.total += row_bytes;
+    p.ckey = p.total; p.total += row_bytes;
+    p.cpos = p.total; p.total += row_bytes;
     p.hist = p.total; p.total += align_up((size_t)num_q * p.n_parts * sia::kCoarseBinsHost * 4);
+    p.reg = p.total; p.total += align_up((size_t)num_q * p.n_reg * 8);
     p.rlen = p.total; p.total += align_up((size_t)num_q * 4);
+}
+
+// The pair kernel scores two queries of one sequence per workgroup; it needs
+// the queries to come in pairs (group even) and an even count.
+int score_group(const sia_queries* qs) {
+    int g = qs->group % 2 == 0 && qs->num_q % 2 == 0 ? 2 : 1;
+    if (env_int("SIA_ROWS_GROUP", 0) == 1) g = 1;
+    return g;
 }
 
 IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bool fp8) {
@@ -152,9 +170,8 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bo
         }
     }
     (void)heads;
-    int g = qs->group % 2 == 0 ? 2 : 1;
-    if (env_int("SIA_ROWS_GROUP", 0) == 1) g = 1;
-    plan_rows(p, qs->num_q, qs->max_visible, g);
+    const int g = score_group(qs);
+    plan_rows(p, qs->num_q, qs->max_visible, g, g == 2 ? sia::kPairRegions : sia::kRowsRegions);
     return p;
 }
 
@@ -252,14 +269,19 @@ int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k
     sia::RowsArgs r{};
     r.part = p.part;
     r.n_parts = p.n_parts;
+    r.topk = topk;
+    r.n_reg = p.n_reg;
     r.ld = p.ld;
-    r.keys = reinterpret_cast<uint32_t*>(ws + p.keys);
+    r.cand_key = reinterpret_cast<uint32_t*>(ws + p.ckey);
+    r.cand_pos = reinterpret_cast<int32_t*>(ws + p.cpos);
+    r.reg = reinterpret_cast<int2*>(ws + p.reg);
     r.hist = reinterpret_cast<uint32_t*>(ws + p.hist);
     r.row_len = reinterpret_cast<int32_t*>(ws + p.rlen);
     e = sia::launch_indexer_rows(a, r, mb, index_k->dim, fp8, p.group, false, st);
     if (e != hipSuccess) return hip_fail(e, "indexer score launch");
-    const sia::SelectArgs sel{r.keys, r.ld, r.hist, r.n_parts, r.row_len, qs->max_visible, qs->num_q, topk,
-                              out_idx, out_score};
+    const sia::SelectArgs sel{r.cand_key, r.cand_pos, r.reg, r.n_reg, r.ld,
+                              reinterpret_cast<uint32_t*>(ws + p.keys), r.hist, r.n_parts, r.row_len,
+                              qs->max_visible, qs->num_q, topk, out_idx, out_score};
     e = sia::launch_topk_rows(sel, st);
     if (e != hipSuccess) return hip_fail(e, "top-k selection launch");
     return SIA_OK;
@@ -280,7 +302,8 @@ int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index
     if (e != hipSuccess) return hip_fail(e, "scores fill");
     const sia::IdxArgs a = idx_args(pt, index_k, qs, q_idx, w, heads, workspace);
     IndexerPlan p;
-    plan_rows(p, qs->num_q, qs->max_visible, qs->group % 2 == 0 ? 2 : 1);
+    const int g = score_group(qs);
+    plan_rows(p, qs->num_q, qs->max_visible, g, 1);
     sia::RowsArgs r{};
     r.part = p.part;
     r.n_parts = p.n_parts;
@@ -295,7 +318,7 @@ int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index
 size_t sia_topk_workspace_size(int32_t num_q, int32_t max_row_len, int32_t topk) {
     if (num_q < 0 || max_row_len < 0 || topk < 1 || topk > 8192) return 0;
     IndexerPlan p;
-    plan_rows(p, num_q, max_row_len, 1);
+    plan_rows(p, num_q, max_row_len, 1, 1);
     return p.total;
 }
 
@@ -307,7 +330,7 @@ int sparse_topk_from_scores(const float* scores, int64_t ld, const int32_t* row_
     if (topk < 1 || topk > 8192) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..8192", topk);
     if (max_row_len < 0 || ld < max_row_len) return fail(SIA_ERR_INVALID_ARG, "need 0 <= max_row_len <= ld");
     IndexerPlan p;
-    plan_rows(p, num_q, max_row_len, 1);
+    plan_rows(p, num_q, max_row_len, 1, 1);
     int rc = check_workspace(workspace, workspace_bytes, p.total);
     if (rc != SIA_OK) return rc;
     if (num_q == 0) return SIA_OK;
@@ -322,13 +345,15 @@ int sparse_topk_from_scores(const float* scores, int64_t ld, const int32_t* row_
     k.part = p.part;
     k.n_parts = p.n_parts;
     k.ld = p.ld;
-    k.keys = reinterpret_cast<uint32_t*>(ws + p.keys);
+    k.cand_key = reinterpret_cast<uint32_t*>(ws + p.ckey);
+    k.cand_pos = reinterpret_cast<int32_t*>(ws + p.cpos);
+    k.reg = reinterpret_cast<int2*>(ws + p.reg);
     k.hist = reinterpret_cast<uint32_t*>(ws + p.hist);
     k.status = reinterpret_cast<uint32_t*>(ws);
     hipError_t e = sia::launch_keys_from_scores(k, st);
     if (e != hipSuccess) return hip_fail(e, "score keys launch");
-    const sia::SelectArgs sel{k.keys, k.ld, k.hist, k.n_parts, row_len, max_row_len, num_q, topk, out_idx,
-                              out_score};
+    const sia::SelectArgs sel{k.cand_key, k.cand_pos, k.reg, p.n_reg, k.ld, reinterpret_cast<uint32_t*>(ws + p.keys),
+                              k.hist, k.n_parts, row_len, max_row_len, num_q, topk, out_idx, out_score};
     e = sia::launch_topk_rows(sel, st);
     if (e != hipSuccess) return hip_fail(e, "top-k selection launch");
     return SIA_OK;
@@ -370,13 +395,13 @@ static int check_attn(const sia_page_table* pt, const sia_paged_cache* kv, const
     if (!qs) return fail(SIA_ERR_INVALID_ARG, "query descriptor is NULL");
     if (qs->num_q < 0) return fail(SIA_ERR_INVALID_ARG, "num_q %d < 0", qs->num_q);
     if (qs->num_q > 0 && !qs->q_seq) return fail(SIA_ERR_INVALID_ARG, "q_seq is NULL");
-    if (heads < 16 || heads % 16 || heads > 1024) return fail(SIA_ERR_UNSUPPORTED, "heads %d: multiple of 16 up to 1024", heads);
+    if (heads < 16 || heads % 16 || heads > 128) return fail(SIA_ERR_UNSUPPORTED, "heads %d: multiple of 16 up to 128", heads);
     if (topk < 1) return fail(SIA_ERR_INVALID_ARG, "topk %d < 1", topk);
     return SIA_OK;
 }
 
 size_t sia_mla_workspace_size(const sia_queries* qs, int32_t heads, int32_t d_v, int32_t topk) {
-    if (!qs || qs->num_q < 0 || heads < 16 || heads % 16 || heads > 1024 || d_v != 512 || topk < 1) return 0;
+    if (!qs || qs->num_q < 0 || heads < 16 || heads % 16 || heads > 128 || d_v != 512 || topk < 1) return 0;
     int hb, ns, rps;
     size_t total;
     attn_plan(qs, heads, topk, hb, ns, rps, total);

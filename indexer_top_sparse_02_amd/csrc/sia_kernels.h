@@ -24,32 +24,49 @@ struct IdxArgs {
 };
 
 // Score pass: a workgroup scores one part (`part` consecutive positions, a
-// multiple of the page size) of the rows of one or two queries.
+// multiple of the page size) of the rows of one or two queries. A position's
+// key is kept only while it reaches the running floor of the part (the coarse
+// bin of its K-th largest key so far); kept keys and their positions are
+// appended to the candidate list of the team (or wave) that scored them. The
+// lists of a query, taken in region order, are in position order.
 struct RowsArgs {
     int32_t part, n_parts;
-    int64_t ld;                // row stride of keys / scores
-    uint32_t* keys;            // [num_q, ld] score keys (0: not a candidate)
-    uint32_t* hist;            // [num_q, n_parts, kCoarseBins] per-part coarse histograms
+    int32_t topk;
+    int32_t n_reg;             // candidate regions per query (n_parts x teams per part)
+    int64_t ld;                // row stride of cand_key / cand_pos / keys / scores
+    uint32_t* cand_key;        // [num_q, ld] appended keys, region r from reg[r].x on
+    int32_t* cand_pos;         // [num_q, ld] their positions
+    int2* reg;                 // [num_q, n_reg] (first entry, count) of each region
+    uint32_t* hist;            // [num_q, n_parts, kCoarseBins] per-part coarse histograms of kept keys
     int32_t* row_len;          // [num_q] visible row length (written by part 0)
     float* scores;             // scores mode: [num_q, ld]
 };
 
-// Keys and per-part histograms from a given score matrix (test hook).
+// Candidates (every key, one region per part) and per-part histograms from a
+// given score matrix (test hook).
 struct KeysFromScoresArgs {
     const float* scores;
     int64_t ld_in;
     const int32_t* row_len;
     int32_t num_q, max_len, part, n_parts;
     int64_t ld;
-    uint32_t* keys;
+    uint32_t* cand_key;
+    int32_t* cand_pos;
+    int2* reg;
     uint32_t* hist;
     uint32_t* status;
 };
 
-// Selection pass: exact Top-K of each key row.
+// Selection pass: exact Top-K of each query's candidate lists. `keys` is a
+// dense [num_q, ld] scratch row used only when a row's candidates at the K-th
+// coarse bin do not fit in LDS.
 struct SelectArgs {
-    const uint32_t* keys;
+    const uint32_t* cand_key;
+    const int32_t* cand_pos;
+    const int2* reg;
+    int32_t n_reg;
     int64_t ld;
+    uint32_t* keys;
     const uint32_t* hist;
     int32_t n_parts;
     const int32_t* row_len;    // clamped to [0, max_len]
@@ -79,7 +96,9 @@ constexpr int kCoarseBinsHost = 2048;   // = kCoarseBins of the selection code
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
 
 constexpr int kRowsThreads = 512;      // eight waves: two per SIMD
+constexpr int kRowsRegions = kRowsThreads / 64;   // candidate regions per part (one per wave)
 constexpr int kPairThreads = 512;      // four teams of two waves (one team per SIMD) per query pair
+constexpr int kPairRegions = kPairThreads / 128;  // candidate regions per part (one per team)
 constexpr int kMaxPartPages = 1024;    // a score-pass part spans at most 65536 positions
 constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 16384;         // candidates the selection pass holds in LDS

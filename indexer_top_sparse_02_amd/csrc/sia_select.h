@@ -185,6 +185,59 @@ constexpr int kCoarseBits = 11;
 constexpr int kCoarseBins = 1 << kCoarseBits;
 __device__ __forceinline__ uint32_t coarse_bin(uint32_t key) { return key >> (32 - kCoarseBits); }
 
+// Floor of the Top-K from a coarse histogram of the keys seen so far: the
+// largest bin b with at least K counted keys in bins >= b, or 0 when fewer than
+// K keys are counted. A key in a lower bin has K larger keys and can never be
+// selected, so it need not be kept; a histogram read while other waves still
+// add to it only undercounts, which lowers b and stays valid. One wave.
+// hist: kCoarseBins counters in LDS. PACKED: two queries per counter (low and
+// high 16 bits; each query's total must stay below 65536, so that sums of the
+// packed words never carry across the halves); results in b0 and b1.
+template <bool PACKED>
+__device__ void coarse_floor(const uint32_t* hist, int K, int& b0, int& b1) {
+    static_assert(kCoarseBins == 32 * kWave, "32 bins per lane");
+    const int l = lane_id();
+    // level 1: lane l sums bins 32 l .. 32 l + 31
+    const u32x4* h4 = reinterpret_cast<const u32x4*>(hist + 32 * l);
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const u32x4 v = h4[i];
+        s += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+    const uint32_t pre = (uint32_t)wave_incl_scan((int)s);
+    const uint32_t tot = (uint32_t)__shfl((int)pre, kWave - 1, kWave);
+    const uint32_t above = tot - pre;   // keys in the bins of higher lanes
+    constexpr uint32_t M = PACKED ? 0xffffu : 0xffffffffu;
+    int lane_of[2];
+#pragma unroll
+    for (int h = 0; h < (PACKED ? 2 : 1); h++) {
+        const uint32_t a = (above >> (16 * h)) & M, c = (s >> (16 * h)) & M;
+        const uint64_t m = __ballot(a < (uint32_t)K && a + c >= (uint32_t)K);
+        lane_of[h] = m ? __builtin_ctzll(m) : -1;
+    }
+    // level 2: lanes 0..31 (query 0) and 32..63 (query 1) take one bin each of
+    // the 32 bins of that query's lane
+    const int h = PACKED ? (l >> 5) : 0;
+    const int L = h ? lane_of[1] : lane_of[0];
+    const int i5 = l & 31;
+    uint32_t c = 0;
+    if (L >= 0) c = (hist[32 * L + i5] >> (16 * h)) & M;
+    // keys in the bins above lane L's (read from lane L, this lane's query)
+    const uint32_t a_l = ((uint32_t)__shfl((int)above, L >= 0 ? L : 0, kWave) >> (16 * h)) & M;
+    if (!PACKED && l >= 32) c = 0;
+    const int p2 = wave_incl_scan((int)c);
+    const int p31 = __shfl(p2, 31, kWave);
+    const int incl = h ? p2 - p31 : p2;
+    const int tot2 = h ? __shfl(p2, kWave - 1, kWave) - p31 : p31;
+    const uint32_t a2 = a_l + (uint32_t)(tot2 - incl);   // keys above bin 32 L + i5
+    const bool hit = L >= 0 && a2 < (uint32_t)K && a2 + c >= (uint32_t)K;
+    const uint64_t hm = __ballot(hit);
+    const uint32_t m0 = (uint32_t)hm, m1 = (uint32_t)(hm >> 32);
+    b0 = m0 ? 32 * lane_of[0] + __builtin_ctz(m0) : 0;
+    b1 = PACKED && m1 ? 32 * lane_of[1] + __builtin_ctz(m1) : 0;
+}
+
 // From a coarse histogram of the candidate keys (kCoarseBins counters in LDS),
 // find the bin that holds the m-th largest key. Returns the bin; `above` = keys
 // in higher bins, `total` = all counted keys. Block-wide (NT threads).

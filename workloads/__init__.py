@@ -260,8 +260,10 @@ def chunk_queries(wl: Workload, c: int) -> Workload:
 
 def subset(wl: Workload, seqs, device="cpu") -> Workload:
     """The queries of sequences ``seqs`` with compact caches holding only those
-    sequences' pages (same page order within each sequence, renumbered, shuffled
-    placement kept). Used to hand a slice of a large workload to the CPU."""
+    sequences' pages. The pages are renumbered contiguously in logical order, so
+    the subset's page table is the identity placement (page placement itself is
+    covered by its own tests). Used to hand a slice of a large workload to the
+    CPU."""
     seqs = [int(s) for s in seqs]
     table = wl.page_table.cpu()
     lens = wl.seq_lens.cpu()
