@@ -42,12 +42,15 @@ static_assert(kCoarseBins == kCoarseBinsHost, "host and device histogram sizes d
 
 // A query's indexer heads in MFMA operand layout. The bf16 form feeds
 // 32x32x16 bf16 MFMAs (fp8 keys are widened to bf16). The fp8 form feeds
-// 32x32x64 fp8 MFMAs on the raw e4m3 key bytes: q * 2^s is split into an e4m3
-// high part and an e4m3 residual times 2^4 (one exponent s per query, chosen so
-// that max|q| * 2^s < 256), and the two products are summed with MFMA scales
-// 2^-s and 2^-(s+4). The split is exact for every element above 2^-21 of the
-// query's largest element (below that the residual underflows), so the scores
-// equal those of the bf16 form up to rounding order.
+// 32x32x64 fp8 MFMAs on the raw e4m3 key bytes: X = q * 2^s is split into an
+// e4m3 high part hi = e4m3(X) and an e4m3 residual lo = e4m3(16 (X - hi)) (one
+// exponent s per query, chosen so that max|q| * 2^s lies in [128, 256)), and
+// the two products are summed with MFMA scales 2^-s and 2^-(s+4). The split is
+// exact wherever |X| >= 2^-6 (e4m3's smallest normal), which covers every
+// element with |q| >= 2^-13 max|q|; below that the residual falls into e4m3's
+// subnormal steps and the element is represented to within 2^-14 2^-s <=
+// 2^-21 max|q|. The scores therefore equal those of the bf16 form up to
+// rounding order and that error on the smallest elements.
 template <int MB, int D, bool FP8>
 struct IdxQuery;
 

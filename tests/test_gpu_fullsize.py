@@ -62,12 +62,22 @@ def _check_rows(s, wl_ref, gpu_rows, idx, top, out, lse, scores, row_len):
 
 @pytest.mark.parametrize("name", ["spec_decode_128k", "decode_b32"])
 def test_full_size_decode_sampled_sequences(name):
+    """Every query row: the fused Top-K is the oracle's selection of the GPU's
+    own scores, bit for bit. Eight sequences spread over the batch: scores,
+    the boundary-band rule and attention against the oracle."""
     s = W.spec(name)
     wl = W.make(s, device="cuda", poison=True)
     _, idx, top, out, lse, scores = _gpu_path(wl, group=s.q_per_seq)
     q_seq = wl.q_seq.cpu().numpy()
     lens = wl.seq_lens.cpu().numpy()
-    for seq in (0, s.batch // 2, s.batch - 1):
+    rl_all = np.minimum(wl.q_pos.cpu().numpy() + 1, lens[q_seq]).astype(np.int32)
+    sel, sel_sc = oracle.topk(scores.cpu().numpy().astype(np.float64), rl_all, s.topk)
+    g_idx = idx.cpu().numpy()
+    assert np.array_equal(g_idx, sel)
+    g_top = top.cpu().numpy().astype(np.float64)
+    assert np.array_equal(g_top[g_idx >= 0], sel_sc[g_idx >= 0])
+    print(f"{name}: selection bit-exact on all {wl.num_q} query rows", flush=True)
+    for seq in np.unique(np.linspace(0, s.batch - 1, 8).astype(int)):
         rows = np.flatnonzero(q_seq == seq)
         sub = W.subset(wl, [seq], device="cpu")
         rl = np.minimum(wl.q_pos.cpu().numpy()[rows] + 1, lens[seq]).astype(np.int32)
@@ -95,12 +105,16 @@ def test_full_size_prefill_16k_sampled_queries():
     _check_rows(s, _sampled_cpu(wl, rows), rows, idx, top, out, lse, scores, rl)
 
 
-def test_full_size_chunked_prefill_last_chunk_sampled_queries():
+@pytest.mark.parametrize("chunk", [0, 7, 15])
+def test_full_size_chunked_prefill_sampled_queries(chunk):
+    """One 8192-query chunk of the 131072-token chunked prefill (the first, a
+    middle and the last), run as the benchmark runs it (one call per chunk
+    against the paged caches); sampled queries against the oracle."""
     s = W.spec("chunked_prefill_128k")
     wl = W.make(s, device="cuda", poison=True)
-    start = wl.num_q - s.chunk
-    w, idx, top, out, lse, scores = _gpu_path(wl, group=s.chunk, queries=(start, wl.num_q))
-    local = np.array([0, 1, 4095, 8190, 8191])
+    start = chunk * s.chunk
+    w, idx, top, out, lse, scores = _gpu_path(wl, group=s.chunk, queries=(start, start + s.chunk))
+    local = np.array([0, 1, 2047, 2048, 4095, 8190, 8191])
     rl = (start + local + 1).astype(np.int32)
-    print(f"chunked_prefill_128k: last chunk, queries {(start + local).tolist()}", flush=True)
+    print(f"chunked_prefill_128k: chunk {chunk}, queries {(start + local).tolist()}", flush=True)
     _check_rows(s, _sampled_cpu(w, local), local, idx, top, out, lse, scores, rl)
