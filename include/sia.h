@@ -200,6 +200,28 @@ int sparse_mla_attention(const sia_page_table *pt, const sia_paged_cache *kv,
                          const int32_t *idx, int32_t topk, float sm_scale, void *out,
                          float *lse, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * sparse_mla_attention without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and validation as
+ * sparse_mla_attention, minus the workspace: the scratch it needs (row-slice
+ * partials, the device status word) lives in a static device array of
+ * SIA_MLA_NOALLOC_MAX_BYTES bytes (64 MiB) that the library holds on each GPU
+ * it runs on until the process ends. It allocates and frees nothing.
+ *  - A call whose sparse_mla_attention workspace size (sia_mla_workspace_size)
+ *    exceeds that maximum returns SIA_ERR_WORKSPACE and launches nothing.
+ *  - Every call on one GPU shares that GPU's array: calls that may overlap on
+ *    one GPU (different streams without ordering, other host threads) race and
+ *    must be serialized by the caller.
+ *  - The device status bits of these calls are not reported (use the workspace
+ *    form to read them).
+ */
+int sparse_mla_attention_noalloc(const sia_page_table *pt, const sia_paged_cache *kv,
+                                 const sia_queries *qs, const void *q, int32_t heads, int32_t d_v,
+                                 const int32_t *idx, int32_t topk, float sm_scale, void *out,
+                                 float *lse, void *stream);
+#define SIA_MLA_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+
 /* ------------------------------------------------------------------ misc */
 
 /*

@@ -29,8 +29,8 @@ DEVSTATUS_BAD_SEQ, DEVSTATUS_BAD_PAGE, DEVSTATUS_ROW_TOO_LONG, DEVSTATUS_BAD_IND
 EXPORTS = [
     "sia_indexer_workspace_size", "sparse_indexer_topk", "sparse_indexer_scores",
     "sia_topk_workspace_size", "sparse_topk_from_scores", "sia_mla_workspace_size",
-    "sparse_mla_attention", "sia_zigzag_assign", "sia_clear_device_status",
-    "sia_read_device_status", "sia_last_error", "sia_version",
+    "sparse_mla_attention", "sparse_mla_attention_noalloc", "sia_zigzag_assign",
+    "sia_clear_device_status", "sia_read_device_status", "sia_last_error", "sia_version",
 ]
 
 
@@ -81,6 +81,8 @@ def lib():
             "sia_mla_workspace_size": (c_sz, [pQ, c_i32, c_i32, c_i32]),
             "sparse_mla_attention": (ctypes.c_int, [pPT, pPC, pQ, P, c_i32, c_i32, P, c_i32, c_f, P, P,
                                                     P, c_sz, P]),
+            "sparse_mla_attention_noalloc": (ctypes.c_int, [pPT, pPC, pQ, P, c_i32, c_i32, P, c_i32, c_f,
+                                                            P, P, P]),
             "sia_zigzag_assign": (ctypes.c_int, [c_i32, ctypes.POINTER(ctypes.c_int32)]),
             "sia_clear_device_status": (ctypes.c_int, [P, P]),
             "sia_read_device_status": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_uint32)]),
@@ -248,6 +250,27 @@ def sparse_mla_attention(page_table, seq_lens, kv, q_seq, q, idx, sm_scale, *, d
                                       int(d_v), _ptr(idx), topk, float(sm_scale), _ptr(out), _ptr(lse),
                                       _ptr(workspace), workspace.numel(), _stream(stream)))
     return out, lse
+
+
+def sparse_mla_attention_noalloc(page_table, seq_lens, kv, q_seq, q, idx, sm_scale, *, d_v=512,
+                                 out=None, lse=None, want_lse=False, stream=None):
+    """Sparse MLA attention with the library's static scratch instead of a
+    workspace (no device allocation inside the library). Returns (out, lse)."""
+    Q, H = int(q.shape[0]), int(q.shape[1])
+    topk = int(idx.shape[1])
+    pt, c = page_table_desc(page_table, seq_lens), cache_desc(kv)
+    qd = Queries(Q, _ptr(q_seq), None, 1, 0)
+    if out is None:
+        out = torch.empty((Q, H, d_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Q, H), dtype=torch.float32, device=q.device)
+    _check(lib().sparse_mla_attention_noalloc(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(qd), _ptr(q),
+                                              H, int(d_v), _ptr(idx), topk, float(sm_scale), _ptr(out),
+                                              _ptr(lse), _stream(stream)))
+    return out, lse
+
+
+MLA_NOALLOC_MAX_BYTES = 64 << 20   # SIA_MLA_NOALLOC_MAX_BYTES of include/sia.h
 
 
 def zigzag_assign(num_shards: int):

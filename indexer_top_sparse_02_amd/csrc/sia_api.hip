@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "sia.h"
@@ -408,21 +409,15 @@ size_t sia_mla_workspace_size(const sia_queries* qs, int32_t heads, int32_t d_v,
     return total;
 }
 
-int sparse_mla_attention(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queries* qs,
-                         const void* q, int32_t heads, int32_t d_v, const int32_t* idx, int32_t topk,
-                         float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-    int rc = check_attn(pt, kv, qs, heads, d_v, topk);
-    if (rc != SIA_OK) return rc;
-    if (qs->num_q > 0 && (!q || !idx || !out)) return fail(SIA_ERR_INVALID_ARG, "q/idx/out is NULL");
-    if (!std::isfinite(sm_scale)) return fail(SIA_ERR_INVALID_ARG, "sm_scale is not finite");
-    int hb, ns, rps;
-    size_t total;
-    attn_plan(qs, heads, topk, hb, ns, rps, total);
-    if ((rc = check_workspace(workspace, workspace_bytes, total)) != SIA_OK) return rc;
-    if (qs->num_q == 0) return SIA_OK;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
+}  // extern "C"
+
+namespace {
+
+// Launches the attention kernels with workspace `ws` (already checked to hold
+// `total` bytes for this plan).
+int mla_run(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queries* qs, const void* q,
+            int heads, int d_v, const int32_t* idx, int topk, float sm_scale, void* out, float* lse,
+            uint8_t* ws, int hb, int ns, int rps, hipStream_t st) {
     sia::AttnArgs a;
     a.page_table = pt->page_table;
     a.seq_lens = pt->seq_lens;
@@ -454,6 +449,87 @@ int sparse_mla_attention(const sia_page_table* pt, const sia_paged_cache* kv, co
         if (e != hipSuccess) return hip_fail(e, "attention combine launch");
     }
     return SIA_OK;
+}
+
+int check_attn_call(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queries* qs, const void* q,
+                    int heads, int d_v, const int32_t* idx, int topk, float sm_scale, void* out) {
+    int rc = check_attn(pt, kv, qs, heads, d_v, topk);
+    if (rc != SIA_OK) return rc;
+    if (qs->num_q > 0 && (!q || !idx || !out)) return fail(SIA_ERR_INVALID_ARG, "q/idx/out is NULL");
+    if (!std::isfinite(sm_scale)) return fail(SIA_ERR_INVALID_ARG, "sm_scale is not finite");
+    return SIA_OK;
+}
+
+// Scratch of sparse_mla_attention_noalloc: one copy per GPU, held until the
+// process ends. Host code never uses the symbol's name as an address (on the
+// host it is only a stand-in); the device address of each GPU's copy is
+// looked up once per device with hipGetSymbolAddress, with that device
+// current, and kept in g_scratch.
+constexpr size_t kNoAllocScratch = SIA_MLA_NOALLOC_MAX_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratch];
+
+namespace {
+
+// Device address of the current GPU's scratch (looked up on its first use).
+int scratch_of_current_device(uint8_t** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SIA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "scratch address");
+        if (!p || reinterpret_cast<uintptr_t>(p) % 256) return fail(SIA_ERR_HIP, "scratch address is not 256-byte aligned");
+        g_scratch[dev] = static_cast<uint8_t*>(p);
+    }
+    *out = g_scratch[dev];
+    return SIA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_attention(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queries* qs,
+                         const void* q, int32_t heads, int32_t d_v, const int32_t* idx, int32_t topk,
+                         float sm_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    int rc = check_attn_call(pt, kv, qs, q, heads, d_v, idx, topk, sm_scale, out);
+    if (rc != SIA_OK) return rc;
+    int hb, ns, rps;
+    size_t total;
+    attn_plan(qs, heads, topk, hb, ns, rps, total);
+    if ((rc = check_workspace(workspace, workspace_bytes, total)) != SIA_OK) return rc;
+    if (qs->num_q == 0) return SIA_OK;
+    return mla_run(pt, kv, qs, q, heads, d_v, idx, topk, sm_scale, out, lse, static_cast<uint8_t*>(workspace),
+                   hb, ns, rps, static_cast<hipStream_t>(stream));
+}
+
+int sparse_mla_attention_noalloc(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queries* qs,
+                                 const void* q, int32_t heads, int32_t d_v, const int32_t* idx, int32_t topk,
+                                 float sm_scale, void* out, float* lse, void* stream) {
+    int rc = check_attn_call(pt, kv, qs, q, heads, d_v, idx, topk, sm_scale, out);
+    if (rc != SIA_OK) return rc;
+    int hb, ns, rps;
+    size_t total;
+    attn_plan(qs, heads, topk, hb, ns, rps, total);
+    if (total > kNoAllocScratch)
+        return fail(SIA_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the no-allocation entry point holds %zu "
+                    "(use sparse_mla_attention with a workspace)", total, kNoAllocScratch);
+    if (qs->num_q == 0) return SIA_OK;
+    uint8_t* ws = nullptr;
+    if ((rc = scratch_of_current_device(&ws)) != SIA_OK) return rc;
+    return mla_run(pt, kv, qs, q, heads, d_v, idx, topk, sm_scale, out, lse, ws, hb, ns, rps,
+                   static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------ misc

@@ -147,3 +147,32 @@ def test_zigzag_covers_every_shard_once_with_balanced_linear_cost(S):
     # with cost linear in the shard index, every full pair costs the same
     full = [sum(p) for p in pairs if len(p) == 2]
     assert len(set(full)) <= 1
+
+
+def test_noalloc_attention_rejects_calls_beyond_its_scratch():
+    """sparse_mla_attention_noalloc checks its scratch need on the host: a call
+    whose row-slice partials exceed SIA_MLA_NOALLOC_MAX_BYTES (64 queries x 4
+    slices of 8192 rows x 128 heads) is refused with SIA_ERR_WORKSPACE before
+    anything is launched; bad shapes are refused like the workspace form's."""
+    buf, pt, c, q, addr = _descs(num_q=64)
+    kv = L.PagedCache(addr, None, 4, 576, 0)
+    f = L.lib().sparse_mla_attention_noalloc
+    rc = f(ctypes.byref(pt), ctypes.byref(kv), ctypes.byref(q), addr, 128, 512, addr, 8192,
+           ctypes.c_float(0.04), addr, None, None)
+    assert rc == L.SIA_ERR_WORKSPACE
+    assert "no-allocation" in L.last_error()
+    need = L.lib().sia_mla_workspace_size(ctypes.byref(q), 128, 512, 8192)
+    assert need > L.MLA_NOALLOC_MAX_BYTES
+    rc = f(ctypes.byref(pt), ctypes.byref(kv), ctypes.byref(q), addr, 24, 512, addr, 256,
+           ctypes.c_float(0.04), addr, None, None)
+    assert rc == L.SIA_ERR_UNSUPPORTED
+    rc = f(ctypes.byref(pt), ctypes.byref(kv), ctypes.byref(q), addr, 128, 512, addr, 256,
+           ctypes.c_float(float("nan")), addr, None, None)
+    assert rc == L.SIA_ERR_INVALID_ARG
+    assert L.MLA_NOALLOC_MAX_BYTES == _header_noalloc_max()
+
+
+def _header_noalloc_max():
+    src = open(os.path.join(ROOT, "include", "sia.h")).read()
+    m = re.search(r"#define SIA_MLA_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    return int(m.group(1)) << int(m.group(2))
