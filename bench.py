@@ -4,15 +4,22 @@ MI355X.
 Default workload: speculative decode, 64 sequences x 131072 positions, two draft
 tokens per sequence (128 query tokens), fp8 index-K (64 heads x 128) with
 per-token scales, Top-2048, bf16 latent KV (576/512) with 128 attention heads,
-page size 64, shuffled page tables. One step = one fused indexer + Top-K pass
-and one sparse attention pass over every query token, with all inputs resident
-in HBM. Prints one JSON line.
+page size 64, shuffled page tables. One step = one indexer + Top-K call and one
+sparse attention call over every query token, with all inputs resident in HBM.
+Prints one JSON line.
+
+Timing: W untimed warmup steps, then K timed steps, each between its own HIP
+events on the stream the library runs on. Between decode steps a 1 GiB buffer
+is written (outside the events) so that no step finds its inputs in the 256 MB
+Infinity Cache left by the previous one. The line reports the median step
+(value, ms_per_step), the minimum and the mean.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -21,20 +28,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+FLUSH_BYTES = 1 << 30   # four times the Infinity Cache
 
 
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="spec_decode_128k")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true",
                    help="leave out the 16K causal prefill figures")
+    p.add_argument("--no-flush", action="store_true",
+                   help="do not evict the Infinity Cache between decode steps")
     p.add_argument("--graph", action="store_true",
-                   help="replay every call from a HIP graph instead of launching it from the host "
-                        "(measured the same as host launches on this path)")
+                   help="replay every call from a HIP graph instead of launching it from the host")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="instead of the path, run a plain device copy of this many bytes "
                         "(calibrates the FETCH_SIZE / WRITE_SIZE counters)")
@@ -94,6 +103,33 @@ def copy_calibration(nbytes: int):
     print(json.dumps({"copy_bytes": src.numel() * 4, "dispatches": 5}))
 
 
+def measured_bandwidth(nbytes: int = 1 << 30, reps: int = 10):
+    """What this GPU's HBM delivers to plain kernels: a device copy (bytes read
+    plus bytes written per second) and a read-only reduction, medians of `reps`."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device="cuda:0")
+
+    def med(fn):
+        ts = []
+        for _ in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts[2:])
+    t_copy = med(lambda: dst.copy_(src))
+    t_read = med(lambda: torch.sum(src, dim=0, out=acc))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_gbs": 2 * nbytes / (t_copy * 1e-3) / 1e9, "read_gbs": nbytes / (t_read * 1e-3) / 1e9,
+            "bytes": nbytes, "note": "device copy counts read + written bytes; read = torch.sum over "
+                                     "the buffer; medians of %d" % reps}
+
+
 def algorithmic_bytes(wl, idx):
     """Bytes the method must move per step: every visible index-K row (+ scale)
     of each sequence once, each selected latent row once per sequence (rows
@@ -115,49 +151,158 @@ def algorithmic_bytes(wl, idx):
     q_bytes = Q * (s.heads_idx * s.dim_idx * 2 + s.heads_idx * 4 + s.heads_attn * 576 * 2)
     out_bytes = Q * (s.heads_attn * 512 * 2 + s.topk * 4)
     pt_bytes = int(((lens + 63) // 64).sum()) * 4
+    del B
     return dict(index_k=idx_bytes, latent=kv_bytes, queries=q_bytes, outputs=out_bytes,
                 page_table=pt_bytes, total=idx_bytes + kv_bytes + q_bytes + out_bytes + pt_bytes,
                 indexer=idx_bytes + Q * (s.heads_idx * s.dim_idx * 2 + s.heads_idx * 4) + pt_bytes
                 + Q * s.topk * 4)
 
 
-def cpu_baseline(wl_gpu, s, budget_s: float = 12.0):
+def prefill_flops(s, wl):
+    """Algorithmic flops of one causal prefill pass: 2*H_I*d_I per visible
+    (query, position) for the indexer, 2*H_A*(576 + 512) per selected
+    (query, row) for attention."""
+    t = wl.q_pos.long().cpu() + 1
+    vis = float(t.sum())
+    sel = float(torch_min(t, s.topk).sum())
+    return 2.0 * s.heads_idx * s.dim_idx * vis, 2.0 * s.heads_attn * (576 + 512) * sel
+
+
+def torch_min(t, k):
+    import torch
+    return torch.clamp(t, max=k)
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def _oracle_cost(s, t):
+    """Closed-form work of the oracle for queries at positions t (numpy array):
+    indexer dot products over t+1 positions, attention over min(t+1, K) rows."""
+    import numpy as np
+    t = np.asarray(t, dtype=np.float64)
+    return float((2.0 * s.heads_idx * s.dim_idx * (t + 1)
+                  + 2.0 * s.heads_attn * (576 + 512) * np.minimum(t + 1, s.topk)).sum())
+
+
+def cpu_baseline(wl_gpu, s, budget_s: float = 12.0, single_s: float = 4.0):
     """The oracle on a bounded sample of the same workload: whole sequences,
-    taken in order until about budget_s seconds of CPU work are done."""
+    eight at a time (so that every host thread has a query), until about
+    budget_s seconds of CPU work are done; then the same with one thread on
+    one sequence."""
     import oracle
     import workloads as W
     oracle.build(force=False)
     nq, dt, seqs = 0, 0.0, 0
-    for seq in range(int(wl_gpu.seq_lens.numel())):
-        sub = W.subset(wl_gpu, [seq], device="cpu")
+    B = int(wl_gpu.seq_lens.numel())
+    while seqs < B and dt < budget_s:
+        batch = list(range(seqs, min(B, seqs + 8)))
+        sub = W.subset(wl_gpu, batch, device="cpu")
         t0 = time.perf_counter()
         oracle.run(sub, attention=True)
         dt += time.perf_counter() - t0
         nq += sub.num_q
-        seqs += 1
-        if dt >= budget_s:
-            break
-    return {"value": nq / dt, "unit": "query tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{nq} query tokens of {seqs} sequences ({s.ctx_hi} positions each) of "
-                      f"{s.name}: indexer, Top-K and attention, {dt:.1f} s"}
+        seqs += len(batch)
+    cores = oracle.num_threads()
+    out = {"value": nq / dt, "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"{nq} query tokens of {seqs} sequences ({s.ctx_hi} positions each) of "
+                     f"{s.name}, eight sequences per call: indexer, Top-K and attention, {dt:.1f} s"}
+    prev = oracle.set_num_threads(1)
+    try:
+        sub = W.subset(wl_gpu, [0], device="cpu")
+        t0 = time.perf_counter()
+        oracle.run(sub, attention=True)
+        d1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(prev)
+    out["single_thread"] = {"value": sub.num_q / d1, "unit": "query tokens/s", "cores": 1,
+                            "sample": f"{sub.num_q} query tokens of sequence 0, {d1:.1f} s"}
+    return out
 
+
+def cpu_prefill_extrapolated(wl_gpu, s, rows_per_chunk: int):
+    """The oracle timed on a seeded, evenly spaced sample of a causal prefill's
+    query rows (rows_per_chunk per chunk of s.chunk queries, or per sequence for
+    a single-shot prefill), extrapolated to the whole prefill with the
+    closed-form cost of every row. An extrapolation, labelled as one."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle
+    oracle.build(force=False)
+    n = wl_gpu.num_q
+    chunk = s.chunk or n
+    rows = []
+    for c in range(n // chunk):
+        rows.extend(np.linspace(c * chunk, (c + 1) * chunk - 1, rows_per_chunk).astype(int).tolist())
+    rows = np.unique(np.array(rows))
+    cpu = lambda t: None if t is None else t.cpu()
+    r = __import__("torch").as_tensor(rows, device=wl_gpu.q_idx.device)
+    sub = dataclasses.replace(wl_gpu, seq_lens=cpu(wl_gpu.seq_lens), page_table=cpu(wl_gpu.page_table),
+                              idx_k=cpu(wl_gpu.idx_k), idx_scale=cpu(wl_gpu.idx_scale), kv=cpu(wl_gpu.kv),
+                              q_idx=wl_gpu.q_idx[r].cpu(), w=wl_gpu.w[r].cpu(), q_attn=wl_gpu.q_attn[r].cpu(),
+                              q_seq=wl_gpu.q_seq[r].cpu(), q_pos=wl_gpu.q_pos[r].cpu())
+    t0 = time.perf_counter()
+    oracle.run(sub, attention=True)
+    dt = time.perf_counter() - t0
+    pos = wl_gpu.q_pos.cpu().numpy()
+    rate = _oracle_cost(s, pos[rows]) / dt            # flop/s the oracle sustained on the sample
+    t_all = _oracle_cost(s, pos) / rate
+    return {"value": n / t_all, "unit": "prefill tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "extrapolated": True,
+            "sample": f"{len(rows)} evenly spaced query rows of {s.name} ({rows_per_chunk} per "
+                      f"{'chunk' if s.chunk else 'sequence'}) timed in {dt:.1f} s, extrapolated to all "
+                      f"{n} rows by the closed-form cost sum_t 2 H_I d_I (t+1) + 2 H_A (576+512) "
+                      f"min(t+1, K)"}
+
+
+# ------------------------------------------------------------------ GPU timing
 
 METRIC = "decode queries/s and HBM GB/s at 128K ctx; prefill tokens/s (indexer+TopK+sparse attn)"
-
 
 GRAPH = False   # replay each call from a HIP graph (set from --graph)
 
 
-def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True):
+def _kernel_nodes(graph) -> int:
+    """Kernel launches recorded in a captured graph, or -1 if torch cannot hand
+    out the graph handle."""
+    import ctypes
+    try:
+        raw = graph.raw_cuda_graph()
+    except Exception:
+        return -1
+    hip = ctypes.CDLL("libamdhip64.so")
+    n = ctypes.c_size_t(0)
+    if hip.hipGraphGetNodes(ctypes.c_void_p(raw), None, ctypes.byref(n)) != 0:
+        return -1
+    nodes = (ctypes.c_void_p * n.value)()
+    if hip.hipGraphGetNodes(ctypes.c_void_p(raw), nodes, ctypes.byref(n)) != 0:
+        return -1
+    kernels = 0
+    for i in range(n.value):
+        t = ctypes.c_int(-1)
+        if hip.hipGraphNodeGetType(ctypes.c_void_p(nodes[i]), ctypes.byref(t)) == 0 and t.value == 0:
+            kernels += 1
+    return kernels
+
+
+def _stats(ts):
+    return {"median": statistics.median(ts), "min": min(ts), "mean": sum(ts) / len(ts)}
+
+
+def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True, flush=None, graph=None):
     """Times `steps` passes of the whole path (indexer + Top-K, then sparse
-    attention) with HIP events on the stream the library runs on. Returns the
-    indices of the last pass, ms per step and ms per phase. `sched` picks the
-    causal prefill tile schedule (-1: the library's default). With GRAPH, each
-    call is captured once into a HIP graph after the eager warmup and the timed
-    steps replay the graphs (the same kernels and arguments, without the host
-    launch path); the events sit between the replays."""
+    attention), each between HIP events on the stream the library runs on
+    (torch's current stream, which the binding passes to the library). With
+    `flush` (a device buffer), the buffer is written between steps, outside the
+    events. Returns the indices of the last pass and per-step statistics (ms)
+    of the step and of each phase, plus the kernel launches of one step (from a
+    captured graph). `sched` picks the causal prefill tile schedule (-1: the
+    library's default). With GRAPH, each call is captured once into a HIP graph
+    after the eager warmup and the timed steps replay the graphs."""
     import torch
+    if graph is None:
+        graph = GRAPH
     dev = wl.q_idx.device
     maxv = int(torch.minimum(wl.q_pos.long() + 1, wl.seq_lens.long()[wl.q_seq.long()]).max())
     ws_i = sia.new_workspace(sia.indexer_workspace_size(wl.page_table, wl.seq_lens, wl.idx_k,
@@ -183,7 +328,14 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True):
         indexer()
         attention()
     torch.cuda.synchronize()
-    if GRAPH:
+    # launches of one step, counted from a graph of it
+    g_step = torch.cuda.CUDAGraph(keep_graph=True)
+    with torch.cuda.graph(g_step):
+        indexer()
+        attention()
+    torch.cuda.synchronize()
+    launches = _kernel_nodes(g_step)
+    if graph:
         g_idx = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_idx):
             indexer()
@@ -198,64 +350,98 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True):
             indexer()
             attention()
         torch.cuda.synchronize()
+    del g_step
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record()
-    for e0, e1, e2 in ev:
+    for i, (e0, e1, e2) in enumerate(ev):
+        if flush is not None:
+            flush.fill_(i & 0x7f)
         e0.record()
         indexer()
         e1.record()
         attention()
         e2.record()
-    t_end.record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / steps
-    idx_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / steps
-    att_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / steps
-    return idx, ms, idx_ms, att_ms
+    step = [e0.elapsed_time(e2) for e0, _, e2 in ev]
+    ph_i = [e0.elapsed_time(e1) for e0, e1, _ in ev]
+    ph_a = [e1.elapsed_time(e2) for _, e1, e2 in ev]
+    return idx, _stats(step), _stats(ph_i), _stats(ph_a), launches
 
 
-def prefill_flops(s, wl):
-    """Algorithmic flops of one causal prefill pass: 2*H_I*d_I per visible
-    (query, position) for the indexer, 2*H_A*(576 + 512) per selected
-    (query, row) for attention."""
-    t = wl.q_pos.long().cpu() + 1
-    vis = float(t.sum())
-    sel = float(torch_min(t, s.topk).sum())
-    return 2.0 * s.heads_idx * s.dim_idx * vis, 2.0 * s.heads_attn * (576 + 512) * sel
-
-
-def torch_min(t, k):
+def wg_balance(sia, wl, s, sched, reps=3):
+    """Per-CU load of the causal prefill indexer under tile schedule `sched`:
+    every workgroup records its CU (hardware ids), start and end; a CU's busy
+    time is the union of its workgroups' intervals. Returns max/mean busy time
+    over the CUs, the mean busy fraction of the kernel's span, and the span
+    (median over `reps` runs)."""
+    import numpy as np
     import torch
-    return torch.clamp(t, max=k)
+    n_wg = (wl.num_q + 3) // 4
+    trace = torch.zeros((n_wg, 4), dtype=torch.int64, device=wl.q_idx.device)
+    res = []
+    for _ in range(reps):
+        trace.zero_()
+        sia.sparse_indexer_topk_traced(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq,
+                                       wl.q_pos, wl.q_idx, wl.w, s.topk, trace, group=wl.num_q,
+                                       sched=sched)
+        torch.cuda.synchronize()
+        t = trace.cpu().numpy().astype(np.uint64)
+        t = t[t[:, 2] > 0]
+        hw = t[:, 0] & np.uint64(0xffffffff)
+        xcc = (t[:, 0] >> np.uint64(32)) & np.uint64(0xf)
+        cu_key = (xcc << np.uint64(8)) | (((hw >> np.uint64(13)) & np.uint64(7)) << np.uint64(5)) | \
+                 (((hw >> np.uint64(12)) & np.uint64(1)) << np.uint64(4)) | ((hw >> np.uint64(8)) & np.uint64(0xf))
+        start, end = t[:, 1].astype(np.int64), t[:, 2].astype(np.int64)
+        busy = {}
+        for k in np.unique(cu_key):
+            m = cu_key == k
+            iv = sorted(zip(start[m], end[m]))
+            tot, cs, ce = 0, iv[0][0], iv[0][1]
+            for a, b in iv[1:]:
+                if a > ce:
+                    tot += ce - cs
+                    cs, ce = a, b
+                else:
+                    ce = max(ce, b)
+            busy[int(k)] = tot + ce - cs
+        b = np.array(list(busy.values()), dtype=np.float64)
+        span = float(end.max() - start.min())
+        res.append({"cus": int(len(b)), "max_over_mean": float(b.max() / b.mean()),
+                    "mean_busy_frac": float(b.mean() / span), "span_ms": span / 1e5})
+    res.sort(key=lambda r: r["span_ms"])
+    return res[len(res) // 2]
 
 
-def prefill_line(wl, s, steps, warmup):
+def prefill_line(wl, s, steps, warmup, cpu=True):
     """Causal prefill: every position of the sequence is a query that sees
-    positions 0..t. Reports tokens/s and MFMA throughput of each phase."""
+    positions 0..t. Reports tokens/s and MFMA throughput of each phase, the
+    indexer's tile schedules timed alone with their per-CU balance."""
     import indexer_top_sparse_02_amd as sia
-    idx, ms, idx_ms, att_ms = time_path(sia, wl, s, wl.num_q, steps, warmup)
+    idx, st, si, sa, launches = time_path(sia, wl, s, wl.num_q, steps, warmup)
+    ms, idx_ms, att_ms = st["median"], si["median"], sa["median"]
     f_idx, f_att = prefill_flops(s, wl)
-    # the causal tile schedules of the fused indexer, timed alone (same results)
-    sched_ms = {}
+    sched_ms, balance = {}, {}
     for name, code in (("naive", 0), ("heavy_first", 1), ("zigzag", 2)):
-        sched_ms[name] = time_path(sia, wl, s, wl.num_q, max(2, steps // 2), 1, sched=code,
-                                   attention_too=False)[2]
+        sched_ms[name] = time_path(sia, wl, s, wl.num_q, max(3, steps // 4), 1, sched=code,
+                                   attention_too=False)[2]["median"]
+        balance[name] = wg_balance(sia, wl, s, code)
     ti, ta = f_idx / (idx_ms * 1e-3) / 1e12, f_att / (att_ms * 1e-3) / 1e12
     dominant = ("sparse_mla_attention call (sparse_mla_kernel)", ta, f_att, att_ms) \
         if att_ms >= idx_ms else ("sparse_indexer_topk call (indexer_stream_kernel)", ti, f_idx, idx_ms)
-    return {
+    line = {
         "metric": METRIC, "value": wl.num_q / (ms * 1e-3), "unit": "prefill tokens/s",
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "ms_per_step": ms, "ms_per_step_min": st["min"], "ms_per_step_mean": st["mean"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded N(0,1) caches and queries, shuffled page table)",
         "config": {"workload": s.name, "tokens": wl.num_q, "indexer_heads": s.heads_idx,
                    "index_dim": s.dim_idx, "topk": s.topk, "attention_heads": s.heads_attn,
                    "page_size": 64, "launch": "hip graph per call" if GRAPH else "eager"},
+        "launches_per_step": launches,
         "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
+        "phases_ms_min": {"indexer_topk": si["min"], "attention": sa["min"]},
         "indexer_schedule_ms": sched_ms,
+        "indexer_schedule_cu_balance": balance,
         "algorithmic_tflop": {"indexer": f_idx / 1e12, "attention": f_att / 1e12},
         "phase_tflops": {"indexer": ti, "attention": ta},
         "mfma_frac_step": (f_idx + f_att) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -264,9 +450,12 @@ def prefill_line(wl, s, steps, warmup):
                      "traffic": None, "algorithmic_tflop_per_call": dominant[2] / 1e12,
                      "call_ms": dominant[3]},
     }
+    if cpu:
+        line["cpu_baseline"] = cpu_prefill_extrapolated(wl, s, 256)
+    return line
 
 
-def chunked_line(wl, s, steps, warmup):
+def chunked_line(wl, s, steps, warmup, cpu=True):
     """Chunked causal prefill: the sequence's queries in chunks of s.chunk, each
     chunk one indexer call and one attention call against the paged caches
     (a chunk's queries see positions 0..t, so later rows already in the cache
@@ -276,9 +465,11 @@ def chunked_line(wl, s, steps, warmup):
     n_chunks = wl.num_q // s.chunk
     chunks = []
     tot_ms = tot_i = tot_a = f_i_all = f_a_all = 0.0
+    launches = 0
     for c in range(n_chunks):
         sub = wl.queries(c * s.chunk, (c + 1) * s.chunk)
-        _, ms, i_ms, a_ms = time_path(sia, sub, s, s.chunk, steps, warmup)
+        _, st, si, sa, la = time_path(sia, sub, s, s.chunk, steps, warmup)
+        ms, i_ms, a_ms = st["median"], si["median"], sa["median"]
         f_i, f_a = prefill_flops(s, sub)
         chunks.append({"chunk": c, "ms": ms, "indexer_ms": i_ms, "attention_ms": a_ms,
                        "indexer_tflops": f_i / (i_ms * 1e-3) / 1e12,
@@ -290,10 +481,11 @@ def chunked_line(wl, s, steps, warmup):
         tot_a += a_ms
         f_i_all += f_i
         f_a_all += f_a
+        launches += max(la, 0)
     dominant = ("sparse_indexer_topk calls (indexer_stream_kernel)", f_i_all / (tot_i * 1e-3) / 1e12,
                 f_i_all, tot_i) if tot_i >= tot_a else \
         ("sparse_mla_attention calls (sparse_mla_kernel)", f_a_all / (tot_a * 1e-3) / 1e12, f_a_all, tot_a)
-    return {
+    line = {
         "metric": METRIC, "value": wl.num_q / (tot_ms * 1e-3), "unit": "prefill tokens/s",
         "ms_per_step": tot_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded fp8 index-K with per-token scales, N(0,1) "
@@ -301,6 +493,7 @@ def chunked_line(wl, s, steps, warmup):
         "config": {"workload": s.name, "tokens": wl.num_q, "chunk": s.chunk, "indexer_heads": s.heads_idx,
                    "index_dim": s.dim_idx, "topk": s.topk, "attention_heads": s.heads_attn,
                    "page_size": 64, "launch": "hip graph per call" if GRAPH else "eager"},
+        "launches_per_step": launches,
         "phases_ms": {"indexer_topk": tot_i, "attention": tot_a},
         "algorithmic_tflop": {"indexer": f_i_all / 1e12, "attention": f_a_all / 1e12},
         "mfma_frac_step": (f_i_all + f_a_all) / (tot_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -310,6 +503,34 @@ def chunked_line(wl, s, steps, warmup):
                      "traffic": None, "algorithmic_tflop_per_call": dominant[2] / 1e12 / n_chunks,
                      "call_ms": dominant[3] / n_chunks},
     }
+    if cpu:
+        line["cpu_baseline"] = cpu_prefill_extrapolated(wl, s, 8)
+    return line
+
+
+def launch_overhead(sia, W, dev, steps, warmup):
+    """The small decode workloads, where a step takes tens of microseconds:
+    host launches against replays of one HIP graph per call (the same kernels
+    and arguments), with the Infinity Cache evicted between steps."""
+    import torch
+    out = {}
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    for name in ("tiny_decode", "decode_b32"):
+        s = W.spec(name)
+        wl = W.make(s, device=dev)
+        r = {}
+        for mode, g in (("eager", False), ("graph", True)):
+            _, st, si, sa, la = time_path(sia, wl, s, s.q_per_seq, steps, warmup, flush=flush, graph=g)
+            r[mode] = {"ms_per_step": st["median"], "ms_per_step_min": st["min"],
+                       "phases_ms": {"indexer_topk": si["median"], "attention": sa["median"]}}
+            r["launches_per_step"] = la
+        r["query_tokens_per_s"] = {m: wl.num_q / (r[m]["ms_per_step"] * 1e-3) for m in ("eager", "graph")}
+        r["graph_saving_us"] = (r["eager"]["ms_per_step"] - r["graph"]["ms_per_step"]) * 1e3
+        out[name] = r
+        del wl
+    del flush
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -332,54 +553,76 @@ def main():
     torch.cuda.set_device(dev)
     s = W.spec(a.config)
     if s.prefill:
+        wl = W.make(s, device=dev)
         if s.chunk:
-            line = chunked_line(W.make(s, device=dev), s, max(1, a.steps // 4), max(1, a.warmup))
+            line = chunked_line(wl, s, max(3, a.steps // 8), max(1, a.warmup), cpu=not a.no_cpu_baseline)
         else:
-            line = prefill_line(W.make(s, device=dev), s, a.steps, a.warmup)
+            line = prefill_line(wl, s, a.steps, a.warmup, cpu=not a.no_cpu_baseline)
         line.update({"n_gpus": 1, "steps": a.steps, "warmup": a.warmup})
         print(json.dumps(line))
         return
+    bw = measured_bandwidth()
     wl = W.make(s, device=dev)
     group = s.q_per_seq
-    idx, ms, idx_ms, att_ms = time_path(sia, wl, s, group, a.steps, a.warmup)
+    flush = None if a.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    idx, st, si, sa, launches = time_path(sia, wl, s, group, a.steps, a.warmup, flush=flush)
+    ms, idx_ms, att_ms = st["median"], si["median"], sa["median"]
     by = algorithmic_bytes(wl, idx)
     step_gbs = by["total"] / (ms * 1e-3) / 1e9
     idx_gbs = by["indexer"] / (idx_ms * 1e-3) / 1e9
+    att_bytes = by["latent"] + wl.num_q * (s.heads_attn * 576 * 2 + s.heads_attn * 512 * 2 + s.topk * 4)
     line = {
         "metric": METRIC,
         "value": wl.num_q / (ms * 1e-3),
         "unit": "query tokens/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "ms_per_step_min": st["min"], "ms_per_step_mean": st["mean"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16",
         "dtype_detail": "fp8 e4m3fn index keys fed raw to fp8 MFMA against a two-term e4m3 split "
-                        "of the bf16 query (equal to the bf16 product up to rounding order), fp32 "
-                        "accumulate; bf16 latent KV with bf16 MFMA; fp32 softmax",
+                        "of the bf16 query (exact for |q| >= 2^-13 max|q|, within 2^-21 max|q| "
+                        "below), fp32 accumulate; bf16 latent KV with bf16 MFMA; fp32 softmax",
         "data": "synthetic (seeded N(0,1) caches and queries, shuffled page tables)",
         "config": {"workload": s.name, "batch": s.batch, "context": s.ctx_hi,
                    "query_tokens": wl.num_q, "indexer_heads": s.heads_idx, "index_dim": s.dim_idx,
                    "topk": s.topk, "attention_heads": s.heads_attn, "page_size": 64,
-                   "launch": "hip graph per call" if GRAPH else "eager"},
+                   "launch": "hip graph per call" if GRAPH else "eager",
+                   "cache_flush_between_steps": flush is not None},
+        "timing": "median of %d steps, each between HIP events; %s" % (
+            a.steps, "1 GiB written between steps (outside the events) to evict the Infinity Cache"
+            if flush is not None else "steps back to back"),
+        "launches_per_step": launches,
         "hbm_gbs_step": step_gbs,
+        "sequences_per_s": s.batch / (ms * 1e-3),
         "phases_ms": {"indexer_topk": idx_ms, "attention": att_ms},
+        "phases_ms_min": {"indexer_topk": si["min"], "attention": sa["min"]},
+        "phase_hbm_gbs": {"indexer_topk": idx_gbs, "attention": att_bytes / (att_ms * 1e-3) / 1e9},
         "algorithmic_bytes": by,
+        "measured_bandwidth": bw,
         "roofline": {"bound": "hbm",
                      "kernel": "sparse_indexer_topk call (indexer_pair_kernel score pass + "
                                "topk_rows_kernel selection pass)",
                      "achieved": idx_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": idx_gbs / PEAK_HBM_GBS, "traffic": measured_traffic(s.name),
+                     "frac_of_measured_copy": idx_gbs / bw["copy_gbs"],
+                     "frac_of_measured_read": idx_gbs / bw["read_gbs"],
                      "algorithmic_bytes_per_call": by["indexer"],
-                     "call_ms": idx_ms},
+                     "call_ms": idx_ms, "call_ms_min": si["min"]},
     }
-    del wl, idx
+    del wl, idx, flush
     torch.cuda.empty_cache()
+    line["small_decode_launch_overhead"] = launch_overhead(sia, W, dev, a.steps, a.warmup)
     if not a.no_prefill:
         ps = W.spec("prefill_16k")
-        line["prefill"] = prefill_line(W.make(ps, device=dev), ps, max(2, a.steps // 4),
-                                       max(1, a.warmup))
+        line["prefill"] = prefill_line(W.make(ps, device=dev), ps, max(10, a.steps // 2),
+                                       max(1, a.warmup), cpu=not a.no_cpu_baseline)
         torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(W.make(s, device=dev), s)
+        cs = W.spec("chunked_prefill_128k")
+        line["cpu_baseline"]["extrapolated"] = {
+            "prefill_16k": line["prefill"]["cpu_baseline"] if "prefill" in line else None,
+            "chunked_prefill_128k": cpu_prefill_extrapolated(W.make(cs, device=dev), cs, 8)}
     print(json.dumps(line))
 
 

@@ -152,6 +152,22 @@ int sparse_indexer_topk(const sia_page_table *pt, const sia_paged_cache *index_k
                         int32_t sched, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Test hook: sparse_indexer_topk with a record of where and when each
+ * workgroup of the causal stream kernel (the prefill path) ran, to measure how
+ * evenly a tile schedule loads the compute units. Results are those of
+ * sparse_indexer_topk. wg_trace: device uint64 [trace_cap, 4]; record i of
+ * workgroup i < trace_cap = {hardware ids (XCC_ID << 32 | HW_ID register:
+ * shader engine, array, CU, SIMD, wave), start, end (a 100 MHz clock shared by
+ * the whole GPU), query tiles the workgroup ran}. Calls that take the decode
+ * path (score + selection passes) write no records.
+ */
+int sparse_indexer_topk_traced(const sia_page_table *pt, const sia_paged_cache *index_k,
+                               const sia_queries *qs, const void *q_idx, const float *w,
+                               int32_t heads, int32_t topk, int32_t *out_idx, float *out_score,
+                               int32_t sched, void *workspace, size_t workspace_bytes, void *stream,
+                               uint64_t *wg_trace, int32_t trace_cap);
+
+/*
  * Test hook: the indexer's scores without selection, computed by the same device
  * code the fused pass uses, so that selection can be checked on identical
  * scores. scores: device fp32 [num_q, ld]; entry s of row j holds the score of

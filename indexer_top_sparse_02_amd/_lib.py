@@ -27,7 +27,8 @@ SCHED_AUTO, SCHED_NAIVE, SCHED_HEAVY_FIRST, SCHED_ZIGZAG = -1, 0, 1, 2
 DEVSTATUS_BAD_SEQ, DEVSTATUS_BAD_PAGE, DEVSTATUS_ROW_TOO_LONG, DEVSTATUS_BAD_INDEX = 1, 2, 4, 8
 
 EXPORTS = [
-    "sia_indexer_workspace_size", "sparse_indexer_topk", "sparse_indexer_scores",
+    "sia_indexer_workspace_size", "sparse_indexer_topk", "sparse_indexer_topk_traced",
+    "sparse_indexer_scores",
     "sia_topk_workspace_size", "sparse_topk_from_scores", "sia_mla_workspace_size",
     "sparse_mla_attention", "sparse_mla_attention_noalloc", "sia_zigzag_assign",
     "sia_clear_device_status", "sia_read_device_status", "sia_last_error", "sia_version",
@@ -74,6 +75,8 @@ def lib():
             "sia_indexer_workspace_size": (c_sz, [pPT, pPC, pQ, c_i32, c_i32]),
             "sparse_indexer_topk": (ctypes.c_int, [pPT, pPC, pQ, P, P, c_i32, c_i32, P, P, c_i32, P,
                                                    c_sz, P]),
+            "sparse_indexer_topk_traced": (ctypes.c_int, [pPT, pPC, pQ, P, P, c_i32, c_i32, P, P, c_i32,
+                                                          P, c_sz, P, P, c_i32]),
             "sparse_indexer_scores": (ctypes.c_int, [pPT, pPC, pQ, P, P, c_i32, P, c_i64, P, c_sz, P]),
             "sia_topk_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
             "sparse_topk_from_scores": (ctypes.c_int, [P, c_i64, P, c_i32, c_i32, c_i32, P, P, P, c_sz,
@@ -186,6 +189,31 @@ def sparse_indexer_topk(page_table, seq_lens, rows, scale, q_seq, q_pos, q_idx, 
                                      _ptr(w), H, int(topk), _ptr(out_idx), _ptr(out_score), int(sched),
                                      _ptr(workspace), workspace.numel(), _stream(stream)))
     return out_idx, out_score
+
+
+def sparse_indexer_topk_traced(page_table, seq_lens, rows, scale, q_seq, q_pos, q_idx, w, topk,
+                               trace, *, group=1, max_visible=None, out_idx=None, sched=SCHED_AUTO,
+                               workspace=None, stream=None):
+    """sparse_indexer_topk that also fills `trace` (int64 [n, 4] on the GPU) with
+    one record per workgroup of the causal stream kernel: hardware ids
+    (XCC_ID << 32 | HW_ID), start and end ticks of a 100 MHz clock, tiles run."""
+    Q, H = int(q_idx.shape[0]), int(q_idx.shape[1])
+    dev = q_idx.device
+    if max_visible is None:
+        max_visible = visible_max(q_seq, q_pos, seq_lens)
+    pt, c = page_table_desc(page_table, seq_lens), cache_desc(rows, scale)
+    q = queries_desc(q_seq, q_pos, group, max_visible)
+    need = lib().sia_indexer_workspace_size(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(q), H,
+                                            int(topk))
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    if out_idx is None:
+        out_idx = torch.empty((Q, topk), dtype=torch.int32, device=dev)
+    _check(lib().sparse_indexer_topk_traced(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(q), _ptr(q_idx),
+                                            _ptr(w), H, int(topk), _ptr(out_idx), None, int(sched),
+                                            _ptr(workspace), workspace.numel(), _stream(stream), _ptr(trace),
+                                            int(trace.shape[0])))
+    return out_idx
 
 
 def sparse_indexer_scores(page_table, seq_lens, rows, scale, q_seq, q_pos, q_idx, w, *, group=1,

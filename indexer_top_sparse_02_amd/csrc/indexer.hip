@@ -1364,6 +1364,10 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
               reinterpret_cast<SelScratch*>(base + (size_t)(S.cap + kWave) * 8)};
     int* pages = reinterpret_cast<int*>(smem + stream_pages_offset(S.cap));
     uint8_t* ring = smem + stream_ring_offset(S.cap, A.max_visible);
+    // optional trace: where (hardware ids of the CU) and when (100 MHz clock)
+    // this workgroup ran, and how many query tiles it took
+    const uint64_t t_start = S.trace ? __builtin_amdgcn_s_memrealtime() : 0;
+    int tiles_run = 0;
 
     // One tile: four consecutive queries of one sequence. Their page ids are staged
     // once in LDS; a query of another sequence is dropped (status bit).
@@ -1389,6 +1393,7 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
         __syncthreads();
         stream_group<MB, D, FP8>(A, S, j, rl, rows, pages, B, ring);
         __syncthreads();
+        tiles_run++;
     };
     if (S.sched == 0) {
         run_tile(blockIdx.x);
@@ -1406,6 +1411,17 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
             if (n >= S.n_tiles) break;
             run_tile(heavy_first_tile(S.n_tiles, n));
         }
+    }
+    if (S.trace && threadIdx.x == 0 && (int)blockIdx.x < S.trace_cap) {
+        const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+        // HW_ID (SE, SH, CU, SIMD, wave) and XCC_ID, read whole
+        const uint32_t hw = (uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 4);
+        const uint32_t xcc = (uint32_t)__builtin_amdgcn_s_getreg((31 << 11) | (0 << 6) | 20);
+        uint64_t* r = S.trace + (int64_t)blockIdx.x * 4;
+        r[0] = ((uint64_t)xcc << 32) | hw;
+        r[1] = t_start;
+        r[2] = t_end;
+        r[3] = (uint64_t)tiles_run;
     }
 }
 

@@ -227,10 +227,14 @@ size_t sia_indexer_workspace_size(const sia_page_table* pt, const sia_paged_cach
     return plan_indexer(qs, topk, heads, index_k->dim, index_k->dtype == SIA_FP8_E4M3FN).total;
 }
 
-int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
-                        const void* q_idx, const float* w, int32_t heads, int32_t topk,
-                        int32_t* out_idx, float* out_score, int32_t sched, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                 const void* q_idx, const float* w, int32_t heads, int32_t topk, int32_t* out_idx,
+                 float* out_score, int32_t sched, void* workspace, size_t workspace_bytes, void* stream,
+                 uint64_t* trace, int32_t trace_cap) {
     int rc = check_indexer_common(pt, index_k, qs, q_idx, w, heads);
     if (rc != SIA_OK) return rc;
     if (topk < 1 || topk > 8192) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..8192", topk);
@@ -255,6 +259,8 @@ int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k
         s.counter = reinterpret_cast<uint32_t*>(ws + 4);
         s.out_idx = out_idx;
         s.out_score = out_score;
+        s.trace = trace;
+        s.trace_cap = trace ? trace_cap : 0;
         int grid = s.n_tiles;
         if (s.sched == 2) grid = sia::zigzag_workers(s.n_tiles);
         if (s.sched == 1) {
@@ -286,6 +292,27 @@ int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k
     e = sia::launch_topk_rows(sel, st);
     if (e != hipSuccess) return hip_fail(e, "top-k selection launch");
     return SIA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                        const void* q_idx, const float* w, int32_t heads, int32_t topk,
+                        int32_t* out_idx, float* out_score, int32_t sched, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    return indexer_topk(pt, index_k, qs, q_idx, w, heads, topk, out_idx, out_score, sched, workspace,
+                        workspace_bytes, stream, nullptr, 0);
+}
+
+int sparse_indexer_topk_traced(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                               const void* q_idx, const float* w, int32_t heads, int32_t topk,
+                               int32_t* out_idx, float* out_score, int32_t sched, void* workspace,
+                               size_t workspace_bytes, void* stream, uint64_t* wg_trace, int32_t trace_cap) {
+    if (!wg_trace || trace_cap < 1) return fail(SIA_ERR_INVALID_ARG, "wg_trace is NULL or trace_cap < 1");
+    return indexer_topk(pt, index_k, qs, q_idx, w, heads, topk, out_idx, out_score, sched, workspace,
+                        workspace_bytes, stream, wg_trace, trace_cap);
 }
 
 int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,

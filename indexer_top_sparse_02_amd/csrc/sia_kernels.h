@@ -80,6 +80,8 @@ struct StreamArgs {
     uint32_t* counter;
     int32_t* out_idx;
     float* out_score;
+    uint64_t* trace;           // optional [trace_cap, 4] per-workgroup records (or null)
+    int32_t trace_cap;
 };
 
 // Launchers; return hipSuccess or the launch error. `mb` = ceil(heads / 32).

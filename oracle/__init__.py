@@ -64,12 +64,19 @@ def lib():
             ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _i32p, ctypes.c_int32,
             ctypes.c_double, _f64p, _f64p]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Use n OpenMP threads from now on; returns the previous count."""
+    return int(lib().oracle_set_num_threads(int(n)))
 
 
 def _np(t, dtype=None):

@@ -266,6 +266,19 @@ int oracle_sparse_mla(int32_t num_q, const int32_t *q_seq, int32_t batch,
     return bad ? -2 : 0;
 }
 
+/* Threads the OpenMP loops above use from now on (n >= 1); returns the previous
+ * count. Only the thread count changes, never what is computed. */
+int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    const int prev = omp_get_max_threads();
+    if (n >= 1) omp_set_num_threads(n);
+    return prev;
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -323,6 +323,63 @@ def test_graph_replay_matches_eager(case):
         assert torch.equal(lse, ref[2])
 
 
+@pytest.mark.parametrize("case", ["decode_fp8", "spec_decode", "tiny_decode"])
+def test_graph_replay_matches_oracle(case):
+    """A decode step (indexer + Top-K, then attention) captured in one HIP graph
+    and replayed three times, with eager work between the replays: every
+    replay's indices are the oracle's selection of the GPU's scores, bit for
+    bit, its sets meet the band rule against the oracle's own selection, and its
+    attention output matches the oracle's on those indices."""
+    import indexer_top_sparse_02_amd as sia
+    r = _run(case)
+    wl, s = r["wl"], r["wl"].spec
+    group = group_of(wl)
+    maxv = int(r["rl"].max())
+    ws_i = sia.new_workspace(sia.indexer_workspace_size(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale,
+                                                        wl.q_seq, wl.q_pos, s.heads_idx, s.topk, group=group,
+                                                        max_visible=maxv), "cuda")
+    ws_a = sia.new_workspace(sia.mla_workspace_size(wl.num_q, s.heads_attn, s.topk), "cuda")
+    idx = torch.empty((wl.num_q, s.topk), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.num_q, s.heads_attn, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((wl.num_q, s.heads_attn), dtype=torch.float32, device="cuda")
+
+    def step():
+        sia.sparse_indexer_topk(wl.page_table, wl.seq_lens, wl.idx_k, wl.idx_scale, wl.q_seq, wl.q_pos,
+                                wl.q_idx, wl.w, s.topk, group=group, max_visible=maxv, out_idx=idx,
+                                workspace=ws_i)
+        sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx, s.sm_scale,
+                                 out=out, lse=lse, workspace=ws_a)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    ref_sel, _ = oracle_topk_of(r["scores"], r["rl"], s.topk)
+    rows = r["rows"]
+    sub = wl.to("cpu")
+    for rep in range(3):
+        idx.fill_(-7)
+        out.zero_()
+        lse.zero_()
+        _ = torch.randn(1 << 20, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        assert np.array_equal(got, ref_sel), rep
+        check_band(got[rows], r["ref_idx"], r["ref_scores"], score_tol(wl))
+        ref_out, ref_lse = oracle.sparse_mla(sub.q_seq[rows], sub.seq_lens.numel(), sub.page_table, sub.kv,
+                                             sub.q_attn[rows], got[rows], s.sm_scale)
+        sel = torch.from_numpy(rows).cuda()
+        check_attention(out[sel], ref_out, lse[sel], ref_lse)
+
+
 def test_page_placement_does_not_change_results():
     s = W.spec("decode_b32", batch=3, ctx_lo=3000, ctx_hi=6000, topk=512, heads_attn=64)
     a = W.make(s, device="cuda", shuffle=False)
