@@ -63,6 +63,11 @@ def lib():
             ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int64, _vp,
             ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _i32p, ctypes.c_int32,
             ctypes.c_double, _f64p, _f64p]
+        L.oracle_quantize_mxfp8.argtypes = [_vp, ctypes.c_int64, _vp, _vp]
+        L.oracle_indexer_scores_mx.argtypes = [
+            ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
+            ctypes.c_int64, _vp, _vp, ctypes.c_int32, _vp, _vp, _f32p, ctypes.c_int32, _f64p,
+            ctypes.c_int64, _i32p]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -172,6 +177,41 @@ def sparse_mla(q_seq, seq_count, page_table, kv, q_attn, idx, sm_scale, d_v=512)
     if rc != 0:
         raise ValueError(f"oracle_sparse_mla failed ({rc})")
     return out, lse
+
+
+def quantize_mxfp8(x):
+    """MXFP8 codes [..., D] and E8M0 scale bytes [..., D/32] of bf16 values x
+    (last dimension a multiple of 32)."""
+    xb = _np(x, np.uint16)
+    D = xb.shape[-1]
+    assert D % 32 == 0
+    codes = np.empty(xb.shape, dtype=np.uint8)
+    scales = np.empty(xb.shape[:-1] + (D // 32,), dtype=np.uint8)
+    rc = lib().oracle_quantize_mxfp8(_p(xb, _vp), xb.size // 32, _p(codes, _vp), _p(scales, _vp))
+    assert rc == 0
+    return codes, scales
+
+
+def indexer_scores_mx(q_seq, q_pos, seq_lens, page_table, k_codes, k_scales, q_codes, q_scales, w,
+                      ld=None):
+    """MXFP8-path scores [Q, ld] (double; -inf where not visible) and row lengths."""
+    q_seq, q_pos = _np(q_seq, np.int32), _np(q_pos, np.int32)
+    seq_lens, table = _np(seq_lens, np.int32), _np(page_table, np.int32)
+    kc, ks = _np(k_codes, np.uint8), _np(k_scales, np.uint8)
+    qc, qs = _np(q_codes, np.uint8), _np(q_scales, np.uint8)
+    wv = _np(w, np.float32)
+    Q, H, D = qc.shape
+    if ld is None:
+        ld = max(1, int(min(q_pos.max(initial=0) + 1, seq_lens.max(initial=0))))
+    scores = np.empty((Q, ld), dtype=np.float64)
+    row_len = np.empty(Q, dtype=np.int32)
+    rc = lib().oracle_indexer_scores_mx(
+        Q, _p(q_seq, _i32p), _p(q_pos, _i32p), len(seq_lens), _p(seq_lens, _i32p), _p(table, _i32p),
+        table.shape[1], kc.shape[0], _p(kc, _vp), _p(ks, _vp), D, _p(qc, _vp), _p(qs, _vp),
+        _p(wv, _f32p), H, _p(scores, _f64p), ld, _p(row_len, _i32p))
+    if rc != 0:
+        raise ValueError(f"oracle_indexer_scores_mx failed ({rc})")
+    return scores, row_len
 
 
 @dataclass

@@ -145,6 +145,112 @@ int oracle_indexer_scores(int32_t num_q, const int32_t *q_seq, const int32_t *q_
     return bad ? -2 : 0;
 }
 
+/*
+ * MXFP8 (the index path's quantized form: "Rapid Adaptation and Inference
+ * Optimization", section 5.1; "Day0 Inference Adaptation ... for a New
+ * Hybrid-Attention LLM Architecture", section 4.2): e4m3 elements, one E8M0
+ * scale 2^(byte - 127) per 32 consecutive elements.
+ */
+static double e8m0_value(uint8_t byte) { return ldexp(1.0, (int)byte - 127); }
+
+/* The e4m3fn code whose value is nearest to v (|v| <= 448), ties to the code
+ * with an even mantissa: a search over every finite non-negative code. */
+static uint8_t nearest_e4m3fn(double v) {
+    const double a = fabs(v);
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c < 0x7F; c++) {
+        const double err = fabs(oracle_e4m3fn_value((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(best | (v < 0.0 && best != 0 ? 0x80 : 0));
+}
+
+/*
+ * Quantize n_groups groups of 32 bf16 values: the scale is 2^e with e the
+ * smallest integer in [-127, 127] for which the group's largest magnitude is
+ * at most 448 * 2^e (the largest e4m3 value, so nothing is clipped); each
+ * element is the e4m3 code nearest to x / 2^e. An all-zero group takes
+ * e = -127.
+ */
+int oracle_quantize_mxfp8(const uint16_t *x, int64_t n_groups, uint8_t *codes, uint8_t *scales) {
+    if (n_groups < 0 || !x || !codes || !scales) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t g = 0; g < n_groups; g++) {
+        double m = 0.0;
+        for (int i = 0; i < 32; i++) {
+            const double a = fabs(oracle_bf16_value(x[g * 32 + i]));
+            if (a > m) m = a;
+        }
+        int e = -127;
+        while (e < 127 && m > ldexp(448.0, e)) e++;
+        scales[g] = (uint8_t)(e + 127);
+        for (int i = 0; i < 32; i++)
+            codes[g * 32 + i] = nearest_e4m3fn(oracle_bf16_value(x[g * 32 + i]) / ldexp(1.0, e));
+    }
+    return 0;
+}
+
+/*
+ * Indexer scores on the MXFP8 path: the query and the index rows are MXFP8,
+ * their values are the stored elements times their block scales, and no
+ * per-token scale applies:
+ *   scores[j*ld + s] = sum_h w[j,h] * max(0, q^[j,h,:] . k^_s)  for s < row_len[j]
+ * k_codes [num_pages*64, dim], k_scales [num_pages*64, dim/32],
+ * q_codes [num_q, heads, dim], q_scales [num_q, heads, dim/32].
+ */
+int oracle_indexer_scores_mx(int32_t num_q, const int32_t *q_seq, const int32_t *q_pos, int32_t batch,
+                             const int32_t *seq_lens, const int32_t *page_table, int32_t max_pages,
+                             int64_t num_pages, const uint8_t *k_codes, const uint8_t *k_scales,
+                             int32_t dim, const uint8_t *q_codes, const uint8_t *q_scales,
+                             const float *w, int32_t heads, double *scores, int64_t ld,
+                             int32_t *row_len) {
+    if (num_q < 0 || !q_seq || !q_pos || !seq_lens || !page_table || !k_codes || !k_scales ||
+        !q_codes || !q_scales || !w || !scores || !row_len || dim <= 0 || dim % 32 || heads <= 0 ||
+        batch <= 0)
+        return -1;
+    const int nb = dim / 32;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t j = 0; j < num_q; j++) {
+        int32_t b = q_seq[j];
+        double *row = scores + (int64_t)j * ld;
+        for (int64_t s = 0; s < ld; s++) row[s] = -INFINITY;
+        row_len[j] = 0;
+        if (b < 0 || b >= batch) { bad = 1; continue; }
+        int64_t n = row_length(q_pos[j], seq_lens[b]);
+        if (n > ld) { bad = 1; continue; }
+        row_len[j] = (int32_t)n;
+        double *qd = (double *)malloc(sizeof(double) * (size_t)heads * dim);
+        double *kd = (double *)malloc(sizeof(double) * (size_t)dim);
+        for (int64_t i = 0; i < (int64_t)heads * dim; i++) {
+            const int64_t e = (int64_t)j * heads * dim + i;   /* element, block e / 32 */
+            qd[i] = oracle_e4m3fn_value(q_codes[e]) *
+                    e8m0_value(q_scales[((int64_t)j * heads + i / dim) * nb + (i % dim) / 32]);
+        }
+        for (int64_t s = 0; s < n; s++) {
+            int64_t r = phys_row(page_table, max_pages, b, s);
+            if (r < 0 || r >= num_pages * SIA_ORACLE_PAGE) { bad = 1; continue; }
+            for (int32_t d = 0; d < dim; d++)
+                kd[d] = oracle_e4m3fn_value(k_codes[r * dim + d]) * e8m0_value(k_scales[r * nb + d / 32]);
+            double acc = 0.0;
+            for (int32_t h = 0; h < heads; h++) {
+                const double *qh = qd + (int64_t)h * dim;
+                double a = 0.0;
+                for (int32_t d = 0; d < dim; d++) a += qh[d] * kd[d];
+                acc += (double)w[(int64_t)j * heads + h] * (a > 0.0 ? a : 0.0);
+            }
+            row[s] = acc;
+        }
+        free(qd);
+        free(kd);
+    }
+    return bad ? -2 : 0;
+}
+
 /* Total order of the selection: higher score first, then lower position.
  * NaN ranks below every number; -0.0 equals +0.0. */
 typedef struct { double v; int32_t s; } cand_t;

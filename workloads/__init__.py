@@ -220,6 +220,45 @@ def make(s: Spec, device="cpu", poison: bool = False, shuffle: bool = True,
     return wl
 
 
+@dataclass
+class MxInputs:
+    """Synthetic MXFP8 index-path inputs for a workload with an fp8 index
+    cache: its e4m3 codes serve as the MXFP8 rows; the E8M0 block scales and
+    an MXFP8 query are drawn here (no quantizer involved)."""
+    k_scales: torch.Tensor   # uint8 [num_pages, 64, d_I / 32]
+    q_codes: torch.Tensor    # uint8 [Q, H_I, d_I] (e4m3 codes of N(0,1) draws)
+    q_scales: torch.Tensor   # uint8 [Q, H_I, d_I / 32]
+
+    def queries(self, start: int, stop: int) -> "MxInputs":
+        return replace(self, q_codes=self.q_codes[start:stop], q_scales=self.q_scales[start:stop])
+
+    def to(self, device) -> "MxInputs":
+        return MxInputs(self.k_scales.to(device), self.q_codes.to(device), self.q_scales.to(device))
+
+
+def make_mx(wl: Workload, scale_lo: int = 124, scale_hi: int = 130, poison: bool = False) -> MxInputs:
+    """MXFP8 inputs for ``wl`` (whose index cache holds e4m3 codes): block
+    scale bytes uniform in [scale_lo, scale_hi] (2^-3 .. 2^3), query codes from
+    N(0,1) cast to e4m3 and their scale bytes likewise. Seeded from the
+    workload's seed. With ``poison``, rows no sequence owns get the E8M0 NaN
+    byte 0xFF."""
+    s = wl.spec
+    assert s.idx_fp8 and s.dim_idx % 32 == 0
+    seeds = [int(x.generate_state(1)[0]) for x in np.random.SeedSequence([s.seed, 0x4D58]).spawn(3)]
+    dev = wl.idx_k.device
+    nb = s.dim_idx // 32
+    k_scales = torch.randint(scale_lo, scale_hi + 1, (wl.num_pages, PAGE, nb), generator=_gen(dev, seeds[0]),
+                             device=dev, dtype=torch.int32).to(torch.uint8)
+    Q = wl.num_q
+    q_codes = _e4m3fn_codes((Q, s.heads_idx, s.dim_idx), _gen(dev, seeds[1]), dev)
+    q_scales = torch.randint(scale_lo, scale_hi + 1, (Q, s.heads_idx, nb), generator=_gen(dev, seeds[2]),
+                             device=dev, dtype=torch.int32).to(torch.uint8)
+    if poison:
+        bad = (~owned_rows_mask(wl)).to(dev)
+        k_scales[bad] = 0xFF
+    return MxInputs(k_scales, q_codes, q_scales)
+
+
 def owned_rows_mask(wl: Workload) -> torch.Tensor:
     """bool [num_pages, 64]: True where some sequence owns the row."""
     table = wl.page_table.cpu().numpy()
