@@ -154,7 +154,9 @@ int oracle_indexer_scores(int32_t num_q, const int32_t *q_seq, const int32_t *q_
 static double e8m0_value(uint8_t byte) { return ldexp(1.0, (int)byte - 127); }
 
 /* The e4m3fn code whose value is nearest to v (|v| <= 448), ties to the code
- * with an even mantissa: a search over every finite non-negative code. */
+ * with an even mantissa: a search over every finite non-negative code for the
+ * magnitude, then v's sign bit (a negative value that rounds to zero gives -0,
+ * as a round-to-nearest conversion keeps the sign). */
 static uint8_t nearest_e4m3fn(double v) {
     const double a = fabs(v);
     int best = 0;
@@ -166,7 +168,7 @@ static uint8_t nearest_e4m3fn(double v) {
             best_err = err;
         }
     }
-    return (uint8_t)(best | (v < 0.0 && best != 0 ? 0x80 : 0));
+    return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
 }
 
 /*

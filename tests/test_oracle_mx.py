@@ -34,6 +34,9 @@ def test_quantizer_matches_its_definition():
     x[1, :32] = 448.0 * 2.0 ** 3                 # largest magnitude exactly 448 * 2^3
     x[1, 32:64] = -448.0 * 2.0 ** -5
     x[2, :32] = 1e-30                            # tiny groups
+    x[5, :32] = 448.0                            # e = 0 with negative values that round to -0
+    x[5, 1:8] = -torch.tensor([1e-6, 5e-4, 9.7e-4, 2e-3, 0.0, 1.9e-3, 1e-30])
+    x[6, 32:64] = -0.0
     xb = _bf16(x)
     codes, scales = oracle.quantize_mxfp8(xb)
     xv = xb.double().numpy().reshape(64, 4, 32)
@@ -46,6 +49,7 @@ def test_quantizer_matches_its_definition():
     assert np.all(e[0] == -127) and np.all(codes[0] == 0)
     assert e[1, 0] == 3 and e[1, 1] == -5
     assert codes[1, 0] == 0x7E and codes[1, 32] == 0xFE          # +448 and -448
+    assert codes[5, 1] == 0x80 and codes[6, 32] == 0x80          # -0 keeps its sign
     # codes: torch's RNE cast of x / 2^e
     scaled = torch.from_numpy(xv / 2.0 ** e[..., None]).float().reshape(64, 128)
     ref = scaled.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
