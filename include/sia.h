@@ -79,7 +79,10 @@ typedef enum {
 
 typedef enum {
     SIA_BF16 = 0,         /* bfloat16 */
-    SIA_FP8_E4M3FN = 1    /* OCP float8 E4M3 (max 448, no infinities) */
+    SIA_FP8_E4M3FN = 1,   /* OCP float8 E4M3 (max 448, no infinities) */
+    SIA_MXFP8_E4M3 = 2    /* MXFP8: E4M3 elements, one E8M0 scale (2^(byte - 127)) per 32
+                             consecutive elements of a row ("Rapid Adaptation ...", section 5.1
+                             "Full Quantization for the Indexer Path"; index caches only) */
 } sia_dtype;
 
 /* Page table shared by the index-K cache and the latent KV cache. */
@@ -91,10 +94,12 @@ typedef struct {
     int32_t page_size;         /* must be 64 */
 } sia_page_table;
 
-/* One paged cache: [num_pages, page_size, dim] rows (+ fp8 per-token scales). */
+/* One paged cache: [num_pages, page_size, dim] rows (+ their scales). */
 typedef struct {
     const void *rows;          /* device [num_pages, 64, dim] elements of `dtype` */
-    const float *scale;        /* device [num_pages, 64]; required for SIA_FP8_E4M3FN, else NULL */
+    const void *scale;         /* device; SIA_FP8_E4M3FN: fp32 [num_pages, 64] per-token scales;
+                                  SIA_MXFP8_E4M3: uint8 E8M0 [num_pages, 64, dim / 32] block scales;
+                                  NULL for SIA_BF16 */
     int64_t num_pages;
     int32_t dim;
     int32_t dtype;             /* sia_dtype */
@@ -150,6 +155,45 @@ int sparse_indexer_topk(const sia_page_table *pt, const sia_paged_cache *index_k
                         const sia_queries *qs, const void *q_idx, const float *w,
                         int32_t heads, int32_t topk, int32_t *out_idx, float *out_score,
                         int32_t sched, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The indexer on the MXFP8 path: an index cache of dtype SIA_MXFP8_E4M3 (dim
+ * 128) and an MXFP8 query,
+ *   score[j,s] = sum_h w[j,h] * max(0, q^[j,h,:] . k^_s)
+ * with q^ and k^ the exact values of the stored elements times their block
+ * scales (no per-token scale). Same selection, outputs, workspace
+ * (sia_indexer_workspace_size with the MXFP8 cache descriptor), scheduling and
+ * error conventions as sparse_indexer_topk.
+ *   q_codes   device uint8 [num_q, heads, dim]       e4m3 codes of the query
+ *   q_scales  device uint8 [num_q, heads, dim / 32]  their E8M0 block scales
+ * ("Rapid Adaptation ...", section 5.1; "Day0 ... New-Architecture LLMs",
+ * section 4 "Layered Quantization": index Q/K in MXFP8.)
+ */
+int sparse_indexer_topk_mxfp8(const sia_page_table *pt, const sia_paged_cache *index_k,
+                              const sia_queries *qs, const uint8_t *q_codes, const uint8_t *q_scales,
+                              const float *w, int32_t heads, int32_t topk, int32_t *out_idx,
+                              float *out_score, int32_t sched, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Test hook: the MXFP8 path's scores (as sparse_indexer_scores). */
+int sparse_indexer_scores_mxfp8(const sia_page_table *pt, const sia_paged_cache *index_k,
+                                const sia_queries *qs, const uint8_t *q_codes,
+                                const uint8_t *q_scales, const float *w, int32_t heads,
+                                float *scores, int64_t ld, void *workspace, size_t workspace_bytes,
+                                void *stream);
+
+/*
+ * Quantize bf16 rows to MXFP8: every group of 32 consecutive elements of a row
+ * gets the scale 2^e with e the smallest integer in [-127, 127] for which the
+ * group's largest magnitude is at most 448 * 2^e (so no element is clipped),
+ * stored as the E8M0 byte e + 127; each element becomes the e4m3 code nearest
+ * to x / 2^e (ties to even). An all-zero group gets e = -127 and zero codes.
+ *   x       device bf16 [rows, dim], finite values; dim a positive multiple of 32
+ *   codes   device uint8 [rows, dim]
+ *   scales  device uint8 [rows, dim / 32]
+ */
+int sia_quantize_mxfp8(const void *x, int64_t rows, int32_t dim, uint8_t *codes, uint8_t *scales,
+                       void *stream);
 
 /*
  * Test hook: sparse_indexer_topk with a record of where and when each

@@ -23,11 +23,13 @@ SIA_ERR_WORKSPACE = -3
 SIA_ERR_HIP = -4
 SIA_BF16 = 0
 SIA_FP8_E4M3FN = 1
+SIA_MXFP8_E4M3 = 2
 SCHED_AUTO, SCHED_NAIVE, SCHED_HEAVY_FIRST, SCHED_ZIGZAG = -1, 0, 1, 2
 DEVSTATUS_BAD_SEQ, DEVSTATUS_BAD_PAGE, DEVSTATUS_ROW_TOO_LONG, DEVSTATUS_BAD_INDEX = 1, 2, 4, 8
 
 EXPORTS = [
     "sia_indexer_workspace_size", "sparse_indexer_topk", "sparse_indexer_topk_traced",
+    "sparse_indexer_topk_mxfp8", "sparse_indexer_scores_mxfp8", "sia_quantize_mxfp8",
     "sparse_indexer_scores",
     "sia_topk_workspace_size", "sparse_topk_from_scores", "sia_mla_workspace_size",
     "sparse_mla_attention", "sparse_mla_attention_noalloc", "sia_zigzag_assign",
@@ -78,6 +80,11 @@ def lib():
             "sparse_indexer_topk_traced": (ctypes.c_int, [pPT, pPC, pQ, P, P, c_i32, c_i32, P, P, c_i32,
                                                           P, c_sz, P, P, c_i32]),
             "sparse_indexer_scores": (ctypes.c_int, [pPT, pPC, pQ, P, P, c_i32, P, c_i64, P, c_sz, P]),
+            "sparse_indexer_topk_mxfp8": (ctypes.c_int, [pPT, pPC, pQ, P, P, P, c_i32, c_i32, P, P, c_i32, P,
+                                                         c_sz, P]),
+            "sparse_indexer_scores_mxfp8": (ctypes.c_int, [pPT, pPC, pQ, P, P, P, c_i32, P, c_i64, P, c_sz,
+                                                           P]),
+            "sia_quantize_mxfp8": (ctypes.c_int, [P, c_i64, c_i32, P, P, P]),
             "sia_topk_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
             "sparse_topk_from_scores": (ctypes.c_int, [P, c_i64, P, c_i32, c_i32, c_i32, P, P, P, c_sz,
                                                        P]),
@@ -129,10 +136,12 @@ def page_table_desc(page_table: torch.Tensor, seq_lens: torch.Tensor) -> PageTab
 
 
 def cache_desc(rows: torch.Tensor, scale: Optional[torch.Tensor] = None) -> PagedCache:
+    """bf16 rows (no scale); e4m3 codes with fp32 per-token scales; or e4m3
+    codes with uint8 E8M0 block scales (MXFP8)."""
     if rows.dtype == torch.bfloat16:
         dt = SIA_BF16
     elif rows.dtype in (torch.uint8, torch.float8_e4m3fn):
-        dt = SIA_FP8_E4M3FN
+        dt = SIA_MXFP8_E4M3 if scale is not None and scale.dtype == torch.uint8 else SIA_FP8_E4M3FN
     else:
         raise ValueError(f"unsupported cache dtype {rows.dtype}")
     return PagedCache(_ptr(rows), _ptr(scale), int(rows.shape[0]), int(rows.shape[2]), dt)
@@ -214,6 +223,65 @@ def sparse_indexer_topk_traced(page_table, seq_lens, rows, scale, q_seq, q_pos, 
                                             _ptr(workspace), workspace.numel(), _stream(stream), _ptr(trace),
                                             int(trace.shape[0])))
     return out_idx
+
+
+def sparse_indexer_topk_mxfp8(page_table, seq_lens, k_codes, k_scales, q_seq, q_pos, q_codes, q_scales, w,
+                              topk, *, group=1, max_visible=None, out_idx=None, out_score=None,
+                              want_score=False, sched=SCHED_AUTO, workspace=None, stream=None):
+    """The MXFP8 index path: MXFP8 cache (e4m3 codes + E8M0 block scales) and
+    MXFP8 query. Returns (idx int32 [Q, topk], score fp32 [Q, topk] or None)."""
+    Q, H = int(q_codes.shape[0]), int(q_codes.shape[1])
+    dev = q_codes.device
+    if max_visible is None:
+        max_visible = visible_max(q_seq, q_pos, seq_lens)
+    pt, c = page_table_desc(page_table, seq_lens), cache_desc(k_codes, k_scales)
+    q = queries_desc(q_seq, q_pos, group, max_visible)
+    need = lib().sia_indexer_workspace_size(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(q), H,
+                                            int(topk))
+    if need == 0:
+        raise SiaError(SIA_ERR_INVALID_ARG, "invalid shapes for the MXFP8 indexer")
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    if out_idx is None:
+        out_idx = torch.empty((Q, topk), dtype=torch.int32, device=dev)
+    if out_score is None and want_score:
+        out_score = torch.empty((Q, topk), dtype=torch.float32, device=dev)
+    _check(lib().sparse_indexer_topk_mxfp8(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(q), _ptr(q_codes),
+                                           _ptr(q_scales), _ptr(w), H, int(topk), _ptr(out_idx),
+                                           _ptr(out_score), int(sched), _ptr(workspace), workspace.numel(),
+                                           _stream(stream)))
+    return out_idx, out_score
+
+
+def sparse_indexer_scores_mxfp8(page_table, seq_lens, k_codes, k_scales, q_seq, q_pos, q_codes, q_scales, w,
+                                *, group=1, max_visible=None, ld=None, stream=None):
+    """MXFP8-path scores without selection: fp32 [Q, ld], -inf where not visible."""
+    Q, H = int(q_codes.shape[0]), int(q_codes.shape[1])
+    if max_visible is None:
+        max_visible = visible_max(q_seq, q_pos, seq_lens)
+    if ld is None:
+        ld = max(1, max_visible)
+    pt, c = page_table_desc(page_table, seq_lens), cache_desc(k_codes, k_scales)
+    q = queries_desc(q_seq, q_pos, group, max_visible)
+    workspace = new_workspace(256, q_codes.device)
+    scores = torch.empty((Q, ld), dtype=torch.float32, device=q_codes.device)
+    _check(lib().sparse_indexer_scores_mxfp8(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(q), _ptr(q_codes),
+                                             _ptr(q_scales), _ptr(w), H, _ptr(scores), int(ld), _ptr(workspace),
+                                             workspace.numel(), _stream(stream)))
+    return scores
+
+
+def quantize_mxfp8(x: torch.Tensor, stream=None):
+    """MXFP8 codes (uint8, shape of x) and E8M0 scale bytes (last dim / 32) of
+    the bf16 tensor x (last dimension a multiple of 32)."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("quantize_mxfp8 takes bf16")
+    D = int(x.shape[-1])
+    rows = x.numel() // D if D else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
+    _check(lib().sia_quantize_mxfp8(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
 
 
 def sparse_indexer_scores(page_table, seq_lens, rows, scale, q_seq, q_pos, q_idx, w, *, group=1,

@@ -40,34 +40,57 @@ static_assert(kCoarseBins == kCoarseBinsHost, "host and device histogram sizes d
 
 // ------------------------------------------------------------ score tile
 
-// A query's indexer heads in MFMA operand layout. The bf16 form feeds
-// 32x32x16 bf16 MFMAs (fp8 keys are widened to bf16). The fp8 form feeds
-// 32x32x64 fp8 MFMAs on the raw e4m3 key bytes: X = q * 2^s is split into an
-// e4m3 high part hi = e4m3(X) and an e4m3 residual lo = e4m3(16 (X - hi)) (one
-// exponent s per query, chosen so that max|q| * 2^s lies in [128, 256)), and
-// the two products are summed with MFMA scales 2^-s and 2^-(s+4). The split is
-// exact wherever |X| >= 2^-6 (e4m3's smallest normal), which covers every
-// element with |q| >= 2^-13 max|q|; below that the residual falls into e4m3's
-// subnormal steps and the element is represented to within 2^-14 2^-s <=
-// 2^-21 max|q|. The scores therefore equal those of the bf16 form up to
-// rounding order and that error on the smallest elements.
-template <int MB, int D, bool FP8>
+// A query's indexer heads in MFMA operand layout, one form per index-row
+// format KF.
+//  * bf16 rows (kRowBf16): 32x32x16 bf16 MFMAs on the bf16 query.
+//  * fp8 rows with a per-token scale (kRowFp8): 32x32x64 fp8 MFMAs on the raw
+//    e4m3 key bytes. X = q * 2^s is split into an e4m3 high part hi = e4m3(X)
+//    and an e4m3 residual lo = e4m3(16 (X - hi)) (one exponent s per query,
+//    chosen so that max|q| * 2^s lies in [128, 256)), and the two products are
+//    summed with MFMA scales 2^-s and 2^-(s+4). The split is exact wherever
+//    |X| >= 2^-6 (e4m3's smallest normal), which covers every element with
+//    |q| >= 2^-13 max|q|; below that the residual falls into e4m3's subnormal
+//    steps and the element is represented to within 2^-14 2^-s <=
+//    2^-21 max|q|. The scores therefore equal those of the bf16 form up to
+//    rounding order and that error on the smallest elements.
+//  * MXFP8 rows (kRowMx): the query is MXFP8 too (e4m3 elements, one E8M0
+//    scale per 32 consecutive elements of a head), so one 32x32x64 fp8 MFMA per
+//    64-wide step takes both operands' block scales per lane: lane half h
+//    holds the h-th 16 bytes of each of the step's two blocks and supplies the
+//    scale of block h, which the MFMA applies to both halves of that block
+//    (A: the head's query, B: the position's row). Products of the dequantized
+//    values are exact in fp32.
+template <int MB, int D, int KF>
 struct IdxQuery;
 
 template <int MB, int D>
-struct IdxQuery<MB, D, false> {
+struct IdxQuery<MB, D, kRowBf16> {
     static constexpr int KS = D / 16;
     bf16x8 a[MB][KS];
     float w[MB][16];
 };
 
 template <int MB, int D>
-struct IdxQuery<MB, D, true> {
+struct IdxQuery<MB, D, kRowFp8> {
     static constexpr int KS = D / 64;
     i32x8 hi[MB][KS], lo[MB][KS];
     int sh, sl;   // E8M0 scales of the two parts
     float w[MB][16];
 };
+
+template <int MB, int D>
+struct IdxQuery<MB, D, kRowMx> {
+    static constexpr int KS = D / 64;
+    i32x8 a[MB][KS];
+    int sa[MB][KS];   // this lane's E8M0 block scale per step
+    float w[MB][16];
+};
+
+// MFMAs per query, 32-position tile and 32-head block.
+template <int D, int KF>
+__host__ __device__ constexpr int mfmas_per_block() {
+    return KF == kRowBf16 ? D / 16 : KF == kRowFp8 ? 2 * (D / 64) : D / 64;
+}
 
 // hb0: first head block (of 32 heads) held, for waves that split a query's heads.
 template <int MB, int D>
@@ -83,13 +106,42 @@ __device__ __forceinline__ void load_weights(const IdxArgs& A, int j, float (&w)
 }
 
 template <int MB, int D>
-__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, false>& q, int hb0 = 0) {
+__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, kRowMx>& q, int hb0 = 0) {
+    constexpr int KS = IdxQuery<MB, D, kRowMx>::KS;
+    const int l = lane_id(), m = l & 31, half = l >> 5;
+    // lane l: head (hb0 + mb)*32 + l%32; of step ks, the (l/32)-th 16 bytes of
+    // block 2 ks (operand bytes 0-15) and of block 2 ks + 1 (bytes 16-31), and
+    // the scale of block 2 ks + l/32 (the MFMA applies lane half h's scale to
+    // k 32h .. 32h + 31 of both halves); heads past the count give zero codes
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+        const int head = (hb0 + mb) * 32 + m;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+            int sc = 127;
+            if (head < A.heads) {
+                const uint8_t* src = A.q8 + ((int64_t)j * A.heads + head) * D + ks * 64 + half * 16;
+                v0 = *reinterpret_cast<const u32x4*>(src);
+                v1 = *reinterpret_cast<const u32x4*>(src + 32);
+                sc = A.q8s[((int64_t)j * A.heads + head) * (D / 32) + 2 * ks + half];
+            }
+            q.a[mb][ks] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                                (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+            q.sa[mb][ks] = sc;
+        }
+    }
+    load_weights<MB, D>(A, j, q.w, hb0);
+}
+
+template <int MB, int D>
+__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, kRowBf16>& q, int hb0 = 0) {
     const int l = lane_id(), m = l & 31, half = l >> 5;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
         const int head = (hb0 + mb) * 32 + m;
 #pragma unroll
-        for (int ks = 0; ks < IdxQuery<MB, D, false>::KS; ks++) {
+        for (int ks = 0; ks < IdxQuery<MB, D, kRowBf16>::KS; ks++) {
             u32x4 v = {0u, 0u, 0u, 0u};
             if (head < A.heads)
                 v = *reinterpret_cast<const u32x4*>(
@@ -101,8 +153,8 @@ __device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB,
 }
 
 template <int MB, int D>
-__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, true>& q, int hb0 = 0) {
-    constexpr int KS = IdxQuery<MB, D, true>::KS;
+__device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB, D, kRowFp8>& q, int hb0 = 0) {
+    constexpr int KS = IdxQuery<MB, D, kRowFp8>::KS;
     const int l = lane_id(), m = l & 31, half = l >> 5;
     // lane l holds head (hb0 + mb)*32 + l%32 and dims 64 ks + 32 (l/32) .. +31 of
     // each step; the query is read twice (the second time from cache): once for
@@ -177,16 +229,22 @@ __device__ __forceinline__ void load_query(const IdxArgs& A, int j, IdxQuery<MB,
 // bf16: lane half h holds the row's chunks h*CPR/2 .. (16-byte chunks, the
 // 32x32x16 operand layout); fp8: for each 64-byte MFMA step ks it holds the 32
 // bytes 64 ks + 32 h .. (chunks 4 ks + 2 h and 4 ks + 2 h + 1).
-template <int D, bool FP8>
+template <int D, int KF>
 struct KTile {
-    static constexpr int BYTES = (D / 2) * (FP8 ? 1 : 2);
+    static constexpr int BYTES = (D / 2) * ((KF != kRowBf16) ? 1 : 2);
     static constexpr int NV = BYTES / 16;
     u32x4 v[NV];
-    float sc;
+    float sc;     // fp8 rows: the token scale; MXFP8 rows: the row's E8M0 block scales (bytes, as bits)
     bool ok;      // this lane's position is visible and its page id valid
-    // 16-byte chunk of the row held in v[i] by lane half h
+    // 16-byte chunk of the row held in v[i] by lane half h. In a 64-element
+    // step of the fp8 MFMA, lane half h holds bytes 0-15 at k 16h.. and bytes
+    // 16-31 at k 32 + 16h..; a block scale covers k 0..31 (from lane half 0)
+    // or 32..63 (from lane half 1). MXFP8 rows follow that layout (chunks
+    // 4 ks + h and 4 ks + 2 + h); fp8 rows with one scale per token may use
+    // any order shared with the query, and take 32 contiguous bytes.
     static __device__ __forceinline__ int chunk(int i, int h) {
-        if constexpr (FP8) return 4 * (i >> 1) + 2 * h + (i & 1);
+        if constexpr (KF == kRowMx) return 4 * (i >> 1) + 2 * (i & 1) + h;
+        else if constexpr (KF != kRowBf16) return 4 * (i >> 1) + 2 * h + (i & 1);
         else return h * NV + i;
     }
 };
@@ -229,18 +287,18 @@ __device__ __forceinline__ int page_of(const IdxArgs& A, int b, int lp) {
 // or whose page is invalid, reads row 0 of the pool instead (always in bounds)
 // and is marked not ok, so that its score is discarded. Keeping loads out of
 // branches lets the compiler wait for exactly the tile being consumed.
-template <int D, bool FP8>
+template <int D, int KF>
 __device__ __forceinline__ void load_ktile(const IdxArgs& A, int page, int pos0, int row_len,
-                                           KTile<D, FP8>& t) {
+                                           KTile<D, KF>& t) {
     const int l = lane_id(), half = l >> 5;
     const int p = pos0 + (l & 31);
     t.ok = page >= 0 && p < row_len;
     const int64_t row = t.ok ? (int64_t)page * kPage + (p & 63) : 0;
-    const uint8_t* src = A.rows + row * (D * (FP8 ? 1 : 2));
+    const uint8_t* src = A.rows + row * (D * ((KF != kRowBf16) ? 1 : 2));
 #pragma unroll
-    for (int i = 0; i < KTile<D, FP8>::NV; i++)
-        t.v[i] = reinterpret_cast<const u32x4*>(src)[KTile<D, FP8>::chunk(i, half)];
-    if constexpr (FP8) t.sc = A.scale[row];
+    for (int i = 0; i < KTile<D, KF>::NV; i++)
+        t.v[i] = reinterpret_cast<const u32x4*>(src)[KTile<D, KF>::chunk(i, half)];
+    if constexpr (KF != kRowBf16) t.sc = A.scale[row];
     else t.sc = 1.f;
 }
 
@@ -259,12 +317,27 @@ __device__ __forceinline__ float add_halves(float x) {
 
 // MFMA half of a tile: the raw q.k products of one query against 32
 // positions (heads x positions accumulators).
-template <int MB, int D, bool FP8>
-__device__ __forceinline__ void tile_mfma(const IdxQuery<MB, D, FP8>& q, const KTile<D, FP8>& t,
+template <int MB, int D, int KF>
+__device__ __forceinline__ void tile_mfma(const IdxQuery<MB, D, KF>& q, const KTile<D, KF>& t,
                                           f32x16 (&acc)[MB]) {
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) acc[mb] = f32x16{};
-    if constexpr (FP8) {
+    if constexpr (KF == kRowMx) {
+        constexpr int KS = D / 64;
+        // the row's four E8M0 bytes; this lane's block of step ks is 2 ks + lane/32
+        const uint32_t rs = __float_as_uint(t.sc) >> (8 * (lane_id() >> 5));
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            const u32x4 v0 = t.v[2 * ks], v1 = t.v[2 * ks + 1];
+            const i32x8 b = {(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                             (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+            const int sb = (int)((rs >> (16 * ks)) & 0xffu);
+#pragma unroll
+            for (int mb = 0; mb < MB; mb++)
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(q.a[mb][ks], b, acc[mb], 0, 0, 0,
+                                                                          q.sa[mb][ks], 0, sb);
+        }
+    } else if constexpr (KF == kRowFp8) {
         constexpr int KS = D / 64;
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
@@ -294,8 +367,8 @@ __device__ __forceinline__ void tile_mfma(const IdxQuery<MB, D, FP8>& q, const K
 // heads is summed on its own and the block sums are added in block order, so a
 // wave holding one block of a query gives the same bits once its partner's block
 // sum is added.
-template <int MB, int D, bool FP8>
-__device__ __forceinline__ float tile_head_sum(const IdxQuery<MB, D, FP8>& q, const f32x16 (&acc)[MB]) {
+template <int MB, int D, int KF>
+__device__ __forceinline__ float tile_head_sum(const IdxQuery<MB, D, KF>& q, const f32x16 (&acc)[MB]) {
     float v = 0.f;
 #pragma unroll
     for (int mb = 0; mb < MB; mb++) {
@@ -314,22 +387,22 @@ __device__ __forceinline__ float tile_head_sum(const IdxQuery<MB, D, FP8>& q, co
 }
 
 // ... times the token scale.
-template <int MB, int D, bool FP8>
-__device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D, FP8>& q, const f32x16 (&acc)[MB],
+template <int MB, int D, int KF>
+__device__ __forceinline__ float tile_epilogue(const IdxQuery<MB, D, KF>& q, const f32x16 (&acc)[MB],
                                                float tsc) {
-    const float v = tile_head_sum<MB, D, FP8>(q, acc);
-    return FP8 ? v * tsc : v;
+    const float v = tile_head_sum<MB, D, KF>(q, acc);
+    return KF == kRowFp8 ? v * tsc : v;
 }
 
 // Scores of the tile's 32 positions for one query; lanes l and l+32 both get
 // the score of position pos0 + l%32 (undefined where the tile lane is not ok).
 // Every kernel scores through tile_mfma + tile_epilogue, so a query and position
 // give the same bits in each of them.
-template <int MB, int D, bool FP8>
-__device__ __forceinline__ float tile_scores(const IdxQuery<MB, D, FP8>& q, const KTile<D, FP8>& t) {
+template <int MB, int D, int KF>
+__device__ __forceinline__ float tile_scores(const IdxQuery<MB, D, KF>& q, const KTile<D, KF>& t) {
     f32x16 acc[MB];
-    tile_mfma<MB, D, FP8>(q, t, acc);
-    return tile_epilogue<MB, D, FP8>(q, acc, t.sc);
+    tile_mfma<MB, D, KF>(q, t, acc);
+    return tile_epilogue<MB, D, KF>(q, acc, t.sc);
 }
 
 // ------------------------------------------------------------ emitters
@@ -421,17 +494,17 @@ __device__ int select_emit(const uint32_t* keys, int n, int cnt, int m_cap, SelS
 // epilogue of tile k - 1, then reads tile k + 1's operands, so the matrix pipe,
 // the vector pipe and the copies overlap. With two queries the waves of a pair
 // copy the same rows at about the same time; the second copy is served from L2.
-template <int D, bool FP8, int G>
+template <int D, int KF, int G>
 struct RowsGeom {
-    static constexpr int R = D * (FP8 ? 1 : 2);          // bytes per row
+    static constexpr int R = D * ((KF != kRowBf16) ? 1 : 2);          // bytes per row
     static constexpr int CPR = R / 16;                   // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
     static constexpr int NWV = kRowsThreads / kWave;
     static constexpr int WPQ = NWV / G;                  // waves per query
     static constexpr int TILE = 32 * R;                  // bytes of one tile
     static constexpr int DMA = TILE / 1024;              // 1 KB copies per tile
-    static constexpr int PER_TILE = DMA + (FP8 ? 1 : 0); // copies per tile (+ scales)
-    static constexpr int SLOT = TILE + (FP8 ? 256 : 0);  // (+ the scales of the tile's page)
+    static constexpr int PER_TILE = DMA + ((KF != kRowBf16) ? 1 : 0); // copies per tile (+ scales)
+    static constexpr int SLOT = TILE + ((KF != kRowBf16) ? 256 : 0);  // (+ the scales of the tile's page)
     static constexpr size_t FIXED = (size_t)G * kCoarseBins * 4 + kMaxPartPages * 4 + 512;
     static constexpr int NS_FIT = (int)((kMaxLds - FIXED) / ((size_t)NWV * SLOT));
     static constexpr int NS = NS_FIT > 4 ? 4 : NS_FIT;   // ring depth
@@ -439,11 +512,11 @@ struct RowsGeom {
     static_assert(NS >= 2, "the ring needs two slots per wave");
 };
 
-template <int MB, int D, bool FP8, int G, bool SCORES>
+template <int MB, int D, int KF, int G, bool SCORES>
 __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, RowsArgs S) {
-    using GM = RowsGeom<D, FP8, G>;
+    using GM = RowsGeom<D, KF, G>;
     constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NWV = GM::NWV, WPQ = GM::WPQ, U = GM::U;
-    constexpr int SLOT = GM::SLOT, NV = KTile<D, FP8>::NV;
+    constexpr int SLOT = GM::SLOT, NV = KTile<D, KF>::NV;
     __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NWV * SLOT];
     __shared__ int pages[kMaxPartPages];
     __shared__ __attribute__((aligned(16))) uint32_t hist[SCORES ? 4 : G * kCoarseBins];
@@ -515,7 +588,7 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
         uint32_t roff[NV];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int cc = KTile<D, FP8>::chunk(i, half);
+            const int cc = KTile<D, KF>::chunk(i, half);
             roff[i] = w * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring)) +
@@ -529,7 +602,7 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
             const uint32_t dst = ring_lds + s * (NWV * SLOT);
 #pragma unroll
             for (int r = 0; r < GM::DMA; r++) dma16_s(base, voff[r], dst + r * 1024);
-            if constexpr (FP8) {
+            if constexpr (KF != kRowBf16) {
                 // the 64 scales of the page, 4 bytes per lane (no lane mask, so
                 // that the loop body stays one basic block)
                 const float* sbase = A.scale + (int64_t)page * kPage;
@@ -537,11 +610,11 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
             }
         };
         // operand reads of the wave's k-th tile from slot s
-        auto fetch = [&](int k, int s, KTile<D, FP8>& t) {
+        auto fetch = [&](int k, int s, KTile<D, KF>& t) {
             const uint8_t* slot = ring + s * (NWV * SLOT);
 #pragma unroll
             for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
-            if constexpr (FP8)
+            if constexpr (KF != kRowBf16)
                 t.sc = *reinterpret_cast<const float*>(slot + w * SLOT + GM::TILE + 4 * (((t0 + k) & 1) * 32 + frow));
             else t.sc = 1.f;
             // (a position on a page whose id is out of range was copied from page 0;
@@ -553,8 +626,8 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
         // row's spare tail and count nowhere. Without branches, so that the
         // compiler keeps the MFMAs where they are issued instead of sinking them
         // into a store branch next to this epilogue.
-        auto finish = [&](int kk, const f32x16 (&acc)[MB], float tsc, bool tok, const IdxQuery<MB, D, FP8>& q) {
-            const float sc = tile_epilogue<MB, D, FP8>(q, acc, tsc);
+        auto finish = [&](int kk, const f32x16 (&acc)[MB], float tsc, bool tok, const IdxQuery<MB, D, KF>& q) {
+            const float sc = tile_epilogue<MB, D, KF>(q, acc, tsc);
             const bool valid = kk >= 0 && kk < n;
             if constexpr (SCORES) {
                 asm volatile("" ::"v"(sc));
@@ -580,10 +653,10 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
         // the first copies go out before the query is read, so that both latencies overlap
 #pragma unroll
         for (int u = 0; u < NS - 1; u++) issue(u, u);
-        IdxQuery<MB, D, FP8> q;
+        IdxQuery<MB, D, KF> q;
         load_query<MB, D>(A, j, q);
         wait_vmcnt_mem<0>();
-        KTile<D, FP8> t;
+        KTile<D, KF> t;
         fetch(0, 0, t);
         f32x16 acc0[MB], acc1[MB];
 #pragma unroll
@@ -597,10 +670,10 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
             for (int u = 0; u < U; u++) {
                 const int k = k0 + u;
                 if (u % 2 == 0) {
-                    tile_mfma<MB, D, FP8>(q, t, acc0);
+                    tile_mfma<MB, D, KF>(q, t, acc0);
                     sc0 = t.sc; ok0 = t.ok;
                 } else {
-                    tile_mfma<MB, D, FP8>(q, t, acc1);
+                    tile_mfma<MB, D, KF>(q, t, acc1);
                     sc1 = t.sc; ok1 = t.ok;
                 }
                 __builtin_amdgcn_sched_barrier(0);   // the MFMAs go out before the epilogue below
@@ -654,16 +727,16 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
 constexpr int kPairUnroll = 8;          // loop unroll (ring slots are static per step)
 constexpr int kPairPartPages = 512;     // a pair part spans at most 32768 positions
 
-template <int D, bool FP8>
+template <int D, int KF>
 struct PairGeom {
-    static constexpr int R = D * (FP8 ? 1 : 2);
+    static constexpr int R = D * ((KF != kRowBf16) ? 1 : 2);
     static constexpr int CPR = R / 16;
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;
     static constexpr int NTEAM = kPairThreads / kWave / 2;
     static constexpr int TILE = 32 * R;
     static constexpr int DMA = TILE / 1024;
-    static constexpr int PER_TILE = DMA + (FP8 ? 1 : 0);
-    static constexpr int SLOT = TILE + (FP8 ? 256 : 0);
+    static constexpr int PER_TILE = DMA + ((KF != kRowBf16) ? 1 : 0);
+    static constexpr int SLOT = TILE + ((KF != kRowBf16) ? 256 : 0);
     static constexpr size_t FIXED = kCoarseBins * 4 + kPairPartPages * 4 + 2 * NTEAM * kWave * 4 + 512;
     static constexpr int NS_FIT = (int)((kMaxLds - FIXED) / ((size_t)NTEAM * SLOT));
     static constexpr int NS = NS_FIT >= 8 ? 8 : (NS_FIT >= 4 ? 4 : 2);   // divides the unroll
@@ -681,12 +754,12 @@ __device__ __forceinline__ void interleave_mfma_valu() {
     }
 }
 
-template <int D, bool FP8, bool SCORES>
+template <int D, int KF, bool SCORES>
 __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
-    using GM = PairGeom<D, FP8>;
+    using GM = PairGeom<D, KF>;
     constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NTEAM = GM::NTEAM, U = kPairUnroll;
-    constexpr int SLOT = GM::SLOT, NV = KTile<D, FP8>::NV;
-    constexpr int NMFMA = FP8 ? 2 * (D / 64) : D / 16;   // MFMAs per query, tile and head block
+    constexpr int SLOT = GM::SLOT, NV = KTile<D, KF>::NV;
+    constexpr int NMFMA = mfmas_per_block<D, KF>();   // MFMAs per query, tile and head block
     __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NTEAM * SLOT];
     __shared__ int pages[kPairPartPages];
     // the part's coarse histograms, query 0 in the low and query 1 in the high
@@ -757,7 +830,7 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
         uint32_t roff[NV];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int cc = KTile<D, FP8>::chunk(i, half);
+            const int cc = KTile<D, KF>::chunk(i, half);
             roff[i] = team * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring)) +
@@ -773,17 +846,17 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             const uint32_t dst = ring_lds + s * (NTEAM * SLOT);
 #pragma unroll
             for (int r = 0; r < GM::DMA; r++) dma16_s(base, voff[r], dst + r * 1024);
-            if constexpr (FP8) {
+            if constexpr (KF != kRowBf16) {
                 // the 64 scales of the page, 4 bytes per lane (no lane mask)
                 const float* sbase = A.scale + (int64_t)page * kPage;
                 dma4_s(sbase, 4 * l, dst + GM::TILE);
             }
         };
-        auto fetch = [&](int k, int s, KTile<D, FP8>& t) {
+        auto fetch = [&](int k, int s, KTile<D, KF>& t) {
             const uint8_t* slot = ring + s * (NTEAM * SLOT);
 #pragma unroll
             for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
-            if constexpr (FP8)
+            if constexpr (KF != kRowBf16)
                 t.sc = *reinterpret_cast<const float*>(slot + team * SLOT + GM::TILE +
                                                        4 * ((tile_of(k) & 1) * 32 + frow));
             else t.sc = 1.f;
@@ -795,7 +868,7 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
         // branch. Positions on a page whose id is out of range were copied from
         // page 0 and are dropped.
         auto finish = [&](int kq, float v, float tsc) {
-            const float sc = FP8 ? v * tsc : v;
+            const float sc = KF == kRowFp8 ? v * tsc : v;
             const int kk = half ? kq - 1 : kq;
             const bool in_run = kk >= 0 && kk < n;
             const int tpos = (t0 + kk) * 32 + frow;   // position within the part
@@ -822,12 +895,12 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
 #pragma unroll
             for (int u = 0; u < NS - 1; u++) issue(u, u);
         }
-        IdxQuery<1, D, FP8> q0, q1;
+        IdxQuery<1, D, KF> q0, q1;
         load_query<1, D>(A, min(j0, A.num_q - 1), q0, hb);
         load_query<1, D>(A, min(j1, A.num_q - 1), q1, hb);
         wait_vmcnt_mem<0>();
         __syncthreads();   // the first copies have landed
-        KTile<D, FP8> t;
+        KTile<D, KF> t;
         fetch(0, 0, t);
         f32x16 a0[1], a1[1];
         a1[0] = f32x16{};
@@ -837,12 +910,12 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             for (int u = 0; u < U; u++) {
                 const int k = k0 + u;
                 // query 0 on tile k, beside query 1's block sum of tile k - 1
-                tile_mfma<1, D, FP8>(q0, t, a0);
-                const float h1 = tile_head_sum<1, D, FP8>(q1, a1);
+                tile_mfma<1, D, KF>(q0, t, a0);
+                const float h1 = tile_head_sum<1, D, KF>(q1, a1);
                 interleave_mfma_valu<NMFMA>();
                 // query 1 on tile k, beside query 0's block sum of tile k
-                tile_mfma<1, D, FP8>(q1, t, a1);
-                const float h0 = tile_head_sum<1, D, FP8>(q0, a0);
+                tile_mfma<1, D, KF>(q1, t, a1);
+                const float h0 = tile_head_sum<1, D, KF>(q0, a0);
                 interleave_mfma_valu<NMFMA>();
                 const float mine = half ? h1 : h0;
                 const float tsc = half ? sc_prev : t.sc;
@@ -871,7 +944,7 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
         }
         // query 1 of the last step
         {
-            const float h1 = tile_head_sum<1, D, FP8>(q1, a1);
+            const float h1 = tile_head_sum<1, D, KF>(q1, a1);
             if (hb == 0) xch[nloop & 1][team][l] = h1;
             lds_barrier();
             if (hb == 1) finish(nloop, xch[nloop & 1][team][l] + h1, sc_prev);
@@ -1122,17 +1195,17 @@ struct WaveBuf {
 // 32-position tile of index-K is copied once from global memory into LDS and
 // read there by all four queries of the workgroup (consecutive positions of one
 // sequence walk almost the same causal rows).
-template <int D, bool FP8>
+template <int D, int KF>
 struct StreamGeom {
-    static constexpr int R = D * (FP8 ? 1 : 2);            // bytes per row
+    static constexpr int R = D * ((KF != kRowBf16) ? 1 : 2);            // bytes per row
     static constexpr int CPR = R / 16;                      // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;     // chunk swizzle mask
     static constexpr int TILE = 32 * R;
     static constexpr int DMA = TILE / 1024;                 // 1 KB copies per tile
     static constexpr int QPT = kStreamThreads / kWave;      // waves (= queries) per workgroup
     static constexpr int CPW = (DMA + QPT - 1) / QPT;       // copies per wave and tile
-    static constexpr int PER_TILE = CPW + (FP8 ? 1 : 0);    // (+ the page's 64 scales)
-    static constexpr int SLOT = TILE + (FP8 ? 256 : 0);
+    static constexpr int PER_TILE = CPW + ((KF != kRowBf16) ? 1 : 0);    // (+ the page's 64 scales)
+    static constexpr int SLOT = TILE + ((KF != kRowBf16) ? 256 : 0);
     static constexpr int NS = TILE <= 4096 ? 8 : 4;         // ring slots
     static constexpr int RING = NS * SLOT;
     static_assert(DMA >= 1 && NS >= 4 && (NS - 1) * PER_TILE < 64, "stream ring geometry");
@@ -1148,11 +1221,11 @@ __host__ __device__ inline size_t stream_ring_bytes(int dim, bool fp8) {
 // wave keeps the keys that beat its threshold tau in its own LDS candidate
 // buffer and re-selects inside it when the buffer fills, then emits its Top-K.
 // Called by all four waves (the ring needs one barrier per tile).
-template <int MB, int D, bool FP8>
+template <int MB, int D, int KF>
 __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int rl, int rl_max,
                              const int* pages, WaveBuf B, uint8_t* ring) {
-    using SG = StreamGeom<D, FP8>;
-    constexpr int NS = SG::NS, R = SG::R, NV = KTile<D, FP8>::NV;
+    using SG = StreamGeom<D, KF>;
+    constexpr int NS = SG::NS, R = SG::R, NV = KTile<D, KF>::NV;
     const int l = lane_id(), half = l >> 5, frow = l & 31;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const bool live = j < A.num_q;
@@ -1160,7 +1233,7 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
     uint32_t tau = 0u;
     const int nt = (rl_max + 31) / 32;
     if (nt > 0) {
-        IdxQuery<MB, D, FP8> q;
+        IdxQuery<MB, D, KF> q;
         load_query<MB, D>(A, live ? j : A.num_q - 1, q);
         // this wave's copies of a tile: tile bytes [1024 r, 1024 r + 1024) land
         // linearly in the slot; lane l fetches the source chunk that belongs at
@@ -1176,7 +1249,7 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         uint32_t roff[NV];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
-            const int cc = KTile<D, FP8>::chunk(i, half);
+            const int cc = KTile<D, KF>::chunk(i, half);
             roff[i] = frow * R + ((cc ^ (frow & SG::SWZ)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring));
@@ -1194,17 +1267,17 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
                 const int r = min(w * SG::CPW + c, SG::DMA - 1);
                 dma16_s(base, voff[c], dst + r * 1024);
             }
-            if constexpr (FP8) dma4_s(A.scale + (int64_t)page * kPage, 4 * l, dst + SG::TILE);
+            if constexpr (KF != kRowBf16) dma4_s(A.scale + (int64_t)page * kPage, 4 * l, dst + SG::TILE);
         };
         // operands of tile k (k may be past the last tile: then the slot holds a
         // clamped copy and no position is visible). t.ok is the visibility only;
         // the page id `pg` is read without a branch and checked when the tile is
         // scored, so nothing waits for these reads before then.
-        auto fetch = [&](int k, KTile<D, FP8>& t, int& pg) {
+        auto fetch = [&](int k, KTile<D, KF>& t, int& pg) {
             const uint8_t* slot = ring + (k % NS) * SG::SLOT;
 #pragma unroll
             for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
-            if constexpr (FP8) t.sc = *reinterpret_cast<const float*>(slot + SG::TILE + 4 * ((k & 1) * 32 + frow));
+            if constexpr (KF != kRowBf16) t.sc = *reinterpret_cast<const float*>(slot + SG::TILE + 4 * ((k & 1) * 32 + frow));
             else t.sc = 1.f;
             t.ok = k * 32 + frow < rl;
             pg = pages[min(k, nt - 1) >> 1];
@@ -1264,7 +1337,7 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
                 wave_sync();
             }
         };
-        constexpr int NMFMA = MB * (FP8 ? 2 * (D / 64) : D / 16);   // MFMAs per tile
+        constexpr int NMFMA = MB * mfmas_per_block<D, KF>();   // MFMAs per tile
         // Tiles 0 .. NS-1 go out first. Step k: the MFMAs of tile k+1 (its
         // operands read from LDS one step earlier) run interleaved with the
         // epilogue of tile k (ReLU, head weights, head sum, key, append), while the
@@ -1280,11 +1353,11 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         // tb holds the operands of the next tile to multiply; A0 / A1 alternate as
         // the accumulators of the tile being finished and of the tile being
         // multiplied (two sets, so that the MFMAs never wait for the epilogue)
-        KTile<D, FP8> tb;
+        KTile<D, KF> tb;
         int pg_b;
         f32x16 A0[MB], A1[MB];
         fetch(0, tb, pg_b);
-        tile_mfma<MB, D, FP8>(q, tb, A0);
+        tile_mfma<MB, D, KF>(q, tb, A0);
         float sc_c = tb.sc;
         bool ok_c = tb.ok;
         int pg_c = pg_b;
@@ -1302,12 +1375,12 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
                 cp_a = copy_page(k + NS + 2);
                 cp_b = copy_page(k + NS + 3);
             }
-            tile_mfma<MB, D, FP8>(q, tb, nxt);   // tile k+1
+            tile_mfma<MB, D, KF>(q, tb, nxt);   // tile k+1
             const float sc_n = tb.sc;
             const bool ok_n = tb.ok;
             const int pg_n = pg_b;
             fetch(k + 2, tb, pg_b);              // (after the MFMAs have read tb)
-            const float sc = tile_epilogue<MB, D, FP8>(q, cur, sc_c);
+            const float sc = tile_epilogue<MB, D, KF>(q, cur, sc_c);
             interleave_mfma_valu<NMFMA>();
             append(sc, ok_c && pg_c >= 0, k);
             sc_c = sc_n;
@@ -1352,7 +1425,7 @@ __host__ __device__ inline size_t stream_smem_bytes(int cap, int max_visible, in
     return stream_ring_offset(cap, max_visible) + stream_ring_bytes(dim, fp8);
 }
 
-template <int MB, int D, bool FP8>
+template <int MB, int D, int KF>
 __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs A, StreamArgs S) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int next_tile;
@@ -1391,7 +1464,7 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
         const int npg = (rows + kPage - 1) / kPage;
         for (int i = threadIdx.x; i < npg; i += kStreamThreads) pages[i] = page_of(A, b0, i);
         __syncthreads();
-        stream_group<MB, D, FP8>(A, S, j, rl, rows, pages, B, ring);
+        stream_group<MB, D, KF>(A, S, j, rl, rows, pages, B, ring);
         __syncthreads();
         tiles_run++;
     };
@@ -1425,6 +1498,48 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
     }
 }
 
+// MXFP8 quantization: four lanes per group of 32 bf16 values (eight each).
+// The group's scale is 2^e with e the smallest integer in [-127, 127] such
+// that the largest magnitude m satisfies m <= 448 * 2^e: with m = f * 2^E,
+// f in [0.5, 1), and 448 = 0.875 * 2^9, that is e = E - 9 when f <= 0.875 and
+// E - 8 otherwise. Elements become e4m3 codes of x / 2^e, rounded to nearest
+// even by the conversion instruction (never above 448 in magnitude).
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* x, int64_t n_groups, uint8_t* codes,
+                                                             uint8_t* scales) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t g = t >> 2;
+    const int part = (int)(t & 3);
+    const bool live = g < n_groups;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (live) v = *reinterpret_cast<const u32x4*>(x + g * 32 + part * 8);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(f[i]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    int e = -127;
+    if (m > 0.f) {
+        int E;
+        const float fr = frexpf(m, &E);
+        e = min(max(E - 9 + (fr > 0.875f ? 1 : 0), -127), 127);
+    }
+    const float inv = ldexpf(1.f, -e);
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0] * inv, f[1] * inv, 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2] * inv, f[3] * inv, lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4] * inv, f[5] * inv, 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6] * inv, f[7] * inv, hi, true);
+    if (live) {
+        *reinterpret_cast<u32x2*>(codes + g * 32 + part * 8) = u32x2{(uint32_t)lo, (uint32_t)hi};
+        if (part == 0) scales[g] = (uint8_t)(e + 127);
+    }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
@@ -1441,35 +1556,37 @@ static hipError_t set_smem(K kernel, size_t bytes) {
     return hipSuccess;
 }
 
-template <int MB, int D, bool FP8, int G, bool SC>
+template <int MB, int D, int KF, int G, bool SC>
 static hipError_t rows_launch(const IdxArgs& a, const RowsArgs& r, hipStream_t st) {
     const int groups = (a.num_q + G - 1) / G;
-    hipLaunchKernelGGL((indexer_rows_kernel<MB, D, FP8, G, SC>), dim3(groups * r.n_parts), dim3(kRowsThreads), 0,
+    hipLaunchKernelGGL((indexer_rows_kernel<MB, D, KF, G, SC>), dim3(groups * r.n_parts), dim3(kRowsThreads), 0,
                        st, a, r);
     return hipGetLastError();
 }
 
-template <int D, bool FP8, bool SC>
+template <int D, int KF, bool SC>
 static hipError_t pair_launch(const IdxArgs& a, const RowsArgs& r, hipStream_t st) {
     const int pairs = (a.num_q + 1) / 2;
-    hipLaunchKernelGGL((indexer_pair_kernel<D, FP8, SC>), dim3(pairs * r.n_parts), dim3(kPairThreads), 0, st, a,
+    hipLaunchKernelGGL((indexer_pair_kernel<D, KF, SC>), dim3(pairs * r.n_parts), dim3(kPairThreads), 0, st, a,
                        r);
     return hipGetLastError();
 }
 
-template <int MB, int D, bool FP8>
+template <int MB, int D, int KF>
 static hipError_t rows_launch3(const IdxArgs& a, const RowsArgs& r, int g, bool sc, hipStream_t st) {
-    if (g == 2) return sc ? pair_launch<D, FP8, true>(a, r, st) : pair_launch<D, FP8, false>(a, r, st);
-    return sc ? rows_launch<MB, D, FP8, 1, true>(a, r, st) : rows_launch<MB, D, FP8, 1, false>(a, r, st);
+    if (g == 2) return sc ? pair_launch<D, KF, true>(a, r, st) : pair_launch<D, KF, false>(a, r, st);
+    return sc ? rows_launch<MB, D, KF, 1, true>(a, r, st) : rows_launch<MB, D, KF, 1, false>(a, r, st);
 }
 
-hipError_t launch_indexer_rows(const IdxArgs& a, const RowsArgs& r, int mb, int dim, bool fp8, int group,
+hipError_t launch_indexer_rows(const IdxArgs& a, const RowsArgs& r, int mb, int dim, int kf, int group,
                                bool scores_mode, hipStream_t st) {
-#define SIA_ROWS(MBv, Dv, F8)                                                  \
-    if (mb == MBv && dim == Dv && fp8 == F8)                                  \
-        return rows_launch3<MBv, Dv, F8>(a, r, group, scores_mode, st);
-    SIA_ROWS(1, 64, false) SIA_ROWS(1, 64, true) SIA_ROWS(1, 128, false) SIA_ROWS(1, 128, true)
-    SIA_ROWS(2, 64, false) SIA_ROWS(2, 64, true) SIA_ROWS(2, 128, false) SIA_ROWS(2, 128, true)
+#define SIA_ROWS(MBv, Dv, KFv)                                                 \
+    if (mb == MBv && dim == Dv && kf == KFv)                                  \
+        return rows_launch3<MBv, Dv, KFv>(a, r, group, scores_mode, st);
+#define SIA_ROWS_KF(MBv, Dv) SIA_ROWS(MBv, Dv, kRowBf16) SIA_ROWS(MBv, Dv, kRowFp8)
+    SIA_ROWS_KF(1, 64) SIA_ROWS_KF(1, 128) SIA_ROWS_KF(2, 64) SIA_ROWS_KF(2, 128)
+    SIA_ROWS(1, 128, kRowMx) SIA_ROWS(2, 128, kRowMx)   // (MXFP8 rows are 128 wide)
+#undef SIA_ROWS_KF
 #undef SIA_ROWS
     return hipErrorInvalidValue;
 }
@@ -1484,20 +1601,20 @@ hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int MB, int D, bool FP8>
+template <int MB, int D, int KF>
 static hipError_t stream_launch(const IdxArgs& a, const StreamArgs& s, int grid, hipStream_t st) {
-    auto k = indexer_stream_kernel<MB, D, FP8>;
-    const size_t smem = stream_smem_bytes(s.cap, a.max_visible, D, FP8);
+    auto k = indexer_stream_kernel<MB, D, KF>;
+    const size_t smem = stream_smem_bytes(s.cap, a.max_visible, D, KF != kRowBf16);
     hipError_t e = set_smem(k, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kStreamThreads), smem, st, a, s);
     return hipGetLastError();
 }
 
-template <int MB, int D, bool FP8>
+template <int MB, int D, int KF>
 static int stream_occupancy(int cap, int max_visible) {
-    auto k = indexer_stream_kernel<MB, D, FP8>;
-    const size_t smem = stream_smem_bytes(cap, max_visible, D, FP8);
+    auto k = indexer_stream_kernel<MB, D, KF>;
+    const size_t smem = stream_smem_bytes(cap, max_visible, D, KF != kRowBf16);
     if (set_smem(k, smem) != hipSuccess) return 1;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k),
@@ -1506,12 +1623,14 @@ static int stream_occupancy(int cap, int max_visible) {
     return n;
 }
 
-hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, bool fp8,
+hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, int kf,
                                  int grid, hipStream_t st) {
-#define SIA_STREAM(MBv, Dv, F8) \
-    if (mb == MBv && dim == Dv && fp8 == F8) return stream_launch<MBv, Dv, F8>(a, s, grid, st);
-    SIA_STREAM(1, 64, false) SIA_STREAM(1, 64, true) SIA_STREAM(1, 128, false) SIA_STREAM(1, 128, true)
-    SIA_STREAM(2, 64, false) SIA_STREAM(2, 64, true) SIA_STREAM(2, 128, false) SIA_STREAM(2, 128, true)
+#define SIA_STREAM(MBv, Dv, KFv) \
+    if (mb == MBv && dim == Dv && kf == KFv) return stream_launch<MBv, Dv, KFv>(a, s, grid, st);
+#define SIA_STREAM_KF(MBv, Dv) SIA_STREAM(MBv, Dv, kRowBf16) SIA_STREAM(MBv, Dv, kRowFp8)
+    SIA_STREAM_KF(1, 64) SIA_STREAM_KF(1, 128) SIA_STREAM_KF(2, 64) SIA_STREAM_KF(2, 128)
+    SIA_STREAM(1, 128, kRowMx) SIA_STREAM(2, 128, kRowMx)
+#undef SIA_STREAM_KF
 #undef SIA_STREAM
     return hipErrorInvalidValue;
 }
@@ -1520,13 +1639,23 @@ size_t indexer_stream_smem(int cap, int max_visible, int dim, bool fp8) {
     return stream_smem_bytes(cap, max_visible, dim, fp8);
 }
 
-int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap, int max_visible) {
-#define SIA_OCC(MBv, Dv, F8) \
-    if (mb == MBv && dim == Dv && fp8 == F8) return stream_occupancy<MBv, Dv, F8>(cap, max_visible);
-    SIA_OCC(1, 64, false) SIA_OCC(1, 64, true) SIA_OCC(1, 128, false) SIA_OCC(1, 128, true)
-    SIA_OCC(2, 64, false) SIA_OCC(2, 64, true) SIA_OCC(2, 128, false) SIA_OCC(2, 128, true)
+int indexer_stream_blocks_per_cu(int mb, int dim, int kf, int cap, int max_visible) {
+#define SIA_OCC(MBv, Dv, KFv) \
+    if (mb == MBv && dim == Dv && kf == KFv) return stream_occupancy<MBv, Dv, KFv>(cap, max_visible);
+#define SIA_OCC_KF(MBv, Dv) SIA_OCC(MBv, Dv, kRowBf16) SIA_OCC(MBv, Dv, kRowFp8)
+    SIA_OCC_KF(1, 64) SIA_OCC_KF(1, 128) SIA_OCC_KF(2, 64) SIA_OCC_KF(2, 128)
+    SIA_OCC(1, 128, kRowMx) SIA_OCC(2, 128, kRowMx)
+#undef SIA_OCC_KF
 #undef SIA_OCC
     return 1;
+}
+
+hipError_t launch_quantize_mxfp8(const uint16_t* x, int64_t n_groups, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t st) {
+    if (n_groups <= 0) return hipSuccess;
+    const int64_t blocks = (n_groups * 4 + 255) / 256;
+    hipLaunchKernelGGL(quantize_mxfp8_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n_groups, codes, scales);
+    return hipGetLastError();
 }
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st) {

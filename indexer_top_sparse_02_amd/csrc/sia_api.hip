@@ -90,10 +90,12 @@ int check_index_cache(const sia_paged_cache* c) {
     if (!c) return fail(SIA_ERR_INVALID_ARG, "index cache descriptor is NULL");
     if (!c->rows) return fail(SIA_ERR_INVALID_ARG, "index cache rows is NULL");
     if (c->num_pages < 1) return fail(SIA_ERR_INVALID_ARG, "num_pages %lld < 1", (long long)c->num_pages);
-    if (c->dtype != SIA_BF16 && c->dtype != SIA_FP8_E4M3FN)
+    if (c->dtype != SIA_BF16 && c->dtype != SIA_FP8_E4M3FN && c->dtype != SIA_MXFP8_E4M3)
         return fail(SIA_ERR_UNSUPPORTED, "index cache dtype %d", c->dtype);
     if (c->dim != 64 && c->dim != 128) return fail(SIA_ERR_UNSUPPORTED, "index dim %d: supported 64, 128", c->dim);
-    if (c->dtype == SIA_FP8_E4M3FN && !c->scale) return fail(SIA_ERR_INVALID_ARG, "fp8 index cache needs scale");
+    if (c->dtype == SIA_MXFP8_E4M3 && c->dim != 128)
+        return fail(SIA_ERR_UNSUPPORTED, "MXFP8 index dim %d: supported 128", c->dim);
+    if (c->dtype != SIA_BF16 && !c->scale) return fail(SIA_ERR_INVALID_ARG, "an fp8 index cache needs its scales");
     if (c->dtype == SIA_BF16 && c->scale) return fail(SIA_ERR_INVALID_ARG, "bf16 index cache takes no scale");
     return SIA_OK;
 }
@@ -149,7 +151,7 @@ int score_group(const sia_queries* qs) {
     return g;
 }
 
-IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bool fp8) {
+IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bool eight_bit) {
     IndexerPlan p;
     const int mode = env_int("SIA_INDEXER_PATH", 0);   // 0 auto, 1 score + select passes, 2 stream
     const bool stream_ok = topk <= 2048 && qs->group % 4 == 0;
@@ -162,9 +164,9 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bo
         // in-buffer re-selection more frequent) until they do
         int cap = std::min(4096, std::max(1024, 2 * topk));
         const int cap_min = std::max(1024, (topk + 256 + 63) / 64 * 64);
-        while (cap > cap_min && sia::indexer_stream_smem(cap, qs->max_visible, dim, fp8) + 64 > sia::kMaxLds)
+        while (cap > cap_min && sia::indexer_stream_smem(cap, qs->max_visible, dim, eight_bit) + 64 > sia::kMaxLds)
             cap = std::max(cap_min, cap - 256);
-        if (sia::indexer_stream_smem(cap, qs->max_visible, dim, fp8) + 64 <= sia::kMaxLds) {
+        if (sia::indexer_stream_smem(cap, qs->max_visible, dim, eight_bit) + 64 <= sia::kMaxLds) {
             p.stream = true;
             p.cap = cap;
             return p;
@@ -176,21 +178,30 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bo
     return p;
 }
 
+// The query of one indexer call: bf16 heads, or MXFP8 codes and block scales.
+struct IdxQueryIn {
+    const void* bf16 = nullptr;
+    const uint8_t* codes = nullptr;
+    const uint8_t* scales = nullptr;
+};
+
 sia::IdxArgs idx_args(const sia_page_table* pt, const sia_paged_cache* c, const sia_queries* qs,
-                      const void* q_idx, const float* w, int heads, void* ws) {
+                      const IdxQueryIn& qin, const float* w, int heads, void* ws) {
     sia::IdxArgs a;
     a.page_table = pt->page_table;
     a.seq_lens = pt->seq_lens;
     a.batch = pt->batch;
     a.max_pages = pt->max_pages;
     a.rows = static_cast<const uint8_t*>(c->rows);
-    a.scale = c->scale;
+    a.scale = static_cast<const float*>(c->scale);
     a.num_pages = c->num_pages;
     a.q_seq = qs->q_seq;
     a.q_pos = qs->q_pos;
     a.num_q = qs->num_q;
     a.max_visible = qs->max_visible;
-    a.q_idx = static_cast<const uint16_t*>(q_idx);
+    a.q_idx = static_cast<const uint16_t*>(qin.bf16);
+    a.q8 = qin.codes;
+    a.q8s = qin.scales;
     a.w = w;
     a.heads = heads;
     a.status = static_cast<uint32_t*>(ws);
@@ -205,13 +216,19 @@ int check_workspace(void* ws, size_t have, size_t need) {
 }
 
 int check_indexer_common(const sia_page_table* pt, const sia_paged_cache* c, const sia_queries* qs,
-                         const void* q_idx, const float* w, int heads) {
+                         const IdxQueryIn& qin, const float* w, int heads) {
     int rc;
     if ((rc = check_page_table(pt)) != SIA_OK) return rc;
     if ((rc = check_index_cache(c)) != SIA_OK) return rc;
     if ((rc = check_queries(qs, pt)) != SIA_OK) return rc;
     if (heads < 1 || heads > 64) return fail(SIA_ERR_UNSUPPORTED, "indexer heads %d: supported 1..64", heads);
-    if (qs->num_q > 0 && (!q_idx || !w)) return fail(SIA_ERR_INVALID_ARG, "q_idx/w is NULL");
+    const bool mx = c->dtype == SIA_MXFP8_E4M3;
+    if (mx && qin.bf16) return fail(SIA_ERR_INVALID_ARG, "an MXFP8 index cache takes an MXFP8 query (the _mxfp8 calls)");
+    if (!mx && qin.codes) return fail(SIA_ERR_INVALID_ARG, "an MXFP8 query needs an MXFP8 index cache");
+    if (qs->num_q > 0 && !w) return fail(SIA_ERR_INVALID_ARG, "w is NULL");
+    if (qs->num_q > 0 && !mx && !qin.bf16) return fail(SIA_ERR_INVALID_ARG, "q_idx is NULL");
+    if (qs->num_q > 0 && mx && (!qin.codes || !qin.scales))
+        return fail(SIA_ERR_INVALID_ARG, "q_codes/q_scales is NULL");
     return SIA_OK;
 }
 
@@ -224,7 +241,7 @@ size_t sia_indexer_workspace_size(const sia_page_table* pt, const sia_paged_cach
     if (check_page_table(pt) != SIA_OK || check_index_cache(index_k) != SIA_OK ||
         check_queries(qs, pt) != SIA_OK || heads < 1 || heads > 64 || topk < 1 || topk > 8192)
         return 0;
-    return plan_indexer(qs, topk, heads, index_k->dim, index_k->dtype == SIA_FP8_E4M3FN).total;
+    return plan_indexer(qs, topk, heads, index_k->dim, index_k->dtype != SIA_BF16).total;
 }
 
 }  // extern "C"
@@ -232,22 +249,22 @@ size_t sia_indexer_workspace_size(const sia_page_table* pt, const sia_paged_cach
 namespace {
 
 int indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
-                 const void* q_idx, const float* w, int32_t heads, int32_t topk, int32_t* out_idx,
+                 const IdxQueryIn& qin, const float* w, int32_t heads, int32_t topk, int32_t* out_idx,
                  float* out_score, int32_t sched, void* workspace, size_t workspace_bytes, void* stream,
                  uint64_t* trace, int32_t trace_cap) {
-    int rc = check_indexer_common(pt, index_k, qs, q_idx, w, heads);
+    int rc = check_indexer_common(pt, index_k, qs, qin, w, heads);
     if (rc != SIA_OK) return rc;
     if (topk < 1 || topk > 8192) return fail(SIA_ERR_UNSUPPORTED, "topk %d: supported 1..8192", topk);
     if (qs->num_q > 0 && !out_idx) return fail(SIA_ERR_INVALID_ARG, "out_idx is NULL");
     if (sched < -1 || sched > 2) return fail(SIA_ERR_INVALID_ARG, "sched %d", sched);
-    const IndexerPlan p = plan_indexer(qs, topk, heads, index_k->dim, index_k->dtype == SIA_FP8_E4M3FN);
+    const IndexerPlan p = plan_indexer(qs, topk, heads, index_k->dim, index_k->dtype != SIA_BF16);
     if ((rc = check_workspace(workspace, workspace_bytes, p.total)) != SIA_OK) return rc;
     if (qs->num_q == 0) return SIA_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const sia::IdxArgs a = idx_args(pt, index_k, qs, q_idx, w, heads, workspace);
+    const sia::IdxArgs a = idx_args(pt, index_k, qs, qin, w, heads, workspace);
     const int mb = heads > 32 ? 2 : 1;
-    const bool fp8 = index_k->dtype == SIA_FP8_E4M3FN;
+    const int kf = index_k->dtype;   // (sia_dtype values are the kernels' row formats)
     hipError_t e;
     if (p.stream) {
         sia::StreamArgs s;
@@ -266,10 +283,10 @@ int indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const
         if (s.sched == 1) {
             e = sia::launch_fill_u32(s.counter, 0u, 1, st);
             if (e != hipSuccess) return hip_fail(e, "counter reset");
-            const int occ = sia::indexer_stream_blocks_per_cu(mb, index_k->dim, fp8, p.cap, qs->max_visible);
+            const int occ = sia::indexer_stream_blocks_per_cu(mb, index_k->dim, kf, p.cap, qs->max_visible);
             grid = std::min<int64_t>(s.n_tiles, (int64_t)occ * device_cus());
         }
-        e = sia::launch_indexer_stream(a, s, mb, index_k->dim, fp8, grid, st);
+        e = sia::launch_indexer_stream(a, s, mb, index_k->dim, kf, grid, st);
         if (e != hipSuccess) return hip_fail(e, "indexer stream launch");
         return SIA_OK;
     }
@@ -284,7 +301,7 @@ int indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const
     r.reg = reinterpret_cast<int2*>(ws + p.reg);
     r.hist = reinterpret_cast<uint32_t*>(ws + p.hist);
     r.row_len = reinterpret_cast<int32_t*>(ws + p.rlen);
-    e = sia::launch_indexer_rows(a, r, mb, index_k->dim, fp8, p.group, false, st);
+    e = sia::launch_indexer_rows(a, r, mb, index_k->dim, kf, p.group, false, st);
     if (e != hipSuccess) return hip_fail(e, "indexer score launch");
     const sia::SelectArgs sel{r.cand_key, r.cand_pos, r.reg, r.n_reg, r.ld,
                               reinterpret_cast<uint32_t*>(ws + p.keys), r.hist, r.n_parts, r.row_len,
@@ -302,7 +319,22 @@ int sparse_indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k
                         const void* q_idx, const float* w, int32_t heads, int32_t topk,
                         int32_t* out_idx, float* out_score, int32_t sched, void* workspace,
                         size_t workspace_bytes, void* stream) {
-    return indexer_topk(pt, index_k, qs, q_idx, w, heads, topk, out_idx, out_score, sched, workspace,
+    IdxQueryIn qin;
+    qin.bf16 = q_idx;
+    return indexer_topk(pt, index_k, qs, qin, w, heads, topk, out_idx, out_score, sched, workspace,
+                        workspace_bytes, stream, nullptr, 0);
+}
+
+int sparse_indexer_topk_mxfp8(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                              const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int32_t heads,
+                              int32_t topk, int32_t* out_idx, float* out_score, int32_t sched, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    IdxQueryIn qin;
+    qin.codes = q_codes;
+    qin.scales = q_scales;
+    if (index_k && index_k->dtype != SIA_MXFP8_E4M3)
+        return fail(SIA_ERR_INVALID_ARG, "sparse_indexer_topk_mxfp8 needs an MXFP8 index cache");
+    return indexer_topk(pt, index_k, qs, qin, w, heads, topk, out_idx, out_score, sched, workspace,
                         workspace_bytes, stream, nullptr, 0);
 }
 
@@ -311,14 +343,20 @@ int sparse_indexer_topk_traced(const sia_page_table* pt, const sia_paged_cache* 
                                int32_t* out_idx, float* out_score, int32_t sched, void* workspace,
                                size_t workspace_bytes, void* stream, uint64_t* wg_trace, int32_t trace_cap) {
     if (!wg_trace || trace_cap < 1) return fail(SIA_ERR_INVALID_ARG, "wg_trace is NULL or trace_cap < 1");
-    return indexer_topk(pt, index_k, qs, q_idx, w, heads, topk, out_idx, out_score, sched, workspace,
+    IdxQueryIn qin;
+    qin.bf16 = q_idx;
+    return indexer_topk(pt, index_k, qs, qin, w, heads, topk, out_idx, out_score, sched, workspace,
                         workspace_bytes, stream, wg_trace, trace_cap);
 }
 
-int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
-                          const void* q_idx, const float* w, int32_t heads, float* scores, int64_t ld,
-                          void* workspace, size_t workspace_bytes, void* stream) {
-    int rc = check_indexer_common(pt, index_k, qs, q_idx, w, heads);
+}  // extern "C"
+
+namespace {
+
+int indexer_scores(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                   const IdxQueryIn& qin, const float* w, int32_t heads, float* scores, int64_t ld,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_indexer_common(pt, index_k, qs, qin, w, heads);
     if (rc != SIA_OK) return rc;
     if (qs->num_q > 0 && !scores) return fail(SIA_ERR_INVALID_ARG, "scores is NULL");
     if (ld < std::max(1, qs->max_visible)) return fail(SIA_ERR_INVALID_ARG, "ld %lld < max_visible %d", (long long)ld, qs->max_visible);
@@ -328,7 +366,7 @@ int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index
     hipError_t e = sia::launch_fill_u32(reinterpret_cast<uint32_t*>(scores), 0xff800000u,
                                         (int64_t)qs->num_q * ld, st);
     if (e != hipSuccess) return hip_fail(e, "scores fill");
-    const sia::IdxArgs a = idx_args(pt, index_k, qs, q_idx, w, heads, workspace);
+    const sia::IdxArgs a = idx_args(pt, index_k, qs, qin, w, heads, workspace);
     IndexerPlan p;
     const int g = score_group(qs);
     plan_rows(p, qs->num_q, qs->max_visible, g, 1);
@@ -337,10 +375,42 @@ int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index
     r.n_parts = p.n_parts;
     r.ld = ld;
     r.scores = scores;
-    e = sia::launch_indexer_rows(a, r, heads > 32 ? 2 : 1, index_k->dim, index_k->dtype == SIA_FP8_E4M3FN,
-                                 p.group, true, st);
+    e = sia::launch_indexer_rows(a, r, heads > 32 ? 2 : 1, index_k->dim, index_k->dtype, p.group, true, st);
     if (e != hipSuccess) return hip_fail(e, "indexer scores launch");
     return SIA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_indexer_scores(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                          const void* q_idx, const float* w, int32_t heads, float* scores, int64_t ld,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    IdxQueryIn qin;
+    qin.bf16 = q_idx;
+    return indexer_scores(pt, index_k, qs, qin, w, heads, scores, ld, workspace, workspace_bytes, stream);
+}
+
+int sparse_indexer_scores_mxfp8(const sia_page_table* pt, const sia_paged_cache* index_k, const sia_queries* qs,
+                                const uint8_t* q_codes, const uint8_t* q_scales, const float* w, int32_t heads,
+                                float* scores, int64_t ld, void* workspace, size_t workspace_bytes, void* stream) {
+    IdxQueryIn qin;
+    qin.codes = q_codes;
+    qin.scales = q_scales;
+    if (index_k && index_k->dtype != SIA_MXFP8_E4M3)
+        return fail(SIA_ERR_INVALID_ARG, "sparse_indexer_scores_mxfp8 needs an MXFP8 index cache");
+    return indexer_scores(pt, index_k, qs, qin, w, heads, scores, ld, workspace, workspace_bytes, stream);
+}
+
+int sia_quantize_mxfp8(const void* x, int64_t rows, int32_t dim, uint8_t* codes, uint8_t* scales, void* stream) {
+    if (rows < 0) return fail(SIA_ERR_INVALID_ARG, "rows %lld < 0", (long long)rows);
+    if (dim < 32 || dim % 32) return fail(SIA_ERR_UNSUPPORTED, "dim %d: a positive multiple of 32", dim);
+    if (rows > 0 && (!x || !codes || !scales)) return fail(SIA_ERR_INVALID_ARG, "x/codes/scales is NULL");
+    if (rows == 0) return SIA_OK;
+    hipError_t e = sia::launch_quantize_mxfp8(static_cast<const uint16_t*>(x), rows * (dim / 32), codes, scales,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SIA_OK : hip_fail(e, "quantize launch");
 }
 
 size_t sia_topk_workspace_size(int32_t num_q, int32_t max_row_len, int32_t topk) {

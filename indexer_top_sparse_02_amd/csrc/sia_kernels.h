@@ -5,19 +5,26 @@
 
 namespace sia {
 
+// Index-row formats: bf16; OCP e4m3 with a per-token fp32 scale; MXFP8 (e4m3
+// with one E8M0 scale per 32 elements of a row).
+constexpr int kRowBf16 = 0, kRowFp8 = 1, kRowMx = 2;
+
 // Everything the indexer kernels read. Device pointers unless noted.
 struct IdxArgs {
     const int32_t* page_table;
     const int32_t* seq_lens;
     int32_t batch, max_pages;
     const uint8_t* rows;       // index-K pool [num_pages, 64, dim]
-    const float* scale;        // [num_pages, 64] (fp8) or null
+    const float* scale;        // [num_pages, 64] fp32 (fp8 rows), [num_pages, 64, dim/32] E8M0 bytes
+                               // (MXFP8 rows; the same 4 bytes per row at dim 128), or null
     int64_t num_pages;
     const int32_t* q_seq;
     const int32_t* q_pos;
     int32_t num_q;
     int32_t max_visible;       // host bound on visible row length
-    const uint16_t* q_idx;     // bf16 [num_q, heads, dim]
+    const uint16_t* q_idx;     // bf16 [num_q, heads, dim] (bf16 and fp8 rows)
+    const uint8_t* q8;         // MXFP8 rows: e4m3 query codes [num_q, heads, dim]
+    const uint8_t* q8s;        //             and E8M0 scales [num_q, heads, dim/32]
     const float* w;            // [num_q, heads]
     int32_t heads;
     uint32_t* status;          // device status word
@@ -84,18 +91,22 @@ struct StreamArgs {
     int32_t trace_cap;
 };
 
-// Launchers; return hipSuccess or the launch error. `mb` = ceil(heads / 32).
-hipError_t launch_indexer_rows(const IdxArgs& a, const RowsArgs& r, int mb, int dim, bool fp8, int group,
+// Launchers; return hipSuccess or the launch error. `mb` = ceil(heads / 32),
+// `kf` the index-row format.
+hipError_t launch_indexer_rows(const IdxArgs& a, const RowsArgs& r, int mb, int dim, int kf, int group,
                                bool scores_mode, hipStream_t st);
 hipError_t launch_keys_from_scores(const KeysFromScoresArgs& k, hipStream_t st);
 hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st);
-hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, bool fp8,
+hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, int kf,
                                  int grid, hipStream_t st);
-int indexer_stream_blocks_per_cu(int mb, int dim, bool fp8, int cap, int max_visible);
+int indexer_stream_blocks_per_cu(int mb, int dim, int kf, int cap, int max_visible);
 size_t indexer_stream_smem(int cap, int max_visible, int dim, bool fp8);
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kCoarseBinsHost = 2048;   // = kCoarseBins of the selection code
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);
+// MXFP8 quantization of n_groups groups of 32 consecutive bf16 values.
+hipError_t launch_quantize_mxfp8(const uint16_t* x, int64_t n_groups, uint8_t* codes, uint8_t* scales,
+                                 hipStream_t st);
 
 constexpr int kRowsThreads = 512;      // eight waves: two per SIMD
 constexpr int kRowsRegions = kRowsThreads / 64;   // candidate regions per part (one per wave)
