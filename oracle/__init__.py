@@ -68,6 +68,9 @@ def lib():
             ctypes.c_int32, _i32p, _i32p, ctypes.c_int32, _i32p, _i32p, ctypes.c_int32,
             ctypes.c_int64, _vp, _vp, ctypes.c_int32, _vp, _vp, _f32p, ctypes.c_int32, _f64p,
             ctypes.c_int64, _i32p]
+        L.oracle_sparse_mla_fp8.argtypes = [
+            ctypes.c_int32, _i32p, ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_int64, _vp, _vp,
+            ctypes.c_int32, _i32p, ctypes.c_int32, ctypes.c_double, _f64p, _f64p]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.restype = ctypes.c_int
         L.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -212,6 +215,29 @@ def indexer_scores_mx(q_seq, q_pos, seq_lens, page_table, k_codes, k_scales, q_c
     if rc != 0:
         raise ValueError(f"oracle_indexer_scores_mx failed ({rc})")
     return scores, row_len
+
+
+def sparse_mla_fp8(q_seq, seq_count, page_table, kv8, q_attn, idx, sm_scale):
+    """Sparse attention over an FP8 latent cache of 656-byte rows ([pages, 64,
+    656] uint8: 512 e4m3 codes, four fp32 block scales, 64 bf16 rope values).
+    Returns (out [Q, H, 512], lse [Q, H]) in double."""
+    qs, table = _np(q_seq, np.int32), _np(page_table, np.int32)
+    kv = _np(kv8, np.uint8)
+    assert kv.shape[-1] == 656
+    q = _np(q_attn, np.uint16)
+    ix = _np(idx, np.int32)
+    Q, H, D = q.shape
+    K = ix.shape[1] if ix.ndim == 2 else 0
+    out = np.zeros((Q, H, 512), dtype=np.float64)
+    lse = np.full((Q, H), -np.inf, dtype=np.float64)
+    if Q == 0 or K == 0:
+        return out, lse
+    rc = lib().oracle_sparse_mla_fp8(Q, _p(qs, _i32p), int(seq_count), _p(table, _i32p), table.shape[1],
+                                     kv.shape[0], _p(kv, _vp), _p(q, _vp), H, _p(ix, _i32p), K,
+                                     float(sm_scale), _p(out, _f64p), _p(lse, _f64p))
+    if rc not in (0, -2):
+        raise ValueError(f"oracle_sparse_mla_fp8 failed ({rc})")
+    return out, lse
 
 
 @dataclass

@@ -387,6 +387,83 @@ int oracle_set_num_threads(int n) {
 #endif
 }
 
+/*
+ * Sparse attention over an FP8 latent cache (the pages' main-attention KV
+ * quantization: "Rapid Adaptation and Inference Optimization", section 5.2;
+ * "Day0 Inference Adaptation ... for New-Architecture LLMs", section 4: per
+ * token, blocks of 128 elements share one scale). Each row is 656 bytes:
+ *   bytes   0..511  e4m3fn codes of latent elements 0..511
+ *   bytes 512..527  four fp32 scales, one per block of 128 latent elements
+ *   bytes 528..655  the 64 rope elements (576 - 512) as bf16
+ * The row's values are code * scale[d / 128] for d < 512 and the bf16 value
+ * for d >= 512; then the same attention as oracle_sparse_mla.
+ */
+int oracle_sparse_mla_fp8(int32_t num_q, const int32_t *q_seq, int32_t batch,
+                          const int32_t *page_table, int32_t max_pages, int64_t num_pages,
+                          const uint8_t *kv_rows, const uint16_t *q, int32_t heads,
+                          const int32_t *idx, int32_t K, double sm_scale, double *out, double *lse) {
+    enum { DK = 576, DV = 512, ROW = 656 };
+    if (num_q < 0 || !q_seq || !page_table || !kv_rows || !q || !idx || !out || !lse || heads <= 0 ||
+        K <= 0 || batch <= 0)
+        return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int32_t j = 0; j < num_q; j++) {
+        int32_t b = q_seq[j];
+        double *oj = out + (int64_t)j * heads * DV;
+        for (int64_t i = 0; i < (int64_t)heads * DV; i++) oj[i] = 0.0;
+        for (int32_t a = 0; a < heads; a++) lse[(int64_t)j * heads + a] = -INFINITY;
+        if (b < 0 || b >= batch) { bad = 1; continue; }
+        int32_t m = 0;
+        double *c = (double *)malloc(sizeof(double) * (size_t)K * DK);
+        for (int32_t i = 0; i < K; i++) {
+            int32_t s = idx[(int64_t)j * K + i];
+            if (s < 0) continue;
+            int64_t r = phys_row(page_table, max_pages, b, s);
+            if (r < 0 || r >= num_pages * SIA_ORACLE_PAGE) { bad = 1; continue; }
+            const uint8_t *row = kv_rows + r * ROW;
+            float sc[4];
+            memcpy(sc, row + 512, sizeof sc);
+            for (int32_t d = 0; d < DV; d++)
+                c[(int64_t)m * DK + d] = oracle_e4m3fn_value(row[d]) * (double)sc[d / 128];
+            for (int32_t d = DV; d < DK; d++) {
+                uint16_t bits;
+                memcpy(&bits, row + 528 + 2 * (d - DV), 2);
+                c[(int64_t)m * DK + d] = oracle_bf16_value(bits);
+            }
+            m++;
+        }
+        if (m == 0) { free(c); continue; }
+        double *qa = (double *)malloc(sizeof(double) * DK);
+        double *z = (double *)malloc(sizeof(double) * (size_t)m);
+        for (int32_t a = 0; a < heads; a++) {
+            for (int32_t d = 0; d < DK; d++) qa[d] = oracle_bf16_value(q[((int64_t)j * heads + a) * DK + d]);
+            double zmax = -INFINITY;
+            for (int32_t i = 0; i < m; i++) {
+                double dot = 0.0;
+                for (int32_t d = 0; d < DK; d++) dot += qa[d] * c[(int64_t)i * DK + d];
+                z[i] = sm_scale * dot;
+                if (z[i] > zmax) zmax = z[i];
+            }
+            double l = 0.0;
+            for (int32_t i = 0; i < m; i++) {
+                z[i] = exp(z[i] - zmax);
+                l += z[i];
+            }
+            double *o = oj + (int64_t)a * DV;
+            for (int32_t i = 0; i < m; i++) {
+                double p = z[i] / l;
+                for (int32_t d = 0; d < DV; d++) o[d] += p * c[(int64_t)i * DK + d];
+            }
+            lse[(int64_t)j * heads + a] = zmax + log(l);
+        }
+        free(qa);
+        free(z);
+        free(c);
+    }
+    return bad ? -2 : 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -259,6 +259,35 @@ def make_mx(wl: Workload, scale_lo: int = 124, scale_hi: int = 130, poison: bool
     return MxInputs(k_scales, q_codes, q_scales)
 
 
+KV8_ROW = 656   # fp8 latent row: 512 e4m3 codes, 4 fp32 block scales, 64 bf16 rope values
+
+
+def make_kv8(wl: Workload, poison: bool = False) -> torch.Tensor:
+    """A synthetic FP8 latent cache [num_pages, 64, 656] (uint8) for ``wl``:
+    per row and block of 128 latent elements a scale ~ U(0.5, 2) / 64, codes of
+    N(0,1) * 64 cast to e4m3fn (so the values are about N(0,1) times the
+    block's U(0.5, 2)), rope values N(0,1) in bf16. Seeded from the workload's
+    seed. With ``poison``, rows no sequence owns get NaN codes and scales."""
+    s = wl.spec
+    seeds = [int(x.generate_state(1)[0]) for x in np.random.SeedSequence([s.seed, 0x4B56]).spawn(3)]
+    dev = wl.kv.device
+    rows = wl.num_pages * PAGE
+    codes = _randn_chunked((rows, D_V), 64.0, _gen(dev, seeds[0]), dev, torch.float8_e4m3fn).view(torch.uint8)
+    scales = (torch.rand((rows, 4), generator=_gen(dev, seeds[1]), device=dev, dtype=torch.float32) * 1.5
+              + 0.5) / 64.0
+    rope = _randn_chunked((rows, DIM_KV - D_V), 1.0, _gen(dev, seeds[2]), dev, torch.bfloat16)
+    out = torch.empty((rows, KV8_ROW), dtype=torch.uint8, device=dev)
+    out[:, :512] = codes
+    out[:, 512:528] = scales.view(torch.uint8).view(rows, 16)
+    out[:, 528:] = rope.view(torch.uint8).view(rows, 128)
+    out = out.view(wl.num_pages, PAGE, KV8_ROW)
+    if poison:
+        bad = (~owned_rows_mask(wl)).to(dev)
+        out[bad, :512] = 0x7F
+        out[bad, 512:528] = torch.tensor([float("nan")] * 4, device=dev).view(torch.uint8)
+    return out
+
+
 def owned_rows_mask(wl: Workload) -> torch.Tensor:
     """bool [num_pages, 64]: True where some sequence owns the row."""
     table = wl.page_table.cpu().numpy()
