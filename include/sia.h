@@ -243,7 +243,17 @@ size_t sia_mla_workspace_size(const sia_queries *qs, int32_t heads, int32_t d_v,
 
 /*
  * Sparse MLA attention over the selected rows of the latent KV cache.
- *   kv        latent cache, dtype bf16, dim 576 (512 latent + 64 rope)
+ *   kv        latent cache, dim 576 (512 latent + 64 rope), scale NULL, in one of two
+ *             row formats:
+ *               SIA_BF16: 576 bf16 values per row;
+ *               SIA_FP8_E4M3FN: 656-byte rows: 512 e4m3 codes, four fp32 scales (one
+ *               per 128 latent values: value = code * scale), then the 64 rope values
+ *               as bf16 ("Rapid Adaptation ...", section 5.2 "Main Attention KV Cache
+ *               Quantization": per token, blocks of 128 share one scale). The fp8
+ *               path multiplies the bf16 query's latent part as two e4m3 terms (one
+ *               exponent per head) against the codes on fp8 matrix cores, applies
+ *               each row's block scales to its logits and folds them into the
+ *               probabilities (bf16) of the value product.
  *   q         device bf16 [num_q, heads, 576]
  *   d_v       value width: the first d_v columns of each row (512)
  *   idx       device int32 [num_q, topk]; logical positions of sequence q_seq[j],

@@ -147,6 +147,17 @@ def cache_desc(rows: torch.Tensor, scale: Optional[torch.Tensor] = None) -> Page
     return PagedCache(_ptr(rows), _ptr(scale), int(rows.shape[0]), int(rows.shape[2]), dt)
 
 
+KV8_ROW_BYTES = 656   # fp8 latent row: 512 e4m3 codes, 4 fp32 block scales, 64 bf16 rope values
+
+
+def kv_desc(kv: torch.Tensor) -> PagedCache:
+    """Latent cache descriptor: bf16 [pages, 64, 576], or fp8 rows as uint8
+    [pages, 64, 656] (512 e4m3 codes, four fp32 scales per 128, 64 bf16 rope)."""
+    if kv.dtype == torch.uint8 and int(kv.shape[2]) == KV8_ROW_BYTES:
+        return PagedCache(_ptr(kv), None, int(kv.shape[0]), 576, SIA_FP8_E4M3FN)
+    return cache_desc(kv)
+
+
 def visible_max(q_seq, q_pos, seq_lens) -> int:
     """max_j min(t_j + 1, n_{b_j}) (synchronizes)."""
     if q_seq.numel() == 0:
@@ -271,15 +282,17 @@ def sparse_indexer_scores_mxfp8(page_table, seq_lens, k_codes, k_scales, q_seq, 
     return scores
 
 
-def quantize_mxfp8(x: torch.Tensor, stream=None):
+def quantize_mxfp8(x: torch.Tensor, codes=None, scales=None, stream=None):
     """MXFP8 codes (uint8, shape of x) and E8M0 scale bytes (last dim / 32) of
     the bf16 tensor x (last dimension a multiple of 32)."""
     if x.dtype != torch.bfloat16:
         raise ValueError("quantize_mxfp8 takes bf16")
     D = int(x.shape[-1])
     rows = x.numel() // D if D else 0
-    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
     _check(lib().sia_quantize_mxfp8(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
@@ -331,7 +344,7 @@ def sparse_mla_attention(page_table, seq_lens, kv, q_seq, q, idx, sm_scale, *, d
     """Sparse MLA attention. Returns (out bf16 [Q, H, d_v], lse fp32 [Q, H] or None)."""
     Q, H = int(q.shape[0]), int(q.shape[1])
     topk = int(idx.shape[1])
-    pt, c = page_table_desc(page_table, seq_lens), cache_desc(kv)
+    pt, c = page_table_desc(page_table, seq_lens), kv_desc(kv)
     qd = Queries(Q, _ptr(q_seq), None, 1, 0)
     need = lib().sia_mla_workspace_size(ctypes.byref(qd), H, int(d_v), topk)
     if need == 0:
@@ -354,7 +367,7 @@ def sparse_mla_attention_noalloc(page_table, seq_lens, kv, q_seq, q, idx, sm_sca
     workspace (no device allocation inside the library). Returns (out, lse)."""
     Q, H = int(q.shape[0]), int(q.shape[1])
     topk = int(idx.shape[1])
-    pt, c = page_table_desc(page_table, seq_lens), cache_desc(kv)
+    pt, c = page_table_desc(page_table, seq_lens), kv_desc(kv)
     qd = Queries(Q, _ptr(q_seq), None, 1, 0)
     if out is None:
         out = torch.empty((Q, H, d_v), dtype=torch.bfloat16, device=q.device)

@@ -36,11 +36,24 @@
 namespace sia {
 
 constexpr int kDK = 576, kDV = 512;
-constexpr int kRowB = kDK * 2;              // bytes per latent row (1152 = 72 chunks of 16)
-constexpr int kRowChunks = kRowB / 16;
 constexpr int kTR = 32;                     // rows per tile
-constexpr int kTileB = kTR * kRowB;         // 36864
-constexpr int kTileCopies = kTileB / 1024;  // 36 copies of 64 lanes x 16 bytes
+
+// Row formats of the latent cache. bf16: 576 values (1152 bytes = 72 chunks
+// of 16). FP8: 512 e4m3 latent codes, four fp32 scales (one per 128 latent
+// values), 64 bf16 rope values (656 bytes = 41 chunks). Tiles of 32 rows are
+// copied 1 KB (64 lanes x 16 bytes) at a time; the fp8 tile's last copy is
+// half full (its spare lanes repeat the tile's last chunk).
+template <bool KV8>
+struct RowFmt {
+    static constexpr int RB = KV8 ? 656 : kDK * 2;        // bytes per row
+    static constexpr int CH = RB / 16;                    // 16-byte chunks per row
+    static constexpr int TB = kTR * RB;                   // bytes per tile
+    static constexpr int CHUNKS = kTR * CH;               // chunks per tile
+    static constexpr int COPIES = (CHUNKS + 63) / 64;     // 1 KB copies per tile
+    static constexpr int SCALES = 512, ROPE = 528;        // (fp8) byte offsets in a row
+};
+constexpr int kRowB = RowFmt<false>::RB;
+constexpr int kTileB = RowFmt<false>::TB;
 constexpr int kPStride = kTR * 2 + 16;      // bytes per head of P (padded: no bank conflicts)
 constexpr int kMaxSliceRows = kAttnMaxSliceRows;
 
@@ -90,9 +103,54 @@ __device__ __forceinline__ void ds_read_tr16x8_barrier(u32x2 (&a)[4], u32x2 (&b)
         : "memory");
 }
 
-// Byte offset of logical 16-byte chunk c of tile row r (chunks are XOR-swizzled
-// by r within aligned groups of eight).
-__device__ __forceinline__ int tile_off(int r, int c) { return r * kRowB + ((c ^ (r & 7)) << 4); }
+// Four 8-bit transposing reads (16 lanes of a group address rows r0 + j/2 and
+// columns c0 + 8 (j % 2): lane j receives column c0 + j of rows r0 .. r0 + 7),
+// then the wait, in one asm block, so that the results are defined when it ends.
+__device__ __forceinline__ void ds_read_tr8x4(const uint8_t* base, const int (&off)[4], u32x2 (&v)[4]) {
+    const uint32_t a = (uint32_t)(uintptr_t)(const SIA_LDS uint8_t*)base;
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %4\n\t"
+        "ds_read_b64_tr_b8 %1, %5\n\t"
+        "ds_read_b64_tr_b8 %2, %6\n\t"
+        "ds_read_b64_tr_b8 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a + off[0]), "v"(a + off[1]), "v"(a + off[2]), "v"(a + off[3])
+        : "memory");
+}
+
+// Eight e4m3 values (bytes in order) as eight bf16 values (exact: e4m3 values
+// are bf16 values).
+__device__ __forceinline__ bf16x8 e4m3x8_bf16x8(u32x2 v) {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.f, false);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], 1.f, true);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.f, false);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], 1.f, true);
+    return as_bf16x8(u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                           __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)});
+}
+
+// Eight bf16 values times eight fp32 factors, rounded to nearest even bf16.
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 p, const float (&sc)[8]) {
+    const u32x4 u = __builtin_bit_cast(u32x4, p);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float lo = __uint_as_float(u[i] << 16) * sc[2 * i];
+        const float hi = __uint_as_float(u[i] & 0xffff0000u) * sc[2 * i + 1];
+        o[i] = f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    }
+    return as_bf16x8(o);
+}
+
+// Byte offset of logical 16-byte chunk c of tile row r. bf16 rows: chunks are
+// XOR-swizzled by r within aligned groups of eight. fp8 rows are stored as
+// they are.
+template <bool KV8 = false>
+__device__ __forceinline__ int tile_off(int r, int c) {
+    if constexpr (KV8) return r * RowFmt<true>::RB + (c << 4);
+    else return r * kRowB + ((c ^ (r & 7)) << 4);
+}
 
 // Max / sum over the 16 lanes of a DPP row (lanes 16g .. 16g+15), by rotations
 // of the row by 8, 4, 2 and 1 lanes.
@@ -115,7 +173,7 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
-template <int HB>
+template <int HB, bool KV8>
 struct MlaGeom {
     static constexpr int NHB = HB / 16;          // 16-head blocks
     static constexpr int NW = 2 * NHB;           // waves: (head block, row block)
@@ -123,8 +181,28 @@ struct MlaGeom {
     static constexpr int CPW = kDV / NW;         // output columns per wave
     static constexpr int NCB = CPW / 16;         // 16-column blocks per wave
     // tile copies per wave: waves below SPLIT issue one more than the rest
-    static constexpr int CP_LO = kTileCopies / NW;
-    static constexpr int SPLIT = kTileCopies % NW;
+    static constexpr int CP_LO = RowFmt<KV8>::COPIES / NW;
+    static constexpr int SPLIT = RowFmt<KV8>::COPIES % NW;
+};
+
+// The query of one wave's 16 heads in MFMA operand layout. bf16 rows: all 576
+// columns as bf16 (32-wide steps of the 16x16x32 bf16 MFMA). fp8 rows: the
+// 512 latent columns enter 16x16x128 fp8 MFMAs against the raw e4m3 codes, the
+// bf16 query split per head into e4m3 hi = e4m3(X) and lo = e4m3(16 (X - hi))
+// with X = q 2^s (one exponent per head, max|q| 2^s in [128, 256)), the two
+// products summed with MFMA scales 2^-s and 2^-(s+4); the 64 rope columns stay
+// bf16.
+template <bool KV8>
+struct MlaQuery;
+template <>
+struct MlaQuery<false> {
+    bf16x8 qa[kDK / 32];
+};
+template <>
+struct MlaQuery<true> {
+    i32x8 hi[4], lo[4];   // latent blocks of 128: this lane's 32 codes of each
+    bf16x8 rope[2];
+    int sh, sl;
 };
 
 // Wave (hb, rb) owns 16 heads
@@ -137,15 +215,19 @@ struct MlaGeom {
 // (dma16): the compiler neither sees nor waits for them, and each wave waits for
 // its own copies of a tile with a counted vmcnt wait before the barrier that
 // publishes the tile to the other waves.
-template <int HB>
+template <int HB, bool KV8>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_kernel(AttnArgs A) {
-    using GM = MlaGeom<HB>;
+    using GM = MlaGeom<HB, KV8>;
+    using RF = RowFmt<KV8>;
     constexpr int NHB = GM::NHB, NW = GM::NW, NT = GM::NT, CPW = GM::CPW, NCB = GM::NCB;
-    constexpr int KS = kDK / 32;   // 18 MFMA steps over a full row
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[kTileB];
-    __shared__ __attribute__((aligned(16))) uint8_t ring1[kTileB];
-    __shared__ __attribute__((aligned(16))) uint8_t ring2[kTileB];
-    __shared__ __attribute__((aligned(16))) uint8_t ring3[kTileB];
+    constexpr int KS = kDK / 32;   // 18 MFMA steps over a full bf16 row
+    // (a slot holds whole 1 KB copies: the fp8 tile's half-full last copy lands
+    // in the slot's spare tail)
+    constexpr int SLOT = RF::COPIES * 1024;
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[SLOT];
+    __shared__ __attribute__((aligned(16))) uint8_t ring3[SLOT];
     __shared__ __attribute__((aligned(16))) uint32_t rows[kMaxSliceRows];
     // P, alpha and the moved flags of tile t are written after the first barrier
     // of iteration t and read after its second; the next writes come after the
@@ -190,11 +272,66 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
 
     // ---- Q of this wave's 16 heads, all 576 columns
     const int hb = w % NHB, rb = w / NHB;
-    bf16x8 qa[KS];
-    {
+    MlaQuery<KV8> Q;
+    if constexpr (!KV8) {
         const uint16_t* qrow = A.q + ((int64_t)j * A.heads + head0 + hb * 16 + jl) * kDK + g * 8;
 #pragma unroll
-        for (int ks = 0; ks < KS; ks++) qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + ks * 32));
+        for (int ks = 0; ks < KS; ks++) Q.qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + ks * 32));
+    } else {
+        // lane (jl, g): head hb*16 + jl; latent block b: elements 128 b + 32 g ..
+        // + 31 (the same positions as its key bytes, so the MFMA pairs them
+        // whatever k it assigns); rope steps: elements 512 + 32 ks + 8 g .. + 7
+        const uint16_t* qrow = A.q + ((int64_t)j * A.heads + head0 + hb * 16 + jl) * kDK;
+        u32x4 v[4][4];
+        float amax = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+                v[b][c] = *reinterpret_cast<const u32x4*>(qrow + 128 * b + 32 * g + 8 * c);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    amax = fmaxf(amax, fabsf(__uint_as_float(v[b][c][e] << 16)));
+                    amax = fmaxf(amax, fabsf(__uint_as_float(v[b][c][e] & 0xffff0000u)));
+                }
+            }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        int sx = 0;
+        if (amax > 0.f) {
+            int e;
+            frexpf(amax, &e);
+            sx = min(max(8 - e, -120), 120);
+        }
+        const float f = ldexpf(1.f, sx);
+        Q.sh = 127 - sx;
+        Q.sl = 127 - sx - 4;
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    float x[4];
+                    x[0] = __uint_as_float(v[b][c][e] << 16) * f;
+                    x[1] = __uint_as_float(v[b][c][e] & 0xffff0000u) * f;
+                    x[2] = __uint_as_float(v[b][c][e + 1] << 16) * f;
+                    x[3] = __uint_as_float(v[b][c][e + 1] & 0xffff0000u) * f;
+                    int h = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+                    h = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], h, true);
+                    float r[4];
+                    r[0] = (x[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0)) * 16.f;
+                    r[1] = (x[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1)) * 16.f;
+                    r[2] = (x[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2)) * 16.f;
+                    r[3] = (x[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3)) * 16.f;
+                    int lo = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+                    lo = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], lo, true);
+                    Q.hi[b][c * 2 + e / 2] = h;
+                    Q.lo[b][c * 2 + e / 2] = lo;
+                }
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++)
+            Q.rope[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 512 + 32 * ks + 8 * g));
     }
 
     // ---- validated, compacted physical row ids of the slice. Thread t owns the
@@ -262,16 +399,19 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
 #pragma unroll
             for (int k = k0; k < k0 + GRP && k < CPMAX; k++) {
                 const int i = w + NW * (k < ncp ? k : ncp - 1);
-                const int q = i * 64 + l;
-                row[k - k0] = rows[min(t * kTR + q / kRowChunks, nr - 1)];
+                const int q = min(i * 64 + l, RF::CHUNKS - 1);
+                row[k - k0] = rows[min(t * kTR + q / RF::CH, nr - 1)];
             }
 #pragma unroll
             for (int k = k0; k < k0 + GRP && k < CPMAX; k++) {
                 const int i = w + NW * (k < ncp ? k : ncp - 1);
-                const int q = i * 64 + l;
-                const int rr = q / kRowChunks, c = q % kRowChunks;
-                const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row[k - k0] * kRowB +
-                                     ((c ^ (rr & 7)) << 4);
+                // (lanes past the tile's last chunk copy that chunk again into
+                // the slot's spare tail)
+                const int q = min(i * 64 + l, RF::CHUNKS - 1);
+                const int rr = q / RF::CH, c = q % RF::CH;
+                const int cs = KV8 ? c : (c ^ (rr & 7));
+                const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row[k - k0] * RF::RB +
+                                     (cs << 4);
                 dma16(src, (SIA_LDS void*)(dst + i * 1024));
             }
         }
@@ -294,10 +434,44 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
         }
     }
 
+    // fp8 rows: the logits of this wave's 16 heads x 16 rows as the latent
+    // blocks' fp8 products times the row's block scales (a0) plus the bf16 rope
+    // products (a1)
+    auto qk8 = [&](const uint8_t* buf, f32x4& a0, f32x4& a1) {
+        if constexpr (KV8) {
+        const uint8_t* row = buf + kn * RF::RB;
+        f32x4 acc[4];
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const u32x4 k0 = *reinterpret_cast<const u32x4*>(row + 128 * b + 32 * g);
+            const u32x4 k1 = *reinterpret_cast<const u32x4*>(row + 128 * b + 32 * g + 16);
+            const i32x8 kb = {(int)k0[0], (int)k0[1], (int)k0[2], (int)k0[3],
+                              (int)k1[0], (int)k1[1], (int)k1[2], (int)k1[3]};
+            acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.hi[b], kb, f32x4{0.f, 0.f, 0.f, 0.f},
+                                                                      0, 0, 0, Q.sh, 0, 127);
+            acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(Q.lo[b], kb, acc[b], 0, 0, 0, Q.sl, 0, 127);
+        }
+        a1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++) {
+            const u32x4 kr = *reinterpret_cast<const u32x4*>(row + RF::ROPE + 2 * (32 * ks + 8 * g));
+            a1 = mfma16(Q.rope[ks], as_bf16x8(kr), a1);
+        }
+        const f32x4 sc = *reinterpret_cast<const f32x4*>(row + RF::SCALES);
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            a0[r] = sc[0] * acc[0][r] + sc[1] * acc[1][r] + sc[2] * acc[2][r] + sc[3] * acc[3][r];
+        }
+    };
     // logits of this wave's 16 heads x 16 rows of the tile in `buf`, as two
     // partial sums (even and odd steps) that the caller adds only where it needs
     // them, so that the vector work in between runs while the MFMAs finish
     auto qk = [&](const uint8_t* buf, f32x4& a0, f32x4& a1) {
+        if constexpr (KV8) {
+            qk8(buf, a0, a1);
+            return;
+        } else {
+        const bf16x8 (&qa)[KS] = Q.qa;
         const int koff[2] = {koffL[0], koffL[1]};
         // the key operands of the next DEPTH steps are in flight during each MFMA
         constexpr int DEPTH = 6;
@@ -324,6 +498,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x008, DEPTH, 0);
+        }
     };
     const float scale_log2 = A.sm_scale * 1.4426950408889634f;
     constexpr float kLazyMax = 8.f;
@@ -436,7 +611,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             // column blocks of tile t (in its slot since the previous iteration)
             // are read on the way into the barrier.
             u32x2 va0[4], vb0[4];
-            {
+            if constexpr (!KV8) {
                 const uint32_t sb = (uint32_t)(uintptr_t)(const SIA_LDS uint8_t*)slot_of(t);
                 uint32_t pa_[4], pb_[4];
 #pragma unroll
@@ -445,6 +620,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
                     pb_[q] = sb + voffL[1][q];
                 }
                 ds_read_tr16x8_barrier(va0, vb0, pa_, pb_);
+            } else {
+                lds_barrier();
             }
             // ---- O = alpha * O + P V of tile t over this wave's columns
             int any = 0;
@@ -475,6 +652,37 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
             for (int h = 0; h < NHB; h++)
                 pa[h] = as_bf16x8(*reinterpret_cast<const u32x4*>(&pbuf[(h * 16 + jl) * kPStride + g * 16]));
             const uint8_t* buf = slot_of(t);
+            if constexpr (KV8) {
+                // fp8 values: row r of column block blk is code * scale[r][blk];
+                // the scale goes into P (rounded to bf16), the codes are read
+                // transposed (one 8-bit read per 16 columns: rows 8g .. 8g+7 of
+                // column jl) and widened to bf16 exactly
+                bf16x8 ps[NHB];
+#pragma unroll
+                for (int c0 = 0; c0 < NCB; c0 += 4) {
+                    if ((c0 * 16) % 128 == 0) {   // first group of a 128-column block
+                        const int blk = (w * CPW + c0 * 16) / 128;
+                        float sc8[8];
+#pragma unroll
+                        for (int e = 0; e < 8; e++)
+                            sc8[e] = *reinterpret_cast<const float*>(buf + (8 * g + e) * RF::RB + RF::SCALES + 4 * blk);
+#pragma unroll
+                        for (int h = 0; h < NHB; h++) ps[h] = scale_bf16x8(pa[h], sc8);
+                    }
+                    int off[4];
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        off[q] = (8 * g + (jl >> 1)) * RF::RB + w * CPW + (c0 + q) * 16 + 8 * (jl & 1);
+                    u32x2 vv[4];
+                    ds_read_tr8x4(buf, off, vv);
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const bf16x8 vb = e4m3x8_bf16x8(vv[q]);
+#pragma unroll
+                        for (int h = 0; h < NHB; h++) o[h][c0 + q] = mfma16(ps[h], vb, o[h][c0 + q]);
+                    }
+                }
+            } else {
             const int(&voff)[2][4] = voffL;
 #pragma unroll
             for (int c0 = 0; c0 < NCB; c0 += 4) {
@@ -500,6 +708,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
 #pragma unroll
                     for (int h = 0; h < NHB; h++) o[h][c0 + q] = mfma16(pa[h], vb, o[h][c0 + q]);
                 }
+            }
             }
         }
     }
@@ -574,20 +783,23 @@ __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs A) {
     if (threadIdx.x == 0 && A.lse) A.lse[j * A.heads + h] = wsum > 0.f ? mx + logf(wsum) : -INFINITY;
 }
 
-template <int HB>
+template <int HB, bool KV8>
 static hipError_t mla_launch(const AttnArgs& a, hipStream_t st) {
     const int n_hb = a.heads / HB;
     const int64_t pairs = (int64_t)a.num_q * a.n_split;
     const int64_t blocks = (pairs + 7) / 8 * 8 * n_hb;
-    hipLaunchKernelGGL(sparse_mla_kernel<HB>, dim3((unsigned)blocks), dim3(MlaGeom<HB>::NT), 0, st, a);
+    hipLaunchKernelGGL((sparse_mla_kernel<HB, KV8>), dim3((unsigned)blocks), dim3(MlaGeom<HB, KV8>::NT), 0, st, a);
     return hipGetLastError();
 }
 
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st) {
-    switch (a.heads_per_block) {
-        case 64: return mla_launch<64>(a, st);
-        case 32: return mla_launch<32>(a, st);
-        case 16: return mla_launch<16>(a, st);
+    switch (a.heads_per_block * 2 + (a.kv8 ? 1 : 0)) {
+        case 128: return mla_launch<64, false>(a, st);
+        case 64: return mla_launch<32, false>(a, st);
+        case 32: return mla_launch<16, false>(a, st);
+        case 129: return mla_launch<64, true>(a, st);
+        case 65: return mla_launch<32, true>(a, st);
+        case 33: return mla_launch<16, true>(a, st);
         default: return hipErrorInvalidValue;
     }
 }

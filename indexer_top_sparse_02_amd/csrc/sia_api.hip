@@ -487,8 +487,10 @@ static int check_attn(const sia_page_table* pt, const sia_paged_cache* kv, const
     if ((rc = check_page_table(pt)) != SIA_OK) return rc;
     if (!kv || !kv->rows) return fail(SIA_ERR_INVALID_ARG, "kv cache descriptor/rows is NULL");
     if (kv->num_pages < 1) return fail(SIA_ERR_INVALID_ARG, "kv num_pages < 1");
-    if (kv->dtype != SIA_BF16) return fail(SIA_ERR_UNSUPPORTED, "kv dtype %d: only bf16", kv->dtype);
+    if (kv->dtype != SIA_BF16 && kv->dtype != SIA_FP8_E4M3FN)
+        return fail(SIA_ERR_UNSUPPORTED, "kv dtype %d: bf16 or fp8 e4m3fn rows", kv->dtype);
     if (kv->dim != 576) return fail(SIA_ERR_UNSUPPORTED, "kv dim %d: only 576", kv->dim);
+    if (kv->scale) return fail(SIA_ERR_INVALID_ARG, "the latent cache takes no separate scale pool (fp8 rows hold their scales)");
     if (d_v != 512) return fail(SIA_ERR_UNSUPPORTED, "d_v %d: only 512", d_v);
     if (!qs) return fail(SIA_ERR_INVALID_ARG, "query descriptor is NULL");
     if (qs->num_q < 0) return fail(SIA_ERR_INVALID_ARG, "num_q %d < 0", qs->num_q);
@@ -521,6 +523,7 @@ int mla_run(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queri
     a.batch = pt->batch;
     a.max_pages = pt->max_pages;
     a.kv = static_cast<const uint16_t*>(kv->rows);
+    a.kv8 = kv->dtype == SIA_FP8_E4M3FN;
     a.num_pages = kv->num_pages;
     a.q_seq = qs->q_seq;
     a.num_q = qs->num_q;

@@ -122,7 +122,8 @@ struct AttnArgs {
     const int32_t* page_table;
     const int32_t* seq_lens;
     int32_t batch, max_pages;
-    const uint16_t* kv;       // bf16 [num_pages, 64, 576]
+    const uint16_t* kv;       // bf16 [num_pages, 64, 576], or (kv8) 656-byte fp8 rows [num_pages, 64, 656]
+    int32_t kv8;
     int64_t num_pages;
     const int32_t* q_seq;
     int32_t num_q;

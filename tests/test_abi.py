@@ -98,7 +98,8 @@ def test_workspace_size_grows_with_context():
     lib = L.lib()
     buf, pt, c, q, addr = _descs(max_pages=2048, max_visible=131072, num_q=128, group=2, batch=64)
     big = lib.sia_indexer_workspace_size(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(q), 64, 2048)
-    # one 4-byte score key per visible position of every query, plus per-part histograms
+    # room for a candidate key and position and a dense key per visible position of
+    # every query (the worst case keeps every position), plus per-part histograms
     assert big >= 128 * 131072 * 4
     q.max_visible = 4000
     small = lib.sia_indexer_workspace_size(ctypes.byref(pt), ctypes.byref(c), ctypes.byref(q), 64, 2048)
@@ -118,7 +119,10 @@ def test_attention_rejects_bad_arguments():
     assert call(d_v=256) == L.SIA_ERR_UNSUPPORTED
     assert call(topk=0) == L.SIA_ERR_INVALID_ARG
     assert call(kvd=L.PagedCache(addr, None, 4, 512, 0)) == L.SIA_ERR_UNSUPPORTED
-    assert call(kvd=L.PagedCache(addr, None, 4, 576, 1)) == L.SIA_ERR_UNSUPPORTED
+    # fp8 latent rows carry their scales: a separate scale pool is refused; MXFP8
+    # is an index-cache format only
+    assert call(kvd=L.PagedCache(addr, addr, 4, 576, 1)) == L.SIA_ERR_INVALID_ARG
+    assert call(kvd=L.PagedCache(addr, None, 4, 576, 2)) == L.SIA_ERR_UNSUPPORTED
     assert call(scale=float("nan")) == L.SIA_ERR_INVALID_ARG
     assert call(ws_bytes=10) == L.SIA_ERR_WORKSPACE
     assert lib.sia_mla_workspace_size(ctypes.byref(q), 128, 512, 2048) >= 256
