@@ -508,6 +508,91 @@ def chunked_line(wl, s, steps, warmup, cpu=True):
     return line
 
 
+def mx_decode(sia, W, wl, s, steps, warmup, flush, ref_idx, idx_bytes):
+    """The same decode step with the pages' layered quantization: the index
+    cache in MXFP8 (the cache's values e4m3 * sigma rounded to bf16, quantized
+    by the library's quantizer once, untimed: a cache is written once and read
+    every step), the bf16 query quantized to MXFP8 inside the timed step, then
+    the MXFP8 indexer + Top-K; attention once over the bf16 latent cache and
+    once over an FP8 latent cache (656-byte rows; synthetic values of the same
+    distribution, as no latent quantizer is part of this path). Reports the
+    steps, the indexer phase (query quantization included) against the HBM
+    roofline, the Top-K hit rate against the bf16-query path, and the FP8
+    attention's gathered bytes and rate."""
+    import numpy as np
+    import torch
+    dev = wl.q_idx.device
+    vals = (wl.idx_k.view(torch.float8_e4m3fn).float() * wl.idx_scale[..., None]).to(torch.bfloat16)
+    kc, ks = sia.quantize_mxfp8(vals)
+    del vals
+    torch.cuda.empty_cache()
+    qc = torch.empty(wl.q_idx.shape, dtype=torch.uint8, device=dev)
+    qs = torch.empty(tuple(wl.q_idx.shape[:-1]) + (s.dim_idx // 32,), dtype=torch.uint8, device=dev)
+    group = s.q_per_seq
+    maxv = int(torch.minimum(wl.q_pos.long() + 1, wl.seq_lens.long()[wl.q_seq.long()]).max())
+    ws_i = sia.new_workspace(sia.indexer_workspace_size(wl.page_table, wl.seq_lens, kc, ks, wl.q_seq, wl.q_pos,
+                                                        s.heads_idx, s.topk, group=group, max_visible=maxv), dev)
+    ws_a = sia.new_workspace(sia.mla_workspace_size(wl.num_q, s.heads_attn, s.topk), dev)
+    idx = torch.empty((wl.num_q, s.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.num_q, s.heads_attn, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.num_q, s.heads_attn), dtype=torch.float32, device=dev)
+
+    def indexer():
+        sia.quantize_mxfp8(wl.q_idx, codes=qc, scales=qs)
+        sia.sparse_indexer_topk_mxfp8(wl.page_table, wl.seq_lens, kc, ks, wl.q_seq, wl.q_pos, qc, qs, wl.w, s.topk,
+                                      group=group, max_visible=maxv, out_idx=idx, workspace=ws_i)
+
+    kv8 = W.make_kv8(wl)
+
+    def attention():
+        sia.sparse_mla_attention(wl.page_table, wl.seq_lens, wl.kv, wl.q_seq, wl.q_attn, idx, s.sm_scale,
+                                 out=out, lse=lse, workspace=ws_a)
+
+    def attention8():
+        sia.sparse_mla_attention(wl.page_table, wl.seq_lens, kv8, wl.q_seq, wl.q_attn, idx, s.sm_scale,
+                                 out=out, lse=lse, workspace=ws_a)
+
+    def timed(att):
+        for _ in range(max(1, warmup)):
+            indexer()
+            att()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i, (e0, e1, e2) in enumerate(ev):
+            if flush is not None:
+                flush.fill_(i & 0x7f)
+            e0.record()
+            indexer()
+            e1.record()
+            att()
+            e2.record()
+        torch.cuda.synchronize()
+        return (_stats([e0.elapsed_time(e2) for e0, _, e2 in ev]), _stats([e0.elapsed_time(e1) for e0, e1, _ in ev]),
+                _stats([e1.elapsed_time(e2) for _, e1, e2 in ev]))
+    st, si, _ = timed(attention)
+    st8, _, sa8 = timed(attention8)
+    key = (wl.q_seq.long()[:, None] * (1 << 32) + idx.long())[idx >= 0]
+    rows8 = int(torch.unique(key).numel())
+    att8_bytes = rows8 * 656 + wl.num_q * (s.heads_attn * 576 * 2 + s.heads_attn * 512 * 2 + s.topk * 4)
+    a, b = idx.cpu().numpy(), ref_idx.cpu().numpy()
+    hits = [len(set(x[x >= 0].tolist()) & set(y[y >= 0].tolist())) / max(1, int((y >= 0).sum()))
+            for x, y in zip(a, b)]
+    gbs = idx_bytes / (si["median"] * 1e-3) / 1e9
+    return {"value": wl.num_q / (st["median"] * 1e-3), "unit": "query tokens/s",
+            "ms_per_step": st["median"], "ms_per_step_min": st["min"],
+            "indexer_ms": si["median"], "indexer_ms_min": si["min"],
+            "indexer_hbm_gbs": gbs, "indexer_frac_of_peak": gbs / PEAK_HBM_GBS,
+            "topk_hit_rate_vs_bf16_query": float(np.mean(hits)), "topk_hit_rate_min": float(np.min(hits)),
+            "fp8_latent_step": {"value": wl.num_q / (st8["median"] * 1e-3), "unit": "query tokens/s",
+                                "ms_per_step": st8["median"], "ms_per_step_min": st8["min"],
+                                "attention_ms": sa8["median"], "attention_bytes": att8_bytes,
+                                "attention_hbm_gbs": att8_bytes / (sa8["median"] * 1e-3) / 1e9},
+            "note": "index cache MXFP8 (e4m3 + E8M0 per 32), query quantized to MXFP8 in the timed step; "
+                    "same algorithmic bytes per row (128 + 4) as the fp8 cache with a token scale; "
+                    "FP8 latent rows 656 B against 1152 B (synthetic values)"}
+
+
 def launch_overhead(sia, W, dev, steps, warmup):
     """The small decode workloads, where a step takes tens of microseconds:
     host launches against replays of one HIP graph per call (the same kernels
@@ -609,6 +694,7 @@ def main():
                      "algorithmic_bytes_per_call": by["indexer"],
                      "call_ms": idx_ms, "call_ms_min": si["min"]},
     }
+    line["quantized_path"] = mx_decode(sia, W, wl, s, a.steps, a.warmup, flush, idx, by["indexer"])
     del wl, idx, flush
     torch.cuda.empty_cache()
     line["small_decode_launch_overhead"] = launch_overhead(sia, W, dev, a.steps, a.warmup)
