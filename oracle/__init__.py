@@ -240,6 +240,25 @@ def sparse_mla_fp8(q_seq, seq_count, page_table, kv8, q_attn, idx, sm_scale):
     return out, lse
 
 
+def indexer_prepare(xq, xh, wq, wk, k_gamma, k_beta, ww, eps):
+    """The indexer's inputs from the projections' inputs, in double precision
+    (all bf16 operands are exact in double):
+        q = xq Wq^T                         [M, heads * dim]
+        k = LayerNorm(xh Wk^T) * gamma + beta   (mean and biased variance over dim)
+        w = xh Ww^T                         [M, heads]
+    ("Rapid Adaptation ...", section 4.3: query projection, key normalization,
+    head-weight projection.) The matrix products are numpy's."""
+    def f64(t):
+        return t.double().cpu().numpy() if hasattr(t, "double") else np.asarray(t, dtype=np.float64)
+    q = f64(xq) @ f64(wq).T
+    kp = f64(xh) @ f64(wk).T
+    mean = kp.mean(axis=1, keepdims=True)
+    var = ((kp - mean) ** 2).mean(axis=1, keepdims=True)
+    k = (kp - mean) / np.sqrt(var + float(eps)) * f64(k_gamma) + f64(k_beta)
+    w = f64(xh) @ f64(ww).T
+    return q, k, w
+
+
 @dataclass
 class Reference:
     scores: np.ndarray
