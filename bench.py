@@ -593,6 +593,52 @@ def mx_decode(sia, W, wl, s, steps, warmup, flush, ref_idx, idx_bytes):
                     "FP8 latent rows 656 B against 1152 B (synthetic values)"}
 
 
+def prepare_streams(sia, W, dev, steps, warmup, dq=1536, dh=7168):
+    """Indexer input preparation for the 128 query tokens of the 128K decode
+    step (query latent width dq, hidden width dh, 64 heads x 128, synthetic
+    weights): the three chains (query projection + MXFP8, key projection +
+    LayerNorm + MXFP8 + cache rows, head-weight projection) on one stream, then
+    on three streams joined by events. Reports both (median of `steps`) and the
+    critical-path saving."""
+    import torch
+    s = W.spec("spec_decode_128k", batch=64, ctx_lo=4096, ctx_hi=4096)
+    wl = W.make(s, device=dev, with_attn=False)
+    mx = W.make_mx(wl)
+    g = torch.Generator(device=dev).manual_seed(7)
+    M = wl.num_q
+    xq = torch.randn(M, dq, generator=g, device=dev).to(torch.bfloat16)
+    xh = torch.randn(M, dh, generator=g, device=dev).to(torch.bfloat16)
+    wq = (torch.randn(64 * 128, dq, generator=g, device=dev) / dq ** 0.5).to(torch.bfloat16)
+    wk = (torch.randn(128, dh, generator=g, device=dev) / dh ** 0.5).to(torch.bfloat16)
+    ww = (torch.randn(64, dh, generator=g, device=dev) / dh ** 0.5).to(torch.bfloat16)
+    gamma = torch.ones(128, device=dev)
+    beta = torch.zeros(128, device=dev)
+    main = torch.cuda.current_stream()
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]
+    events = [torch.cuda.Event() for _ in range(3)]
+    out = {}
+    for name, streams in (("one_stream", [main, main, main]), ("three_streams", [main] + side)):
+        def run():
+            sia.indexer_prepare(xq, xh, wq, wk, gamma, beta, ww, wl.page_table, wl.seq_lens, wl.idx_k,
+                                mx.k_scales, wl.q_seq, wl.q_pos, streams=streams, events=events)
+        for _ in range(max(1, warmup)):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(main)
+            run()
+            e1.record(main)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        out[name] = _stats(ts)
+    out["saving_us"] = (out["one_stream"]["median"] - out["three_streams"]["median"]) * 1e3
+    out["config"] = {"tokens": M, "dq": dq, "dh": dh, "heads": 64, "dim": 128,
+                     "weights_mb": (64 * 128 * dq + 128 * dh + 64 * dh) * 2 / 1e6}
+    return out
+
+
 def launch_overhead(sia, W, dev, steps, warmup):
     """The small decode workloads, where a step takes tens of microseconds:
     host launches against replays of one HIP graph per call (the same kernels
@@ -698,6 +744,7 @@ def main():
     del wl, idx, flush
     torch.cuda.empty_cache()
     line["small_decode_launch_overhead"] = launch_overhead(sia, W, dev, a.steps, a.warmup)
+    line["input_preparation"] = prepare_streams(sia, W, dev, a.steps, a.warmup)
     if not a.no_prefill:
         ps = W.spec("prefill_16k")
         line["prefill"] = prefill_line(W.make(ps, device=dev), ps, max(10, a.steps // 2),

@@ -236,6 +236,60 @@ int sparse_topk_from_scores(const float *scores, int64_t ld, const int32_t *row_
                             int32_t *out_idx, float *out_score, void *workspace,
                             size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------ input preparation */
+
+/*
+ * Projection weights of the indexer's inputs (bf16, out x in like a linear
+ * layer): the query heads from the query latent xq, the index key and the head
+ * weights from the hidden state xh.
+ */
+typedef struct {
+    const void *wq;        /* device bf16 [heads * dim, dq] */
+    const void *wk;        /* device bf16 [dim, dh] */
+    const float *k_gamma;  /* device fp32 [dim]: LayerNorm scale of the key */
+    const float *k_beta;   /* device fp32 [dim]: LayerNorm shift of the key */
+    const void *ww;        /* device bf16 [heads, dh] */
+    int32_t dq, dh;        /* input widths, multiples of 16 */
+    int32_t heads;         /* indexer heads, 1..64 */
+    int32_t dim;           /* index dim, 128 */
+    float eps;             /* LayerNorm epsilon */
+} sia_indexer_weights;
+
+/* Bytes of workspace sia_indexer_prepare needs for num_q tokens (0 if invalid). */
+size_t sia_indexer_prepare_workspace_size(const sia_indexer_weights *W, int32_t num_q);
+
+/*
+ * Indexer input preparation for the MXFP8 index path, on three streams
+ * ("Rapid Adaptation ...", section 4.3 "Multi-Stream Parallel Preparation";
+ * "Day0 ... New-Architecture LLMs", section 3.2 "Three-Stream Coordination for
+ * Indexer Input Preparation"). For the num_q tokens of qs (sequence q_seq[t],
+ * position q_pos[t]):
+ *   streams[0]: q = xq Wq^T (bf16), quantized to MXFP8 -> q_codes, q_scales
+ *   streams[1]: k = LayerNorm(xh Wk^T) * gamma + beta, rounded to bf16, quantized
+ *               to MXFP8 and written into index_k (dtype SIA_MXFP8_E4M3, dim 128)
+ *               at row q_pos[t] of sequence q_seq[t] (the only input this call
+ *               writes)
+ *   streams[2]: w = xh Ww^T (fp32) -> w_out
+ * The chains fork from streams[0] (events[0] recorded there first, so work
+ * enqueued on streams[0] before the call is visible to all three) and join back
+ * into streams[0] (events[1], events[2]), so the indexer enqueued on
+ * streams[0] afterwards sees all its inputs. The same stream may be passed
+ * three times (a serial chain). Streams and events are the caller's (hipStream_t,
+ * hipEvent_t; NULL streams are the default stream).
+ *   xq        device bf16 [num_q, dq];  xh device bf16 [num_q, dh]
+ *   q_codes   device uint8 [num_q, heads, dim];  q_scales uint8 [num_q, heads, dim/32]
+ *   w_out     device fp32 [num_q, heads]
+ *   q_bf16    device bf16 [num_q, heads, dim] or NULL: the query before quantization
+ *   k_bf16    device bf16 [num_q, dim] or NULL: the key before quantization
+ * A token whose sequence, position or page is out of range writes no key row
+ * and sets SIA_DEVSTATUS_BAD_PAGE in the workspace status word.
+ */
+int sia_indexer_prepare(const sia_indexer_weights *W, const void *xq, const void *xh,
+                        const sia_page_table *pt, const sia_paged_cache *index_k,
+                        const sia_queries *qs, uint8_t *q_codes, uint8_t *q_scales, float *w_out,
+                        void *q_bf16, void *k_bf16, void *workspace, size_t workspace_bytes,
+                        void *const *streams, void *const *events);
+
 /* ------------------------------------------------------------------ stage 2 */
 
 /* Bytes of workspace sparse_mla_attention needs (always >= 256). */

@@ -30,6 +30,7 @@ DEVSTATUS_BAD_SEQ, DEVSTATUS_BAD_PAGE, DEVSTATUS_ROW_TOO_LONG, DEVSTATUS_BAD_IND
 EXPORTS = [
     "sia_indexer_workspace_size", "sparse_indexer_topk", "sparse_indexer_topk_traced",
     "sparse_indexer_topk_mxfp8", "sparse_indexer_scores_mxfp8", "sia_quantize_mxfp8",
+    "sia_indexer_prepare_workspace_size", "sia_indexer_prepare",
     "sparse_indexer_scores",
     "sia_topk_workspace_size", "sparse_topk_from_scores", "sia_mla_workspace_size",
     "sparse_mla_attention", "sparse_mla_attention_noalloc", "sia_zigzag_assign",
@@ -52,6 +53,13 @@ class PageTable(ctypes.Structure):
 class PagedCache(ctypes.Structure):
     _fields_ = [("rows", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("num_pages", ctypes.c_int64), ("dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class IndexerWeights(ctypes.Structure):
+    _fields_ = [("wq", ctypes.c_void_p), ("wk", ctypes.c_void_p), ("k_gamma", ctypes.c_void_p),
+                ("k_beta", ctypes.c_void_p), ("ww", ctypes.c_void_p), ("dq", ctypes.c_int32),
+                ("dh", ctypes.c_int32), ("heads", ctypes.c_int32), ("dim", ctypes.c_int32),
+                ("eps", ctypes.c_float)]
 
 
 class Queries(ctypes.Structure):
@@ -85,6 +93,10 @@ def lib():
             "sparse_indexer_scores_mxfp8": (ctypes.c_int, [pPT, pPC, pQ, P, P, P, c_i32, P, c_i64, P, c_sz,
                                                            P]),
             "sia_quantize_mxfp8": (ctypes.c_int, [P, c_i64, c_i32, P, P, P]),
+            "sia_indexer_prepare_workspace_size": (c_sz, [ctypes.POINTER(IndexerWeights), c_i32]),
+            "sia_indexer_prepare": (ctypes.c_int, [ctypes.POINTER(IndexerWeights), P, P, pPT, pPC, pQ, P, P, P,
+                                                   P, P, P, c_sz, ctypes.POINTER(ctypes.c_void_p),
+                                                   ctypes.POINTER(ctypes.c_void_p)]),
             "sia_topk_workspace_size": (c_sz, [c_i32, c_i32, c_i32]),
             "sparse_topk_from_scores": (ctypes.c_int, [P, c_i64, P, c_i32, c_i32, c_i32, P, P, P, c_sz,
                                                        P]),
@@ -295,6 +307,42 @@ def quantize_mxfp8(x: torch.Tensor, codes=None, scales=None, stream=None):
         scales = torch.empty(tuple(x.shape[:-1]) + (D // 32,), dtype=torch.uint8, device=x.device)
     _check(lib().sia_quantize_mxfp8(_ptr(x), rows, D, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
+
+
+def indexer_prepare(xq, xh, wq, wk, k_gamma, k_beta, ww, page_table, seq_lens, k_codes, k_scales, q_seq, q_pos,
+                    *, eps=1e-6, streams=None, events=None, q_bf16=None, k_bf16=None, workspace=None):
+    """Three-stream indexer input preparation (MXFP8 path): returns (q_codes,
+    q_scales, w) and writes the tokens' MXFP8 keys into (k_codes, k_scales) at
+    (q_seq, q_pos). `streams`: three torch streams (default: the current stream
+    three times, a serial chain); the result joins back into streams[0]."""
+    M = int(xq.shape[0])
+    dim = int(wk.shape[0])
+    heads = int(ww.shape[0])
+    dev = xq.device
+    W = IndexerWeights(_ptr(wq), _ptr(wk), _ptr(k_gamma), _ptr(k_beta), _ptr(ww), int(xq.shape[1]),
+                       int(xh.shape[1]), heads, dim, float(eps))
+    need = lib().sia_indexer_prepare_workspace_size(ctypes.byref(W), M)
+    if need == 0:
+        raise SiaError(SIA_ERR_INVALID_ARG, "invalid shapes for the input preparation")
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    if streams is None:
+        streams = [torch.cuda.current_stream()] * 3
+    if events is None:
+        events = [torch.cuda.Event() for _ in range(3)]
+    pt, c = page_table_desc(page_table, seq_lens), cache_desc(k_codes, k_scales)
+    q = queries_desc(q_seq, q_pos, 1, 0)
+    q_codes = torch.empty((M, heads, dim), dtype=torch.uint8, device=dev)
+    q_scales = torch.empty((M, heads, dim // 32), dtype=torch.uint8, device=dev)
+    w = torch.empty((M, heads), dtype=torch.float32, device=dev)
+    for e, st in zip(events, [streams[0], streams[1], streams[2]]):
+        e.record(st)   # (makes sure every event exists before its handle is taken)
+    sh = (ctypes.c_void_p * 3)(*[st.cuda_stream for st in streams])
+    eh = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
+    _check(lib().sia_indexer_prepare(ctypes.byref(W), _ptr(xq), _ptr(xh), ctypes.byref(pt), ctypes.byref(c),
+                                     ctypes.byref(q), _ptr(q_codes), _ptr(q_scales), _ptr(w), _ptr(q_bf16),
+                                     _ptr(k_bf16), _ptr(workspace), workspace.numel(), sh, eh))
+    return q_codes, q_scales, w
 
 
 def sparse_indexer_scores(page_table, seq_lens, rows, scale, q_seq, q_pos, q_idx, w, *, group=1,

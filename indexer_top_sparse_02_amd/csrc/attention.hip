@@ -53,7 +53,6 @@ struct RowFmt {
     static constexpr int SCALES = 512, ROPE = 528;        // (fp8) byte offsets in a row
 };
 constexpr int kRowB = RowFmt<false>::RB;
-constexpr int kTileB = RowFmt<false>::TB;
 constexpr int kPStride = kTR * 2 + 16;      // bytes per head of P (padded: no bank conflicts)
 constexpr int kMaxSliceRows = kAttnMaxSliceRows;
 

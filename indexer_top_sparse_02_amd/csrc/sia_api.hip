@@ -457,6 +457,146 @@ int sparse_topk_from_scores(const float* scores, int64_t ld, const int32_t* row_
     return SIA_OK;
 }
 
+// ------------------------------------------------------------ input preparation
+
+}  // extern "C"
+
+namespace {
+
+struct PrepPlan {
+    int sq = 1, sk = 1, sw = 1;                   // K slices per projection
+    size_t pq = 0, pk = 0, pw = 0, qb = 0;       // workspace offsets
+    size_t total = kHeader;
+};
+
+// K slices: enough workgroups (64 x 64 tiles x slices) for about two per CU,
+// each slice at least 256 wide and a multiple of 16.
+int prep_slices(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
+    int64_t sl = ceil_div(2 * (int64_t)device_cus(), tiles);
+    sl = std::max<int64_t>(1, std::min<int64_t>(sl, K / 256));
+    return (int)sl;
+}
+int64_t slice_width(int64_t K, int slices) { return ceil_div(ceil_div(K, slices), 16) * 16; }
+
+PrepPlan plan_prepare(const sia_indexer_weights* W, int64_t M) {
+    PrepPlan p;
+    const int64_t nq = (int64_t)W->heads * W->dim;
+    p.sq = prep_slices(M, nq, W->dq);
+    p.sk = prep_slices(M, W->dim, W->dh);
+    p.sw = prep_slices(M, W->heads, W->dh);
+    p.pq = p.total; p.total += align_up((size_t)p.sq * M * nq * 4);
+    p.pk = p.total; p.total += align_up((size_t)p.sk * M * W->dim * 4);
+    p.pw = p.total; p.total += align_up((size_t)p.sw * M * W->heads * 4);
+    p.qb = p.total; p.total += align_up((size_t)M * nq * 2);
+    return p;
+}
+
+int check_prepare_weights(const sia_indexer_weights* W) {
+    if (!W) return fail(SIA_ERR_INVALID_ARG, "weights descriptor is NULL");
+    if (!W->wq || !W->wk || !W->ww || !W->k_gamma || !W->k_beta)
+        return fail(SIA_ERR_INVALID_ARG, "a projection weight is NULL");
+    if (W->dim != 128) return fail(SIA_ERR_UNSUPPORTED, "index dim %d: supported 128", W->dim);
+    if (W->heads < 1 || W->heads > 64) return fail(SIA_ERR_UNSUPPORTED, "indexer heads %d: supported 1..64", W->heads);
+    if (W->dq < 16 || W->dq % 16 || W->dh < 16 || W->dh % 16)
+        return fail(SIA_ERR_UNSUPPORTED, "input widths %d, %d: positive multiples of 16", W->dq, W->dh);
+    if (!(W->eps >= 0.f) || !std::isfinite(W->eps)) return fail(SIA_ERR_INVALID_ARG, "eps %g", (double)W->eps);
+    return SIA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sia_indexer_prepare_workspace_size(const sia_indexer_weights* W, int32_t num_q) {
+    if (!W || num_q < 0 || W->dim != 128 || W->heads < 1 || W->heads > 64 || W->dq < 16 || W->dh < 16) return 0;
+    return plan_prepare(W, num_q).total;
+}
+
+int sia_indexer_prepare(const sia_indexer_weights* W, const void* xq, const void* xh, const sia_page_table* pt,
+                        const sia_paged_cache* index_k, const sia_queries* qs, uint8_t* q_codes, uint8_t* q_scales,
+                        float* w_out, void* q_bf16, void* k_bf16, void* workspace, size_t workspace_bytes,
+                        void* const* streams, void* const* events) {
+    int rc;
+    if ((rc = check_prepare_weights(W)) != SIA_OK) return rc;
+    if ((rc = check_page_table(pt)) != SIA_OK) return rc;
+    if ((rc = check_index_cache(index_k)) != SIA_OK) return rc;
+    if (index_k->dtype != SIA_MXFP8_E4M3) return fail(SIA_ERR_UNSUPPORTED, "the prepared keys are MXFP8 index rows");
+    if (!qs || qs->num_q < 0) return fail(SIA_ERR_INVALID_ARG, "query descriptor");
+    if (!streams || !events) return fail(SIA_ERR_INVALID_ARG, "streams/events is NULL");
+    if (!events[0] || !events[1] || !events[2]) return fail(SIA_ERR_INVALID_ARG, "an event is NULL");
+    const int64_t M = qs->num_q;
+    if (M > 0 && (!qs->q_seq || !qs->q_pos || !xq || !xh || !q_codes || !q_scales || !w_out))
+        return fail(SIA_ERR_INVALID_ARG, "an input or output is NULL");
+    const PrepPlan p = plan_prepare(W, M);
+    if ((rc = check_workspace(workspace, workspace_bytes, p.total)) != SIA_OK) return rc;
+    if (M == 0) return SIA_OK;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    hipStream_t s0 = static_cast<hipStream_t>(streams[0]), s1 = static_cast<hipStream_t>(streams[1]),
+                s2 = static_cast<hipStream_t>(streams[2]);
+    hipEvent_t e0 = static_cast<hipEvent_t>(events[0]), e1 = static_cast<hipEvent_t>(events[1]),
+               e2 = static_cast<hipEvent_t>(events[2]);
+    hipError_t e;
+    // fork
+    if ((e = hipEventRecord(e0, s0)) != hipSuccess) return hip_fail(e, "fork event");
+    if ((e = hipStreamWaitEvent(s1, e0, 0)) != hipSuccess) return hip_fail(e, "fork wait");
+    if ((e = hipStreamWaitEvent(s2, e0, 0)) != hipSuccess) return hip_fail(e, "fork wait");
+    const int64_t nq = (int64_t)W->heads * W->dim;
+    // chain 1: query projection, then MXFP8
+    {
+        sia::GemmArgs g{static_cast<const uint16_t*>(xq), static_cast<const uint16_t*>(W->wq),
+                        reinterpret_cast<float*>(ws + p.pq), (int32_t)M, (int32_t)nq, W->dq,
+                        (int32_t)slice_width(W->dq, p.sq)};
+        if ((e = sia::launch_proj_gemm(g, s0)) != hipSuccess) return hip_fail(e, "query projection");
+        uint16_t* qb = q_bf16 ? static_cast<uint16_t*>(q_bf16) : reinterpret_cast<uint16_t*>(ws + p.qb);
+        if ((e = sia::launch_proj_reduce(g.part, (int)ceil_div(W->dq, g.k_slice), M * nq, qb, nullptr, s0)) != hipSuccess)
+            return hip_fail(e, "query reduce");
+        if ((e = sia::launch_quantize_mxfp8(qb, M * nq / 32, q_codes, q_scales, s0)) != hipSuccess)
+            return hip_fail(e, "query quantize");
+    }
+    // chain 2: key projection, LayerNorm, MXFP8, cache rows
+    {
+        sia::GemmArgs g{static_cast<const uint16_t*>(xh), static_cast<const uint16_t*>(W->wk),
+                        reinterpret_cast<float*>(ws + p.pk), (int32_t)M, W->dim, W->dh,
+                        (int32_t)slice_width(W->dh, p.sk)};
+        if ((e = sia::launch_proj_gemm(g, s1)) != hipSuccess) return hip_fail(e, "key projection");
+        sia::KeyPrepArgs k{};
+        k.part = g.part;
+        k.splits = (int)ceil_div(W->dh, g.k_slice);
+        k.M = (int32_t)M;
+        k.eps = W->eps;
+        k.gamma = W->k_gamma;
+        k.beta = W->k_beta;
+        k.k_out = static_cast<uint16_t*>(k_bf16);
+        k.q_seq = qs->q_seq;
+        k.q_pos = qs->q_pos;
+        k.page_table = pt->page_table;
+        k.batch = pt->batch;
+        k.max_pages = pt->max_pages;
+        k.num_pages = index_k->num_pages;
+        k.codes = static_cast<uint8_t*>(const_cast<void*>(index_k->rows));
+        k.scales = static_cast<uint8_t*>(const_cast<void*>(index_k->scale));
+        k.status = reinterpret_cast<uint32_t*>(ws);
+        if ((e = sia::launch_key_norm_quant(k, s1)) != hipSuccess) return hip_fail(e, "key normalize");
+    }
+    // chain 3: head-weight projection
+    {
+        sia::GemmArgs g{static_cast<const uint16_t*>(xh), static_cast<const uint16_t*>(W->ww),
+                        reinterpret_cast<float*>(ws + p.pw), (int32_t)M, W->heads, W->dh,
+                        (int32_t)slice_width(W->dh, p.sw)};
+        if ((e = sia::launch_proj_gemm(g, s2)) != hipSuccess) return hip_fail(e, "weight projection");
+        if ((e = sia::launch_proj_reduce(g.part, (int)ceil_div(W->dh, g.k_slice), M * W->heads, nullptr, w_out, s2)) !=
+            hipSuccess)
+            return hip_fail(e, "weight reduce");
+    }
+    // join
+    if ((e = hipEventRecord(e1, s1)) != hipSuccess) return hip_fail(e, "join event");
+    if ((e = hipEventRecord(e2, s2)) != hipSuccess) return hip_fail(e, "join event");
+    if ((e = hipStreamWaitEvent(s0, e1, 0)) != hipSuccess) return hip_fail(e, "join wait");
+    if ((e = hipStreamWaitEvent(s0, e2, 0)) != hipSuccess) return hip_fail(e, "join wait");
+    return SIA_OK;
+}
+
 // ------------------------------------------------------------ attention
 
 static int attn_plan(const sia_queries* qs, int heads, int topk, int& hb, int& n_split, int& rows_per_split,

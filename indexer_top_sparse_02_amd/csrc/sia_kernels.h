@@ -117,6 +117,35 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelCap = 16384;         // candidates the selection pass holds in LDS
 constexpr int kStreamThreads = 256;    // four waves, one query each
 
+// Input preparation: projections out[M, N] = x[M, K] W[N, K]^T as fp32
+// partials per K slice ([splits, M, N]), then reductions.
+struct GemmArgs {
+    const uint16_t* x;        // bf16 [M, K]
+    const uint16_t* w;        // bf16 [N, K]
+    float* part;              // [splits, M, N]
+    int32_t M, N, K, k_slice; // K and k_slice multiples of 16
+};
+struct KeyPrepArgs {
+    const float* part;        // [splits, M, 128] key projection partials
+    int32_t splits, M;
+    float eps;
+    const float* gamma;       // [128]
+    const float* beta;        // [128]
+    uint16_t* k_out;          // bf16 [M, 128] or null
+    const int32_t* q_seq;
+    const int32_t* q_pos;
+    const int32_t* page_table;
+    int32_t batch, max_pages;
+    int64_t num_pages;
+    uint8_t* codes;           // MXFP8 index cache rows [num_pages, 64, 128]
+    uint8_t* scales;          // [num_pages, 64, 4]
+    uint32_t* status;
+};
+hipError_t launch_proj_gemm(const GemmArgs& g, hipStream_t st);
+hipError_t launch_proj_reduce(const float* part, int splits, int64_t mn, uint16_t* out_bf16, float* out_f32,
+                              hipStream_t st);
+hipError_t launch_key_norm_quant(const KeyPrepArgs& k, hipStream_t st);
+
 // Attention.
 struct AttnArgs {
     const int32_t* page_table;
