@@ -509,7 +509,7 @@ int check_prepare_weights(const sia_indexer_weights* W) {
 extern "C" {
 
 size_t sia_indexer_prepare_workspace_size(const sia_indexer_weights* W, int32_t num_q) {
-    if (!W || num_q < 0 || W->dim != 128 || W->heads < 1 || W->heads > 64 || W->dq < 16 || W->dh < 16) return 0;
+    if (num_q < 0 || check_prepare_weights(W) != SIA_OK) return 0;
     return plan_prepare(W, num_q).total;
 }
 
