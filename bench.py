@@ -31,6 +31,22 @@ PEAK_BF16_TFLOPS = 2500.0
 FLUSH_BYTES = 1 << 30   # four times the Infinity Cache
 
 
+class CacheFlush:
+    """Evicts the L2 and Infinity Cache contents between timed steps by reading
+    FLUSH_BYTES of another buffer (a reduction into one word). A read leaves no
+    dirty lines behind, so the next step does not pay for writing them back, as
+    it would after a fill of the buffer."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.acc = torch.zeros((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, dim=0, out=self.acc)
+
+
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -104,16 +120,32 @@ def copy_calibration(nbytes: int):
 
 
 def measured_bandwidth(nbytes: int = 1 << 30, reps: int = 10):
-    """What this GPU's HBM delivers to plain kernels: a device copy (bytes read
-    plus bytes written per second) and a read-only reduction, medians of `reps`."""
+    """What this GPU's HBM delivers to plain kernels, medians of `reps` after a
+    read flush of the caches: a streaming read with 16-byte non-temporal loads
+    (the calibration kernel of libsia_probe.so), torch's read-only reduction and
+    a device copy (bytes read plus bytes written per second)."""
+    import ctypes
     import torch
+    from indexer_top_sparse_02_amd import build as _build
     src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     acc = torch.empty((), dtype=torch.float32, device="cuda:0")
+    sink = torch.zeros(2048, dtype=torch.int32, device="cuda:0")
+    flush = CacheFlush("cuda:0")
+    probe = ctypes.CDLL(_build.PROBE_LIB)
+    probe.sia_probe_stream_read.restype = ctypes.c_int
+    probe.sia_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+
+    def stream_read():
+        st = torch.cuda.current_stream().cuda_stream
+        rc = probe.sia_probe_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), st)
+        if rc != 0:
+            raise RuntimeError(f"stream read probe failed ({rc})")
 
     def med(fn):
         ts = []
         for _ in range(reps + 2):
+            flush()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
@@ -121,13 +153,18 @@ def measured_bandwidth(nbytes: int = 1 << 30, reps: int = 10):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         return statistics.median(ts[2:])
+    t_stream = med(stream_read)
     t_copy = med(lambda: dst.copy_(src))
-    t_read = med(lambda: torch.sum(src, dim=0, out=acc))
-    del src, dst
+    t_sum = med(lambda: torch.sum(src, dim=0, out=acc))
+    del src, dst, flush
     torch.cuda.empty_cache()
-    return {"copy_gbs": 2 * nbytes / (t_copy * 1e-3) / 1e9, "read_gbs": nbytes / (t_read * 1e-3) / 1e9,
-            "bytes": nbytes, "note": "device copy counts read + written bytes; read = torch.sum over "
-                                     "the buffer; medians of %d" % reps}
+    return {"read_gbs": nbytes / (t_stream * 1e-3) / 1e9,
+            "torch_sum_gbs": nbytes / (t_sum * 1e-3) / 1e9,
+            "copy_gbs": 2 * nbytes / (t_copy * 1e-3) / 1e9,
+            "bytes": nbytes,
+            "note": "read = one sweep with 16-byte non-temporal loads (2048 workgroups); torch_sum = "
+                    "torch.sum over the buffer; copy counts read + written bytes; each after a read "
+                    "flush, medians of %d" % reps}
 
 
 def algorithmic_bytes(wl, idx):
@@ -294,7 +331,7 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True, fl
     """Times `steps` passes of the whole path (indexer + Top-K, then sparse
     attention), each between HIP events on the stream the library runs on
     (torch's current stream, which the binding passes to the library). With
-    `flush` (a device buffer), the buffer is written between steps, outside the
+    `flush` (a CacheFlush), a buffer is read between steps, outside the
     events. Returns the indices of the last pass and per-step statistics (ms)
     of the step and of each phase, plus the kernel launches of one step (from a
     captured graph). `sched` picks the causal prefill tile schedule (-1: the
@@ -356,7 +393,7 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True, fl
     torch.cuda.synchronize()
     for i, (e0, e1, e2) in enumerate(ev):
         if flush is not None:
-            flush.fill_(i & 0x7f)
+            flush()
         e0.record()
         indexer()
         e1.record()
@@ -561,7 +598,7 @@ def mx_decode(sia, W, wl, s, steps, warmup, flush, ref_idx, idx_bytes):
                torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for i, (e0, e1, e2) in enumerate(ev):
             if flush is not None:
-                flush.fill_(i & 0x7f)
+                flush()
             e0.record()
             indexer()
             e1.record()
@@ -645,7 +682,7 @@ def launch_overhead(sia, W, dev, steps, warmup):
     and arguments), with the Infinity Cache evicted between steps."""
     import torch
     out = {}
-    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = CacheFlush(dev)
     for name in ("tiny_decode", "decode_b32"):
         s = W.spec(name)
         wl = W.make(s, device=dev)
@@ -695,7 +732,7 @@ def main():
     bw = measured_bandwidth()
     wl = W.make(s, device=dev)
     group = s.q_per_seq
-    flush = None if a.no_flush else torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush = None if a.no_flush else CacheFlush(dev)
     idx, st, si, sa, launches = time_path(sia, wl, s, group, a.steps, a.warmup, flush=flush)
     ms, idx_ms, att_ms = st["median"], si["median"], sa["median"]
     by = algorithmic_bytes(wl, idx)
@@ -720,7 +757,8 @@ def main():
                    "launch": "hip graph per call" if GRAPH else "eager",
                    "cache_flush_between_steps": flush is not None},
         "timing": "median of %d steps, each between HIP events; %s" % (
-            a.steps, "1 GiB written between steps (outside the events) to evict the Infinity Cache"
+            a.steps, "1 GiB of another buffer read between steps (outside the events) to evict the L2 and "
+            "Infinity Cache without leaving dirty lines"
             if flush is not None else "steps back to back"),
         "launches_per_step": launches,
         "hbm_gbs_step": step_gbs,

@@ -3,7 +3,9 @@
     python -m indexer_top_sparse_02_amd.build
 
 Every .hip file under csrc/ is compiled to an object with hipcc for gfx950,
-then linked into indexer_top_sparse_02_amd/libsia.so.
+then linked into indexer_top_sparse_02_amd/libsia.so. The streaming-read
+calibration kernel under csrc/probe/ becomes libsia_probe.so, which only the
+benchmark loads.
 """
 from __future__ import annotations
 
@@ -19,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsia.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "read_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libsia_probe.so")
 ARCH = os.environ.get("SIA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -57,6 +61,11 @@ def build(jobs: int = 4) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    r = subprocess.run([HIPCC, *FLAGS, "-shared", "-o", PROBE_LIB + ".tmp", PROBE_SRC], capture_output=True,
+                       text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

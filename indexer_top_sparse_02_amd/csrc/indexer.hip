@@ -601,7 +601,7 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
             const uint8_t* base = A.rows + row0 * R;
             const uint32_t dst = ring_lds + s * (NWV * SLOT);
 #pragma unroll
-            for (int r = 0; r < GM::DMA; r++) dma16_s(base, voff[r], dst + r * 1024);
+            for (int r = 0; r < GM::DMA; r++) dma16_s_nt(base, voff[r], dst + r * 1024);
             if constexpr (KF != kRowBf16) {
                 // the 64 scales of the page, 4 bytes per lane (no lane mask, so
                 // that the loop body stays one basic block)
@@ -745,19 +745,23 @@ struct PairGeom {
 
 // Scheduling hint for a step: each of the query's MFMAs followed by the vector
 // instructions that fit in its shadow.
-template <int NMFMA>
+template <int NMFMA, int NVALU = 16>
 __device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
     for (int i = 0; i < NMFMA; i++) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // then up to sixteen VALU (its shadow)
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, NVALU, 0);   // then up to NVALU VALU (its shadow)
     }
 }
+
 
 template <int D, int KF, bool SCORES>
 __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
     using GM = PairGeom<D, KF>;
     constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NTEAM = GM::NTEAM, U = kPairUnroll;
+    // tiles read from LDS ahead of their step (a second register copy of a
+    // tile, to read two ahead, pushes the waves past 256 registers)
+    constexpr int FD = 1;
     constexpr int SLOT = GM::SLOT, NV = KTile<D, KF>::NV;
     constexpr int NMFMA = mfmas_per_block<D, KF>();   // MFMAs per query, tile and head block
     __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NTEAM * SLOT];
@@ -838,14 +842,14 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
         // tile of the team's k-th step: clamped into the run (a padding step
         // repeats the last tile; a team without tiles reads the part's last one)
         auto tile_of = [&](int k) { return min(t0 + max(min(k, n - 1), 0), ntiles - 1); };
-        auto issue = [&](int k, int s) {   // copier only
+        auto issue = [&](int k, int s, int pg) {   // copier only; pg: the tile's page id
             const int t = tile_of(k);
-            const int page = max(__builtin_amdgcn_readfirstlane(pages[t >> 1]), 0);
+            const int page = max(__builtin_amdgcn_readfirstlane(pg), 0);
             const int64_t row0 = (int64_t)page * kPage + (t & 1) * 32;
             const uint8_t* base = A.rows + row0 * R;
             const uint32_t dst = ring_lds + s * (NTEAM * SLOT);
 #pragma unroll
-            for (int r = 0; r < GM::DMA; r++) dma16_s(base, voff[r], dst + r * 1024);
+            for (int r = 0; r < GM::DMA; r++) dma16_s_nt(base, voff[r], dst + r * 1024);
             if constexpr (KF != kRowBf16) {
                 // the 64 scales of the page, 4 bytes per lane (no lane mask)
                 const float* sbase = A.scale + (int64_t)page * kPage;
@@ -862,75 +866,119 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             else t.sc = 1.f;
         };
         // finisher: lanes 0..31 hold query 0 of step kq, lanes 32..63 query 1 of
-        // step kq - 1. A key that reaches its query's floor is appended to the
-        // query's candidate list of this team; a lane that keeps nothing (padding
-        // steps included) writes to the row's spare tail, so the loop body has no
-        // branch. Positions on a page whose id is out of range were copied from
+        // step kq - 1. finish_prep (vector work, beside the MFMAs) decides which
+        // keys reach their query's floor `fk` and where they go in the query's
+        // candidate list of this team; finish_commit (after them) writes only
+        // those. Positions on a page whose id is out of range were copied from
         // page 0 and are dropped.
-        auto finish = [&](int kq, float v, float tsc) {
-            const float sc = KF == kRowFp8 ? v * tsc : v;
+        struct Fin {
+            int64_t at;      // candidate slot (scores: score index)
+            uint32_t key;
+            float sc;
+            bool take;
+        };
+        auto finish_prep = [&](int kq, float v, float tsc, uint32_t fk) -> Fin {
+            Fin f;
+            f.sc = KF == kRowFp8 ? v * tsc : v;
             const int kk = half ? kq - 1 : kq;
-            const bool in_run = kk >= 0 && kk < n;
+            const bool in_run = (kk >= 0) & (kk < n);
             const int tpos = (t0 + kk) * 32 + frow;   // position within the part
-            const bool tok = in_run && tpos < (half ? valid1 : valid0) && pages[tile_of(kk) >> 1] >= 0;
+            const int pg = pages[tile_of(kk) >> 1];
+            const bool tok = in_run & (tpos < (half ? valid1 : valid0)) & (pg >= 0);
             const int64_t row = (int64_t)(half ? j1s : j0) * S.ld;
             if constexpr (SCORES) {
-                if (tok) S.scores[row + pos0 + tpos] = sc;
+                f.take = tok;
+                f.at = row + pos0 + tpos;
+                f.key = 0u;
             } else {
-                const uint32_t key = score_key(sc) & (0u - (uint32_t)tok);
-                const bool take = key >= floor_key[half];
-                const uint64_t mask = __ballot(take);
+                f.key = score_key(f.sc) & (0u - (uint32_t)tok);
+                f.take = f.key >= fk;
+                const uint64_t mask = __ballot(f.take);
                 const uint32_t m0 = (uint32_t)mask, m1 = (uint32_t)(mask >> 32);
                 const int rank = (half ? cnt1 : cnt0) + __popc((half ? m1 : m0) & ((1u << frow) - 1u));
-                const int64_t at = take ? row + rbase + rank : row + S.ld - 64 + frow;
-                S.cand_key[at] = key;
-                S.cand_pos[at] = pos0 + tpos;
-                atomicAdd(&hist[take ? coarse_bin(key) : (uint32_t)l], take ? (half ? 0x10000u : 1u) : 0u);
+                f.at = row + rbase + rank;
                 cnt0 += __popc(m0);
                 cnt1 += __popc(m1);
+            }
+            return f;
+        };
+        auto finish_commit = [&](const Fin& f, int kq) {
+            if (f.take) {
+                if constexpr (SCORES) {
+                    S.scores[f.at] = f.sc;
+                } else {
+                    const int kk = half ? kq - 1 : kq;
+                    S.cand_key[f.at] = f.key;
+                    S.cand_pos[f.at] = pos0 + (t0 + kk) * 32 + frow;
+                    atomicAdd(&hist[coarse_bin(f.key)], half ? 0x10000u : 1u);
+                }
             }
         };
 
         if (hb == 0) {
 #pragma unroll
-            for (int u = 0; u < NS - 1; u++) issue(u, u);
+            for (int u = 0; u < NS - 1; u++) issue(u, u, pages[tile_of(u) >> 1]);
         }
+        // copier: page id of the tile that step k copies, read a step ahead
+        int pg_next = pages[tile_of(NS - 1) >> 1];
         IdxQuery<1, D, KF> q0, q1;
         load_query<1, D>(A, min(j0, A.num_q - 1), q0, hb);
         load_query<1, D>(A, min(j1, A.num_q - 1), q1, hb);
         wait_vmcnt_mem<0>();
         __syncthreads();   // the first copies have landed
-        KTile<D, KF> t;
-        fetch(0, 0, t);
+        // tiles k .. k + FD - 1 are in registers at the top of step k
+        KTile<D, KF> tb[FD];
+#pragma unroll
+        for (int i = 0; i < FD; i++) fetch(i, i, tb[i]);
         f32x16 a0[1], a1[1];
         a1[0] = f32x16{};
-        float sc_prev = 0.f;
-        for (int k0 = 0; k0 < nloop; k0 += U) {
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int k = k0 + u;
-                // query 0 on tile k, beside query 1's block sum of tile k - 1
-                tile_mfma<1, D, KF>(q0, t, a0);
-                const float h1 = tile_head_sum<1, D, KF>(q1, a1);
-                interleave_mfma_valu<NMFMA>();
-                // query 1 on tile k, beside query 0's block sum of tile k
-                tile_mfma<1, D, KF>(q1, t, a1);
-                const float h0 = tile_head_sum<1, D, KF>(q0, a0);
-                interleave_mfma_valu<NMFMA>();
-                const float mine = half ? h1 : h0;
-                const float tsc = half ? sc_prev : t.sc;
-                sc_prev = t.sc;
-                if (hb == 0) {
-                    xch[k & 1][team][l] = mine;
-                    issue(k + NS - 1, (u + NS - 1) % NS);   // refills the slot of tile k - 1
-                    wait_vmcnt_mem<(NS - 2) * GM::PER_TILE>();   // tile k + 1 has landed
-                }
-                lds_barrier();
-                if (hb == 1) finish(k, xch[k & 1][team][l] + mine, tsc);
+        float mine_p = 0.f;                 // finisher: own block sums of step k - 1
+        uint32_t fk = 1u;                   // finisher: this lane's query's floor
+        float sc_p1 = 0.f, sc_p2 = 0.f;     // token scales of the tiles of steps k - 1, k - 2
+        // One step of a role: query 0's MFMAs on tile k beside query 1's block
+        // sums of tile k - 1 and (finisher) the completion of step k - 1, whose
+        // copier block sums were exchanged at the previous barrier; then query
+        // 1's MFMAs on tile k beside query 0's block sums of tile k. The copier
+        // then refills the slot of tile k - 1 and waits until tile k + FD has
+        // landed; after the barrier every wave reads tile k + FD from LDS.
+        auto step = [&](auto fin_tag, int k, int u) {
+            constexpr bool FIN = decltype(fin_tag)::value;
+            KTile<D, KF>& tc = tb[u % FD];
+            // scheduling fences keep each group of vector work beside the MFMAs
+            // it is meant to hide behind (without them the block sums are
+            // hoisted to right behind their own MFMAs)
+            __builtin_amdgcn_sched_barrier(0);
+            tile_mfma<1, D, KF>(q0, tc, a0);
+            const float h1 = tile_head_sum<1, D, KF>(q1, a1);
+            Fin fin{};
+            if constexpr (FIN) {
+                if (u == 0) fk = SCORES ? 0u : floor_key[half];   // the floors move once per round
+                fin = finish_prep(k - 1, xch[(k - 1) & 1][team][l] + mine_p, half ? sc_p2 : sc_p1, fk);
+            }
+            interleave_mfma_valu<NMFMA, FIN ? 24 : 12>();
+            __builtin_amdgcn_sched_barrier(0);
+            tile_mfma<1, D, KF>(q1, tc, a1);
+            const float h0 = tile_head_sum<1, D, KF>(q0, a0);
+            interleave_mfma_valu<NMFMA>();
+            __builtin_amdgcn_sched_barrier(0);
+            const float mine = half ? h1 : h0;
+            sc_p2 = sc_p1;
+            sc_p1 = tc.sc;
+            if constexpr (!FIN) {
+                xch[k & 1][team][l] = mine;
+                const int pg = pg_next;
+                pg_next = pages[tile_of(k + NS) >> 1];
+                issue(k + NS - 1, (u + NS - 1) % NS, pg);      // refills the slot of tile k - 1
+                wait_vmcnt_mem<(NS - 1 - FD) * GM::PER_TILE>();   // tile k + FD has landed
+            } else {
+                mine_p = mine;
+                finish_commit(fin, k - 1);
                 if constexpr (!SCORES) {
                     // once per unrolled round, team 0's finisher raises both
-                    // queries' floors from the part's histogram
-                    if (u == U - 1 && hb == 1 && team == 0) {
+                    // queries' floors from the part's histogram (a snapshot
+                    // taken while other teams add to it undercounts, so the
+                    // floor stays a lower bound)
+                    if (u == U - 1 && team == 0) {
                         int b0, b1;
                         coarse_floor<true>(hist, S.topk, b0, b1);
                         if (l == 0) {
@@ -939,15 +987,33 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
                         }
                     }
                 }
-                fetch(k + 1, (u + 1) % NS, t);
             }
-        }
-        // query 1 of the last step
+            lds_barrier();
+            fetch(k + FD, (u + FD) % NS, tc);
+        };
+        // the two roles run separate, branch-free loop bodies with the same
+        // barriers
+        auto run = [&](auto fin_tag) {
+            for (int k0 = 0; k0 < nloop; k0 += U) {
+#pragma unroll
+                for (int u = 0; u < U; u++) step(fin_tag, k0 + u, u);
+            }
+        };
+        if (hb == 0) run(std::integral_constant<bool, false>{});
+        else run(std::integral_constant<bool, true>{});
+        // drain: query 1's block sums of the last tile; the finisher completes
+        // the last two steps
         {
             const float h1 = tile_head_sum<1, D, KF>(q1, a1);
-            if (hb == 0) xch[nloop & 1][team][l] = h1;
+            if (hb == 0) {
+                xch[nloop & 1][team][l] = h1;
+            } else {
+                if constexpr (!SCORES) fk = floor_key[half];
+                finish_commit(finish_prep(nloop - 1, xch[(nloop - 1) & 1][team][l] + mine_p,
+                                          half ? sc_p2 : sc_p1, fk), nloop - 1);
+            }
             lds_barrier();
-            if (hb == 1) finish(nloop, xch[nloop & 1][team][l] + h1, sc_prev);
+            if (hb == 1) finish_commit(finish_prep(nloop, xch[nloop & 1][team][l] + h1, sc_p1, fk), nloop);
         }
         wait_vmcnt_mem<0>();
     }
