@@ -38,6 +38,18 @@ namespace sia {
 
 static_assert(kCoarseBins == kCoarseBinsHost, "host and device histogram sizes differ");
 
+// XOR applied to the 16-byte chunk index of row `row` of a tile of rows with
+// CPR chunks each, staged in LDS. The operand reads take one chunk of 16
+// consecutive rows per 16 lanes; with 64 banks of 4 bytes, rows of CPR chunks
+// repeat their bank pattern every 16 / CPR rows, so the XOR takes the row
+// index divided by that (8 chunks: (row / 2) % 8), which puts the 16 reads on
+// 16 distinct bank groups. The XOR stays inside the row.
+template <int CPR>
+__device__ __forceinline__ int row_swz(int row) {
+    static_assert(CPR == 4 || CPR == 8 || CPR == 16, "rows of 64, 128 or 256 bytes");
+    return (row / (16 / CPR)) & (CPR - 1);
+}
+
 // ------------------------------------------------------------ score tile
 
 // A query's indexer heads in MFMA operand layout, one form per index-row
@@ -498,7 +510,6 @@ template <int D, int KF, int G>
 struct RowsGeom {
     static constexpr int R = D * ((KF != kRowBf16) ? 1 : 2);          // bytes per row
     static constexpr int CPR = R / 16;                   // 16-byte chunks per row
-    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
     static constexpr int NWV = kRowsThreads / kWave;
     static constexpr int WPQ = NWV / G;                  // waves per query
     static constexpr int TILE = 32 * R;                  // bytes of one tile
@@ -582,14 +593,14 @@ __global__ __launch_bounds__(kRowsThreads) void indexer_rows_kernel(IdxArgs A, R
         for (int r = 0; r < GM::DMA; r++) {
             const int gi = r * kWave + l;
             const int row = gi / CPR, cc = gi % CPR;
-            voff[r] = row * R + ((cc ^ (row & GM::SWZ)) << 4);
+            voff[r] = row * R + ((cc ^ row_swz<CPR>(row)) << 4);
         }
         // operand reads: lane half `half` of row frow
         uint32_t roff[NV];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int cc = KTile<D, KF>::chunk(i, half);
-            roff[i] = w * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
+            roff[i] = w * SLOT + frow * R + ((cc ^ row_swz<CPR>(frow)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring)) +
                                   w * SLOT;
@@ -731,7 +742,6 @@ template <int D, int KF>
 struct PairGeom {
     static constexpr int R = D * ((KF != kRowBf16) ? 1 : 2);
     static constexpr int CPR = R / 16;
-    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;
     static constexpr int NTEAM = kPairThreads / kWave / 2;
     static constexpr int TILE = 32 * R;
     static constexpr int DMA = TILE / 1024;
@@ -759,9 +769,6 @@ template <int D, int KF, bool SCORES>
 __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, RowsArgs S) {
     using GM = PairGeom<D, KF>;
     constexpr int NS = GM::NS, R = GM::R, CPR = GM::CPR, NTEAM = GM::NTEAM, U = kPairUnroll;
-    // tiles read from LDS ahead of their step (a second register copy of a
-    // tile, to read two ahead, pushes the waves past 256 registers)
-    constexpr int FD = 1;
     constexpr int SLOT = GM::SLOT, NV = KTile<D, KF>::NV;
     constexpr int NMFMA = mfmas_per_block<D, KF>();   // MFMAs per query, tile and head block
     __shared__ __attribute__((aligned(16))) uint8_t ring[NS * NTEAM * SLOT];
@@ -829,13 +836,13 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
         for (int r = 0; r < GM::DMA; r++) {
             const int gi = r * kWave + l;
             const int row = gi / CPR, cc = gi % CPR;
-            voff[r] = row * R + ((cc ^ (row & GM::SWZ)) << 4);
+            voff[r] = row * R + ((cc ^ row_swz<CPR>(row)) << 4);
         }
         uint32_t roff[NV];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int cc = KTile<D, KF>::chunk(i, half);
-            roff[i] = team * SLOT + frow * R + ((cc ^ (frow & GM::SWZ)) << 4);
+            roff[i] = team * SLOT + frow * R + ((cc ^ row_swz<CPR>(frow)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring)) +
                                   team * SLOT;
@@ -866,7 +873,8 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             else t.sc = 1.f;
         };
         // finisher: lanes 0..31 hold query 0 of step kq, lanes 32..63 query 1 of
-        // step kq - 1. finish_prep (vector work, beside the MFMAs) decides which
+        // step kq - 1 (pg: the page id of this lane's tile). finish_prep (vector
+        // work, beside the MFMAs) decides which
         // keys reach their query's floor `fk` and where they go in the query's
         // candidate list of this team; finish_commit (after them) writes only
         // those. Positions on a page whose id is out of range were copied from
@@ -877,13 +885,12 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             float sc;
             bool take;
         };
-        auto finish_prep = [&](int kq, float v, float tsc, uint32_t fk) -> Fin {
+        auto finish_prep = [&](int kq, float v, float tsc, uint32_t fk, int pg) -> Fin {
             Fin f;
             f.sc = KF == kRowFp8 ? v * tsc : v;
             const int kk = half ? kq - 1 : kq;
             const bool in_run = (kk >= 0) & (kk < n);
             const int tpos = (t0 + kk) * 32 + frow;   // position within the part
-            const int pg = pages[tile_of(kk) >> 1];
             const bool tok = in_run & (tpos < (half ? valid1 : valid0)) & (pg >= 0);
             const int64_t row = (int64_t)(half ? j1s : j0) * S.ld;
             if constexpr (SCORES) {
@@ -926,24 +933,31 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
         load_query<1, D>(A, min(j1, A.num_q - 1), q1, hb);
         wait_vmcnt_mem<0>();
         __syncthreads();   // the first copies have landed
-        // tiles k .. k + FD - 1 are in registers at the top of step k
-        KTile<D, KF> tb[FD];
-#pragma unroll
-        for (int i = 0; i < FD; i++) fetch(i, i, tb[i]);
+        // tile k is in registers at the top of step k: each step reads the next
+        // tile from LDS before its barrier (the tile was published one barrier
+        // earlier), so that the read completes behind the barrier and the next
+        // step's MFMAs find their operands
+        KTile<D, KF> tc;
+        fetch(0, 0, tc);
         f32x16 a0[1], a1[1];
         a1[0] = f32x16{};
         float mine_p = 0.f;                 // finisher: own block sums of step k - 1
-        uint32_t fk = 1u;                   // finisher: this lane's query's floor
+        float xv = 0.f;                     // finisher: the copier's block sums of step k - 1
+        int pgv = 0;                        // finisher: page id of its lanes' tile of step k - 1
+        uint32_t fk = SCORES ? 0u : floor_key[half];   // finisher: this lane's query's floor
         float sc_p1 = 0.f, sc_p2 = 0.f;     // token scales of the tiles of steps k - 1, k - 2
+        // page id of the tile whose completion finish_prep takes at step j + 1
+        auto page_for = [&](int j) { return pages[tile_of(half ? j - 1 : j) >> 1]; };
         // One step of a role: query 0's MFMAs on tile k beside query 1's block
-        // sums of tile k - 1 and (finisher) the completion of step k - 1, whose
-        // copier block sums were exchanged at the previous barrier; then query
-        // 1's MFMAs on tile k beside query 0's block sums of tile k. The copier
-        // then refills the slot of tile k - 1 and waits until tile k + FD has
-        // landed; after the barrier every wave reads tile k + FD from LDS.
+        // sums of tile k - 1 and (finisher) the vector half of completing step
+        // k - 1, whose copier block sums were read after the previous barrier;
+        // then query 1's MFMAs on tile k beside query 0's block sums of tile k.
+        // Then the copier hands its block sums over, reads tile k + 1, refills
+        // the slot of tile k - 1 and waits until tile k + 2 has landed; the
+        // finisher reads tile k + 1 and writes the kept candidates. After the
+        // barrier the finisher reads what the next completion needs.
         auto step = [&](auto fin_tag, int k, int u) {
             constexpr bool FIN = decltype(fin_tag)::value;
-            KTile<D, KF>& tc = tb[u % FD];
             // scheduling fences keep each group of vector work beside the MFMAs
             // it is meant to hide behind (without them the block sums are
             // hoisted to right behind their own MFMAs)
@@ -951,10 +965,7 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             tile_mfma<1, D, KF>(q0, tc, a0);
             const float h1 = tile_head_sum<1, D, KF>(q1, a1);
             Fin fin{};
-            if constexpr (FIN) {
-                if (u == 0) fk = SCORES ? 0u : floor_key[half];   // the floors move once per round
-                fin = finish_prep(k - 1, xch[(k - 1) & 1][team][l] + mine_p, half ? sc_p2 : sc_p1, fk);
-            }
+            if constexpr (FIN) fin = finish_prep(k - 1, xv + mine_p, half ? sc_p2 : sc_p1, fk, pgv);
             interleave_mfma_valu<NMFMA, FIN ? 24 : 12>();
             __builtin_amdgcn_sched_barrier(0);
             tile_mfma<1, D, KF>(q1, tc, a1);
@@ -968,10 +979,13 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
                 xch[k & 1][team][l] = mine;
                 const int pg = pg_next;
                 pg_next = pages[tile_of(k + NS) >> 1];
+                lds_wait_all();                                // the block sums are written
+                fetch(k + 1, (u + 1) % NS, tc);
                 issue(k + NS - 1, (u + NS - 1) % NS, pg);      // refills the slot of tile k - 1
-                wait_vmcnt_mem<(NS - 1 - FD) * GM::PER_TILE>();   // tile k + FD has landed
+                wait_vmcnt_mem<(NS - 3) * GM::PER_TILE>();    // tile k + 2 has landed
             } else {
                 mine_p = mine;
+                fetch(k + 1, (u + 1) % NS, tc);
                 finish_commit(fin, k - 1);
                 if constexpr (!SCORES) {
                     // once per unrolled round, team 0's finisher raises both
@@ -985,11 +999,18 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
                             floor_key[0] = max((uint32_t)b0 << (32 - kCoarseBits), 1u);
                             floor_key[1] = max((uint32_t)b1 << (32 - kCoarseBits), 1u);
                         }
+                        lds_wait_all();                        // the floors are written
                     }
                 }
             }
-            lds_barrier();
-            fetch(k + FD, (u + FD) % NS, tc);
+            barrier_only();
+            if constexpr (FIN) {
+                xv = xch[k & 1][team][l];
+                pgv = page_for(k);
+                if constexpr (!SCORES) {
+                    if (u == U - 1) fk = floor_key[half];      // the floors move once per round
+                }
+            }
         };
         // the two roles run separate, branch-free loop bodies with the same
         // barriers
@@ -1008,12 +1029,11 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             if (hb == 0) {
                 xch[nloop & 1][team][l] = h1;
             } else {
-                if constexpr (!SCORES) fk = floor_key[half];
-                finish_commit(finish_prep(nloop - 1, xch[(nloop - 1) & 1][team][l] + mine_p,
-                                          half ? sc_p2 : sc_p1, fk), nloop - 1);
+                finish_commit(finish_prep(nloop - 1, xv + mine_p, half ? sc_p2 : sc_p1, fk, pgv), nloop - 1);
             }
             lds_barrier();
-            if (hb == 1) finish_commit(finish_prep(nloop, xch[nloop & 1][team][l] + h1, sc_p1, fk), nloop);
+            if (hb == 1)
+                finish_commit(finish_prep(nloop, xch[nloop & 1][team][l] + h1, sc_p1, fk, page_for(nloop)), nloop);
         }
         wait_vmcnt_mem<0>();
     }
@@ -1265,7 +1285,6 @@ template <int D, int KF>
 struct StreamGeom {
     static constexpr int R = D * ((KF != kRowBf16) ? 1 : 2);            // bytes per row
     static constexpr int CPR = R / 16;                      // 16-byte chunks per row
-    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;     // chunk swizzle mask
     static constexpr int TILE = 32 * R;
     static constexpr int DMA = TILE / 1024;                 // 1 KB copies per tile
     static constexpr int QPT = kStreamThreads / kWave;      // waves (= queries) per workgroup
@@ -1303,20 +1322,20 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         load_query<MB, D>(A, live ? j : A.num_q - 1, q);
         // this wave's copies of a tile: tile bytes [1024 r, 1024 r + 1024) land
         // linearly in the slot; lane l fetches the source chunk that belongs at
-        // slot byte 1024 r + 16 l (logical chunk c of a row sits at c ^ (row & SWZ))
+        // slot byte 1024 r + 16 l (logical chunk c of a row sits at c ^ row_swz(row))
         uint32_t voff[SG::CPW];
 #pragma unroll
         for (int c = 0; c < SG::CPW; c++) {
             const int r = min(w * SG::CPW + c, SG::DMA - 1);
             const int gi = r * 1024 + 16 * l;
             const int row = gi / R, cc = (gi % R) / 16;
-            voff[c] = row * R + ((cc ^ (row & SG::SWZ)) << 4);
+            voff[c] = row * R + ((cc ^ row_swz<SG::CPR>(row)) << 4);
         }
         uint32_t roff[NV];
 #pragma unroll
         for (int i = 0; i < NV; i++) {
             const int cc = KTile<D, KF>::chunk(i, half);
-            roff[i] = frow * R + ((cc ^ (frow & SG::SWZ)) << 4);
+            roff[i] = frow * R + ((cc ^ row_swz<SG::CPR>(frow)) << 4);
         }
         const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((SIA_LDS uint8_t*)ring));
         // page id of tile k's copy (clamped to the last tile, so that every wave

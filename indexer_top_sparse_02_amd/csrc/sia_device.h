@@ -139,6 +139,15 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Workgroup barrier that waits for nothing: this wave's LDS reads still in
+// flight complete behind it (the compiler waits for their results where they
+// are used). The caller makes its own writes that others read after the
+// barrier complete first (lds_wait_all).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// This wave's LDS (and scalar memory) operations complete.
+__device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 // D[16x16] += A[16x32] * B[32x16], bf16 in, fp32 accumulate.
 // Lane l holds A row l%16, k = 8*(l/16)+i; B column l%16, k = 8*(l/16)+i;
 // accumulator register r holds D[4*(l/16) + r][l%16].
