@@ -372,7 +372,13 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True, fl
         attention()
     torch.cuda.synchronize()
     launches = _kernel_nodes(g_step)
-    if graph:
+    whole = graph == "step"
+    if whole:
+        # one graph for the whole step: one replay launches every kernel of it
+        for _ in range(max(1, warmup)):
+            g_step.replay()
+        torch.cuda.synchronize()
+    elif graph:
         g_idx = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g_idx):
             indexer()
@@ -387,7 +393,6 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True, fl
             indexer()
             attention()
         torch.cuda.synchronize()
-    del g_step
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
@@ -395,12 +400,19 @@ def time_path(sia, wl, s, group, steps, warmup, sched=-1, attention_too=True, fl
         if flush is not None:
             flush()
         e0.record()
-        indexer()
-        e1.record()
-        attention()
+        if whole:
+            g_step.replay()
+        else:
+            indexer()
+            e1.record()
+            attention()
         e2.record()
     torch.cuda.synchronize()
+    del g_step
     step = [e0.elapsed_time(e2) for e0, _, e2 in ev]
+    if whole:   # (no event between the phases inside one graph)
+        nan = {"median": float("nan"), "min": float("nan"), "mean": float("nan")}
+        return idx, _stats(step), nan, nan, launches
     ph_i = [e0.elapsed_time(e1) for e0, e1, _ in ev]
     ph_a = [e1.elapsed_time(e2) for _, e1, e2 in ev]
     return idx, _stats(step), _stats(ph_i), _stats(ph_a), launches
@@ -678,8 +690,9 @@ def prepare_streams(sia, W, dev, steps, warmup, dq=1536, dh=7168):
 
 def launch_overhead(sia, W, dev, steps, warmup):
     """The small decode workloads, where a step takes tens of microseconds:
-    host launches against replays of one HIP graph per call (the same kernels
-    and arguments), with the Infinity Cache evicted between steps."""
+    host launches against replays of one HIP graph per call and of one graph
+    for the whole step (the same kernels and arguments), with the caches evicted
+    between steps."""
     import torch
     out = {}
     flush = CacheFlush(dev)
@@ -687,13 +700,16 @@ def launch_overhead(sia, W, dev, steps, warmup):
         s = W.spec(name)
         wl = W.make(s, device=dev)
         r = {}
-        for mode, g in (("eager", False), ("graph", True)):
+        for mode, g in (("eager", False), ("graph", True), ("graph_step", "step")):
             _, st, si, sa, la = time_path(sia, wl, s, s.q_per_seq, steps, warmup, flush=flush, graph=g)
-            r[mode] = {"ms_per_step": st["median"], "ms_per_step_min": st["min"],
-                       "phases_ms": {"indexer_topk": si["median"], "attention": sa["median"]}}
+            r[mode] = {"ms_per_step": st["median"], "ms_per_step_min": st["min"]}
+            if g != "step":
+                r[mode]["phases_ms"] = {"indexer_topk": si["median"], "attention": sa["median"]}
             r["launches_per_step"] = la
-        r["query_tokens_per_s"] = {m: wl.num_q / (r[m]["ms_per_step"] * 1e-3) for m in ("eager", "graph")}
+        r["query_tokens_per_s"] = {m: wl.num_q / (r[m]["ms_per_step"] * 1e-3)
+                                   for m in ("eager", "graph", "graph_step")}
         r["graph_saving_us"] = (r["eager"]["ms_per_step"] - r["graph"]["ms_per_step"]) * 1e3
+        r["graph_step_saving_us"] = (r["eager"]["ms_per_step"] - r["graph_step"]["ms_per_step"]) * 1e3
         out[name] = r
         del wl
     del flush
