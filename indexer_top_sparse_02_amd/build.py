@@ -33,8 +33,12 @@ FLAGS = [
 ]
 
 
-# Per-file code generation options (none at present).
-FILE_FLAGS: dict = {}
+# Per-file code generation options. attention.hip: MFMA results of the
+# compiler's own MFMAs in vector registers (its default once a kernel uses
+# accumulation registers, as the whole-tile attention kernel does for its query
+# operand, is to put them in accumulation registers and copy them back and
+# forth around the vector arithmetic on them).
+FILE_FLAGS: dict = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -755,6 +755,467 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 512))) void sparse_mla_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-tile variant for bf16 rows: workgroup = (query, block of 16 NWV heads,
+// slice of the selected rows), NWV waves, wave w owning heads 16 w .. 16 w + 15
+// of the block and ALL 32 rows of every tile. Per tile a wave computes
+//   S^T = K Q^T   (rows x heads, 2 row blocks x 18 steps of 16x16x32 MFMAs; the
+//                  query slice, 72 registers, stays in registers)
+//   softmax       per head against the lazily moved reference maximum; every
+//                 statistic of a head lives in the lanes of that head (column jl
+//                 of S^T), so nothing is exchanged between waves
+//   O^T += V^T P^T (32 column blocks, one MFMA each; P^T is the softmax output
+//                 as it sits in registers, the value operand comes from
+//                 transposing LDS reads)
+// so one barrier per tile (the copy ring) is the only synchronisation. The K
+// dimension of P V runs over the tile rows in the order the S^T accumulators
+// hold them: slot 8 g + i is row 4 g + i (i < 4) or 16 + 4 g + (i - 4), and the
+// value reads fetch the same rows. Output accumulator register r of column
+// block cb holds column 16 cb + 4 g + r of head jl, so the rescale and the final
+// normalisation are lane-local too.
+//
+// Tile layout in LDS: 36 blocks of 1 KB, block p holding the 16-byte chunks 2p
+// and 2p + 1 of all 32 rows, 32 bytes per row (row r at 32 r). A Q K^T operand
+// read then takes 16 rows x 16 bytes spread over 512 contiguous bytes and a
+// transposing value read 4 rows x 32 contiguous bytes per 16 lanes, forms the
+// LDS serves at close to its full rate (reads of 16-byte pieces of 16 rows 1152
+// bytes apart run at about half of it, whatever the chunk swizzle). Every
+// operand read is one base address per lane plus an immediate, and so is every
+// copy: copy i fills block i with 32 bytes of each of the tile's 32 rows.
+// ---------------------------------------------------------------------------
+
+// Global -> LDS copy of 16 bytes per lane from src + OFF (OFF a byte immediate
+// within the instruction's signed 13-bit range) to lds + 16 lane; otherwise as
+// dma16. The instruction adds its offset to the LDS address as well (M0 + OFF +
+// 16 lane), so M0 carries lds - OFF.
+template <int OFF>
+__device__ __forceinline__ void dma16_imm(const void* src, SIA_LDS void* lds) {
+    static_assert(OFF >= 0 && OFF < 4096, "global instruction offset range");
+    const uint32_t m = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)) - (uint32_t)OFF);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2" ::"v"(src), "{m0}"(m), "n"(OFF) : "memory");
+}
+
+// Two fp32 values rounded to nearest even bf16 (the hardware conversion),
+// packed (a in the low half).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, bf16x2v{static_cast<__bf16>(a), static_cast<__bf16>(b)});
+}
+
+// S^T block (+)= K Q^T with the query operand held in accumulation registers:
+// the query slice is loop-invariant and only ever read by these MFMAs, which
+// leaves the vector registers to the output accumulators (whose rescale is
+// vector arithmetic). The compiler inserts no hazard waits around inline
+// assembly: the key operand comes from LDS reads (the compiler waits for them
+// before the asm), the query's accumulation registers are written once, long
+// before (see qk_settle), and the result is read by vector code only after
+// qk_settle or after a whole P V pass of MFMAs.
+__device__ __forceinline__ void mfma16_qk0(f32x4& d, const bf16x8& k, const bf16x8& q) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(k), "a"(q));
+}
+__device__ __forceinline__ void mfma16_qk(f32x4& d, const bf16x8& k, const bf16x8& q) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(k), "a"(q));
+}
+// 32 wait states after the last MFMA, then the two logit blocks are defined.
+__device__ __forceinline__ void qk_settle(f32x4 (&s)[2]) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s[0]), "+v"(s[1]));
+}
+
+// Transposing 16-bit read (compiler form): rows k0 .. k0 + 3 of one column, as
+// described at ds_read_tr16.
+__device__ __forceinline__ u32x2 ds_read_tr16_c(const uint8_t* p) {
+    typedef short s16x4v __attribute__((ext_vector_type(4)));
+    const s16x4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SIA_LDS s16x4v*)(const SIA_LDS uint8_t*)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Copies K .. N-1 of one wave: block hb + NHB k from src + k STEP.
+template <int K, int N, int STEP, int NHB>
+__device__ __forceinline__ void wave_copies(const uint8_t* src, uint8_t* dst, int hb) {
+    if constexpr (K < N) {
+        dma16_imm<K * STEP>(src, (SIA_LDS void*)(dst + (hb + NHB * K) * 1024));
+        wave_copies<K + 1, N, STEP, NHB>(src, dst, hb);
+    }
+}
+
+// NHB blocks of 16 heads per workgroup; RH = 1: one wave per head block over
+// 32-row tiles; RH = 2: 64-row tiles, two waves per head block, wave rh taking
+// rows 32 rh .. 32 rh + 31 of every tile with a softmax of its own, the two
+// merged by log-sum-exp at the end (twice the waves per SIMD for the same LDS
+// traffic and MFMA work, where one workgroup per query and head block leaves a
+// single wave per SIMD exposed to every latency).
+template <int NHB, int RH>
+struct WaveGeom {
+    static constexpr int NW = NHB * RH;                   // waves
+    static constexpr int HB = 16 * NHB;                   // heads per workgroup
+    static constexpr int NT = NW * kWave;
+    static constexpr int TR = 32 * RH;                    // rows per tile
+    static constexpr int AHEAD = 4 / RH - 1;              // tiles issued ahead of the one computed
+    // copies of a 32-row sub-tile: blocks hb + NHB k, by the waves of row half rh
+    static constexpr int CP_LO = RowFmt<false>::COPIES / NHB;
+    static constexpr int SPLIT = RowFmt<false>::COPIES % NHB;   // head blocks below issue one more
+    static constexpr int CPMAX = CP_LO + (SPLIT ? 1 : 0);
+    // Q K^T of tile t+1 runs before the softmax of tile t only where a wave has
+    // the registers for two tiles' logits (one wave per SIMD)
+    static constexpr bool PIPE = NW <= 4 && RH == 1;
+    // the query slice in accumulation registers (Q K^T as inline assembly): only
+    // with one wave per SIMD; at two the compiler would split the 256 registers
+    // evenly between the two kinds
+    static constexpr bool QA = NW <= 4;
+};
+
+template <int NHB, int RH>
+__global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnArgs A) {
+    using GM = WaveGeom<NHB, RH>;
+    constexpr int HB = GM::HB, NT = GM::NT, NW = GM::NW, CPMAX = GM::CPMAX, TR = GM::TR, AHEAD = GM::AHEAD;
+    constexpr int TB = RowFmt<false>::TB;
+    constexpr int KS = kDK / 32;    // 18 Q K^T steps
+    constexpr int NCB = kDV / 16;   // 32 output column blocks
+    static_assert(RowFmt<false>::CHUNKS == RowFmt<false>::COPIES * 64, "a tile is whole 1 KB copies");
+    static_assert(RH == 1 || RH == 2, "row halves");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][TB];
+    __shared__ __attribute__((aligned(16))) uint32_t rows[kMaxSliceRows];
+    __shared__ int scan_s[16];
+    __shared__ __attribute__((aligned(16))) float xm[RH == 2 ? NW : 1][16], xl[RH == 2 ? NW : 1][16];
+
+    const int tid = threadIdx.x, l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int hb = w % NHB, rh = w / NHB;   // head block, row half
+    const int g = l >> 4, jl = l & 15;
+    const int n_hb = A.heads / HB;
+
+    // head blocks of one (query, slice) run on the same XCD one after another
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int num_pairs = A.num_q * A.n_split;
+    const int P = (slot / n_hb) * 8 + xcd;
+    const int hbk = slot % n_hb;
+    if (P >= num_pairs) return;
+    const int pair = num_pairs - 1 - P;
+    const int j = pair / A.n_split, sp = pair % A.n_split;
+    const int head0 = hbk * HB + 16 * hb;   // this wave's first head
+
+    int b = A.q_seq[j];
+    const bool seq_ok = b >= 0 && b < A.batch;
+    if (!seq_ok) {
+        if (tid == 0) atomicOr(A.status, kBadSeq);
+        b = 0;
+    }
+    const int n_b = seq_ok ? A.seq_lens[b] : 0;
+    const int r0 = sp * A.rows_per_split;
+    const int r1 = seq_ok ? min(A.topk, r0 + A.rows_per_split) : r0;
+
+    // ---- the wave's query as the B operand of Q K^T: step s, head head0 + jl,
+    // dims 32 s + 8 g .. + 7
+    bf16x8 qb[KS];
+    {
+        const uint16_t* qrow = A.q + ((int64_t)j * A.heads + head0 + jl) * kDK + g * 8;
+#pragma unroll
+        for (int s = 0; s < KS; s++) qb[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + s * 32));
+        // into the accumulation registers, then the wait states a vector write
+        // needs before an MFMA reads what it wrote
+        if constexpr (GM::QA) {
+#pragma unroll
+            for (int s = 0; s < KS; s++) asm volatile("" : "+a"(qb[s]));
+            asm volatile("s_nop 7" ::: "memory");
+        }
+    }
+
+    // ---- validated, compacted physical row ids of the slice (as in
+    // sparse_mla_kernel)
+    constexpr int RPT = kMaxSliceRows / NT;
+    int nr = 0;
+    {
+        int sidx[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int r = r0 + tid * RPT + i;
+            sidx[i] = r < r1 ? A.idx[(int64_t)j * A.topk + r] : -1;
+        }
+        int pg[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
+            const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
+            pg[i] = in ? A.page_table[(int64_t)b * A.max_pages + (s >> 6)] : -1;
+            if (s >= 0 && !in) atomicOr(A.status, kBadIndex);
+        }
+        uint32_t row[RPT];
+        int keep = 0;
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
+            const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
+            const bool ok = in && pg[i] >= 0 && pg[i] < A.num_pages;
+            if (in && !ok) atomicOr(A.status, kBadPage);
+            row[i] = ok ? (uint32_t)pg[i] * kPage + (uint32_t)(s & 63) : 0xffffffffu;
+            keep += ok;
+        }
+        int pre, tot;
+        scan1<NT>(keep, pre, tot, scan_s);
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            if (row[i] != 0xffffffffu) rows[pre++] = row[i];
+        }
+        nr = tot;
+    }
+    __syncthreads();
+    const int ntiles = (nr + TR - 1) / TR;
+    wait_vmcnt<0>();
+
+    // 32-row sub-tile rh of tile t lives in ring slot (RH t + rh) % 4
+    auto sub_of = [&](int t) -> uint8_t* { return ring[(RH * t + rh) & 3]; };
+    // copies of tile t by wave (hb, rh): copy k fills block i = hb + NHB k of
+    // sub-tile rh: lane l takes chunk 2 i + l % 2 of row 32 rh + l / 2 (rows past
+    // the slice repeat its last row). A wave with one copy fewer repeats its
+    // last one, so that every wave issues CPMAX copies per tile.
+    auto issue = [&](int t) {
+        uint8_t* dst = sub_of(t);
+        const uint32_t row = rows[min(t * TR + 32 * rh + (l >> 1), nr - 1)];
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row * kRowB + 32 * hb + 16 * (l & 1);
+        constexpr int STEP = 32 * NHB;   // source bytes between a wave's copies
+        wave_copies<0, GM::CP_LO, STEP, NHB>(src, dst, hb);
+        if constexpr (GM::SPLIT) {
+            // one more copy: block hb + NHB CP_LO where it exists, else a repeat
+            const int k = hb < GM::SPLIT ? GM::CP_LO : GM::CP_LO - 1;
+            dma16_imm<0>(src + STEP * k, (SIA_LDS void*)(dst + (hb + NHB * k) * 1024));
+        }
+    };
+
+    // key operand of row block rb, step s: sub-tile row 16 rb + jl, chunk 4 s + g
+    // (block 2 s + g / 2, half g % 2): kbase + 2048 s + 512 rb
+    const int kbase = (g >> 1) * 1024 + jl * 32 + (g & 1) * 16;
+    // value operand of column block cb, read e: lane addresses sub-tile row
+    // 16 e + 4 g + jl / 4, chunk 2 cb + (jl / 2) % 2 (block cb), byte 8 (jl % 2):
+    // vbase + 1024 cb + 512 e
+    const int vbase = (4 * g + (jl >> 2)) * 32 + ((jl >> 1) & 1) * 16 + 8 * (jl & 1);
+
+    // S^T of sub-tile `buf` for the wave's heads: s[rb] register r = logit of
+    // sub-tile row 16 rb + 4 g + r and head jl
+    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2]) {
+        constexpr int DEPTH = GM::QA ? 3 : 2;   // steps whose key operands are in flight
+        auto kread = [&](int st, int rb) -> bf16x8 {
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kbase + st * 2048 + rb * 512));
+        };
+        bf16x8 kb[DEPTH][2];
+#pragma unroll
+        for (int i = 0; i < DEPTH; i++) {
+            kb[i][0] = kread(i, 0);
+            kb[i][1] = kread(i, 1);
+        }
+#pragma unroll
+        for (int st = 0; st < KS; st++) {
+            const bf16x8 k0 = kb[st % DEPTH][0], k1 = kb[st % DEPTH][1];
+            if (st + DEPTH < KS) {
+                kb[st % DEPTH][0] = kread(st + DEPTH, 0);
+                kb[st % DEPTH][1] = kread(st + DEPTH, 1);
+            }
+            if constexpr (GM::QA) {
+                if (st == 0) {
+                    mfma16_qk0(s[0], k0, qb[st]);
+                    mfma16_qk0(s[1], k1, qb[st]);
+                } else {
+                    mfma16_qk(s[0], k0, qb[st]);
+                    mfma16_qk(s[1], k1, qb[st]);
+                }
+            } else {
+                const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                s[0] = mfma16(k0, qb[st], st == 0 ? z : s[0]);
+                s[1] = mfma16(k1, qb[st], st == 0 ? z : s[1]);
+            }
+        }
+    };
+
+    const float scale_log2 = A.sm_scale * 1.4426950408889634f;
+    constexpr float kLazyMax = 8.f;
+    // reference maximum of head jl and the running sum over this lane's rows;
+    // the finite start keeps exp2 of a masked logit at 0 in a wave that has not
+    // met a valid row yet (a row half can start with an empty sub-tile)
+    float m_ref = -1e30f, l_run = 0.f;
+    f32x4 o[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; cb++) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // softmax of the wave's sub-tile of tile t from its logits: P^T (bf16,
+    // B-operand layout) for P V; moves the reference (rescaling O and the sum)
+    // where a logit exceeds it by more than kLazyMax
+    auto softmax = [&](int t, const f32x4 (&s)[2]) -> bf16x8 {
+        float x[2][4];
+        bool over = false;
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const bool valid = t * TR + 32 * rh + rb * 16 + 4 * g + r < nr;
+                x[rb][r] = valid ? s[rb][r] * scale_log2 : -INFINITY;
+                over |= x[rb][r] > m_ref + kLazyMax;
+            }
+        if (__builtin_amdgcn_readfirstlane(__ballot(over) != 0ull ? 1 : 0)) {
+            float tm = x[0][0];
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) tm = __builtin_fmaxf(tm, x[rb][r]);
+            tm = __builtin_fmaxf(tm, __shfl_xor(tm, 16));
+            tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32));
+            const bool mv = tm > m_ref + kLazyMax;
+            const float al = mv ? __builtin_amdgcn_exp2f(m_ref - tm) : 1.f;
+            m_ref = mv ? tm : m_ref;
+            l_run *= al;
+            if (__builtin_amdgcn_readfirstlane(__ballot(mv) != 0ull ? 1 : 0)) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; cb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) o[cb][r] *= al;
+            }
+        }
+        float p[2][4];
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                p[rb][r] = __builtin_amdgcn_exp2f(x[rb][r] - m_ref);
+                l_run += p[rb][r];
+            }
+        return as_bf16x8(u32x4{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                               pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])});
+    };
+
+    // O^T += V^T P^T over sub-tile `buf`: column block cb takes two transposing
+    // reads (rows 4 g .., 16 + 4 g ..: its eight k slots, in P's order); the
+    // reads of the next VD blocks are in flight during each MFMA
+    auto pv = [&](const uint8_t* buf, const bf16x8 pk) {
+        constexpr int VD = GM::QA ? 4 : 2;
+        auto vread = [&](int cb) -> bf16x8 {
+            const u32x2 a = ds_read_tr16_c(buf + vbase + 1024 * cb);
+            const u32x2 bb = ds_read_tr16_c(buf + vbase + 1024 * cb + 512);
+            return as_bf16x8(u32x4{a[0], a[1], bb[0], bb[1]});
+        };
+        bf16x8 vb[VD];
+#pragma unroll
+        for (int i = 0; i < VD; i++) vb[i] = vread(i);
+#pragma unroll
+        for (int cb = 0; cb < NCB; cb++) {
+            const bf16x8 v = vb[cb % VD];
+            if (cb + VD < NCB) vb[cb % VD] = vread(cb + VD);
+            o[cb] = mfma16(v, pk, o[cb]);
+        }
+    };
+
+    if (ntiles > 0) {
+        // every wave issues exactly CPMAX copies per tile, so "tile t landed" is
+        // "at most CPMAX copies per later tile still outstanding"
+#pragma unroll
+        for (int t = 0; t < AHEAD; t++)
+            if (t < ntiles) issue(t);
+        if constexpr (GM::PIPE) {
+            if (ntiles > 2) wait_vmcnt_mem<2 * CPMAX>();
+            else if (ntiles > 1) wait_vmcnt_mem<CPMAX>();
+            else wait_vmcnt_mem<0>();
+            lds_barrier();
+            f32x4 s[2];
+            qk(sub_of(0), s);
+            qk_settle(s);
+            for (int t = 0; t < ntiles; t++) {
+                // tile t+1 has landed (tile t+2's copies may still be in
+                // flight), the slot of tile t-1 is free
+                if (t + 2 < ntiles) wait_vmcnt_mem<CPMAX>();
+                else wait_vmcnt_mem<0>();
+                lds_barrier();
+                if (t + 3 < ntiles) issue(t + 3);
+                f32x4 sn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+                if (t + 1 < ntiles) qk(sub_of(t + 1), sn);
+                const bf16x8 pk = softmax(t, s);
+                pv(sub_of(t), pk);
+                // (the next tile's logits are taken over only after this
+                // tile's P V MFMAs have issued)
+                qk_settle(sn);
+                s[0] = sn[0];
+                s[1] = sn[1];
+            }
+        } else {
+            for (int t = 0; t < ntiles; t++) {
+                // tile t has landed (the AHEAD - 1 tiles after it may still be
+                // in flight), the slots of tile t-1 are free
+                if (AHEAD > 2 && t + 2 < ntiles) wait_vmcnt_mem<(AHEAD > 2 ? 2 : 0) * CPMAX>();
+                else if (AHEAD > 1 && t + 1 < ntiles) wait_vmcnt_mem<(AHEAD > 1 ? 1 : 0) * CPMAX>();
+                else wait_vmcnt_mem<0>();
+                lds_barrier();
+                if (t + AHEAD < ntiles) issue(t + AHEAD);
+                f32x4 s[2];
+                qk(sub_of(t), s);
+                qk_settle(s);
+                const bf16x8 pk = softmax(t, s);
+                pv(sub_of(t), pk);
+            }
+        }
+    }
+    wait_vmcnt<0>();
+
+    // ---- finalize: the sums of the four lane groups; with two row halves the
+    // halves merge first (log-sum-exp), wave rh finishing output columns
+    // 256 rh .. 256 rh + 255 from its own and its partner's accumulators
+    float lt = l_run;
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    float m_fin = m_ref, a_own = 1.f, a_oth = 0.f;
+    constexpr int NCBF = NCB / RH;   // column blocks this wave finishes: rh NCBF ..
+    const f32x4* xo = nullptr;
+    if constexpr (RH == 2) {
+        // the ring is free once every wave has left the loop
+        __syncthreads();
+        f32x4* mine = reinterpret_cast<f32x4*>(&ring[0][0]) + w * (NCBF * kWave);
+        // (selects between static indices: an index that depends on rh would put
+        // the accumulator array in scratch memory)
+#pragma unroll
+        for (int c = 0; c < NCBF; c++) mine[c * kWave + l] = rh == 0 ? o[NCBF + c] : o[c];
+        if (g == 0) {
+            xm[w][jl] = m_ref;
+            xl[w][jl] = lt;
+        }
+        __syncthreads();
+        const int pw = hb + NHB * (1 - rh);
+        const float mp = xm[pw][jl], lp = xl[pw][jl];
+        m_fin = __builtin_fmaxf(m_ref, mp);
+        a_own = __builtin_amdgcn_exp2f(m_ref - m_fin);
+        a_oth = __builtin_amdgcn_exp2f(mp - m_fin);
+        lt = lt * a_own + lp * a_oth;
+        xo = reinterpret_cast<const f32x4*>(&ring[0][0]) + pw * (NCBF * kWave);
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int64_t head = head0 + jl;
+    const int cb_first = rh * NCBF;
+    auto final_block = [&](int c) -> f32x4 {
+        f32x4 v = rh == 0 ? o[c] : o[(RH - 1) * NCBF + c];
+        if constexpr (RH == 2) {
+            const f32x4 u = xo[c * kWave + l];
+#pragma unroll
+            for (int r = 0; r < 4; r++) v[r] = v[r] * a_own + u[r] * a_oth;
+        }
+        return v * inv;
+    };
+    if (A.n_split > 1) {
+        float* dst = A.part_o + (((int64_t)j * A.n_split + sp) * A.heads + head) * kDV + 4 * g + 16 * cb_first;
+#pragma unroll
+        for (int c = 0; c < NCBF; c++) *reinterpret_cast<f32x4*>(dst + c * 16) = final_block(c);
+    } else {
+        uint16_t* dst = A.out + ((int64_t)j * A.heads + head) * kDV + 4 * g + 16 * cb_first;
+#pragma unroll
+        for (int c = 0; c < NCBF; c++) {
+            const f32x4 v = final_block(c);
+            *reinterpret_cast<u32x2*>(dst + c * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        }
+    }
+    if (g == 0 && rh == 0) {
+        const float lse = lt > 0.f ? (m_fin + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+        if (A.n_split > 1)
+            A.part_lse[((int64_t)j * A.n_split + sp) * A.heads + head] = lse;
+        else if (A.lse)
+            A.lse[(int64_t)j * A.heads + head] = lse;
+    }
+}
+
 // Merge of the row slices of one (query, head) by log-sum-exp.
 __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs A) {
     const int64_t jh = blockIdx.x;            // query * heads + head
@@ -791,7 +1252,27 @@ static hipError_t mla_launch(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int NHB, int RH>
+static hipError_t mla_wave_launch(const AttnArgs& a, hipStream_t st) {
+    using GM = WaveGeom<NHB, RH>;
+    const int n_hb = a.heads / GM::HB;
+    const int64_t pairs = (int64_t)a.num_q * a.n_split;
+    const int64_t blocks = (pairs + 7) / 8 * 8 * n_hb;
+    hipLaunchKernelGGL((sparse_mla_wave_kernel<NHB, RH>), dim3((unsigned)blocks), dim3(GM::NT), 0, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st) {
+    if (a.wave_heads && !a.kv8) {
+        switch (a.heads_per_block * 4 + a.wave_heads) {
+            case 128 * 4 + 1: return mla_wave_launch<8, 1>(a, st);
+            case 64 * 4 + 1: return mla_wave_launch<4, 1>(a, st);
+            case 32 * 4 + 1: return mla_wave_launch<2, 1>(a, st);
+            case 64 * 4 + 2: return mla_wave_launch<4, 2>(a, st);
+            case 32 * 4 + 2: return mla_wave_launch<2, 2>(a, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.heads_per_block * 2 + (a.kv8 ? 1 : 0)) {
         case 128: return mla_launch<64, false>(a, st);
         case 64: return mla_launch<32, false>(a, st);

@@ -601,7 +601,16 @@ int sia_indexer_prepare(const sia_indexer_weights* W, const void* xq, const void
 
 static int attn_plan(const sia_queries* qs, int heads, int topk, int& hb, int& n_split, int& rows_per_split,
                      size_t& total) {
-    hb = heads % 64 == 0 ? 64 : heads % 32 == 0 ? 32 : 16;
+    // bf16 rows take the whole-tile kernel (SIA_ATTN_WAVE=0 selects the
+    // row-split one): 128 heads per workgroup where that alone gives every CU a
+    // workgroup (each selected row is then gathered once per query), else 64
+    int hb_max = 64;
+    if (env_int("SIA_ATTN_WAVE", 1)) {
+        const int forced = env_int("SIA_ATTN_HB", 0);
+        if (forced > 0) hb_max = forced >= 128 ? 128 : 64;
+        else if (heads % 128 == 0 && (int64_t)qs->num_q * (heads / 128) >= device_cus()) hb_max = 128;
+    }
+    hb = heads % hb_max == 0 ? hb_max : heads % 64 == 0 ? 64 : heads % 32 == 0 ? 32 : 16;
     const int64_t base = (int64_t)qs->num_q * (heads / hb);
     // one workgroup per CU is resident (LDS); split the rows only as far as it
     // takes to give every CU one, keeping at least two tiles per slice and at
@@ -675,7 +684,11 @@ int mla_run(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queri
     a.sm_scale = sm_scale;
     a.n_split = ns;
     a.rows_per_split = rps;
-    a.heads_per_block = hb;
+    // bf16 rows: the whole-tile kernel where a block is 32 heads or more; fp8
+    // rows: the row-split kernel, at most 64 heads per workgroup
+    a.wave_heads = !a.kv8 && hb >= 32 && env_int("SIA_ATTN_WAVE", 1) ? 1 : 0;
+    if (a.wave_heads && hb <= 64 && env_int("SIA_ATTN_RH", 1) == 2) a.wave_heads = 2;
+    a.heads_per_block = a.kv8 ? std::min(hb, 64) : hb;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;
     a.part_o = ns > 1 ? reinterpret_cast<float*>(ws + kHeader) : nullptr;

@@ -162,6 +162,9 @@ struct AttnArgs {
     int32_t topk;
     float sm_scale;
     int32_t n_split, rows_per_split, heads_per_block;
+    int32_t wave_heads;       // bf16 rows: 0 = row-split kernel; 1 = one wave per 16 heads over whole
+                              // 32-row tiles (P in registers); 2 = two waves per 16 heads, each over
+                              // one half of 64-row tiles
     uint16_t* out;            // bf16 [num_q, heads, d_v]  (n_split == 1)
     float* lse;               // [num_q, heads] or null
     float* part_o;            // [num_q, n_split, heads, d_v] fp32 (n_split > 1)

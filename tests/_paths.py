@@ -24,6 +24,18 @@ def score_tol(wl) -> float:
 
 ATTN_TOL = 2e-2   # relative L2 error of each (query, head) output row
 
+# Attention kernels of the bf16 latent cache, chosen by the library's plan
+# through its environment: the row-split kernel (two waves per 16 heads, P
+# exchanged through LDS) and the whole-tile kernel with 64 or 128 heads per
+# workgroup (one wave per 16 heads over all rows of a tile), or with 64 heads
+# and two waves per 16 heads, one per half of each 64-row tile.
+ATTN_KERNELS = {
+    "rowsplit": dict(SIA_ATTN_WAVE=0, SIA_ATTN_RH=1),
+    "wave64": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=64, SIA_ATTN_RH=1),
+    "wave128": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=128, SIA_ATTN_RH=1),
+    "wave64x2": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=64, SIA_ATTN_RH=2),
+}
+
 
 @contextlib.contextmanager
 def env(**kv):

@@ -14,7 +14,7 @@ import torch
 import indexer_top_sparse_02_amd as sia
 import oracle
 import workloads as W
-from _paths import (check_attention, check_band, check_scores, env, gpu_attention, gpu_scores,
+from _paths import (ATTN_KERNELS, check_attention, check_band, check_scores, env, gpu_attention, gpu_scores,
                     gpu_topk, oracle_topk_of, row_lengths, score_tol)
 
 pytestmark = pytest.mark.gpu
@@ -125,7 +125,8 @@ def test_bad_query_sequence_is_flagged_and_selects_nothing():
     assert torch.equal(out[[0, 2]].view(torch.int16), ref_out[[0, 2]].view(torch.int16))
 
 
-def test_attention_index_past_sequence_is_skipped():
+@pytest.mark.parametrize("kernel", list(ATTN_KERNELS))
+def test_attention_index_past_sequence_is_skipped(kernel):
     """Stage-2 indices >= n_b are skipped and flag BAD_INDEX; the output equals
     the oracle's over the remaining entries."""
     s = W.spec("decode_b32", batch=2, ctx_lo=3000, ctx_hi=3500, topk=256, heads_attn=32)
@@ -135,8 +136,10 @@ def test_attention_index_past_sequence_is_skipped():
     bad = idx.clone()
     bad[0, 5] = int(n[0]) + 3
     bad[1, 100] = int(n[1]) + 1000
-    ws_a = sia.new_workspace(sia.mla_workspace_size(wl.num_q, s.heads_attn, s.topk), "cuda")
-    out, lse = _attention(wl, bad, ws_a)
+    print(f"attention past-sequence indices: kernel {kernel}", flush=True)
+    with env(**ATTN_KERNELS[kernel]):
+        ws_a = sia.new_workspace(sia.mla_workspace_size(wl.num_q, s.heads_attn, s.topk), "cuda")
+        out, lse = _attention(wl, bad, ws_a)
     assert sia.read_device_status(ws_a) & sia.DEVSTATUS_BAD_INDEX
     ia = bad.cpu().numpy().copy()
     ia[0, 5] = -1
@@ -145,8 +148,9 @@ def test_attention_index_past_sequence_is_skipped():
     check_attention(out, ref_out, lse, ref_lse)
 
 
+@pytest.mark.parametrize("kernel", list(ATTN_KERNELS))
 @pytest.mark.parametrize("heads_attn", [16, 64, 128])
-def test_attention_unsorted_duplicate_and_interior_padding(heads_attn):
+def test_attention_unsorted_duplicate_and_interior_padding(heads_attn, kernel):
     """Stage-2 index lists in any order, with duplicates (a duplicate counts
     twice) and -1 entries in the middle, against the oracle on the same lists.
     Lists of 300 entries span several 32-row tiles and a ragged one."""
@@ -162,8 +166,9 @@ def test_attention_unsorted_duplicate_and_interior_padding(heads_attn):
         r[200:230] = r[100:130]                           # a duplicated block
         rows.append(r)
     ia = np.stack(rows)
-    print(f"attention index lists: heads {heads_attn}", flush=True)
-    out, lse = _attention(wl, torch.from_numpy(ia).cuda())
+    print(f"attention index lists: heads {heads_attn} kernel {kernel}", flush=True)
+    with env(**ATTN_KERNELS[kernel]):
+        out, lse = _attention(wl, torch.from_numpy(ia).cuda())
     ref_out, ref_lse = _oracle_attention(wl, ia)
     check_attention(out, ref_out, lse, ref_lse)
 

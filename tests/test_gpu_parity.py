@@ -9,8 +9,8 @@ import torch
 
 import oracle
 import workloads as W
-from _paths import (check_attention, check_band, check_scores, env, gpu_attention, gpu_scores, group_of,
-                    gpu_topk, oracle_topk_of, row_lengths, score_tol)
+from _paths import (ATTN_KERNELS, check_attention, check_band, check_scores, env, gpu_attention, gpu_scores,
+                    group_of, gpu_topk, oracle_topk_of, row_lengths, score_tol)
 
 pytestmark = pytest.mark.gpu
 
@@ -105,11 +105,14 @@ def test_end_to_end_sets_within_band(case):
     check_band(got, r["ref_idx"], r["ref_scores"], score_tol(r["wl"]))
 
 
+@pytest.mark.parametrize("kernel", list(ATTN_KERNELS))
 @pytest.mark.parametrize("case", list(CASES))
-def test_attention_matches_oracle(case):
+def test_attention_matches_oracle(case, kernel):
     r = _run(case)
     wl, rows = r["wl"], r["rows"]
-    out, lse = gpu_attention(wl, r["idx"])
+    print(f"attention {case} kernel {kernel}", flush=True)
+    with env(**ATTN_KERNELS[kernel]):
+        out, lse = gpu_attention(wl, r["idx"])
     sub = wl.to("cpu").queries(0, wl.num_q)
     idx = r["idx"].cpu().numpy()[rows]
     ref_out, ref_lse = oracle.sparse_mla(sub.q_seq[rows], sub.seq_lens.numel(), sub.page_table, sub.kv,
@@ -470,14 +473,16 @@ def test_no_queries_is_a_no_op():
     assert out.shape[0] == 0
 
 
-def test_topk_of_all_positions_is_dense_causal_attention():
+@pytest.mark.parametrize("kernel", list(ATTN_KERNELS))
+def test_topk_of_all_positions_is_dense_causal_attention(kernel):
     s = W.spec("prefill_16k", ctx_lo=700, ctx_hi=700, topk=1024, heads_attn=32)
     wl = W.make(s, device="cuda")
     idx, _ = gpu_topk(wl)
     got = idx.cpu().numpy()
     L = 700
     assert np.array_equal(got[:, :L] >= 0, np.tril(np.ones((L, L), bool)))
-    out, _ = gpu_attention(wl, idx)
+    with env(**ATTN_KERNELS[kernel]):
+        out, _ = gpu_attention(wl, idx)
     # dense causal attention over the logical latent rows (fp32, CPU)
     t = wl.page_table.cpu()[0].long()
     pos = torch.arange(L)
