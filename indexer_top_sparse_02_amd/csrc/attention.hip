@@ -918,7 +918,7 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
         if constexpr (GM::QA) {
 #pragma unroll
             for (int s = 0; s < KS; s++) asm volatile("" : "+a"(qb[s]));
-            asm volatile("s_nop 7" ::: "memory");
+            asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
         }
     }
 
@@ -1216,6 +1216,352 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
     }
 }
 
+// ---------------------------------------------------------------------------
+// Wide whole-tile variant for bf16 rows: 128 heads per workgroup in 4 waves of
+// 32 (one wave per SIMD). As in sparse_mla_wave_kernel every wave takes all 32
+// rows of a tile, but with two 16-head blocks per wave each key and value
+// operand read from LDS feeds two MFMAs, which halves the LDS traffic per
+// flop. Registers: the query slice (2 x 72) in vector registers and the output
+// accumulators (2 x 32 blocks of 4 = 256) in the accumulation registers; the
+// P V MFMAs are inline assembly on those, and no vector instruction touches
+// the accumulators inside the loop (the compiler would otherwise keep copies of
+// them in vector registers): the rare rescale when a reference maximum moves
+// goes through a per-wave LDS buffer, as does the final normalisation.
+// ---------------------------------------------------------------------------
+constexpr int kWideNW = 4;                       // waves
+constexpr int kWideHB = 32 * kWideNW;            // heads per workgroup
+constexpr int kWideCP = RowFmt<false>::COPIES / kWideNW;   // copies per wave and tile
+static_assert(RowFmt<false>::COPIES % kWideNW == 0, "copies split evenly");
+
+// O^T block += V^T P^T with the accumulator in accumulation registers. The
+// compiler inserts no hazard waits around inline assembly: P (written by
+// vector instructions) goes through p_settle first; the value operand comes
+// from LDS reads the compiler waits for.
+__device__ __forceinline__ void mfma16_pv_acc(f32x4& d, const bf16x8& v, const bf16x8& p) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(v), "v"(p));
+}
+// 16 wait states after the vector instructions that wrote P^T of both head
+// blocks (a read of an operand fewer than 6 wait states after its write has
+// returned the old contents), then P^T is defined.
+__device__ __forceinline__ void p_settle(bf16x8 (&pk)[2]) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(pk[0]), "+v"(pk[1]));
+}
+// An accumulation-register block set to zero by an MFMA of zero operands.
+__device__ __forceinline__ void acc_zero(f32x4& d, const bf16x8& z) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %1, 0" : "=a"(d) : "v"(z));
+}
+// Accumulation-register block -> LDS (16 bytes per lane at lds), and back.
+__device__ __forceinline__ void acc_to_lds(uint32_t lds, const f32x4& d) {
+    asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(lds), "a"(d) : "memory");
+}
+__device__ __forceinline__ void acc_from_lds(uint32_t lds, f32x4& d) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=a"(d) : "v"(lds) : "memory");
+}
+
+__global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnArgs A) {
+    constexpr int NT = kWideNW * kWave, HB = kWideHB;
+    constexpr int TB = RowFmt<false>::TB;
+    constexpr int KS = kDK / 32;    // 18 Q K^T steps
+    constexpr int NCB = kDV / 16;   // 32 output column blocks
+    __shared__ __attribute__((aligned(16))) uint8_t ring[4][TB];
+    __shared__ __attribute__((aligned(16))) uint32_t rows[kMaxSliceRows];
+    __shared__ int scan_s[16];
+    __shared__ __attribute__((aligned(16))) f32x4 resc[kWideNW][kWave];   // per-wave rescale buffer
+
+    const int tid = threadIdx.x, l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int g = l >> 4, jl = l & 15;
+    const int n_hb = A.heads / HB;
+
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int num_pairs = A.num_q * A.n_split;
+    const int P = (slot / n_hb) * 8 + xcd;
+    const int hbk = slot % n_hb;
+    if (P >= num_pairs) return;
+    const int pair = num_pairs - 1 - P;
+    const int j = pair / A.n_split, sp = pair % A.n_split;
+    const int head0 = hbk * HB + 32 * w;   // this wave's first head; block h: head0 + 16 h
+
+    int b = A.q_seq[j];
+    const bool seq_ok = b >= 0 && b < A.batch;
+    if (!seq_ok) {
+        if (tid == 0) atomicOr(A.status, kBadSeq);
+        b = 0;
+    }
+    const int n_b = seq_ok ? A.seq_lens[b] : 0;
+    const int r0 = sp * A.rows_per_split;
+    const int r1 = seq_ok ? min(A.topk, r0 + A.rows_per_split) : r0;
+
+    // ---- the wave's query as the B operand of Q K^T: block h, step s: head
+    // head0 + 16 h + jl, dims 32 s + 8 g .. + 7
+    bf16x8 qb[2][KS];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        const uint16_t* qrow = A.q + ((int64_t)j * A.heads + head0 + 16 * h + jl) * kDK + g * 8;
+#pragma unroll
+        for (int s = 0; s < KS; s++) qb[h][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + s * 32));
+    }
+
+    // ---- validated, compacted physical row ids of the slice (as in
+    // sparse_mla_kernel)
+    constexpr int RPT = kMaxSliceRows / NT;
+    int nr = 0;
+    {
+        int sidx[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int r = r0 + tid * RPT + i;
+            sidx[i] = r < r1 ? A.idx[(int64_t)j * A.topk + r] : -1;
+        }
+        int pg[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
+            const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
+            pg[i] = in ? A.page_table[(int64_t)b * A.max_pages + (s >> 6)] : -1;
+            if (s >= 0 && !in) atomicOr(A.status, kBadIndex);
+        }
+        uint32_t row[RPT];
+        int keep = 0;
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
+            const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
+            const bool ok = in && pg[i] >= 0 && pg[i] < A.num_pages;
+            if (in && !ok) atomicOr(A.status, kBadPage);
+            row[i] = ok ? (uint32_t)pg[i] * kPage + (uint32_t)(s & 63) : 0xffffffffu;
+            keep += ok;
+        }
+        int pre, tot;
+        scan1<NT>(keep, pre, tot, scan_s);
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            if (row[i] != 0xffffffffu) rows[pre++] = row[i];
+        }
+        nr = tot;
+    }
+    __syncthreads();
+    const int ntiles = (nr + kTR - 1) / kTR;
+    wait_vmcnt<0>();
+
+    // copies of tile t (layout as in sparse_mla_wave_kernel): copy k of wave w
+    // fills block w + 4 k with chunk 2 (w + 4 k) + l % 2 of tile row l / 2
+    auto issue = [&](int t) {
+        uint8_t* dst = ring[t & 3];
+        const uint32_t row = rows[min(t * kTR + (l >> 1), nr - 1)];
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row * kRowB + 32 * w + 16 * (l & 1);
+        wave_copies<0, kWideCP, 32 * kWideNW, kWideNW>(src, dst, w);
+    };
+    const int kbase = (g >> 1) * 1024 + jl * 32 + (g & 1) * 16;
+    const int vbase = (4 * g + (jl >> 2)) * 32 + ((jl >> 1) & 1) * 16 + 8 * (jl & 1);
+
+    const float scale_log2 = A.sm_scale * 1.4426950408889634f;
+    constexpr float kLazyMax = 8.f;
+    // reference maximum and running sum (over this lane's rows) of the lane's
+    // head in each block
+    float m_ref[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
+    // S^T of tile `buf`: s[rb][h] register r = logit of row 16 rb + 4 g + r and
+    // head head0 + 16 h + jl; each key operand read serves both head blocks.
+    // With xe/pk given, step st < 16 also computes exponential st of the
+    // previous tile's prepared logits (the 16 of this lane: block st / 8, row
+    // block (st / 4) % 2, register st % 4), so that they run beside the MFMAs,
+    // and the last step packs them into P^T.
+    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2][2], const float (*xe)[2][4] = nullptr,
+                  bf16x8* pk = nullptr) {
+        float pe[2][2][4];
+        constexpr int DEPTH = 3;
+        auto kread = [&](int st, int rb) -> bf16x8 {
+            return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kbase + st * 2048 + rb * 512));
+        };
+        bf16x8 kb[DEPTH][2];
+#pragma unroll
+        for (int i = 0; i < DEPTH; i++) {
+            kb[i][0] = kread(i, 0);
+            kb[i][1] = kread(i, 1);
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < KS; st++) {
+            const bf16x8 k0 = kb[st % DEPTH][0], k1 = kb[st % DEPTH][1];
+            if (st + DEPTH < KS) {
+                kb[st % DEPTH][0] = kread(st + DEPTH, 0);
+                kb[st % DEPTH][1] = kread(st + DEPTH, 1);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                s[0][h] = mfma16(k0, qb[h][st], st == 0 ? z : s[0][h]);
+                s[1][h] = mfma16(k1, qb[h][st], st == 0 ? z : s[1][h]);
+            }
+            if (xe != nullptr && st < 16) {
+                const int h = st >> 3, rb = (st >> 2) & 1, r = st & 3;
+                pe[h][rb][r] = __builtin_amdgcn_exp2f(xe[h][rb][r] - m_ref[h]);
+                l_run[h] += pe[h][rb][r];
+            }
+        }
+        if (xe != nullptr) {
+#pragma unroll
+            for (int h = 0; h < 2; h++)
+                pk[h] = as_bf16x8(u32x4{pack_bf16x2(pe[h][0][0], pe[h][0][1]), pack_bf16x2(pe[h][0][2], pe[h][0][3]),
+                                        pack_bf16x2(pe[h][1][0], pe[h][1][1]), pack_bf16x2(pe[h][1][2], pe[h][1][3])});
+        }
+    };
+
+    f32x4 o[2][NCB];
+    {
+        bf16x8 zb = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+        asm volatile("s_nop 7\n\ts_nop 7" : "+v"(zb));   // (wait states after its vector write)
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int cb = 0; cb < NCB; cb++) acc_zero(o[h][cb], zb);
+    }
+    const uint32_t resc_lds = (uint32_t)(uintptr_t)(SIA_LDS f32x4*)&resc[w][l];
+
+    // Logits of tile t for both head blocks, scaled to log2 units and masked
+    // past the slice (x[h][rb][r]); moves a block's reference where a logit
+    // exceeds it by more than kLazyMax, rescaling that block's accumulators
+    // through LDS and its sum (in tile 0 the accumulators are still zero).
+    auto prep = [&](int t, const f32x4 (&s)[2][2], float (&x)[2][2][4]) {
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            bool over = false;
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const bool valid = t * kTR + rb * 16 + 4 * g + r < nr;
+                    x[h][rb][r] = valid ? s[rb][h][r] * scale_log2 : -INFINITY;
+                    over |= x[h][rb][r] > m_ref[h] + kLazyMax;
+                }
+            if (__builtin_amdgcn_readfirstlane(__ballot(over) != 0ull ? 1 : 0)) {
+                float tm = x[h][0][0];
+#pragma unroll
+                for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) tm = __builtin_fmaxf(tm, x[h][rb][r]);
+                tm = __builtin_fmaxf(tm, __shfl_xor(tm, 16));
+                tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32));
+                const bool mv = tm > m_ref[h] + kLazyMax;
+                const float al = mv ? __builtin_amdgcn_exp2f(m_ref[h] - tm) : 1.f;
+                m_ref[h] = mv ? tm : m_ref[h];
+                l_run[h] *= al;
+                if (t > 0 && __builtin_amdgcn_readfirstlane(__ballot(mv) != 0ull ? 1 : 0)) {
+                    // (the previous tile's P V MFMAs wrote these accumulators:
+                    // 32 wait states before the LDS writes read them)
+                    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+                    for (int cb = 0; cb < NCB; cb++) {
+                        acc_to_lds(resc_lds, o[h][cb]);
+                        f32x4 v = resc[w][l];
+                        v *= al;
+                        resc[w][l] = v;
+                        lds_wait_all();
+                        acc_from_lds(resc_lds, o[h][cb]);
+                    }
+                }
+            }
+        }
+    };
+    // O^T += V^T P^T over tile `buf`: each value operand (two transposing reads)
+    // serves both head blocks
+    auto pv = [&](const uint8_t* buf, const bf16x8 (&pk)[2]) {
+        constexpr int VD = 4;
+        auto vread = [&](int cb) -> bf16x8 {
+            const u32x2 a = ds_read_tr16_c(buf + vbase + 1024 * cb);
+            const u32x2 bb = ds_read_tr16_c(buf + vbase + 1024 * cb + 512);
+            return as_bf16x8(u32x4{a[0], a[1], bb[0], bb[1]});
+        };
+        bf16x8 vb[VD];
+#pragma unroll
+        for (int i = 0; i < VD; i++) vb[i] = vread(i);
+#pragma unroll
+        for (int cb = 0; cb < NCB; cb++) {
+            const bf16x8 v = vb[cb % VD];
+            if (cb + VD < NCB) vb[cb % VD] = vread(cb + VD);
+            mfma16_pv_acc(o[0][cb], v, pk[0]);
+            mfma16_pv_acc(o[1][cb], v, pk[1]);
+        }
+    };
+
+    if (ntiles > 0) {
+        // Q K^T of tile t+1 goes out before the softmax of tile t, so that the
+        // matrix cores work through it while the softmax runs
+        issue(0);
+        if (ntiles > 1) issue(1);
+        if (ntiles > 2) issue(2);
+        if (ntiles > 2) wait_vmcnt_mem<2 * kWideCP>();
+        else if (ntiles > 1) wait_vmcnt_mem<kWideCP>();
+        else wait_vmcnt_mem<0>();
+        lds_barrier();
+        float x[2][2][4];
+        {
+            f32x4 s[2][2];
+            qk(ring[0], s);
+            prep(0, s, x);
+        }
+        for (int t = 0; t < ntiles; t++) {
+            // tile t+1 has landed (tile t+2's copies may still be in flight),
+            // the slot of tile t-1 is free
+            if (t + 2 < ntiles) wait_vmcnt_mem<kWideCP>();
+            else wait_vmcnt_mem<0>();
+            lds_barrier();
+            if (t + 3 < ntiles) issue(t + 3);
+            // No branch from here to the end of P V: one scheduling region in
+            // which the exponentials of tile t sit between the MFMAs of the next
+            // tile's Q K^T. (In the last iteration that Q K^T reads a slot of
+            // stale rows and its result is not used.)
+            f32x4 sn[2][2];
+            bf16x8 pk[2];
+            qk(ring[(t + 1) & 3], sn, x, pk);
+            p_settle(pk);
+            pv(ring[t & 3], pk);
+            if (t + 1 < ntiles) prep(t + 1, sn, x);
+        }
+    }
+    wait_vmcnt<0>();
+
+    // ---- finalize: each head block's accumulators through this wave's part of
+    // the (now free) ring: 32 blocks x 1 KB, normalized on the way out
+    __syncthreads();
+    // the last P V MFMAs are read by the LDS writes below: 32 wait states first
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    f32x4* stage = reinterpret_cast<f32x4*>(&ring[0][0]) + w * (NCB * kWave);
+    const uint32_t stage_lds = (uint32_t)(uintptr_t)(SIA_LDS f32x4*)stage;
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+        float lt = l_run[h];
+        lt += __shfl_xor(lt, 16);
+        lt += __shfl_xor(lt, 32);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NCB; cb++) acc_to_lds(stage_lds + (cb * kWave + l) * 16, o[h][cb]);
+        lds_wait_all();
+        const int64_t head = head0 + 16 * h + jl;
+        if (A.n_split > 1) {
+            float* dst = A.part_o + (((int64_t)j * A.n_split + sp) * A.heads + head) * kDV + 4 * g;
+#pragma unroll
+            for (int cb = 0; cb < NCB; cb++) *reinterpret_cast<f32x4*>(dst + cb * 16) = stage[cb * kWave + l] * inv;
+        } else {
+            uint16_t* dst = A.out + ((int64_t)j * A.heads + head) * kDV + 4 * g;
+#pragma unroll
+            for (int cb = 0; cb < NCB; cb++) {
+                const f32x4 v = stage[cb * kWave + l] * inv;
+                *reinterpret_cast<u32x2*>(dst + cb * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            }
+        }
+        // (the next block's writes reuse the stage only after these reads)
+        lds_wait_all();
+        if (g == 0) {
+            const float lse = lt > 0.f ? (m_ref[h] + log2f(lt)) * 0.6931471805599453f : -INFINITY;
+            if (A.n_split > 1)
+                A.part_lse[((int64_t)j * A.n_split + sp) * A.heads + head] = lse;
+            else if (A.lse)
+                A.lse[(int64_t)j * A.heads + head] = lse;
+        }
+    }
+}
+
 // Merge of the row slices of one (query, head) by log-sum-exp.
 __global__ __launch_bounds__(128) void mla_combine_kernel(AttnArgs A) {
     const int64_t jh = blockIdx.x;            // query * heads + head
@@ -1263,6 +1609,12 @@ static hipError_t mla_wave_launch(const AttnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_sparse_mla(const AttnArgs& a, hipStream_t st) {
+    if (a.wave_heads == 3 && !a.kv8 && a.heads_per_block == kWideHB) {
+        const int64_t pairs = (int64_t)a.num_q * a.n_split;
+        const int64_t blocks = (pairs + 7) / 8 * 8 * (a.heads / kWideHB);
+        hipLaunchKernelGGL(sparse_mla_wide_kernel, dim3((unsigned)blocks), dim3(kWideNW * kWave), 0, st, a);
+        return hipGetLastError();
+    }
     if (a.wave_heads && !a.kv8) {
         switch (a.heads_per_block * 4 + a.wave_heads) {
             case 128 * 4 + 1: return mla_wave_launch<8, 1>(a, st);

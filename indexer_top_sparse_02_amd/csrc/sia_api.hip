@@ -688,6 +688,7 @@ int mla_run(const sia_page_table* pt, const sia_paged_cache* kv, const sia_queri
     // rows: the row-split kernel, at most 64 heads per workgroup
     a.wave_heads = !a.kv8 && hb >= 32 && env_int("SIA_ATTN_WAVE", 1) ? 1 : 0;
     if (a.wave_heads && hb <= 64 && env_int("SIA_ATTN_RH", 1) == 2) a.wave_heads = 2;
+    if (a.wave_heads && hb == 128 && env_int("SIA_ATTN_WIDE", 1)) a.wave_heads = 3;
     a.heads_per_block = a.kv8 ? std::min(hb, 64) : hb;
     a.out = static_cast<uint16_t*>(out);
     a.lse = lse;

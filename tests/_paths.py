@@ -28,12 +28,14 @@ ATTN_TOL = 2e-2   # relative L2 error of each (query, head) output row
 # through its environment: the row-split kernel (two waves per 16 heads, P
 # exchanged through LDS) and the whole-tile kernel with 64 or 128 heads per
 # workgroup (one wave per 16 heads over all rows of a tile), or with 64 heads
-# and two waves per 16 heads, one per half of each 64-row tile.
+# and two waves per 16 heads, one per half of each 64-row tile, or with 128
+# heads in four waves of 32.
 ATTN_KERNELS = {
-    "rowsplit": dict(SIA_ATTN_WAVE=0, SIA_ATTN_RH=1),
-    "wave64": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=64, SIA_ATTN_RH=1),
-    "wave128": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=128, SIA_ATTN_RH=1),
-    "wave64x2": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=64, SIA_ATTN_RH=2),
+    "rowsplit": dict(SIA_ATTN_WAVE=0, SIA_ATTN_RH=1, SIA_ATTN_WIDE=0),
+    "wave64": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=64, SIA_ATTN_RH=1, SIA_ATTN_WIDE=0),
+    "wave128": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=128, SIA_ATTN_RH=1, SIA_ATTN_WIDE=0),
+    "wave64x2": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=64, SIA_ATTN_RH=2, SIA_ATTN_WIDE=0),
+    "wide128": dict(SIA_ATTN_WAVE=1, SIA_ATTN_HB=128, SIA_ATTN_RH=1, SIA_ATTN_WIDE=1),
 }
 
 
