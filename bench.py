@@ -476,7 +476,7 @@ def prefill_line(wl, s, steps, warmup, cpu=True):
                                    attention_too=False)[2]["median"]
         balance[name] = wg_balance(sia, wl, s, code)
     ti, ta = f_idx / (idx_ms * 1e-3) / 1e12, f_att / (att_ms * 1e-3) / 1e12
-    dominant = ("sparse_mla_attention call (sparse_mla_kernel)", ta, f_att, att_ms) \
+    dominant = ("sparse_mla_attention call (sparse_mla_wide_kernel: 128 heads per workgroup)", ta, f_att, att_ms) \
         if att_ms >= idx_ms else ("sparse_indexer_topk call (indexer_stream_kernel)", ti, f_idx, idx_ms)
     line = {
         "metric": METRIC, "value": wl.num_q / (ms * 1e-3), "unit": "prefill tokens/s",
@@ -533,7 +533,7 @@ def chunked_line(wl, s, steps, warmup, cpu=True):
         launches += max(la, 0)
     dominant = ("sparse_indexer_topk calls (indexer_stream_kernel)", f_i_all / (tot_i * 1e-3) / 1e12,
                 f_i_all, tot_i) if tot_i >= tot_a else \
-        ("sparse_mla_attention calls (sparse_mla_kernel)", f_a_all / (tot_a * 1e-3) / 1e12, f_a_all, tot_a)
+        ("sparse_mla_attention calls (sparse_mla_wide_kernel: 128 heads per workgroup)", f_a_all / (tot_a * 1e-3) / 1e12, f_a_all, tot_a)
     line = {
         "metric": METRIC, "value": wl.num_q / (tot_ms * 1e-3), "unit": "prefill tokens/s",
         "ms_per_step": tot_ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
