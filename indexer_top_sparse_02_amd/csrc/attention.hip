@@ -991,9 +991,20 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
     // vbase + 1024 cb + 512 e
     const int vbase = (4 * g + (jl >> 2)) * 32 + ((jl >> 1) & 1) * 16 + 8 * (jl & 1);
 
+    const float scale_log2 = A.sm_scale * 1.4426950408889634f;
+    constexpr float kLazyMax = 8.f;
+    // reference maximum of head jl and the running sum over this lane's rows;
+    // the finite start keeps exp2 of a masked logit at 0 in a wave that has not
+    // met a valid row yet (a row half can start with an empty sub-tile)
+    float m_ref = -1e30f, l_run = 0.f;
+
     // S^T of sub-tile `buf` for the wave's heads: s[rb] register r = logit of
-    // sub-tile row 16 rb + 4 g + r and head jl
-    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2]) {
+    // sub-tile row 16 rb + 4 g + r and head jl. With xe/pk given, step st < 8
+    // also computes exponential st of the previous tile's prepared logits (row
+    // block st / 4, register st % 4), so that they run beside the MFMAs, and the
+    // loop's end packs them into P^T.
+    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2], const float (*xe)[4] = nullptr, bf16x8* pk = nullptr) {
+        float pe[2][4];
         constexpr int DEPTH = GM::QA ? 3 : 2;   // steps whose key operands are in flight
         auto kread = [&](int st, int rb) -> bf16x8 {
             return as_bf16x8(*reinterpret_cast<const u32x4*>(buf + kbase + st * 2048 + rb * 512));
@@ -1024,15 +1035,17 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 s[0] = mfma16(k0, qb[st], st == 0 ? z : s[0]);
                 s[1] = mfma16(k1, qb[st], st == 0 ? z : s[1]);
             }
+            if (xe != nullptr && st < 8) {
+                const int rb = st >> 2, r = st & 3;
+                pe[rb][r] = __builtin_amdgcn_exp2f(xe[rb][r] - m_ref);
+                l_run += pe[rb][r];
+            }
         }
+        if (xe != nullptr)
+            *pk = as_bf16x8(u32x4{pack_bf16x2(pe[0][0], pe[0][1]), pack_bf16x2(pe[0][2], pe[0][3]),
+                                  pack_bf16x2(pe[1][0], pe[1][1]), pack_bf16x2(pe[1][2], pe[1][3])});
     };
 
-    const float scale_log2 = A.sm_scale * 1.4426950408889634f;
-    constexpr float kLazyMax = 8.f;
-    // reference maximum of head jl and the running sum over this lane's rows;
-    // the finite start keeps exp2 of a masked logit at 0 in a wave that has not
-    // met a valid row yet (a row half can start with an empty sub-tile)
-    float m_ref = -1e30f, l_run = 0.f;
     f32x4 o[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; cb++) o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1082,6 +1095,40 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                                pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])});
     };
 
+    // Logits of the wave's sub-tile of tile t, scaled to log2 units and masked
+    // past the slice (x[rb][r]); moves the reference where a logit exceeds it by
+    // more than kLazyMax, rescaling O and the sum.
+    auto prep = [&](int t, const f32x4 (&s)[2], float (&x)[2][4]) {
+        bool over = false;
+#pragma unroll
+        for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const bool valid = t * TR + 32 * rh + rb * 16 + 4 * g + r < nr;
+                x[rb][r] = valid ? s[rb][r] * scale_log2 : -INFINITY;
+                over |= x[rb][r] > m_ref + kLazyMax;
+            }
+        if (__builtin_amdgcn_readfirstlane(__ballot(over) != 0ull ? 1 : 0)) {
+            float tm = x[0][0];
+#pragma unroll
+            for (int rb = 0; rb < 2; rb++)
+#pragma unroll
+                for (int r = 0; r < 4; r++) tm = __builtin_fmaxf(tm, x[rb][r]);
+            tm = __builtin_fmaxf(tm, __shfl_xor(tm, 16));
+            tm = __builtin_fmaxf(tm, __shfl_xor(tm, 32));
+            const bool mv = tm > m_ref + kLazyMax;
+            const float al = mv ? __builtin_amdgcn_exp2f(m_ref - tm) : 1.f;
+            m_ref = mv ? tm : m_ref;
+            l_run *= al;
+            if (__builtin_amdgcn_readfirstlane(__ballot(mv) != 0ull ? 1 : 0)) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; cb++)
+#pragma unroll
+                    for (int r = 0; r < 4; r++) o[cb][r] *= al;
+            }
+        }
+    };
+
     // O^T += V^T P^T over sub-tile `buf`: column block cb takes two transposing
     // reads (rows 4 g .., 16 + 4 g ..: its eight k slots, in P's order); the
     // reads of the next VD blocks are in flight during each MFMA
@@ -1114,9 +1161,13 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
             else if (ntiles > 1) wait_vmcnt_mem<CPMAX>();
             else wait_vmcnt_mem<0>();
             lds_barrier();
-            f32x4 s[2];
-            qk(sub_of(0), s);
-            qk_settle(s);
+            float x[2][4];
+            {
+                f32x4 s[2];
+                qk(sub_of(0), s);
+                qk_settle(s);
+                prep(0, s, x);
+            }
             for (int t = 0; t < ntiles; t++) {
                 // tile t+1 has landed (tile t+2's copies may still be in
                 // flight), the slot of tile t-1 is free
@@ -1124,15 +1175,18 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 else wait_vmcnt_mem<0>();
                 lds_barrier();
                 if (t + 3 < ntiles) issue(t + 3);
-                f32x4 sn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-                if (t + 1 < ntiles) qk(sub_of(t + 1), sn);
-                const bf16x8 pk = softmax(t, s);
+                // One branch-free block: Q K^T of tile t+1 with the exponentials
+                // of tile t between its MFMAs, then P V of tile t (in the last
+                // iteration that Q K^T reads a slot of stale rows and its result
+                // is not used). The logits of tile t+1 are prepared after P V.
+                f32x4 sn[2];
+                bf16x8 pk;
+                qk(sub_of(t + 1), sn, x, &pk);
                 pv(sub_of(t), pk);
-                // (the next tile's logits are taken over only after this
-                // tile's P V MFMAs have issued)
-                qk_settle(sn);
-                s[0] = sn[0];
-                s[1] = sn[1];
+                if (t + 1 < ntiles) {
+                    qk_settle(sn);
+                    prep(t + 1, sn, x);
+                }
             }
         } else {
             for (int t = 0; t < ntiles; t++) {
