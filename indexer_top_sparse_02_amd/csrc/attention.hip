@@ -1401,9 +1401,11 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
 
     // copies of tile t (layout as in sparse_mla_wave_kernel): copy k of wave w
     // fills block w + 4 k with chunk 2 (w + 4 k) + l % 2 of tile row l / 2
-    auto issue = [&](int t) {
+    // (the row id of a tile is read from LDS one tile ahead of its copies, so
+    // that the copies do not wait for that read)
+    auto row_of = [&](int t) -> uint32_t { return rows[min(t * kTR + (l >> 1), nr - 1)]; };
+    auto issue = [&](int t, uint32_t row) {
         uint8_t* dst = ring[t & 3];
-        const uint32_t row = rows[min(t * kTR + (l >> 1), nr - 1)];
         const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row * kRowB + 32 * w + 16 * (l & 1);
         wave_copies<0, kWideCP, 32 * kWideNW, kWideNW>(src, dst, w);
     };
@@ -1519,20 +1521,22 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
     };
     // O^T += V^T P^T over tile `buf`: each value operand (two transposing reads)
     // serves both head blocks
-    auto pv = [&](const uint8_t* buf, const bf16x8 (&pk)[2]) {
-        constexpr int VD = 4;
-        auto vread = [&](int cb) -> bf16x8 {
-            const u32x2 a = ds_read_tr16_c(buf + vbase + 1024 * cb);
-            const u32x2 bb = ds_read_tr16_c(buf + vbase + 1024 * cb + 512);
-            return as_bf16x8(u32x4{a[0], a[1], bb[0], bb[1]});
-        };
-        bf16x8 vb[VD];
+    // (the first VD value operands are read by pv_pre, before P is settled)
+    constexpr int VD = 4;
+    auto vread = [&](const uint8_t* buf, int cb) -> bf16x8 {
+        const u32x2 a = ds_read_tr16_c(buf + vbase + 1024 * cb);
+        const u32x2 bb = ds_read_tr16_c(buf + vbase + 1024 * cb + 512);
+        return as_bf16x8(u32x4{a[0], a[1], bb[0], bb[1]});
+    };
+    auto pv_pre = [&](const uint8_t* buf, bf16x8 (&vb)[VD]) {
 #pragma unroll
-        for (int i = 0; i < VD; i++) vb[i] = vread(i);
+        for (int i = 0; i < VD; i++) vb[i] = vread(buf, i);
+    };
+    auto pv = [&](const uint8_t* buf, const bf16x8 (&pk)[2], bf16x8 (&vb)[VD]) {
 #pragma unroll
         for (int cb = 0; cb < NCB; cb++) {
             const bf16x8 v = vb[cb % VD];
-            if (cb + VD < NCB) vb[cb % VD] = vread(cb + VD);
+            if (cb + VD < NCB) vb[cb % VD] = vread(buf, cb + VD);
             mfma16_pv_acc(o[0][cb], v, pk[0]);
             mfma16_pv_acc(o[1][cb], v, pk[1]);
         }
@@ -1541,9 +1545,10 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
     if (ntiles > 0) {
         // Q K^T of tile t+1 goes out before the softmax of tile t, so that the
         // matrix cores work through it while the softmax runs
-        issue(0);
-        if (ntiles > 1) issue(1);
-        if (ntiles > 2) issue(2);
+        issue(0, row_of(0));
+        if (ntiles > 1) issue(1, row_of(1));
+        if (ntiles > 2) issue(2, row_of(2));
+        uint32_t row_next = row_of(3);
         if (ntiles > 2) wait_vmcnt_mem<2 * kWideCP>();
         else if (ntiles > 1) wait_vmcnt_mem<kWideCP>();
         else wait_vmcnt_mem<0>();
@@ -1560,7 +1565,10 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
             if (t + 2 < ntiles) wait_vmcnt_mem<kWideCP>();
             else wait_vmcnt_mem<0>();
             lds_barrier();
-            if (t + 3 < ntiles) issue(t + 3);
+            if (t + 3 < ntiles) {
+                issue(t + 3, row_next);
+                row_next = row_of(t + 4);
+            }
             // No branch from here to the end of P V: one scheduling region in
             // which the exponentials of tile t sit between the MFMAs of the next
             // tile's Q K^T. (In the last iteration that Q K^T reads a slot of
@@ -1568,8 +1576,10 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
             f32x4 sn[2][2];
             bf16x8 pk[2];
             qk(ring[(t + 1) & 3], sn, x, pk);
+            bf16x8 vb[VD];
+            pv_pre(ring[t & 3], vb);
             p_settle(pk);
-            pv(ring[t & 3], pk);
+            pv(ring[t & 3], pk, vb);
             if (t + 1 < ntiles) prep(t + 1, sn, x);
         }
     }
