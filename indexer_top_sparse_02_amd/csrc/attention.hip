@@ -970,9 +970,11 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
     // sub-tile rh: lane l takes chunk 2 i + l % 2 of row 32 rh + l / 2 (rows past
     // the slice repeat its last row). A wave with one copy fewer repeats its
     // last one, so that every wave issues CPMAX copies per tile.
-    auto issue = [&](int t) {
+    // (the row id of a tile is read from LDS one tile ahead of its copies, so
+    // that the copies do not wait for that read)
+    auto row_of = [&](int t) -> uint32_t { return rows[min(t * TR + 32 * rh + (l >> 1), nr - 1)]; };
+    auto issue = [&](int t, uint32_t row) {
         uint8_t* dst = sub_of(t);
-        const uint32_t row = rows[min(t * TR + 32 * rh + (l >> 1), nr - 1)];
         const uint8_t* src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row * kRowB + 32 * hb + 16 * (l & 1);
         constexpr int STEP = 32 * NHB;   // source bytes between a wave's copies
         wave_copies<0, GM::CP_LO, STEP, NHB>(src, dst, hb);
@@ -1155,7 +1157,8 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
         // "at most CPMAX copies per later tile still outstanding"
 #pragma unroll
         for (int t = 0; t < AHEAD; t++)
-            if (t < ntiles) issue(t);
+            if (t < ntiles) issue(t, row_of(t));
+        uint32_t row_next = row_of(AHEAD);
         if constexpr (GM::PIPE) {
             if (ntiles > 2) wait_vmcnt_mem<2 * CPMAX>();
             else if (ntiles > 1) wait_vmcnt_mem<CPMAX>();
@@ -1174,7 +1177,10 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 if (t + 2 < ntiles) wait_vmcnt_mem<CPMAX>();
                 else wait_vmcnt_mem<0>();
                 lds_barrier();
-                if (t + 3 < ntiles) issue(t + 3);
+                if (t + 3 < ntiles) {
+                    issue(t + 3, row_next);
+                    row_next = row_of(t + 4);
+                }
                 // One branch-free block: Q K^T of tile t+1 with the exponentials
                 // of tile t between its MFMAs, then P V of tile t (in the last
                 // iteration that Q K^T reads a slot of stale rows and its result
@@ -1196,7 +1202,10 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 else if (AHEAD > 1 && t + 1 < ntiles) wait_vmcnt_mem<(AHEAD > 1 ? 1 : 0) * CPMAX>();
                 else wait_vmcnt_mem<0>();
                 lds_barrier();
-                if (t + AHEAD < ntiles) issue(t + AHEAD);
+                if (t + AHEAD < ntiles) {
+                    issue(t + AHEAD, row_next);
+                    row_next = row_of(t + AHEAD + 1);
+                }
                 f32x4 s[2];
                 qk(sub_of(t), s);
                 qk_settle(s);
