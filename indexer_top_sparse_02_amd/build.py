@@ -33,12 +33,14 @@ FLAGS = [
 ]
 
 
-# Per-file code generation options. attention.hip: MFMA results of the
-# compiler's own MFMAs in vector registers (its default once a kernel uses
-# accumulation registers, as the whole-tile attention kernel does for its query
-# operand, is to put them in accumulation registers and copy them back and
-# forth around the vector arithmetic on them).
-FILE_FLAGS: dict = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file code generation options: MFMA results in vector registers. The
+# compiler's default for a kernel that needs more than 256 registers, or that
+# uses accumulation registers itself (the whole-tile attention kernel holds its
+# query operand there), is to put MFMA results in accumulation registers and
+# copy them back and forth around the vector arithmetic on them (the causal
+# prefill indexer's head sums, the attention softmax).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS: dict = {"attention.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM}
 
 
 def _compile(src: str) -> str:

@@ -479,14 +479,15 @@ struct EmitFinalBuf {
 // Select the top min(m_cap, cnt) of keys[0..n) and emit them in index order;
 // cnt = the number of nonzero keys, known to the caller.
 template <int NT, typename Emit>
-__device__ int select_emit(const uint32_t* keys, int n, int cnt, int m_cap, SelScratch* s, Emit&& emit) {
+__device__ int select_emit(const uint32_t* keys, int n, int cnt, int m_cap, SelScratch* s, Emit&& emit,
+                           uint32_t* spare = nullptr) {
     const int m = min(m_cap, cnt);
     if (m <= 0) return 0;
     if (m == cnt) {
         ordered_compact<NT>(keys, n, 0u, 0, s, emit);   // every nonzero key
     } else {
         int ties;
-        const uint32_t T = radix_threshold<NT>(keys, n, m, s, ties);
+        const uint32_t T = radix_threshold<NT>(keys, n, m, s, ties, spare);
         ordered_compact<NT>(keys, n, T, ties, s, emit);
     }
     return m;
@@ -1271,11 +1272,24 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
 
 // ------------------------------------------------------------ stream kernel
 
+// A wave's candidate buffer: keys and positions in the workspace (global
+// memory, cap entries each plus one spare entry per lane for the branch-free
+// append), its selection scratch and the 64 spare counters of the selection's
+// branch-free histogram adds in LDS.
 struct WaveBuf {
     uint32_t* key;
     int32_t* pos;
     SelScratch* sel;
+    uint32_t* spare;
 };
+
+// Orders a wave's global stores to its candidate buffer before its later loads
+// of the buffer in other lanes (all lanes of a wave run on one CU, whose L1 the
+// stores write through).
+__device__ __forceinline__ void buffer_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // Geometry of the K ring the four waves of a stream workgroup share: every
 // 32-position tile of index-K is copied once from global memory into LDS and
@@ -1380,16 +1394,16 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             B.pos[at] = p;
             cnt += __popcll(mask);
         };
+        uint32_t* const spare = B.spare;
         // re-selects inside the buffer once it may not take another tile
         auto reselect = [&]() {
             if (cnt > S.cap - 32) {
                 // keep the Top-K seen so far (or a superset of it); later keys
                 // equal to the new threshold lose to the kept ones
-                wave_sync();
                 int ties;
                 const int n4 = (cnt + 3) & ~3;
                 for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
-                wave_sync();
+                buffer_fence();
                 // After the first re-selection the buffered keys lie close
                 // together, and a superset of the Top-K is usually enough: every
                 // key >= L, L found in one histogram pass, with later keys appended
@@ -1402,7 +1416,7 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
                 int above = 0, low = 32;
                 if (tau != 0u) {
                     int kept;
-                    const uint32_t L = wave_select_floor(B.key, n4, S.topk, B.sel, kept, pm, above, low);
+                    const uint32_t L = wave_select_floor(B.key, n4, S.topk, B.sel, kept, pm, above, low, spare);
                     if (L != 0u && kept <= S.topk + (S.cap - S.topk) / 2) {
                         ordered_compact<kWave, true>(B.key, n4, L, 0x7fffffff, B.sel, EmitInPlace{B.key, B.pos, {}});
                         cnt = kept;
@@ -1414,12 +1428,12 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
                 if (!done) {
                     // exact: the bits under pm are settled (none on the first
                     // re-selection), the rest is refined
-                    T = radix_refine<kWave>(B.key, n4, T, pm, S.topk - above, low, B.sel, ties);
+                    T = radix_refine<kWave>(B.key, n4, T, pm, S.topk - above, low, B.sel, ties, spare);
                     ordered_compact<kWave, true>(B.key, n4, T, ties, B.sel, EmitInPlace{B.key, B.pos, {}});
                     cnt = S.topk;
                     tau = T;
                 }
-                wave_sync();
+                buffer_fence();
             }
         };
         constexpr int NMFMA = MB * mfmas_per_block<D, KF>();   // MFMAs per tile
@@ -1481,13 +1495,12 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
     if (live) {
         int32_t* oi = S.out_idx + (int64_t)j * S.topk;
         float* os = S.out_score ? S.out_score + (int64_t)j * S.topk : nullptr;
-        wave_sync();
         const int n4 = (cnt + 3) & ~3;
         for (int i = cnt + l; i < n4; i += kWave) B.key[i] = 0u;
-        wave_sync();
+        buffer_fence();
         // (the buffer's first cnt entries are its nonzero keys: only keys above
         // tau >= 0 are appended, and the re-selections keep nonzero keys)
-        const int m = select_emit<kWave>(B.key, n4, cnt, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}});
+        const int m = select_emit<kWave>(B.key, n4, cnt, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}}, B.spare);
         for (int r = m + l; r < S.topk; r += kWave) {
             oi[r] = -1;
             if (os) os[r] = -INFINITY;
@@ -1496,32 +1509,34 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
     }
 }
 
-// a wave's candidate keys and positions (cap entries each, plus one spare entry
-// per lane for the branch-free append) and its selection scratch
-__host__ __device__ inline size_t stream_wave_bytes(int cap) {
-    return (size_t)(cap + kWave) * 8 + sizeof(SelScratch);
+// LDS of a stream workgroup: the K ring (at 0), the staged page ids of the
+// longest row, then per wave its selection scratch and 64 spare counters.
+struct StreamSel {
+    SelScratch sel;
+    uint32_t spare[kWave];
+};
+__host__ __device__ inline size_t stream_sel_offset(int max_visible, int dim, bool fp8) {
+    const size_t pages_end = stream_ring_bytes(dim, fp8) + (size_t)(max_visible + kPage - 1) / kPage * 4;
+    return (pages_end + 15) / 16 * 16;
 }
-__host__ __device__ inline size_t stream_pages_offset(int cap) { return 4 * stream_wave_bytes(cap); }
-__host__ __device__ inline size_t stream_ring_offset(int cap, int max_visible) {
-    const size_t pages_end = stream_pages_offset(cap) + (size_t)(max_visible + kPage - 1) / kPage * 4;
-    return (pages_end + 255) / 256 * 256;
-}
-__host__ __device__ inline size_t stream_smem_bytes(int cap, int max_visible, int dim, bool fp8) {
-    return stream_ring_offset(cap, max_visible) + stream_ring_bytes(dim, fp8);
+__host__ __device__ inline size_t stream_smem_bytes(int max_visible, int dim, bool fp8) {
+    return stream_sel_offset(max_visible, dim, fp8) + 4 * sizeof(StreamSel);
 }
 
+// Two workgroups per CU (256 registers per wave): while one selects inside its
+// candidate buffers, the other's MFMAs and vector work keep the SIMDs busy.
 template <int MB, int D, int KF>
-__global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs A, StreamArgs S) {
+__global__ __launch_bounds__(kStreamThreads, 2) void indexer_stream_kernel(IdxArgs A, StreamArgs S) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int next_tile;
     __shared__ int tile_seq, tile_rows;
     constexpr int QPT = kStreamThreads / kWave;   // queries per tile, one per wave
     const int w = threadIdx.x / kWave;
-    uint8_t* base = smem + w * stream_wave_bytes(S.cap);
-    WaveBuf B{reinterpret_cast<uint32_t*>(base), reinterpret_cast<int32_t*>(base + (size_t)(S.cap + kWave) * 4),
-              reinterpret_cast<SelScratch*>(base + (size_t)(S.cap + kWave) * 8)};
-    int* pages = reinterpret_cast<int*>(smem + stream_pages_offset(S.cap));
-    uint8_t* ring = smem + stream_ring_offset(S.cap, A.max_visible);
+    StreamSel* ss = reinterpret_cast<StreamSel*>(smem + stream_sel_offset(A.max_visible, D, KF != kRowBf16)) + w;
+    uint32_t* gb = S.buf + ((int64_t)blockIdx.x * QPT + w) * 2 * (S.cap + kWave);
+    WaveBuf B{gb, reinterpret_cast<int32_t*>(gb + S.cap + kWave), &ss->sel, ss->spare};
+    int* pages = reinterpret_cast<int*>(smem + stream_ring_bytes(D, KF != kRowBf16));
+    uint8_t* ring = smem;
     // optional trace: where (hardware ids of the CU) and when (100 MHz clock)
     // this workgroup ran, and how many query tiles it took
     const uint64_t t_start = S.trace ? __builtin_amdgcn_s_memrealtime() : 0;
@@ -1553,21 +1568,22 @@ __global__ __launch_bounds__(kStreamThreads) void indexer_stream_kernel(IdxArgs 
         __syncthreads();
         tiles_run++;
     };
-    if (S.sched == 0) {
-        run_tile(blockIdx.x);
-    } else if (S.sched == 2) {
-        const int t0 = zigzag_shard(S.n_tiles, blockIdx.x, 0);
-        const int t1 = zigzag_shard(S.n_tiles, blockIdx.x, 1);
-        if (t1 >= 0) run_tile(t1);   // heavier one first
-        if (t0 >= 0) run_tile(t0);
-    } else {
-        for (;;) {
-            if (threadIdx.x == 0) next_tile = (int)atomicAdd(S.counter, 1u);
-            __syncthreads();
-            const int n = next_tile;
-            __syncthreads();
-            if (n >= S.n_tiles) break;
-            run_tile(heavy_first_tile(S.n_tiles, n));
+    // Persistent workgroups (their number sized so that all are resident) take
+    // work items from a counter: naive = tiles in index order, heavy-first =
+    // tiles from the last, zigzag = the pairs (i, T-1-i), heavier tile first.
+    const int n_items = S.sched == 2 ? zigzag_workers(S.n_tiles) : S.n_tiles;
+    for (;;) {
+        if (threadIdx.x == 0) next_tile = (int)atomicAdd(S.counter, 1u);
+        __syncthreads();
+        const int n = next_tile;
+        __syncthreads();
+        if (n >= n_items) break;
+        const int ta = S.sched == 0 ? n : S.sched == 2 ? zigzag_shard(S.n_tiles, n, 1) : heavy_first_tile(S.n_tiles, n);
+        const int tb = S.sched == 2 ? zigzag_shard(S.n_tiles, n, 0) : -1;
+#pragma unroll 1
+        for (int r = 0; r < 2; r++) {
+            const int t = r == 0 ? ta : tb;
+            if (t >= 0) run_tile(t);
         }
     }
     if (S.trace && threadIdx.x == 0 && (int)blockIdx.x < S.trace_cap) {
@@ -1689,7 +1705,7 @@ hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st) {
 template <int MB, int D, int KF>
 static hipError_t stream_launch(const IdxArgs& a, const StreamArgs& s, int grid, hipStream_t st) {
     auto k = indexer_stream_kernel<MB, D, KF>;
-    const size_t smem = stream_smem_bytes(s.cap, a.max_visible, D, KF != kRowBf16);
+    const size_t smem = stream_smem_bytes(a.max_visible, D, KF != kRowBf16);
     hipError_t e = set_smem(k, smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kStreamThreads), smem, st, a, s);
@@ -1697,9 +1713,9 @@ static hipError_t stream_launch(const IdxArgs& a, const StreamArgs& s, int grid,
 }
 
 template <int MB, int D, int KF>
-static int stream_occupancy(int cap, int max_visible) {
+static int stream_occupancy(int max_visible) {
     auto k = indexer_stream_kernel<MB, D, KF>;
-    const size_t smem = stream_smem_bytes(cap, max_visible, D, KF != kRowBf16);
+    const size_t smem = stream_smem_bytes(max_visible, D, KF != kRowBf16);
     if (set_smem(k, smem) != hipSuccess) return 1;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(k),
@@ -1720,13 +1736,13 @@ hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, 
     return hipErrorInvalidValue;
 }
 
-size_t indexer_stream_smem(int cap, int max_visible, int dim, bool fp8) {
-    return stream_smem_bytes(cap, max_visible, dim, fp8);
+size_t indexer_stream_smem(int max_visible, int dim, bool fp8) {
+    return stream_smem_bytes(max_visible, dim, fp8);
 }
 
-int indexer_stream_blocks_per_cu(int mb, int dim, int kf, int cap, int max_visible) {
+int indexer_stream_blocks_per_cu(int mb, int dim, int kf, int max_visible) {
 #define SIA_OCC(MBv, Dv, KFv) \
-    if (mb == MBv && dim == Dv && kf == KFv) return stream_occupancy<MBv, Dv, KFv>(cap, max_visible);
+    if (mb == MBv && dim == Dv && kf == KFv) return stream_occupancy<MBv, Dv, KFv>(max_visible);
 #define SIA_OCC_KF(MBv, Dv) SIA_OCC(MBv, Dv, kRowBf16) SIA_OCC(MBv, Dv, kRowFp8)
     SIA_OCC_KF(1, 64) SIA_OCC_KF(1, 128) SIA_OCC_KF(2, 64) SIA_OCC_KF(2, 128)
     SIA_OCC(1, 128, kRowMx) SIA_OCC(2, 128, kRowMx)

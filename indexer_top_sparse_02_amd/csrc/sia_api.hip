@@ -109,6 +109,7 @@ struct IndexerPlan {
     int n_reg = 0;               // candidate regions per query
     int64_t ld = 0;              // row stride of the candidate and key rows
     size_t keys = 0, ckey = 0, cpos = 0, hist = 0, reg = 0, rlen = 0;   // workspace offsets
+    size_t sbuf = 0;             // stream candidate buffers
     int cap = 0;                 // stream buffer capacity
     size_t total = kHeader;
 };
@@ -158,19 +159,17 @@ IndexerPlan plan_indexer(const sia_queries* qs, int topk, int heads, int dim, bo
     bool stream = stream_ok && qs->num_q >= 256 && qs->max_visible > 2 * topk;
     if (mode == 1) stream = false;
     if (mode == 2) stream = stream_ok;
-    if (stream) {
-        // the candidate buffers, the staged page ids and the K ring must fit in
-        // LDS: the buffers shrink (down to K + 256 keys, which only makes the
-        // in-buffer re-selection more frequent) until they do
-        int cap = std::min(4096, std::max(1024, 2 * topk));
-        const int cap_min = std::max(1024, (topk + 256 + 63) / 64 * 64);
-        while (cap > cap_min && sia::indexer_stream_smem(cap, qs->max_visible, dim, eight_bit) + 64 > sia::kMaxLds)
-            cap = std::max(cap_min, cap - 256);
-        if (sia::indexer_stream_smem(cap, qs->max_visible, dim, eight_bit) + 64 <= sia::kMaxLds) {
-            p.stream = true;
-            p.cap = cap;
-            return p;
-        }
+    if (stream && sia::indexer_stream_smem(qs->max_visible, dim, eight_bit) + 64 <= sia::kMaxLds) {
+        // LDS holds the K ring, the staged page ids and the selection scratch;
+        // each wave of the persistent grid (at most kStreamBlocksPerCu
+        // workgroups per CU) has a candidate buffer of cap keys and positions
+        // (+ a spare entry per lane) in the workspace
+        p.stream = true;
+        p.cap = std::min(4096, std::max(1024, 2 * topk));
+        const int64_t waves = (int64_t)sia::kStreamBlocksPerCu * device_cus() * (sia::kStreamThreads / 64);
+        p.sbuf = p.total;
+        p.total += align_up((size_t)waves * 2 * (p.cap + 64) * 4);
+        return p;
     }
     (void)heads;
     const int g = score_group(qs);
@@ -274,18 +273,18 @@ int indexer_topk(const sia_page_table* pt, const sia_paged_cache* index_k, const
         s.sched = sched < 0 ? env_int("SIA_SCHED", 1) : sched;
         if (s.sched < 0 || s.sched > 2) s.sched = 1;
         s.counter = reinterpret_cast<uint32_t*>(ws + 4);
+        s.buf = reinterpret_cast<uint32_t*>(ws + p.sbuf);
         s.out_idx = out_idx;
         s.out_score = out_score;
         s.trace = trace;
         s.trace_cap = trace ? trace_cap : 0;
-        int grid = s.n_tiles;
-        if (s.sched == 2) grid = sia::zigzag_workers(s.n_tiles);
-        if (s.sched == 1) {
-            e = sia::launch_fill_u32(s.counter, 0u, 1, st);
-            if (e != hipSuccess) return hip_fail(e, "counter reset");
-            const int occ = sia::indexer_stream_blocks_per_cu(mb, index_k->dim, kf, p.cap, qs->max_visible);
-            grid = std::min<int64_t>(s.n_tiles, (int64_t)occ * device_cus());
-        }
+        // persistent workgroups, all resident, pulling work items from the counter
+        e = sia::launch_fill_u32(s.counter, 0u, 1, st);
+        if (e != hipSuccess) return hip_fail(e, "counter reset");
+        const int items = s.sched == 2 ? sia::zigzag_workers(s.n_tiles) : s.n_tiles;
+        const int occ = std::min(sia::kStreamBlocksPerCu,
+                                 sia::indexer_stream_blocks_per_cu(mb, index_k->dim, kf, qs->max_visible));
+        const int grid = (int)std::min<int64_t>(items, (int64_t)occ * device_cus());
         e = sia::launch_indexer_stream(a, s, mb, index_k->dim, kf, grid, st);
         if (e != hipSuccess) return hip_fail(e, "indexer stream launch");
         return SIA_OK;

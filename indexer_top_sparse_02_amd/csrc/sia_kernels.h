@@ -85,6 +85,7 @@ struct SelectArgs {
 struct StreamArgs {
     int32_t topk, cap, n_tiles, sched;
     uint32_t* counter;
+    uint32_t* buf;             // candidate buffers: 2 * (cap + 64) words per wave of the grid
     int32_t* out_idx;
     float* out_score;
     uint64_t* trace;           // optional [trace_cap, 4] per-workgroup records (or null)
@@ -99,8 +100,9 @@ hipError_t launch_keys_from_scores(const KeysFromScoresArgs& k, hipStream_t st);
 hipError_t launch_topk_rows(const SelectArgs& s, hipStream_t st);
 hipError_t launch_indexer_stream(const IdxArgs& a, const StreamArgs& s, int mb, int dim, int kf,
                                  int grid, hipStream_t st);
-int indexer_stream_blocks_per_cu(int mb, int dim, int kf, int cap, int max_visible);
-size_t indexer_stream_smem(int cap, int max_visible, int dim, bool fp8);
+int indexer_stream_blocks_per_cu(int mb, int dim, int kf, int max_visible);
+size_t indexer_stream_smem(int max_visible, int dim, bool fp8);
+constexpr int kStreamBlocksPerCu = 2;   // (the kernel's launch bound)
 constexpr size_t kMaxLds = 160 * 1024;
 constexpr int kCoarseBinsHost = 2048;   // = kCoarseBins of the selection code
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t st);

@@ -38,19 +38,29 @@ __device__ __forceinline__ int sel_tid() {
 }
 
 // hist[digit] += 1 for every active lane (LDS atomics; digits of the coarse
-// and refinement passes are spread enough that conflicts stay low).
-__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t digit, bool active) {
-    if (active) atomicAdd(&hist[digit], 1u);
+// and refinement passes are spread enough that conflicts stay low). One wave
+// (NT = 64): branch-free, an inactive lane adds to its own counter spare[lane]
+// instead (64 LDS counters the caller lends, never read), so that the adds of a
+// group of keys go out back to back with no exec-mask changes between them.
+template <int NT>
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t* spare, uint32_t digit, bool active) {
+    if constexpr (NT == kWave) atomicAdd(active ? hist + digit : spare + lane_id(), 1u);
+    else if (active) atomicAdd(&hist[digit], 1u);
 }
+
+// Keys per thread and round of the histogram passes: four 16-byte groups, read
+// before any of the round's adds.
+constexpr int kHistGroups = 4;
 
 // Step 1, refinement: the bits above `lowbit` are settled (`prefix` under
 // `pmask`) and `rem` elements matching the prefix are still to be taken. Finds
 // the remaining low bits in passes of up to 8 bits. keys: LDS, readable in
 // groups of four (16-byte aligned; entries past n may hold anything). Returns
-// T; `ties` = number of key == T elements to keep.
+// T; `ties` = number of key == T elements to keep. spare: 64 LDS counters for
+// the branch-free adds of one wave (NT = 64 only).
 template <int NT>
 __device__ uint32_t radix_refine(const uint32_t* keys, int n, uint32_t prefix, uint32_t pmask,
-                                 int rem, int lowbit, SelScratch* s, int& ties) {
+                                 int rem, int lowbit, SelScratch* s, int& ties, uint32_t* spare = nullptr) {
     const int tid = sel_tid<NT>();
     while (lowbit > 0) {
         const int width = lowbit < 8 ? lowbit : 8;
@@ -58,13 +68,21 @@ __device__ uint32_t radix_refine(const uint32_t* keys, int n, uint32_t prefix, u
         const uint32_t dmask = (1u << width) - 1u;
         for (int i = tid; i < 256; i += NT) s->hist[i] = 0;
         sel_sync<NT>();
-        for (int i = tid * 4; i < n; i += NT * 4) {
-            u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
+        for (int i0 = tid * 4; i0 < n; i0 += NT * 4 * kHistGroups) {
+            u32x4 kk[kHistGroups];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                const uint32_t k = k4[e];
-                hist_add(s->hist, (k >> shift) & dmask, i + e < n && k != 0u && (k & pmask) == prefix);
+            for (int u = 0; u < kHistGroups; u++) {
+                const int i = i0 + u * NT * 4;
+                kk[u] = i < n ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
             }
+#pragma unroll
+            for (int u = 0; u < kHistGroups; u++)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const uint32_t k = kk[u][e];
+                    hist_add<NT>(s->hist, spare, (k >> shift) & dmask,
+                                 i0 + u * NT * 4 + e < n && k != 0u && (k & pmask) == prefix);
+                }
         }
         sel_sync<NT>();
         if (tid < kWave) {
@@ -99,8 +117,9 @@ __device__ uint32_t radix_refine(const uint32_t* keys, int n, uint32_t prefix, u
 
 // Step 1 from scratch: all 32 bits.
 template <int NT>
-__device__ uint32_t radix_threshold(const uint32_t* keys, int n, int m, SelScratch* s, int& ties) {
-    return radix_refine<NT>(keys, n, 0u, 0u, m, 32, s, ties);
+__device__ uint32_t radix_threshold(const uint32_t* keys, int n, int m, SelScratch* s, int& ties,
+                                    uint32_t* spare = nullptr) {
+    return radix_refine<NT>(keys, n, 0u, 0u, m, 32, s, ties, spare);
 }
 
 // One wave, a superset of the Top-m in one histogram pass. The leading bits on
@@ -114,20 +133,28 @@ __device__ uint32_t radix_threshold(const uint32_t* keys, int n, int m, SelScrat
 // number of nonzero keys. For an exact threshold from there, `pmask_out` and
 // `above` give the settled bits and the number of keys above digit b, and `low`
 // the number of bits still open (the arguments radix_refine continues from).
+// spare: 64 LDS counters for the branch-free histogram adds.
 __device__ uint32_t wave_select_floor(const uint32_t* keys, int n, int m, SelScratch* s, int& kept,
-                                     uint32_t& pmask_out, int& above_out, int& low) {
+                                     uint32_t& pmask_out, int& above_out, int& low, uint32_t* spare) {
     const int l = lane_id();
     uint32_t a = ~0u, o = 0u;
-    for (int i = l * 4; i < n; i += kWave * 4) {
-        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
+    for (int i0 = l * 4; i0 < n; i0 += kWave * 4 * kHistGroups) {
+        u32x4 kk[kHistGroups];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const uint32_t k = k4[e];
-            if (i + e < n && k != 0u) {
-                a &= k;
-                o |= k;
-            }
+        for (int u = 0; u < kHistGroups; u++) {
+            const int i = i0 + u * kWave * 4;
+            kk[u] = i < n ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int u = 0; u < kHistGroups; u++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t k = kk[u][e];
+                if (i0 + u * kWave * 4 + e < n && k != 0u) {
+                    a &= k;
+                    o |= k;
+                }
+            }
     }
 #pragma unroll
     for (int d = kWave / 2; d >= 1; d >>= 1) {
@@ -142,13 +169,20 @@ __device__ uint32_t wave_select_floor(const uint32_t* keys, int n, int m, SelScr
     const uint32_t pmask = lead == 0 ? 0u : ~0u << (32 - lead);
     for (int i = l; i < 256; i += kWave) s->hist[i] = 0;
     wave_sync();
-    for (int i = l * 4; i < n; i += kWave * 4) {
-        const u32x4 k4 = *reinterpret_cast<const u32x4*>(keys + i);
+    for (int i0 = l * 4; i0 < n; i0 += kWave * 4 * kHistGroups) {
+        u32x4 kk[kHistGroups];
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const uint32_t k = k4[e];
-            hist_add(s->hist, (k >> shift) & dmask, i + e < n && k != 0u);
+        for (int u = 0; u < kHistGroups; u++) {
+            const int i = i0 + u * kWave * 4;
+            kk[u] = i < n ? *reinterpret_cast<const u32x4*>(keys + i) : u32x4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int u = 0; u < kHistGroups; u++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const uint32_t k = kk[u][e];
+                hist_add<kWave>(s->hist, spare, (k >> shift) & dmask, i0 + u * kWave * 4 + e < n && k != 0u);
+            }
     }
     wave_sync();
     {

@@ -30,9 +30,9 @@ STUB(hipError_t launch_proj_reduce(const float*, int, int64_t, uint16_t*, float*
 STUB(hipError_t launch_key_norm_quant(const KeyPrepArgs&, hipStream_t))
 STUB(hipError_t launch_sparse_mla(const AttnArgs&, hipStream_t))
 STUB(hipError_t launch_mla_combine(const AttnArgs&, hipStream_t))
-int indexer_stream_blocks_per_cu(int, int, int, int, int) { return 1; }
-size_t indexer_stream_smem(int cap, int max_visible, int dim, bool fp8) {
-    return (size_t)cap * 8 * 4 + (size_t)(max_visible + 63) / 64 * 4 + (size_t)dim * (fp8 ? 1 : 2) * 32 * 8;
+int indexer_stream_blocks_per_cu(int, int, int, int) { return 2; }
+size_t indexer_stream_smem(int max_visible, int dim, bool fp8) {
+    return (size_t)(max_visible + 63) / 64 * 4 + (size_t)dim * (fp8 ? 1 : 2) * 32 * 8 + 4 * 1360;
 }
 }  // namespace sia
 

@@ -1,7 +1,8 @@
 """The traced indexer entry point (per-workgroup CU ids and timestamps of the
 causal stream kernel) returns the untraced call's indices bit for bit under
 every tile schedule, and its records are complete and consistent: one per
-workgroup, ends after starts, every query tile accounted for once."""
+workgroup of the persistent grid, ends after starts, every query tile
+accounted for once."""
 import numpy as np
 import pytest
 import torch
@@ -29,7 +30,7 @@ def test_traced_stream_kernel_matches_and_records(sched):
     used = t[t[:, 2] != 0]
     assert len(used) >= 1
     assert np.all(used[:, 2] >= used[:, 1])
-    # every query tile ran exactly once over all workgroups
+    # every query tile ran exactly once over all workgroups, which are
+    # persistent (at most two per CU, each pulling tiles from a counter)
     assert int(used[:, 3].sum()) == n_tiles
-    if sched == 0:
-        assert len(used) == n_tiles and np.all(used[:, 3] == 1)
+    assert len(used) <= 2 * torch.cuda.get_device_properties(0).multi_processor_count
