@@ -1285,10 +1285,16 @@ struct WaveBuf {
 
 // Orders a wave's global stores to its candidate buffer before its later loads
 // of the buffer in other lanes (all lanes of a wave run on one CU, whose L1 the
-// stores write through).
+// stores write through), then waits for every vector memory access in flight
+// (vmcnt 0; expcnt and lgkmcnt left open) as a compiler-visible wait: the
+// compiler's own tracking then knows that nothing of the selection is pending
+// where its path joins the scoring loop again, and does not make the loop's
+// next MFMA wait for all outstanding memory accesses (the ring copies among
+// them) there.
 __device__ __forceinline__ void buffer_fence() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
 // Geometry of the K ring the four waves of a stream workgroup share: every
@@ -1389,7 +1395,7 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             const uint32_t k = score_key(sc) & (0u - (uint32_t)(l < 32 && ok));
             const bool take = k > tau;
             const uint64_t mask = __ballot(take);
-            const int at = take ? cnt + lanes_below(mask) : S.cap + l;
+            const uint32_t at = take ? (uint32_t)cnt + lanes_below(mask) : (uint32_t)(S.cap + l);
             B.key[at] = k;
             B.pos[at] = p;
             cnt += __popcll(mask);
@@ -1531,7 +1537,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void indexer_stream_kernel(IdxAr
     __shared__ int next_tile;
     __shared__ int tile_seq, tile_rows;
     constexpr int QPT = kStreamThreads / kWave;   // queries per tile, one per wave
-    const int w = threadIdx.x / kWave;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     StreamSel* ss = reinterpret_cast<StreamSel*>(smem + stream_sel_offset(A.max_visible, D, KF != kRowBf16)) + w;
     uint32_t* gb = S.buf + ((int64_t)blockIdx.x * QPT + w) * 2 * (S.cap + kWave);
     WaveBuf B{gb, reinterpret_cast<int32_t*>(gb + S.cap + kWave), &ss->sel, ss->spare};
