@@ -435,19 +435,24 @@ struct EmitFinal {
     }
 };
 
-// In-place compaction of a wave's LDS buffer: positions of the round are read
-// before any of the round's writes.
+// In-place compaction of a stream wave's candidate buffer (global memory):
+// positions of the round are read before any of the round's writes, as two
+// 16-byte groups issued together with the keys (the buffer holds cap + 64
+// entries, so the groups stay inside it), so that a round costs one memory
+// round trip.
 struct EmitInPlace {
     uint32_t* key;
     int32_t* pos;
     int32_t p4[8];
-    __device__ void prefetch(int i, u32x4 k4, uint32_t T) {
+    __device__ void prefetch(int i, u32x4, uint32_t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(pos + i);
 #pragma unroll
-        for (int e = 0; e < 4; e++) p4[e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
+        for (int e = 0; e < 4; e++) p4[e] = (int32_t)v[e];
     }
-    __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
+    __device__ void prefetch2(int i, u32x4, uint32_t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(pos + i);
 #pragma unroll
-        for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
+        for (int e = 0; e < 4; e++) p4[4 + e] = (int32_t)v[e];
     }
     __device__ void operator()(int rank, int, int e, uint32_t k) const {
         key[rank] = k;
@@ -468,6 +473,31 @@ struct EmitFinalBuf {
     __device__ void prefetch2(int i, u32x4 k4, uint32_t T) {
 #pragma unroll
         for (int e = 0; e < 4; e++) p4[4 + e] = (k4[e] != 0u && k4[e] >= T) ? pos[i + e] : 0;
+    }
+    __device__ void operator()(int rank, int, int e, uint32_t k) const {
+        if (rank >= cap) return;
+        idx[rank] = p4[e];
+        if (score) score[rank] = key_score(k);
+    }
+};
+
+// The stream kernel's final emission from a wave's candidate buffer (global
+// memory, cap + 64 entries): positions read as 16-byte groups beside the keys.
+struct EmitFinalStream {
+    const int32_t* pos;
+    int32_t* idx;
+    float* score;
+    int cap;
+    int32_t p4[8];
+    __device__ void prefetch(int i, u32x4, uint32_t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(pos + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[e] = (int32_t)v[e];
+    }
+    __device__ void prefetch2(int i, u32x4, uint32_t) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(pos + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) p4[4 + e] = (int32_t)v[e];
     }
     __device__ void operator()(int rank, int, int e, uint32_t k) const {
         if (rank >= cap) return;
@@ -1313,7 +1343,8 @@ struct StreamGeom {
     static constexpr int SLOT = TILE + ((KF != kRowBf16) ? 256 : 0);
     static constexpr int NS = TILE <= 4096 ? 8 : 4;         // ring slots
     static constexpr int RING = NS * SLOT;
-    static_assert(DMA >= 1 && NS >= 4 && (NS - 1) * PER_TILE < 64, "stream ring geometry");
+    static_assert(DMA >= 1 && NS >= 4 && (NS - 1) * PER_TILE < 64 && (NS - 4) * PER_TILE + 2 * (NS - 2) < 64,
+                  "stream ring geometry");
 };
 
 __host__ __device__ inline size_t stream_ring_bytes(int dim, bool fp8) {
@@ -1328,7 +1359,7 @@ __host__ __device__ inline size_t stream_ring_bytes(int dim, bool fp8) {
 // Called by all four waves (the ring needs one barrier per tile).
 template <int MB, int D, int KF>
 __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int rl, int rl_max,
-                             const int* pages, WaveBuf B, uint8_t* ring) {
+                             const int* pages, WaveBuf B, uint8_t* ring, int* votes) {
     using SG = StreamGeom<D, KF>;
     constexpr int NS = SG::NS, R = SG::R, NV = KTile<D, KF>::NV;
     const int l = lane_id(), half = l >> 5, frow = l & 31;
@@ -1390,6 +1421,7 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         // appends the key of position ti*32 + l (score sc, lanes 0..31) if it beats
         // tau. Branch-free: a lane that does not take writes to its own spare entry
         // past the buffer (so the MFMAs issued before it stay where they are).
+        // Exactly two global stores per step (the ring's copy waits count them).
         auto append = [&](float sc, bool ok, int ti) {
             const int p = ti * 32 + (l & 31);
             const uint32_t k = score_key(sc) & (0u - (uint32_t)(l < 32 && ok));
@@ -1401,9 +1433,11 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             cnt += __popcll(mask);
         };
         uint32_t* const spare = B.spare;
-        // re-selects inside the buffer once it may not take another tile
+        // re-selects inside the buffer (the whole workgroup does so at once, when
+        // any of its waves might not take the next two tiles; a wave that holds
+        // at most K keys has nothing to drop)
         auto reselect = [&]() {
-            if (cnt > S.cap - 32) {
+            if (cnt > S.topk) {
                 // keep the Top-K seen so far (or a superset of it); later keys
                 // equal to the new threshold lose to the kept ones
                 int ties;
@@ -1468,17 +1502,29 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         int pg_c = pg_b;
         fetch(1, tb, pg_b);
         auto step = [&](int k, f32x16 (&cur)[MB], f32x16 (&nxt)[MB], bool sync) {
-            reselect();
             if (sync) {
-                // tiles k+2 and k+3 have landed (the copies of tiles k+4 .. k+NS-1
-                // may still be in flight); after the barrier every wave's part of
-                // them is visible
-                wait_vmcnt_mem<(NS - 4) * SG::PER_TILE>();
+                // Each wave votes for a re-selection when its buffer might not
+                // take the appends of this step and the next (at most 64 keys);
+                // the votes alternate between two sets of flags, so that a set
+                // is rewritten only after every wave has read it.
+                int* vote = votes + 4 * ((k >> 1) & 1);
+                if (l == 0) vote[w] = cnt > S.cap - 64;
+                // tiles k+2 and k+3 have landed; after the barrier every wave's
+                // part of them is visible, and so is every vote. Vector memory
+                // accesses complete in issue order, and issued after those
+                // copies are the copies of tiles k+4 .. k+NS-1 and, once the loop
+                // runs in full, the appends of the last NS-2 steps (two stores
+                // each), which may stay in flight; the first steps wait as if
+                // no append had been made.
+                if (k >= NS - 2) wait_vmcnt_mem<(NS - 4) * SG::PER_TILE + 2 * (NS - 2)>();
+                else wait_vmcnt_mem<(NS - 4) * SG::PER_TILE>();
                 lds_barrier();
                 issue(k + NS, cp_a);
                 issue(k + NS + 1, cp_b);
                 cp_a = copy_page(k + NS + 2);
                 cp_b = copy_page(k + NS + 3);
+                const int any = __builtin_amdgcn_readfirstlane(vote[0] | vote[1] | vote[2] | vote[3]);
+                if (any) reselect();
             }
             tile_mfma<MB, D, KF>(q, tb, nxt);   // tile k+1
             const float sc_n = tb.sc;
@@ -1506,7 +1552,7 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         buffer_fence();
         // (the buffer's first cnt entries are its nonzero keys: only keys above
         // tau >= 0 are appended, and the re-selections keep nonzero keys)
-        const int m = select_emit<kWave>(B.key, n4, cnt, S.topk, B.sel, EmitFinalBuf{B.pos, oi, os, S.topk, {}}, B.spare);
+        const int m = select_emit<kWave>(B.key, n4, cnt, S.topk, B.sel, EmitFinalStream{B.pos, oi, os, S.topk, {}}, B.spare);
         for (int r = m + l; r < S.topk; r += kWave) {
             oi[r] = -1;
             if (os) os[r] = -INFINITY;
@@ -1536,6 +1582,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void indexer_stream_kernel(IdxAr
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int next_tile;
     __shared__ int tile_seq, tile_rows;
+    __shared__ int votes[2][4];   // re-selection votes of the four waves (two alternating sets)
     constexpr int QPT = kStreamThreads / kWave;   // queries per tile, one per wave
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     StreamSel* ss = reinterpret_cast<StreamSel*>(smem + stream_sel_offset(A.max_visible, D, KF != kRowBf16)) + w;
@@ -1570,7 +1617,7 @@ __global__ __launch_bounds__(kStreamThreads, 2) void indexer_stream_kernel(IdxAr
         const int npg = (rows + kPage - 1) / kPage;
         for (int i = threadIdx.x; i < npg; i += kStreamThreads) pages[i] = page_of(A, b0, i);
         __syncthreads();
-        stream_group<MB, D, KF>(A, S, j, rl, rows, pages, B, ring);
+        stream_group<MB, D, KF>(A, S, j, rl, rows, pages, B, ring, &votes[0][0]);
         __syncthreads();
         tiles_run++;
     };

@@ -319,18 +319,21 @@ __device__ void ordered_compact(const uint32_t* keys, int n, uint32_t T, int tie
         u32x4 ka = {0u, 0u, 0u, 0u}, kb = {0u, 0u, 0u, 0u};
         if (i < n) ka = *reinterpret_cast<const u32x4*>(keys + i);
         if (i + 4 < n) kb = *reinterpret_cast<const u32x4*>(keys + i + 4);
-        int gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             if (i + e >= n) ka[e] = 0u;
             if (i + 4 + e >= n) kb[e] = 0u;
+        }
+        // index-based reads of the elements that may be kept start before the
+        // counts and the scan, so their latency overlaps them
+        emit.prefetch(i, ka, T);
+        emit.prefetch2(i + 4, kb, T);
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
             gt += (ka[e] > T) + (kb[e] > T);
             eq += (ka[e] == T) + (kb[e] == T);
         }
-        // index-based reads of the elements that may be kept start before the
-        // scan, so their latency overlaps it
-        emit.prefetch(i, ka, T);
-        emit.prefetch2(i + 4, kb, T);
         int gpre, epre, gtot, etot;
         scan2<NT>(gt, eq, gpre, epre, gtot, etot, s->scan);
         int eq_before = run_eq + epre;

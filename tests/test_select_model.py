@@ -6,8 +6,11 @@ threshold tau (strictly). When the buffer is full it is re-selected: the first
 time to exactly the Top-K (tau = the K-th key), later to a superset found in one
 histogram pass (every key >= L, where L is the bits all buffered keys share
 followed by the digit of the K-th largest key; tau = L), unless that superset is
-too large, in which case the exact threshold is taken. The final selection over
-the buffer is exact, ties going to the lower position.
+too large, in which case the exact threshold is taken. The four queries of a
+workgroup re-select together: at a tile boundary where any of them might
+overflow, every one holding more than K keys re-selects, so a buffer may also be
+re-selected before it is full. The final selection over the buffer is exact,
+ties going to the lower position.
 
 This model restates those rules in plain Python and checks, on random rows with
 many ties and on rising and falling rows, that the result equals the brute-force
@@ -69,11 +72,13 @@ def superset_floor(buf, k):
     raise AssertionError("fewer keys than k")
 
 
-def stream_topk(keys: np.ndarray, k: int, cap: int) -> list[int]:
+def stream_topk(keys: np.ndarray, k: int, cap: int, votes=frozenset()) -> list[int]:
+    """`votes`: positions before which a partner's vote makes this buffer
+    re-select although it is not full (only if it holds more than k keys)."""
     buf: list[tuple[int, int]] = []
     tau = 0
     for p, key in enumerate(int(x) for x in keys):
-        if len(buf) > cap - 1:
+        if len(buf) > cap - 1 or (p in votes and len(buf) > k):
             if tau != 0:
                 L, kept = superset_floor(buf, k)
                 if L != 0 and kept <= k + (cap - k) // 2:
@@ -109,6 +114,9 @@ def test_stream_buffer_rules_give_exact_topk(pattern, k, cap):
         keys = (np.arange(n, dtype=np.uint64) // 7) * 3 + 0xBF000000
     keys[rng.integers(0, n, size=n // 10)] = 0   # non-candidates (invisible positions)
     assert stream_topk(keys, k, cap) == brute_topk(keys, k)
+    # partners' votes at random tile boundaries (32 positions)
+    votes = frozenset(int(v) * 32 for v in rng.integers(1, n // 32, size=n // 128))
+    assert stream_topk(keys, k, cap, votes) == brute_topk(keys, k)
 
 
 def test_model_detects_a_wrong_tie_rule():
