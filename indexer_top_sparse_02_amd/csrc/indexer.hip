@@ -1343,8 +1343,8 @@ struct StreamGeom {
     static constexpr int SLOT = TILE + ((KF != kRowBf16) ? 256 : 0);
     static constexpr int NS = TILE <= 4096 ? 8 : 4;         // ring slots
     static constexpr int RING = NS * SLOT;
-    static_assert(DMA >= 1 && NS >= 4 && (NS - 1) * PER_TILE < 64 && (NS - 4) * PER_TILE + 2 * (NS - 2) < 64,
-                  "stream ring geometry");
+    static_assert(DMA >= 1 && (NS == 4 || NS == 8) && (NS - 1) * PER_TILE < 64 &&
+                  (NS - 4) * PER_TILE + 2 * (NS - 2) < 64, "stream ring geometry");
 };
 
 __host__ __device__ inline size_t stream_ring_bytes(int dim, bool fp8) {
@@ -1408,9 +1408,11 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         // operands of tile k (k may be past the last tile: then the slot holds a
         // clamped copy and no position is visible). t.ok is the visibility only;
         // the page id `pg` is read without a branch and checked when the tile is
-        // scored, so nothing waits for these reads before then.
-        auto fetch = [&](int k, KTile<D, KF>& t, int& pg) {
-            const uint8_t* slot = ring + (k % NS) * SG::SLOT;
+        // scored, so nothing waits for these reads before then. The slot index
+        // (k mod NS) is a compile-time constant: the ring sits at LDS address 0,
+        // so each read's address is this lane's offset plus an immediate.
+        auto fetch = [&](int k, auto slot_c, KTile<D, KF>& t, int& pg) {
+            const uint8_t* slot = ring + decltype(slot_c)::value * SG::SLOT;
 #pragma unroll
             for (int i = 0; i < NV; i++) t.v[i] = *reinterpret_cast<const u32x4*>(slot + roff[i]);
             if constexpr (KF != kRowBf16) t.sc = *reinterpret_cast<const float*>(slot + SG::TILE + 4 * ((k & 1) * 32 + frow));
@@ -1495,20 +1497,24 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
         KTile<D, KF> tb;
         int pg_b;
         f32x16 A0[MB], A1[MB];
-        fetch(0, tb, pg_b);
+        fetch(0, std::integral_constant<int, 0>{}, tb, pg_b);
         tile_mfma<MB, D, KF>(q, tb, A0);
         float sc_c = tb.sc;
         bool ok_c = tb.ok;
         int pg_c = pg_b;
-        fetch(1, tb, pg_b);
-        auto step = [&](int k, f32x16 (&cur)[MB], f32x16 (&nxt)[MB], bool sync) {
-            if (sync) {
-                // Each wave votes for a re-selection when its buffer might not
-                // take the appends of this step and the next (at most 64 keys);
-                // the votes alternate between two sets of flags, so that a set
-                // is rewritten only after every wave has read it.
-                int* vote = votes + 4 * ((k >> 1) & 1);
-                if (l == 0) vote[w] = cnt > S.cap - 64;
+        fetch(1, std::integral_constant<int, 1>{}, tb, pg_b);
+        // step k = k0 + P with k0 a multiple of NS: P (the phase) fixes the ring
+        // slots at compile time; the waves meet at even phases
+        auto step = [&](int k, f32x16 (&cur)[MB], f32x16 (&nxt)[MB], auto phase) {
+            constexpr int P = decltype(phase)::value;
+            if constexpr (P % 2 == 0) {
+                // At phase 0 each wave votes for a re-selection when its buffer
+                // might not take the appends of the next NS steps (at most 32 NS
+                // keys); the votes alternate between two sets of flags, so that
+                // a set is rewritten only after every wave has read it.
+                int* vote = votes + 4 * ((k / NS) & 1);
+                if constexpr (P == 0)
+                    if (l == 0) vote[w] = cnt > S.cap - 32 * NS;
                 // tiles k+2 and k+3 have landed; after the barrier every wave's
                 // part of them is visible, and so is every vote. Vector memory
                 // accesses complete in issue order, and issued after those
@@ -1523,14 +1529,16 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
                 issue(k + NS + 1, cp_b);
                 cp_a = copy_page(k + NS + 2);
                 cp_b = copy_page(k + NS + 3);
-                const int any = __builtin_amdgcn_readfirstlane(vote[0] | vote[1] | vote[2] | vote[3]);
-                if (any) reselect();
+                if constexpr (P == 0) {
+                    const int any = __builtin_amdgcn_readfirstlane(vote[0] | vote[1] | vote[2] | vote[3]);
+                    if (any) reselect();
+                }
             }
             tile_mfma<MB, D, KF>(q, tb, nxt);   // tile k+1
             const float sc_n = tb.sc;
             const bool ok_n = tb.ok;
             const int pg_n = pg_b;
-            fetch(k + 2, tb, pg_b);              // (after the MFMAs have read tb)
+            fetch(k + 2, std::integral_constant<int, (P + 2) % NS>{}, tb, pg_b);   // (after the MFMAs have read tb)
             const float sc = tile_epilogue<MB, D, KF>(q, cur, sc_c);
             interleave_mfma_valu<NMFMA>();
             append(sc, ok_c && pg_c >= 0, k);
@@ -1538,9 +1546,24 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             ok_c = ok_n;
             pg_c = pg_n;
         };
-        for (int k = 0; k < nt; k += 2) {
-            step(k, A0, A1, true);
-            if (k + 1 < nt) step(k + 1, A1, A0, false);
+        // the loop unrolled by NS steps (A0 / A1 alternate between even and odd steps)
+        for (int k0 = 0; k0 < nt; k0 += NS) {
+            auto run = [&](auto phase) {
+                constexpr int P = decltype(phase)::value;
+                if (k0 + P >= nt) return false;
+                if constexpr (P % 2 == 0) step(k0 + P, A0, A1, phase);
+                else step(k0 + P, A1, A0, phase);
+                return true;
+            };
+            using std::integral_constant;
+            if (!(run(integral_constant<int, 0>{}) && run(integral_constant<int, 1>{}) &&
+                  run(integral_constant<int, 2>{}) && run(integral_constant<int, 3>{})))
+                break;
+            if constexpr (NS == 8) {
+                if (!(run(integral_constant<int, 4>{}) && run(integral_constant<int, 5>{}) &&
+                      run(integral_constant<int, 6>{}) && run(integral_constant<int, 7>{})))
+                    break;
+            }
         }
         wait_vmcnt_mem<0>();
     }
