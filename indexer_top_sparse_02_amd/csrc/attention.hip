@@ -839,6 +839,39 @@ __device__ __forceinline__ void wave_copies(const uint8_t* src, uint8_t* dst, in
     }
 }
 
+// Copy K alone of the same set (K a std::integral_constant), so that a loop
+// can spread a tile's copies between its MFMAs.
+template <int STEP, int NHB, typename KC>
+__device__ __forceinline__ void wave_copy_k(KC, const uint8_t* src, uint8_t* dst, int hb) {
+    constexpr int K = KC::value;
+    dma16_imm<K * STEP>(src, (SIA_LDS void*)(dst + (hb + NHB * K) * 1024));
+}
+
+// Calls f(std::integral_constant<int, k>{}) for k in 0 .. 8 (in an unrolled loop
+// k is a constant and the switch folds away).
+template <typename F>
+__device__ __forceinline__ void with_copy_index(int k, F&& f) {
+    using std::integral_constant;
+    switch (k) {
+        case 0: f(integral_constant<int, 0>{}); break;
+        case 1: f(integral_constant<int, 1>{}); break;
+        case 2: f(integral_constant<int, 2>{}); break;
+        case 3: f(integral_constant<int, 3>{}); break;
+        case 4: f(integral_constant<int, 4>{}); break;
+        case 5: f(integral_constant<int, 5>{}); break;
+        case 6: f(integral_constant<int, 6>{}); break;
+        case 7: f(integral_constant<int, 7>{}); break;
+        case 8: f(integral_constant<int, 8>{}); break;
+        default: break;
+    }
+}
+
+// A copy issuer that issues nothing.
+struct NoCopies {
+    template <typename KC>
+    __device__ void operator()(KC) const {}
+};
+
 // NHB blocks of 16 heads per workgroup; RH = 1: one wave per head block over
 // 32-row tiles; RH = 2: 64-row tiles, two waves per head block, wave rh taking
 // rows 32 rh .. 32 rh + 31 of every tile with a softmax of its own, the two
@@ -1431,9 +1464,12 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
     // With xe/pk given, step st < 16 also computes exponential st of the
     // previous tile's prepared logits (the 16 of this lane: block st / 8, row
     // block (st / 4) % 2, register st % 4), so that they run beside the MFMAs,
-    // and the last step packs them into P^T.
-    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2][2], const float (*xe)[2][4] = nullptr,
-                  bf16x8* pk = nullptr) {
+    // and the last step packs them into P^T. After the MFMAs of odd step st,
+    // cp issues copy st / 2 of a later tile (cp: NoCopies, or an issuer of one
+    // of the kWideCP = 9 copies), so that the copies' address work runs beside
+    // the MFMAs too.
+    static_assert(kWideCP <= 9 && 2 * kWideCP <= KS, "copies spread over the Q K^T steps");
+    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2][2], const float (*xe)[2][4], bf16x8* pk, auto cp) {
         float pe[2][2][4];
         constexpr int DEPTH = 3;
         auto kread = [&](int st, int rb) -> bf16x8 {
@@ -1463,6 +1499,7 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
                 pe[h][rb][r] = __builtin_amdgcn_exp2f(xe[h][rb][r] - m_ref[h]);
                 l_run[h] += pe[h][rb][r];
             }
+            if (st % 2 == 1 && st / 2 < kWideCP) with_copy_index(st / 2, cp);
         }
         if (xe != nullptr) {
 #pragma unroll
@@ -1565,7 +1602,7 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
         float x[2][2][4];
         {
             f32x4 s[2][2];
-            qk(ring[0], s);
+            qk(ring[0], s, nullptr, nullptr, NoCopies{});
             prep(0, s, x);
         }
         for (int t = 0; t < ntiles; t++) {
@@ -1574,17 +1611,19 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
             if (t + 2 < ntiles) wait_vmcnt_mem<kWideCP>();
             else wait_vmcnt_mem<0>();
             lds_barrier();
-            if (t + 3 < ntiles) {
-                issue(t + 3, row_next);
-                row_next = row_of(t + 4);
-            }
             // No branch from here to the end of P V: one scheduling region in
-            // which the exponentials of tile t sit between the MFMAs of the next
-            // tile's Q K^T. (In the last iteration that Q K^T reads a slot of
-            // stale rows and its result is not used.)
+            // which the exponentials of tile t and the copies of tile t+3 sit
+            // between the MFMAs of the next tile's Q K^T. (In the last iteration
+            // that Q K^T reads a slot of stale rows and its result is not used;
+            // the copies of a tile past the last, of the slice's last row, land
+            // in the free slot of tile t-1 and are not read.)
+            const uint8_t* cp_src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row_next * kRowB + 32 * w + 16 * (l & 1);
+            uint8_t* cp_dst = ring[(t + 3) & 3];
+            row_next = row_of(t + 4);
+            auto copier = [&](auto kc) { wave_copy_k<32 * kWideNW, kWideNW>(kc, cp_src, cp_dst, w); };
             f32x4 sn[2][2];
             bf16x8 pk[2];
-            qk(ring[(t + 1) & 3], sn, x, pk);
+            qk(ring[(t + 1) & 3], sn, x, pk, copier);
             bf16x8 vb[VD];
             pv_pre(ring[t & 3], vb);
             p_settle(pk);
