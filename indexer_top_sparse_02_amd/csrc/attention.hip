@@ -847,23 +847,22 @@ __device__ __forceinline__ void wave_copy_k(KC, const uint8_t* src, uint8_t* dst
     dma16_imm<K * STEP>(src, (SIA_LDS void*)(dst + (hb + NHB * K) * 1024));
 }
 
-// Calls f(std::integral_constant<int, k>{}) for k in 0 .. 8 (in an unrolled loop
-// k is a constant and the switch folds away).
-template <typename F>
+// Calls f(std::integral_constant<int, k>{}) for 0 <= k < N (in an unrolled
+// loop k is a constant and the tests fold away).
+template <int N, int K = 0, typename F>
 __device__ __forceinline__ void with_copy_index(int k, F&& f) {
-    using std::integral_constant;
-    switch (k) {
-        case 0: f(integral_constant<int, 0>{}); break;
-        case 1: f(integral_constant<int, 1>{}); break;
-        case 2: f(integral_constant<int, 2>{}); break;
-        case 3: f(integral_constant<int, 3>{}); break;
-        case 4: f(integral_constant<int, 4>{}); break;
-        case 5: f(integral_constant<int, 5>{}); break;
-        case 6: f(integral_constant<int, 6>{}); break;
-        case 7: f(integral_constant<int, 7>{}); break;
-        case 8: f(integral_constant<int, 8>{}); break;
-        default: break;
+    if constexpr (K < N) {
+        if (k == K) f(std::integral_constant<int, K>{});
+        else with_copy_index<N, K + 1>(k, f);
     }
+}
+
+// The copies of a later tile spread over a tile's 18 Q K^T steps: after step st
+// go copies st CP / 18 .. (st + 1) CP / 18 - 1 (CP of them per tile).
+template <int CP, int KS, typename F>
+__device__ __forceinline__ void copies_after_step(int st, F&& f) {
+#pragma unroll
+    for (int k = st * CP / KS; k < (st + 1) * CP / KS; k++) with_copy_index<CP>(k, f);
 }
 
 // A copy issuer that issues nothing.
@@ -901,6 +900,9 @@ struct WaveGeom {
 template <int NHB, int RH>
 __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnArgs A) {
     using GM = WaveGeom<NHB, RH>;
+    // (the pipelined loop spreads a tile's copies over the Q K^T steps: every
+    // wave must issue the same count, CP_LO)
+    static_assert(!GM::PIPE || GM::SPLIT == 0, "spread copies: the same count in every wave");
     constexpr int HB = GM::HB, NT = GM::NT, NW = GM::NW, CPMAX = GM::CPMAX, TR = GM::TR, AHEAD = GM::AHEAD;
     constexpr int TB = RowFmt<false>::TB;
     constexpr int KS = kDK / 32;    // 18 Q K^T steps
@@ -1037,8 +1039,10 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
     // sub-tile row 16 rb + 4 g + r and head jl. With xe/pk given, step st < 8
     // also computes exponential st of the previous tile's prepared logits (row
     // block st / 4, register st % 4), so that they run beside the MFMAs, and the
-    // loop's end packs them into P^T.
-    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2], const float (*xe)[4] = nullptr, bf16x8* pk = nullptr) {
+    // loop's end packs them into P^T. After the MFMAs of step st, cp issues that
+    // step's share of a later tile's CPMAX copies (cp: NoCopies, or an issuer of
+    // one copy).
+    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2], const float (*xe)[4], bf16x8* pk, auto cp) {
         float pe[2][4];
         constexpr int DEPTH = GM::QA ? 3 : 2;   // steps whose key operands are in flight
         auto kread = [&](int st, int rb) -> bf16x8 {
@@ -1075,6 +1079,7 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 pe[rb][r] = __builtin_amdgcn_exp2f(xe[rb][r] - m_ref);
                 l_run += pe[rb][r];
             }
+            copies_after_step<CPMAX, KS>(st, cp);
         }
         if (xe != nullptr)
             *pk = as_bf16x8(u32x4{pack_bf16x2(pe[0][0], pe[0][1]), pack_bf16x2(pe[0][2], pe[0][3]),
@@ -1200,7 +1205,7 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
             float x[2][4];
             {
                 f32x4 s[2];
-                qk(sub_of(0), s);
+                qk(sub_of(0), s, nullptr, nullptr, NoCopies{});
                 qk_settle(s);
                 prep(0, s, x);
             }
@@ -1210,17 +1215,19 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 if (t + 2 < ntiles) wait_vmcnt_mem<CPMAX>();
                 else wait_vmcnt_mem<0>();
                 lds_barrier();
-                if (t + 3 < ntiles) {
-                    issue(t + 3, row_next);
-                    row_next = row_of(t + 4);
-                }
                 // One branch-free block: Q K^T of tile t+1 with the exponentials
-                // of tile t between its MFMAs, then P V of tile t (in the last
-                // iteration that Q K^T reads a slot of stale rows and its result
-                // is not used). The logits of tile t+1 are prepared after P V.
+                // of tile t and the copies of tile t+3 between its MFMAs, then
+                // P V of tile t (in the last iteration that Q K^T reads a slot of
+                // stale rows and its result is not used; copies of a tile past
+                // the last bring the slice's last row into the free slot of tile
+                // t-1, unread). The logits of tile t+1 are prepared after P V.
+                const uint8_t* cp_src = reinterpret_cast<const uint8_t*>(A.kv) + (int64_t)row_next * kRowB + 32 * hb + 16 * (l & 1);
+                uint8_t* cp_dst = sub_of(t + 3);
+                row_next = row_of(t + 4);
+                auto copier = [&](auto kc) { wave_copy_k<32 * NHB, NHB>(kc, cp_src, cp_dst, hb); };
                 f32x4 sn[2];
                 bf16x8 pk;
-                qk(sub_of(t + 1), sn, x, &pk);
+                qk(sub_of(t + 1), sn, x, &pk, copier);
                 pv(sub_of(t), pk);
                 if (t + 1 < ntiles) {
                     qk_settle(sn);
@@ -1240,7 +1247,7 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                     row_next = row_of(t + AHEAD + 1);
                 }
                 f32x4 s[2];
-                qk(sub_of(t), s);
+                qk(sub_of(t), s, nullptr, nullptr, NoCopies{});
                 qk_settle(s);
                 const bf16x8 pk = softmax(t, s);
                 pv(sub_of(t), pk);
@@ -1464,11 +1471,10 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
     // With xe/pk given, step st < 16 also computes exponential st of the
     // previous tile's prepared logits (the 16 of this lane: block st / 8, row
     // block (st / 4) % 2, register st % 4), so that they run beside the MFMAs,
-    // and the last step packs them into P^T. After the MFMAs of odd step st,
-    // cp issues copy st / 2 of a later tile (cp: NoCopies, or an issuer of one
-    // of the kWideCP = 9 copies), so that the copies' address work runs beside
+    // and the last step packs them into P^T. After the MFMAs of step st, cp
+    // issues that step's share of a later tile's kWideCP copies (cp: NoCopies,
+    // or an issuer of one copy), so that the copies' address work runs beside
     // the MFMAs too.
-    static_assert(kWideCP <= 9 && 2 * kWideCP <= KS, "copies spread over the Q K^T steps");
     auto qk = [&](const uint8_t* buf, f32x4 (&s)[2][2], const float (*xe)[2][4], bf16x8* pk, auto cp) {
         float pe[2][2][4];
         constexpr int DEPTH = 3;
@@ -1499,7 +1505,7 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
                 pe[h][rb][r] = __builtin_amdgcn_exp2f(xe[h][rb][r] - m_ref[h]);
                 l_run[h] += pe[h][rb][r];
             }
-            if (st % 2 == 1 && st / 2 < kWideCP) with_copy_index(st / 2, cp);
+            copies_after_step<kWideCP, KS>(st, cp);
         }
         if (xe != nullptr) {
 #pragma unroll
