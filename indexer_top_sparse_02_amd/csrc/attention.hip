@@ -871,6 +871,11 @@ struct NoCopies {
     __device__ void operator()(KC) const {}
 };
 
+// A value-operand reader that reads nothing.
+struct NoReads {
+    __device__ void operator()(int) const {}
+};
+
 // NHB blocks of 16 heads per workgroup; RH = 1: one wave per head block over
 // 32-row tiles; RH = 2: 64-row tiles, two waves per head block, wave rh taking
 // rows 32 rh .. 32 rh + 31 of every tile with a softmax of its own, the two
@@ -1041,8 +1046,10 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
     // block st / 4, register st % 4), so that they run beside the MFMAs, and the
     // loop's end packs them into P^T. After the MFMAs of step st, cp issues that
     // step's share of a later tile's CPMAX copies (cp: NoCopies, or an issuer of
-    // one copy).
-    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2], const float (*xe)[4], bf16x8* pk, auto cp) {
+    // one copy); in the last VD steps (no key reads left) vr(i) reads value
+    // operand i of the P V that follows (vr: NoReads, or its reader).
+    constexpr int VD = GM::QA ? 4 : 2;
+    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2], const float (*xe)[4], bf16x8* pk, auto cp, auto vr) {
         float pe[2][4];
         constexpr int DEPTH = GM::QA ? 3 : 2;   // steps whose key operands are in flight
         auto kread = [&](int st, int rb) -> bf16x8 {
@@ -1080,6 +1087,7 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 l_run += pe[rb][r];
             }
             copies_after_step<CPMAX, KS>(st, cp);
+            if (st >= KS - VD) vr(st - (KS - VD));
         }
         if (xe != nullptr)
             *pk = as_bf16x8(u32x4{pack_bf16x2(pe[0][0], pe[0][1]), pack_bf16x2(pe[0][2], pe[0][3]),
@@ -1172,20 +1180,21 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
     // O^T += V^T P^T over sub-tile `buf`: column block cb takes two transposing
     // reads (rows 4 g .., 16 + 4 g ..: its eight k slots, in P's order); the
     // reads of the next VD blocks are in flight during each MFMA
-    auto pv = [&](const uint8_t* buf, const bf16x8 pk) {
-        constexpr int VD = GM::QA ? 4 : 2;
-        auto vread = [&](int cb) -> bf16x8 {
-            const u32x2 a = ds_read_tr16_c(buf + vbase + 1024 * cb);
-            const u32x2 bb = ds_read_tr16_c(buf + vbase + 1024 * cb + 512);
-            return as_bf16x8(u32x4{a[0], a[1], bb[0], bb[1]});
-        };
-        bf16x8 vb[VD];
+    auto vread = [&](const uint8_t* buf, int cb) -> bf16x8 {
+        const u32x2 a = ds_read_tr16_c(buf + vbase + 1024 * cb);
+        const u32x2 bb = ds_read_tr16_c(buf + vbase + 1024 * cb + 512);
+        return as_bf16x8(u32x4{a[0], a[1], bb[0], bb[1]});
+    };
+    // (vb: the first VD value operands, read beforehand when `pre` is true)
+    auto pv = [&](const uint8_t* buf, const bf16x8 pk, bf16x8 (&vb)[VD], bool pre) {
+        if (!pre) {
 #pragma unroll
-        for (int i = 0; i < VD; i++) vb[i] = vread(i);
+            for (int i = 0; i < VD; i++) vb[i] = vread(buf, i);
+        }
 #pragma unroll
         for (int cb = 0; cb < NCB; cb++) {
             const bf16x8 v = vb[cb % VD];
-            if (cb + VD < NCB) vb[cb % VD] = vread(cb + VD);
+            if (cb + VD < NCB) vb[cb % VD] = vread(buf, cb + VD);
             o[cb] = mfma16(v, pk, o[cb]);
         }
     };
@@ -1205,7 +1214,7 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
             float x[2][4];
             {
                 f32x4 s[2];
-                qk(sub_of(0), s, nullptr, nullptr, NoCopies{});
+                qk(sub_of(0), s, nullptr, nullptr, NoCopies{}, NoReads{});
                 qk_settle(s);
                 prep(0, s, x);
             }
@@ -1227,8 +1236,10 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                 auto copier = [&](auto kc) { wave_copy_k<32 * NHB, NHB>(kc, cp_src, cp_dst, hb); };
                 f32x4 sn[2];
                 bf16x8 pk;
-                qk(sub_of(t + 1), sn, x, &pk, copier);
-                pv(sub_of(t), pk);
+                bf16x8 vb[VD];
+                auto vreader = [&](int i) { vb[i] = vread(sub_of(t), i); };
+                qk(sub_of(t + 1), sn, x, &pk, copier, vreader);
+                pv(sub_of(t), pk, vb, true);
                 if (t + 1 < ntiles) {
                     qk_settle(sn);
                     prep(t + 1, sn, x);
@@ -1247,10 +1258,11 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
                     row_next = row_of(t + AHEAD + 1);
                 }
                 f32x4 s[2];
-                qk(sub_of(t), s, nullptr, nullptr, NoCopies{});
+                qk(sub_of(t), s, nullptr, nullptr, NoCopies{}, NoReads{});
                 qk_settle(s);
                 const bf16x8 pk = softmax(t, s);
-                pv(sub_of(t), pk);
+                bf16x8 vb[VD];
+                pv(sub_of(t), pk, vb, false);
             }
         }
     }
@@ -1474,8 +1486,10 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
     // and the last step packs them into P^T. After the MFMAs of step st, cp
     // issues that step's share of a later tile's kWideCP copies (cp: NoCopies,
     // or an issuer of one copy), so that the copies' address work runs beside
-    // the MFMAs too.
-    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2][2], const float (*xe)[2][4], bf16x8* pk, auto cp) {
+    // the MFMAs too; in the last VD steps (no key reads left) vr(i) reads value
+    // operand i of the P V that follows (vr: NoReads, or its reader).
+    constexpr int VD = 4;
+    auto qk = [&](const uint8_t* buf, f32x4 (&s)[2][2], const float (*xe)[2][4], bf16x8* pk, auto cp, auto vr) {
         float pe[2][2][4];
         constexpr int DEPTH = 3;
         auto kread = [&](int st, int rb) -> bf16x8 {
@@ -1506,6 +1520,7 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
                 l_run[h] += pe[h][rb][r];
             }
             copies_after_step<kWideCP, KS>(st, cp);
+            if (st >= KS - VD) vr(st - (KS - VD));
         }
         if (xe != nullptr) {
 #pragma unroll
@@ -1573,16 +1588,11 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
     };
     // O^T += V^T P^T over tile `buf`: each value operand (two transposing reads)
     // serves both head blocks
-    // (the first VD value operands are read by pv_pre, before P is settled)
-    constexpr int VD = 4;
+    // (the first VD value operands are read during the preceding Q K^T)
     auto vread = [&](const uint8_t* buf, int cb) -> bf16x8 {
         const u32x2 a = ds_read_tr16_c(buf + vbase + 1024 * cb);
         const u32x2 bb = ds_read_tr16_c(buf + vbase + 1024 * cb + 512);
         return as_bf16x8(u32x4{a[0], a[1], bb[0], bb[1]});
-    };
-    auto pv_pre = [&](const uint8_t* buf, bf16x8 (&vb)[VD]) {
-#pragma unroll
-        for (int i = 0; i < VD; i++) vb[i] = vread(buf, i);
     };
     auto pv = [&](const uint8_t* buf, const bf16x8 (&pk)[2], bf16x8 (&vb)[VD]) {
 #pragma unroll
@@ -1608,7 +1618,7 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
         float x[2][2][4];
         {
             f32x4 s[2][2];
-            qk(ring[0], s, nullptr, nullptr, NoCopies{});
+            qk(ring[0], s, nullptr, nullptr, NoCopies{}, NoReads{});
             prep(0, s, x);
         }
         for (int t = 0; t < ntiles; t++) {
@@ -1629,9 +1639,9 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
             auto copier = [&](auto kc) { wave_copy_k<32 * kWideNW, kWideNW>(kc, cp_src, cp_dst, w); };
             f32x4 sn[2][2];
             bf16x8 pk[2];
-            qk(ring[(t + 1) & 3], sn, x, pk, copier);
             bf16x8 vb[VD];
-            pv_pre(ring[t & 3], vb);
+            auto vreader = [&](int i) { vb[i] = vread(ring[t & 3], i); };
+            qk(ring[(t + 1) & 3], sn, x, pk, copier, vreader);
             p_settle(pk);
             pv(ring[t & 3], pk, vb);
             if (t + 1 < ntiles) prep(t + 1, sn, x);
