@@ -936,16 +936,11 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
     const int j = pair / A.n_split, sp = pair % A.n_split;
     const int head0 = hbk * HB + 16 * hb;   // this wave's first head
 
-    int b = A.q_seq[j];
-    const bool seq_ok = b >= 0 && b < A.batch;
-    if (!seq_ok) {
-        if (tid == 0) atomicOr(A.status, kBadSeq);
-        b = 0;
-    }
-    const int n_b = seq_ok ? A.seq_lens[b] : 0;
-    const int r0 = sp * A.rows_per_split;
-    const int r1 = seq_ok ? min(A.topk, r0 + A.rows_per_split) : r0;
-
+    // The prologue's global reads in two rounds: the query slice, the sequence
+    // id and the slice's indices (none depends on another), then the sequence
+    // length and the page table entries of the indices (the query moves into
+    // the accumulation registers only after the row list is built, so that its
+    // loads do not hold up the rest).
     // ---- the wave's query as the B operand of Q K^T: step s, head head0 + jl,
     // dims 32 s + 8 g .. + 7
     bf16x8 qb[KS];
@@ -953,32 +948,45 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
         const uint16_t* qrow = A.q + ((int64_t)j * A.heads + head0 + jl) * kDK + g * 8;
 #pragma unroll
         for (int s = 0; s < KS; s++) qb[s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + s * 32));
-        // into the accumulation registers, then the wait states a vector write
-        // needs before an MFMA reads what it wrote
-        if constexpr (GM::QA) {
+    }
+    const int r0 = sp * A.rows_per_split;
+    const int r1_all = min(A.topk, r0 + A.rows_per_split);
+    constexpr int RPT = kMaxSliceRows / NT;
+    int sidx[RPT];
 #pragma unroll
-            for (int s = 0; s < KS; s++) asm volatile("" : "+a"(qb[s]));
-            asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
-        }
+    for (int i = 0; i < RPT; i++) {
+        const int r = r0 + tid * RPT + i;
+        sidx[i] = r < r1_all ? A.idx[(int64_t)j * A.topk + r] : -1;
+    }
+    int b = A.q_seq[j];
+    const bool seq_ok = b >= 0 && b < A.batch;
+    if (!seq_ok) {
+        if (tid == 0) atomicOr(A.status, kBadSeq);
+        b = 0;
+    }
+    if (!seq_ok) {
+#pragma unroll
+        for (int i = 0; i < RPT; i++) sidx[i] = -1;
     }
 
     // ---- validated, compacted physical row ids of the slice (as in
     // sparse_mla_kernel)
-    constexpr int RPT = kMaxSliceRows / NT;
     int nr = 0;
     {
-        int sidx[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; i++) {
-            const int r = r0 + tid * RPT + i;
-            sidx[i] = r < r1 ? A.idx[(int64_t)j * A.topk + r] : -1;
-        }
+        // (the page table entry of every index inside the table's span, read
+        // beside the sequence length; the length check follows)
         int pg[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; i++) {
             const int s = sidx[i];
+            pg[i] = s >= 0 && s < A.max_pages * kPage ? A.page_table[(int64_t)b * A.max_pages + (s >> 6)] : -1;
+        }
+        const int n_b = seq_ok ? A.seq_lens[b] : 0;
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
             const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
-            pg[i] = in ? A.page_table[(int64_t)b * A.max_pages + (s >> 6)] : -1;
+            if (!in) pg[i] = -1;
             if (s >= 0 && !in) atomicOr(A.status, kBadIndex);
         }
         uint32_t row[RPT];
@@ -999,6 +1007,13 @@ __global__ __launch_bounds__(NHB * RH * kWave) void sparse_mla_wave_kernel(AttnA
             if (row[i] != 0xffffffffu) rows[pre++] = row[i];
         }
         nr = tot;
+    }
+    // the query into the accumulation registers, then the wait states a vector
+    // write needs before an MFMA reads what it wrote
+    if constexpr (GM::QA) {
+#pragma unroll
+        for (int s = 0; s < KS; s++) asm volatile("" : "+a"(qb[s]));
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
     }
     __syncthreads();
     const int ntiles = (nr + TR - 1) / TR;
@@ -1398,16 +1413,9 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
     const int j = pair / A.n_split, sp = pair % A.n_split;
     const int head0 = hbk * HB + 32 * w;   // this wave's first head; block h: head0 + 16 h
 
-    int b = A.q_seq[j];
-    const bool seq_ok = b >= 0 && b < A.batch;
-    if (!seq_ok) {
-        if (tid == 0) atomicOr(A.status, kBadSeq);
-        b = 0;
-    }
-    const int n_b = seq_ok ? A.seq_lens[b] : 0;
-    const int r0 = sp * A.rows_per_split;
-    const int r1 = seq_ok ? min(A.topk, r0 + A.rows_per_split) : r0;
-
+    // The prologue's global reads in two rounds: the query slices, the
+    // sequence id and the slice's indices (none depends on another), then the
+    // sequence length and the page table entries of the indices.
     // ---- the wave's query as the B operand of Q K^T: block h, step s: head
     // head0 + 16 h + jl, dims 32 s + 8 g .. + 7
     bf16x8 qb[2][KS];
@@ -1417,24 +1425,44 @@ __global__ __launch_bounds__(kWideNW * kWave) void sparse_mla_wide_kernel(AttnAr
 #pragma unroll
         for (int s = 0; s < KS; s++) qb[h][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + s * 32));
     }
+    const int r0 = sp * A.rows_per_split;
+    const int r1_all = min(A.topk, r0 + A.rows_per_split);
+    constexpr int RPT = kMaxSliceRows / NT;
+    int sidx[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; i++) {
+        const int r = r0 + tid * RPT + i;
+        sidx[i] = r < r1_all ? A.idx[(int64_t)j * A.topk + r] : -1;
+    }
+    int b = A.q_seq[j];
+    const bool seq_ok = b >= 0 && b < A.batch;
+    if (!seq_ok) {
+        if (tid == 0) atomicOr(A.status, kBadSeq);
+        b = 0;
+    }
+    if (!seq_ok) {
+#pragma unroll
+        for (int i = 0; i < RPT; i++) sidx[i] = -1;
+    }
 
     // ---- validated, compacted physical row ids of the slice (as in
     // sparse_mla_kernel)
-    constexpr int RPT = kMaxSliceRows / NT;
     int nr = 0;
     {
-        int sidx[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; i++) {
-            const int r = r0 + tid * RPT + i;
-            sidx[i] = r < r1 ? A.idx[(int64_t)j * A.topk + r] : -1;
-        }
+        // (the page table entry of every index inside the table's span, read
+        // beside the sequence length; the length check follows)
         int pg[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; i++) {
             const int s = sidx[i];
+            pg[i] = s >= 0 && s < A.max_pages * kPage ? A.page_table[(int64_t)b * A.max_pages + (s >> 6)] : -1;
+        }
+        const int n_b = seq_ok ? A.seq_lens[b] : 0;
+#pragma unroll
+        for (int i = 0; i < RPT; i++) {
+            const int s = sidx[i];
             const bool in = s >= 0 && s < n_b && s < A.max_pages * kPage;
-            pg[i] = in ? A.page_table[(int64_t)b * A.max_pages + (s >> 6)] : -1;
+            if (!in) pg[i] = -1;
             if (s >= 0 && !in) atomicOr(A.status, kBadIndex);
         }
         uint32_t row[RPT];
