@@ -239,6 +239,53 @@ def test_stream_reselection_on_rising_scores(fp8):
     assert np.array_equal(g_top[g_idx >= 0], ref_sc[g_idx >= 0])
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_stream_group_reselection_with_mixed_rows(fp8):
+    """The four queries of a stream workgroup re-select together when any of
+    them might overflow its buffer. Here they differ (query j % 4: scores
+    rising along the row, so that its buffer fills again and again and votes;
+    falling, so that after its first re-selection it holds exactly K keys and
+    skips the vote's re-selections; flat, the rising and falling parts summed,
+    with ties everywhere; and random), so that re-selections run in buffers that
+    are not full, with and without ties. Indices and scores must be the
+    oracle's selection of the GPU's own scores, bit for bit."""
+    s = W.spec("prefill_16k", ctx_lo=6000, ctx_hi=6000, topk=256, idx_fp8=fp8, heads_attn=16)
+    wl = W.make(s, device="cuda", poison=True, with_attn=False)
+    n = 6000
+    pos = torch.arange(n, device="cuda")
+    phys = wl.page_table[0].long()[pos // 64] * 64 + pos % 64
+    flat = wl.idx_k.view(-1, s.dim_idx)
+    # (the other elements keep their random values: they score the random query)
+    row = flat[phys].view(torch.float8_e4m3fn).float() if fp8 else flat[phys].float()
+    row[:, 0] = (pos // 7).float() / 64.0 + 0.25
+    row[:, 1] = ((n - 1 - pos) // 7).float() / 64.0 + 0.25
+    if fp8:
+        flat[phys] = row.to(torch.float8_e4m3fn).view(torch.uint8)
+        wl.idx_scale.view(-1)[phys] = 1.0
+    else:
+        flat[phys] = row.to(torch.bfloat16)
+    pattern = torch.arange(wl.num_q, device="cuda") % 4
+    q = wl.q_idx[:, 0, :].float()
+    q[pattern < 3] = 0.0
+    q[pattern == 0, 0] = 1.0
+    q[pattern == 1, 1] = 1.0
+    q[pattern == 2, 0] = 1.0
+    q[pattern == 2, 1] = 1.0
+    wl.q_idx.zero_()
+    wl.q_idx[:, 0, :] = q.to(torch.bfloat16)
+    wl.w.zero_()
+    wl.w[:, 0] = 1.0
+    sc = gpu_scores(wl)
+    rl = row_lengths(wl)
+    with env(SIA_INDEXER_PATH=2):
+        got, top = gpu_topk(wl)
+    ref, ref_sc = oracle_topk_of(sc, rl, s.topk)
+    g_idx = got.cpu().numpy()
+    assert np.array_equal(g_idx, ref)
+    g_top = top.cpu().numpy().astype(np.float64)
+    assert np.array_equal(g_top[g_idx >= 0], ref_sc[g_idx >= 0])
+
+
 @pytest.mark.parametrize("sched", [0, 1, 2])
 def test_prefill_schedules_agree(sched):
     s = W.spec("prefill_16k", ctx_lo=1500, ctx_hi=1500, topk=128, idx_fp8=True)
