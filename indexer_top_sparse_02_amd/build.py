@@ -40,7 +40,13 @@ FLAGS = [
 # copy them back and forth around the vector arithmetic on them (the causal
 # prefill indexer's head sums, the attention softmax).
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-FILE_FLAGS: dict = {"attention.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM}
+# The score passes place each MFMA group and the vector work meant to run in
+# its shadow between scheduling fences. Machine sinking moves MFMAs (which touch
+# no memory) past those fences toward the first use of their result, i.e. into
+# the next step and across its barrier; the vector work on that result then
+# waits for the group it was meant to hide behind.
+_NO_SINK = ["-mllvm", "-disable-machine-sink"]
+FILE_FLAGS: dict = {"attention.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM + _NO_SINK}
 
 
 def _compile(src: str) -> str:

@@ -784,8 +784,11 @@ struct PairGeom {
     static_assert(NS_FIT >= 4, "the pair ring needs four slots per team at least");
 };
 
-// Scheduling hint for a step: each of the query's MFMAs followed by the vector
-// instructions that fit in its shadow.
+// Scheduling hint for a step: each of the query's MFMAs followed by up to NVALU
+// vector instructions. NVALU spreads the group's vector work over all of its
+// MFMAs, so that some of it still follows the last one: the head sums of the
+// next group read this group's results, which are ready only a full MFMA after
+// its last issue (the wait states otherwise become s_nop stalls).
 template <int NMFMA, int NVALU = 16>
 __device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
@@ -997,7 +1000,7 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             const float h1 = tile_head_sum<1, D, KF>(q1, a1);
             Fin fin{};
             if constexpr (FIN) fin = finish_prep(k - 1, xv + mine_p, half ? sc_p2 : sc_p1, fk, pgv);
-            interleave_mfma_valu<NMFMA, FIN ? 24 : 12>();
+            interleave_mfma_valu<NMFMA, FIN ? 12 : 6>();
             __builtin_amdgcn_sched_barrier(0);
             tile_mfma<1, D, KF>(q1, tc, a1);
             const float h0 = tile_head_sum<1, D, KF>(q0, a0);
