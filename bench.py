@@ -73,12 +73,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_traffic_spec_decode_128k.
 
 
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources with comments and blank space removed, so that
-    only a change of the code itself invalidates a counter figure."""
+    """Hash of the kernel sources with comments and blank space removed, and of
+    the build script (whose code generation options change the kernels too), so
+    that only a change of the code itself invalidates a counter figure."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES + ["../build.py"]:
         with open(os.path.join(ROOT, "indexer_top_sparse_02_amd", "csrc", f)) as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
