@@ -51,8 +51,16 @@ FILE_FLAGS: dict = {"attention.hip": _VGPR_FORM, "indexer.hip": _VGPR_FORM + _NO
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+    extra = FILE_FLAGS.get(os.path.basename(src), [])
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0 and _NO_SINK[1] in extra and _NO_SINK[1] in r.stderr:
+        # a compiler without that option: build with its default code placement
+        print(f"{os.path.basename(src)}: compiler rejects {_NO_SINK[1]}; building without it", file=sys.stderr)
+        kept = [f for i, f in enumerate(extra) if f != _NO_SINK[1] and not (f == "-mllvm" and i + 1 < len(extra)
+                                                                            and extra[i + 1] == _NO_SINK[1])]
+        cmd = [HIPCC, *FLAGS, *kept, "-c", src, "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
     noise = "is not a recognized feature for this target"
