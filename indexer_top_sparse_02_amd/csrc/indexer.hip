@@ -1543,7 +1543,9 @@ __device__ void stream_group(const IdxArgs& A, const StreamArgs& S, int j, int r
             const int pg_n = pg_b;
             fetch(k + 2, std::integral_constant<int, (P + 2) % NS>{}, tb, pg_b);   // (after the MFMAs have read tb)
             const float sc = tile_epilogue<MB, D, KF>(q, cur, sc_c);
-            interleave_mfma_valu<NMFMA>();
+            // (vector instructions per MFMA, measured per key format: bf16
+            // tiles have twice the MFMAs of fp8 tiles for the same epilogue)
+            interleave_mfma_valu<NMFMA, KF == kRowBf16 ? 8 : KF == kRowFp8 ? 12 : 16>();
             append(sc, ok_c && pg_c >= 0, k);
             sc_c = sc_n;
             ok_c = ok_n;
