@@ -789,6 +789,8 @@ struct PairGeom {
 // MFMAs, so that some of it still follows the last one: the head sums of the
 // next group read this group's results, which are ready only a full MFMA after
 // its last issue (the wait states otherwise become s_nop stalls).
+// (The spreads below were measured per key format: MXFP8 tiles take half the
+// MFMAs of fp8 tiles with the query's two terms, for the same vector work.)
 template <int NMFMA, int NVALU = 16>
 __device__ __forceinline__ void interleave_mfma_valu() {
 #pragma unroll
@@ -1000,11 +1002,11 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
             const float h1 = tile_head_sum<1, D, KF>(q1, a1);
             Fin fin{};
             if constexpr (FIN) fin = finish_prep(k - 1, xv + mine_p, half ? sc_p2 : sc_p1, fk, pgv);
-            interleave_mfma_valu<NMFMA, FIN ? 12 : 6>();
+            interleave_mfma_valu<NMFMA, KF == kRowMx ? (FIN ? 36 : 18) : (FIN ? 12 : 6)>();
             __builtin_amdgcn_sched_barrier(0);
             tile_mfma<1, D, KF>(q1, tc, a1);
             const float h0 = tile_head_sum<1, D, KF>(q0, a0);
-            interleave_mfma_valu<NMFMA>();
+            interleave_mfma_valu<NMFMA, KF == kRowMx ? 40 : 16>();
             __builtin_amdgcn_sched_barrier(0);
             const float mine = half ? h1 : h0;
             sc_p2 = sc_p1;
