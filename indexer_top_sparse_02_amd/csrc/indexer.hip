@@ -1018,16 +1018,12 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
                 lds_wait_all();                                // the block sums are written
                 fetch(k + 1, (u + 1) % NS, tc);
                 issue(k + NS - 1, (u + NS - 1) % NS, pg);      // refills the slot of tile k - 1
-                wait_vmcnt_mem<(NS - 3) * GM::PER_TILE>();    // tile k + 2 has landed
-            } else {
-                mine_p = mine;
-                fetch(k + 1, (u + 1) % NS, tc);
-                finish_commit(fin, k - 1);
                 if constexpr (!SCORES) {
-                    // once per unrolled round, team 0's finisher raises both
-                    // queries' floors from the part's histogram (a snapshot
-                    // taken while other teams add to it undercounts, so the
-                    // floor stays a lower bound)
+                    // once per unrolled round, team 0's copier (which waits at
+                    // the barrier for its finisher anyway) raises both queries'
+                    // floors from the part's histogram (a snapshot taken while
+                    // the finishers add to it undercounts, so the floor stays a
+                    // lower bound)
                     if (u == U - 1 && team == 0) {
                         int b0, b1;
                         coarse_floor<true>(hist, S.topk, b0, b1);
@@ -1038,6 +1034,13 @@ __global__ __launch_bounds__(kPairThreads) void indexer_pair_kernel(IdxArgs A, R
                         lds_wait_all();                        // the floors are written
                     }
                 }
+                wait_vmcnt_mem<(NS - 3) * GM::PER_TILE>();    // tile k + 2 has landed
+
+            } else {
+                mine_p = mine;
+                fetch(k + 1, (u + 1) % NS, tc);
+                finish_commit(fin, k - 1);
+
             }
             barrier_only();
             if constexpr (FIN) {
