@@ -1266,9 +1266,29 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(SelectArgs S) {
             if (all) {
                 ordered_compact<kSelThreads>(ckey, nc, 0u, 0, &sel, EmitFinalBuf{cpos, oi, os, S.topk, {}});
             } else {
-                int ties;
-                const uint32_t T = radix_refine<kSelThreads>(ckey, nc, bin_lo, ~0u << (32 - kCoarseBits),
-                                                             m - above, 32 - kCoarseBits, &sel, ties);
+                // the remaining 21 bits in two passes of 11 and 10 bits, over
+                // the counters of the coarse histogram (free once its bin is
+                // known; fewer block-wide rounds than passes of 8 bits)
+                uint32_t T = bin_lo, tmask = ~0u << (32 - kCoarseBits);
+                int ties = m - above;
+#pragma unroll
+                for (int pass = 0; pass < 2; pass++) {
+                    const int width = pass == 0 ? 11 : 32 - kCoarseBits - 11;
+                    const int shift = pass == 0 ? 32 - kCoarseBits - 11 : 0;
+                    const uint32_t dmask = (1u << width) - 1u;
+                    for (int i = tid; i < kCoarseBins; i += kSelThreads) hist[i] = 0u;
+                    __syncthreads();
+                    for (int i = tid; i < nc; i += kSelThreads) {
+                        const uint32_t k = ckey[i];
+                        if ((k & tmask) == T) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+                    }
+                    __syncthreads();
+                    int ab, tot;
+                    const int d = coarse_select<kSelThreads>(hist, ties, &sel, ab, tot);
+                    T |= (uint32_t)d << shift;
+                    tmask |= dmask << shift;
+                    ties -= ab;
+                }
                 ordered_compact<kSelThreads>(ckey, nc, T, ties, &sel, EmitFinalBuf{cpos, oi, os, S.topk, {}});
             }
         } else {
