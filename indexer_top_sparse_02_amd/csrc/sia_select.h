@@ -3,7 +3,8 @@
 // The order is (score descending, position ascending); keys come from
 // score_key(), so "larger key" is "larger score" and equal keys are equal
 // scores. Selection runs in two steps:
-//   1. radix threshold: four 8-bit passes, most significant digit first, find the
+//   1. radix threshold: passes of up to 8 bits (four from scratch; callers that
+//      know the leading bits refine only the rest), most significant first, find the
 //      key T of the m-th element and how many elements with key == T to keep;
 //   2. ordered compaction: walk the keys in index order and emit every key > T
 //      plus the first `ties` keys == T, so the output is ascending in index and
@@ -11,7 +12,7 @@
 // Keys equal to 0 mark non-candidates; callers pass m <= number of nonzero keys,
 // which keeps T >= 1 so that 0 keys are never emitted.
 //
-// NT = 64: one wave works alone (no block barriers); NT = 256 or 512: the whole
+// NT = 64: one wave works alone (no block barriers); NT = a larger block size: the whole
 // block cooperates and every thread must call.
 #pragma once
 #include "sia_device.h"
